@@ -1,0 +1,189 @@
+"""Python binding of libbtq: one function per C entry point, same names.
+
+The functions only marshal arguments. They check tensor dtypes, shapes and
+devices, allocate outputs and workspaces with torch when the caller passes
+none, and hand raw device pointers and torch's current HIP stream to the C
+ABI. Every step of the codec runs in the library's HIP kernels; nothing
+here computes on tensor values.
+
+Layouts (contiguous, row-major, last index fastest):
+  x           int16 [P,T,H]  bf16 bit patterns (torch.bfloat16 is also accepted)
+  run_min/max float32 [P,H]
+  scale, rscale float32 [P,H];  zero_point uint8 [P,H]
+  outlier_idx int32 [k];  fmap int32 [H];  cmap int32 [H-k]
+  packed      uint8 [P,T,ceil((H-k)/2)];  outliers int16 [P,T,k]
+  y           float32 [T,H]
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+
+def _stream(dev: torch.device, stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None or t.numel() == 0 else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtypes, shape, dev) -> None:
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device != dev:
+        raise ValueError(f"{name}: on {t.device}, expected {dev}")
+
+
+_BF16 = (torch.int16, torch.bfloat16)
+
+
+def _bits(x: torch.Tensor) -> torch.Tensor:
+    return x.view(torch.int16) if x.dtype == torch.bfloat16 else x
+
+
+def _device(x: torch.Tensor) -> torch.device:
+    if x.device.type != "cuda":
+        raise ValueError("libbtq runs on the GPU: pass device tensors")
+    return x.device
+
+
+def btq_packed_row_bytes(H: int, k: int) -> int:
+    n = _lib.load().btq_packed_row_bytes(H, k)
+    if n < 0:
+        raise ValueError(f"invalid H={H}, k={k}")
+    return int(n)
+
+
+def btq_calib_workspace_bytes(P: int, T: int, H: int) -> int:
+    return int(_lib.load().btq_calib_workspace_bytes(P, T, H))
+
+
+def btq_select_workspace_bytes(P: int, H: int) -> int:
+    return int(_lib.load().btq_select_workspace_bytes(P, H))
+
+
+def btq_calib_update(x: torch.Tensor, run_min: torch.Tensor, run_max: torch.Tensor,
+                     momentum: float, first_batch: bool,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Fold one calibration batch x [P,T,H] into run_min/run_max [P,H] in place."""
+    dev = _device(x)
+    P, T, H = x.shape
+    _need(x, "x", _BF16, (P, T, H), dev)
+    _need(run_min, "run_min", (torch.float32,), (P, H), dev)
+    _need(run_max, "run_max", (torch.float32,), (P, H), dev)
+    need = btq_calib_workspace_bytes(P, T, H)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    lib = _lib.load()
+    st = lib.btq_calib_update(_ptr(_bits(x)), P, T, H, float(momentum), int(bool(first_batch)),
+                              _ptr(run_min), _ptr(run_max), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(dev, stream))
+    _lib.check(st, "btq_calib_update")
+
+
+def btq_select_outliers(run_min: torch.Tensor, run_max: torch.Tensor, k: int, out: dict = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Parameters and the BF16 feature set from the running extremes.
+
+    Returns a dict with scale, rscale, zero_point, outlier_idx, fmap, cmap.
+    """
+    dev = _device(run_min)
+    P, H = run_min.shape
+    _need(run_min, "run_min", (torch.float32,), (P, H), dev)
+    _need(run_max, "run_max", (torch.float32,), (P, H), dev)
+    if not 0 <= k <= H:
+        raise ValueError(f"k={k} outside [0, H={H}]")
+    o = dict(out or {})
+    o.setdefault("scale", torch.empty((P, H), dtype=torch.float32, device=dev))
+    o.setdefault("rscale", torch.empty((P, H), dtype=torch.float32, device=dev))
+    o.setdefault("zero_point", torch.empty((P, H), dtype=torch.uint8, device=dev))
+    o.setdefault("outlier_idx", torch.empty((k,), dtype=torch.int32, device=dev))
+    o.setdefault("fmap", torch.empty((H,), dtype=torch.int32, device=dev))
+    o.setdefault("cmap", torch.empty((H - k,), dtype=torch.int32, device=dev))
+    for name, dt, shp in (("scale", torch.float32, (P, H)), ("rscale", torch.float32, (P, H)),
+                          ("zero_point", torch.uint8, (P, H)), ("outlier_idx", torch.int32, (k,)),
+                          ("fmap", torch.int32, (H,)), ("cmap", torch.int32, (H - k,))):
+        _need(o[name], name, (dt,), shp, dev)
+    need = btq_select_workspace_bytes(P, H)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    lib = _lib.load()
+    st = lib.btq_select_outliers(_ptr(run_min), _ptr(run_max), P, H, k, _ptr(o["scale"]),
+                                 _ptr(o["rscale"]), _ptr(o["zero_point"]), _ptr(o["outlier_idx"]),
+                                 _ptr(o["fmap"]), _ptr(o["cmap"]), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(),
+                                 _stream(dev, stream))
+    _lib.check(st, "btq_select_outliers")
+    return o
+
+
+def btq_compress_pack(x: torch.Tensor, k: int, rscale: torch.Tensor, zero_point: torch.Tensor,
+                      outlier_idx: torch.Tensor, cmap: torch.Tensor,
+                      packed: Optional[torch.Tensor] = None,
+                      outliers: Optional[torch.Tensor] = None, stream=None):
+    """Sender message of every shard: (packed uint8 [P,T,Bq], outliers int16 [P,T,k])."""
+    dev = _device(x)
+    P, T, H = x.shape
+    _need(x, "x", _BF16, (P, T, H), dev)
+    Bq = btq_packed_row_bytes(H, k)
+    _need(rscale, "rscale", (torch.float32,), (P, H), dev)
+    _need(zero_point, "zero_point", (torch.uint8,), (P, H), dev)
+    _need(outlier_idx, "outlier_idx", (torch.int32,), (k,), dev)
+    _need(cmap, "cmap", (torch.int32,), (H - k,), dev)
+    if packed is None:
+        packed = torch.empty((P, T, Bq), dtype=torch.uint8, device=dev)
+    if outliers is None:
+        outliers = torch.empty((P, T, k), dtype=torch.int16, device=dev)
+    _need(packed, "packed", (torch.uint8,), (P, T, Bq), dev)
+    _need(outliers, "outliers", _BF16, (P, T, k), dev)
+    lib = _lib.load()
+    st = lib.btq_compress_pack(_ptr(_bits(x)), P, T, H, k, _ptr(rscale), _ptr(zero_point),
+                               _ptr(outlier_idx), _ptr(cmap), _ptr(packed), _ptr(_bits(outliers)),
+                               _stream(dev, stream))
+    _lib.check(st, "btq_compress_pack")
+    return packed, outliers
+
+
+def btq_decompress_reduce(packed: torch.Tensor, outliers: torch.Tensor, H: int,
+                          scale: torch.Tensor, zero_point: torch.Tensor,
+                          outlier_idx: torch.Tensor, cmap: torch.Tensor,
+                          y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Receiver: y float32 [T,H] = sum over shards of the dequantized messages."""
+    dev = _device(packed)
+    P, T, Bq = packed.shape
+    k = outliers.shape[2]
+    if Bq != btq_packed_row_bytes(H, k):
+        raise ValueError(f"packed rows of {Bq} bytes do not match H={H}, k={k}")
+    _need(packed, "packed", (torch.uint8,), (P, T, Bq), dev)
+    _need(outliers, "outliers", _BF16, (P, T, k), dev)
+    _need(scale, "scale", (torch.float32,), (P, H), dev)
+    _need(zero_point, "zero_point", (torch.uint8,), (P, H), dev)
+    _need(outlier_idx, "outlier_idx", (torch.int32,), (k,), dev)
+    _need(cmap, "cmap", (torch.int32,), (H - k,), dev)
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _need(y, "y", (torch.float32,), (T, H), dev)
+    lib = _lib.load()
+    st = lib.btq_decompress_reduce(_ptr(packed), _ptr(_bits(outliers)), P, T, H, k, _ptr(scale),
+                                   _ptr(zero_point), _ptr(outlier_idx), _ptr(cmap), _ptr(y),
+                                   _stream(dev, stream))
+    _lib.check(st, "btq_decompress_reduce")
+    return y
+
+
+def btq_status_str(status: int) -> str:
+    return _lib.load().btq_status_str(status).decode()
+
+
+def btq_version() -> str:
+    return _lib.load().btq_version().decode()

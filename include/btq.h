@@ -1,0 +1,178 @@
+/*
+ * btq.h -- C ABI of libbtq, the hybrid int4/BF16 codec for tensor-parallel
+ * partial sums on AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: the page "Revolutionizing LLM Inference: The Power of
+ * Efficient Low-Bit Communication" (aiexpert.world), a summary of the paper
+ * "Towards Efficient Low-Bit Communication for Tensor Parallel LLM Inference".
+ * Its section "The Hybrid Quantization Algorithm" gives three steps:
+ *   Calibration  -- per-feature parameters from moving averages of the
+ *                   minimum and maximum observed on each device;
+ *   Selection    -- rank features by quantization range and keep a number
+ *                   of them in BF16;
+ *   Inference    -- the selected features stay BF16 and the others are sent
+ *                   as 4-bit integers; after communication everything is
+ *                   converted back and summed across devices.
+ * Section "Combating Quantization Errors with Tensor Parallelism" places the
+ * quantization on each device's partial sum, before the sum.
+ *
+ * One call per step. Here all P shards' partial sums sit in one GPU's HBM,
+ * so the exchange between devices is the identity: the buffers written by
+ * btq_compress_pack are the ones read by btq_decompress_reduce.
+ *
+ * Conventions shared by every call
+ *  - Tensor pointers are DEVICE pointers (hipMalloc'd or from PyTorch) to
+ *    caller-owned, contiguous, row-major memory with the last index fastest.
+ *    The library never allocates, frees or keeps them.
+ *  - bf16 values are raw 16-bit patterns (uint16_t).
+ *  - A pointer must be aligned to its element type. Faster paths are taken
+ *    when x/packed/outliers/y are 16-byte aligned and H, H-k are multiples
+ *    of 8; every other layout runs on a slower general path.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call checks its arguments on the host, enqueues its kernels on
+ *    `stream` and returns. It does not synchronize, print, throw or abort.
+ *    The library holds no mutable global state, so calls on different
+ *    streams may run concurrently as long as their buffers do not overlap.
+ *  - Return value: BTQ_OK (0) or a negative btq_status. On an argument or
+ *    shape error nothing is enqueued and no HIP call is made. A fault while
+ *    the kernels run surfaces at the caller's next synchronization.
+ *  - Sizes: 1 <= P <= 65535, 1 <= H <= 2^30, 0 <= k <= H, T >= 0, and
+ *    P*T*H < 2^62. T == 0 is an empty batch: compress and decompress do
+ *    nothing, and calibration rejects it (its min/max would be undefined).
+ *  - Floating point: every fp32 step is one IEEE round-to-nearest-even
+ *    operation. Divisions are correctly rounded. Nothing is flushed to zero.
+ *    Inputs must be finite; NaN and Inf give unspecified (but in-bounds)
+ *    results.
+ */
+#ifndef BTQ_H
+#define BTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BTQ_OK = 0,
+  BTQ_ERR_ARG = -1,        /* null pointer, or momentum outside [0,1] / NaN    */
+  BTQ_ERR_SHAPE = -2,      /* P, T, H or k out of range                         */
+  BTQ_ERR_ALIGN = -3,      /* pointer not aligned to its element type           */
+  BTQ_ERR_WORKSPACE = -4,  /* workspace smaller than the *_workspace_bytes size */
+  BTQ_ERR_HIP = -5         /* a kernel launch failed (hipGetLastError, cleared)  */
+} btq_status;
+
+/*
+ * Calibration -- "The Hybrid Quantization Algorithm", Calibration bullet.
+ *
+ * For every shard p and feature h, takes the batch minimum and maximum over
+ * the T tokens of x[p,:,h]. Then it updates the running extremes:
+ *   first_batch != 0 : run = batch value
+ *   otherwise        : run = fl(fl(a*run) + fl(c*batch)),  a = momentum,
+ *                      c = fl(1 - a), all fp32 (moving average; the page
+ *                      gives no formula -- the momentum weights the old value)
+ *   x        bf16 [P,T,H]   in
+ *   run_min  fp32 [P,H]     in/out (ignored on input when first_batch != 0)
+ *   run_max  fp32 [P,H]     in/out
+ *   workspace  device scratch of at least btq_calib_workspace_bytes(P,T,H)
+ *              bytes (may be NULL if that size is 0); its contents are
+ *              overwritten and need no initial value.
+ * Batch extremes are exact, and -0 and +0 count as equal. The result does
+ * not depend on how the kernels split the token axis.
+ */
+int btq_calib_update(const uint16_t *x, int64_t P, int64_t T, int64_t H,
+                     float momentum, int first_batch,
+                     float *run_min, float *run_max,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+size_t btq_calib_workspace_bytes(int64_t P, int64_t T, int64_t H);
+
+/*
+ * Selection -- "The Hybrid Quantization Algorithm", Calibration bullet
+ * (per-feature parameters) and Selection bullet (rank by range, keep k).
+ *
+ * Per (p,h):  lo = min(run_min,0), hi = max(run_max,0), width = hi - lo,
+ *             scale = width/15 (1 if below 2^-126), rscale = 1/scale,
+ *             zero_point = clamp(rint_half_even(-lo/scale), 0, 15).
+ * Per h:      score = width[0,h] + width[1,h] + ... (fp32, p ascending).
+ * The k features with the highest score are kept in BF16 (ties: lower h
+ * first). They are shared by all shards, because the receiver must know
+ * every sender's layout.
+ *   run_min, run_max  fp32 [P,H]  in
+ *   scale, rscale     fp32 [P,H]  out
+ *   zero_point        u8   [P,H]  out, values 0..15
+ *   outlier_idx       i32  [k]    out, the BF16 features in ascending h
+ *   fmap              i32  [H]    out, fmap[h] = j (the int4 slot of h), or
+ *                                 -1-i when h = outlier_idx[i]
+ *   cmap              i32  [H-k]  out, cmap[j] = h of int4 slot j (ascending)
+ *   workspace  at least btq_select_workspace_bytes(P,H) bytes of scratch.
+ * Pointers for zero-length outputs (k == 0, or k == H for cmap) may be NULL.
+ */
+int btq_select_outliers(const float *run_min, const float *run_max,
+                        int64_t P, int64_t H, int64_t k,
+                        float *scale, float *rscale, uint8_t *zero_point,
+                        int32_t *outlier_idx, int32_t *fmap, int32_t *cmap,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+size_t btq_select_workspace_bytes(int64_t P, int64_t H);
+
+/*
+ * Sender side of inference -- "The Hybrid Quantization Algorithm", Inference
+ * bullet; quantization before the sum per "Combating Quantization Errors
+ * with Tensor Parallelism".
+ *
+ * For each token row (p,t), the int4 slots j = 0..H-k-1 take feature
+ * h = cmap[j]:  q = clamp(rint_half_even(fl(x*rscale[p,h])) + zero_point[p,h], 0, 15)
+ * and are packed two per byte: slot 2b in the low nibble of byte b, slot
+ * 2b+1 in the high nibble. An odd H-k leaves the last high nibble 0. The BF16
+ * features are copied bit for bit: outliers[p,t,i] = x[p,t,outlier_idx[i]].
+ *   x          bf16 [P,T,H]                       in
+ *   rscale     fp32 [P,H], zero_point u8 [P,H]    in (from btq_select_outliers)
+ *   outlier_idx i32 [k], cmap i32 [H-k]           in (from btq_select_outliers)
+ *   packed     u8   [P,T,btq_packed_row_bytes(H,k)]  out (rows are unpadded)
+ *   outliers   bf16 [P,T,k]                       out
+ * The maps are trusted: outlier_idx and cmap must partition 0..H-1, each in
+ * ascending order, as btq_select_outliers writes them.
+ */
+int btq_compress_pack(const uint16_t *x, int64_t P, int64_t T, int64_t H, int64_t k,
+                      const float *rscale, const uint8_t *zero_point,
+                      const int32_t *outlier_idx, const int32_t *cmap,
+                      uint8_t *packed, uint16_t *outliers, void *stream);
+
+/*
+ * Receiver side of inference -- "The Hybrid Quantization Algorithm",
+ * Inference bullet (convert back, sum across devices).
+ *
+ * y[t,h] = sum over p = 0..P-1 of term_p, in fp32, where
+ *   int4 feature h = cmap[j]:       term_p = (q_p - zero_point[p,h]) * scale[p,h]
+ *                                   (q_p = nibble j of packed row (p,t))
+ *   BF16 feature h = outlier_idx[i]: term_p = the bf16 value outliers[p,t,i]
+ * BF16 features are summed in p order starting from 0, so they match a
+ * sequential fp32 sum bit for bit. int4 features may be evaluated as
+ * fma(q_p, scale, acc) plus a per-feature constant -sum_p zero_point*scale,
+ * which stays within 1e-3*|y| + 1e-2*max_p scale[p,h] of the sequential sum.
+ *   packed, outliers  as written by btq_compress_pack (P shards)  in
+ *   scale fp32 [P,H], zero_point u8 [P,H], outlier_idx [k], cmap [H-k]  in
+ *   y    fp32 [T,H]  out
+ */
+int btq_decompress_reduce(const uint8_t *packed, const uint16_t *outliers,
+                          int64_t P, int64_t T, int64_t H, int64_t k,
+                          const float *scale, const uint8_t *zero_point,
+                          const int32_t *outlier_idx, const int32_t *cmap,
+                          float *y, void *stream);
+
+/* Bytes per packed row: ceil((H-k)/2); -1 if H < 1 or k is outside [0,H]. */
+int64_t btq_packed_row_bytes(int64_t H, int64_t k);
+
+/* Static text for a btq_status value (never NULL). */
+const char *btq_status_str(int status);
+
+/* Library version, "major.minor.patch". */
+const char *btq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BTQ_H */

@@ -1,0 +1,96 @@
+"""Shared drivers for the GPU-vs-oracle parity tests.
+
+Both sides always see one tensor: the inputs are drawn on the GPU by
+`workloads`, the HIP path reads them in place, and the oracle reads a host
+copy. No oracle input or expected value comes from the HIP path.
+"""
+from __future__ import annotations
+
+import os
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+from oracle import oracle as O
+import workloads as W
+
+# Reduced-output tolerance: |y_gpu - y_oracle| <= 1e-3*|y_oracle| + 1e-2*max_p scale[p,h]
+TOL_REL = 1e-3
+TOL_ABS_SCALE = 1e-2
+
+POOL = ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    return W.to_u16(t)
+
+
+def oracle_calib(x: np.ndarray, mn, mx, momentum: float, first: bool):
+    """Oracle calibration step, one shard per thread (shards are independent)."""
+    P = x.shape[0]
+
+    def one(p):
+        return O.calib_update(x[p:p + 1], None if first else mn[p:p + 1],
+                              None if first else mx[p:p + 1], momentum, first)
+
+    res = list(POOL.map(one, range(P)))
+    return (np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res]))
+
+
+def oracle_compress_rows(x: np.ndarray, sel: dict, rows=None):
+    """Oracle message for token rows `rows` (all if None), shard-parallel."""
+    if rows is not None:
+        x = x[:, rows, :]
+    P = x.shape[0]
+
+    def one(p):
+        return O.compress_pack(x[p:p + 1], sel["rscale"][p:p + 1], sel["zero_point"][p:p + 1],
+                               sel["idx"], sel["cmap"])
+
+    res = list(POOL.map(one, range(P)))
+    return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
+
+
+def assert_stats_equal(gpu: torch.Tensor, orc: np.ndarray, name: str) -> None:
+    g = gpu.cpu().numpy()
+    bad = g != orc          # by value: -0 == +0
+    assert not bad.any(), f"{name}: {int(bad.sum())} of {bad.size} differ, first at {np.argwhere(bad)[0]}"
+
+
+def assert_bits_equal(gpu: torch.Tensor, orc: np.ndarray, name: str) -> None:
+    g = gpu.cpu().contiguous().numpy()
+    o = np.ascontiguousarray(orc)
+    assert g.shape == o.shape, f"{name}: shape {g.shape} vs {o.shape}"
+    gb = g.view(np.uint8).reshape(-1)
+    ob = o.view(np.uint8).reshape(-1)
+    if gb.size != ob.size or not np.array_equal(gb, ob):
+        first = np.argmax(gb != ob) if gb.size == ob.size else -1
+        raise AssertionError(f"{name}: bytes differ (first differing byte {first})")
+
+
+def assert_selection_equal(sel_gpu: dict, sel_orc: dict) -> None:
+    assert_bits_equal(sel_gpu["scale"], sel_orc["scale"], "scale")
+    assert_bits_equal(sel_gpu["rscale"], sel_orc["rscale"], "rscale")
+    assert_bits_equal(sel_gpu["zero_point"], sel_orc["zero_point"], "zero_point")
+    assert_bits_equal(sel_gpu["outlier_idx"], sel_orc["idx"].astype(np.int32), "outlier_idx")
+    assert_bits_equal(sel_gpu["fmap"], sel_orc["fmap"].astype(np.int32), "fmap")
+    assert_bits_equal(sel_gpu["cmap"], sel_orc["cmap"].astype(np.int32), "cmap")
+
+
+def assert_y_close(y_gpu: np.ndarray, y_orc: np.ndarray, scale: np.ndarray, idx) -> None:
+    tol = TOL_REL * np.abs(y_orc) + TOL_ABS_SCALE * scale.max(0)[None, :]
+    err = np.abs(y_gpu.astype(np.float64) - y_orc.astype(np.float64))
+    bad = ~(err <= tol)
+    assert not bad.any(), (f"y: {int(bad.sum())} outside tolerance; worst excess "
+                           f"{float(np.max(err - tol))} at {np.argwhere(bad)[0]}")
+    idx = np.asarray(idx, np.int64)
+    if idx.size:   # BF16 features are summed in the oracle's order: exact
+        assert np.array_equal(y_gpu[:, idx].view(np.uint32), y_orc[:, idx].view(np.uint32)), \
+            "y: BF16 feature columns not bit-exact"

@@ -1,0 +1,143 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+that include/btq.h declares, and rejects bad arguments before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_tensor_activation_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "btq.h")
+
+OK, ARG, SHAPE, ALIGN, WS = (_lib.BTQ_OK, _lib.BTQ_ERR_ARG, _lib.BTQ_ERR_SHAPE,
+                             _lib.BTQ_ERR_ALIGN, _lib.BTQ_ERR_WORKSPACE)
+# Fake, never dereferenced "device" addresses: every call below returns from
+# host-side validation before it touches the HIP runtime.
+A = 0x10000          # 64 KiB aligned
+BIG = 1 << 40
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(btq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 9
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+
+
+def test_status_strings_and_version(lib):
+    for s in (OK, ARG, SHAPE, ALIGN, WS, _lib.BTQ_ERR_HIP, 17):
+        assert lib.btq_status_str(s)
+    assert re.fullmatch(rb"\d+\.\d+\.\d+", lib.btq_version())
+
+
+def test_size_helpers(lib):
+    assert lib.btq_packed_row_bytes(4096, 64) == 2016
+    assert lib.btq_packed_row_bytes(5, 2) == 2
+    assert lib.btq_packed_row_bytes(8, 8) == 0
+    assert lib.btq_packed_row_bytes(8, 9) == -1
+    assert lib.btq_packed_row_bytes(0, 0) == -1
+    assert lib.btq_select_workspace_bytes(8, 4096) == 4096 * 4
+    assert lib.btq_select_workspace_bytes(0, 4096) == 0
+    n = lib.btq_calib_workspace_bytes(8, 2048, 4096)
+    assert n > 0 and n % (2 * 8 * 4096 * 4) == 0
+    assert lib.btq_calib_workspace_bytes(8, 0, 4096) == 0
+
+
+def calib(lib, x=A, P=2, T=4, H=16, m=0.9, rmin=A, rmax=A, ws=A, wsb=BIG):
+    return lib.btq_calib_update(x, P, T, H, m, 0, rmin, rmax, ws, wsb, None)
+
+
+def test_calib_validation(lib):
+    assert calib(lib, P=0) == SHAPE
+    assert calib(lib, T=0) == SHAPE
+    assert calib(lib, H=0) == SHAPE
+    assert calib(lib, P=70000) == SHAPE
+    assert calib(lib, H=(1 << 30) + 1) == SHAPE
+    assert calib(lib, P=65535, T=1 << 40, H=1 << 20) == SHAPE     # P*T*H overflow
+    assert calib(lib, x=None) == ARG
+    assert calib(lib, rmin=None) == ARG
+    assert calib(lib, m=-0.1) == ARG
+    assert calib(lib, m=1.5) == ARG
+    assert calib(lib, m=float("nan")) == ARG
+    assert calib(lib, x=A + 1) == ALIGN
+    assert calib(lib, rmax=A + 2) == ALIGN
+    assert calib(lib, ws=None) == ARG
+    assert calib(lib, wsb=8) == WS
+    assert calib(lib, ws=A + 2) == ALIGN
+
+
+def select(lib, rmin=A, rmax=A, P=2, H=16, k=4, sc=A, rs=A, zp=A, idx=A, fmap=A, cmap=A, ws=A,
+           wsb=BIG):
+    return lib.btq_select_outliers(rmin, rmax, P, H, k, sc, rs, zp, idx, fmap, cmap, ws, wsb, None)
+
+
+def test_select_validation(lib):
+    assert select(lib, k=-1) == SHAPE
+    assert select(lib, k=17) == SHAPE
+    assert select(lib, P=0) == SHAPE
+    assert select(lib, sc=None) == ARG
+    assert select(lib, fmap=None) == ARG
+    assert select(lib, idx=None) == ARG
+    assert select(lib, cmap=None) == ARG
+    assert select(lib, ws=None) == ARG
+    assert select(lib, wsb=4) == WS
+    assert select(lib, sc=A + 1) == ALIGN
+    assert select(lib, cmap=A + 2) == ALIGN
+    # zero-length outputs may be NULL; these pass validation, so they are not
+    # called here (they would launch).
+
+
+def compress(lib, x=A, P=2, T=4, H=16, k=4, rs=A, zp=A, idx=A, cmap=A, pk=A, ol=A):
+    return lib.btq_compress_pack(x, P, T, H, k, rs, zp, idx, cmap, pk, ol, None)
+
+
+def test_compress_validation(lib):
+    assert compress(lib, k=17) == SHAPE
+    assert compress(lib, T=-1) == SHAPE
+    assert compress(lib, P=0) == SHAPE
+    assert compress(lib, rs=None) == ARG
+    assert compress(lib, idx=None) == ARG
+    assert compress(lib, cmap=None) == ARG
+    assert compress(lib, x=None) == ARG
+    assert compress(lib, pk=None) == ARG
+    assert compress(lib, ol=None) == ARG
+    assert compress(lib, x=A + 1) == ALIGN
+    assert compress(lib, rs=A + 2) == ALIGN
+    assert compress(lib, ol=A + 1) == ALIGN
+    # T == 0 is an empty batch: valid, nothing enqueued
+    assert compress(lib, T=0, x=None, pk=None, ol=None) == OK
+    # zero-length maps may be NULL
+    assert compress(lib, T=0, k=0, idx=None) == OK
+    assert compress(lib, T=0, k=16, cmap=None) == OK
+
+
+def decompress(lib, pk=A, ol=A, P=2, T=4, H=16, k=4, sc=A, zp=A, idx=A, cmap=A, y=A):
+    return lib.btq_decompress_reduce(pk, ol, P, T, H, k, sc, zp, idx, cmap, y, None)
+
+
+def test_decompress_validation(lib):
+    assert decompress(lib, k=17) == SHAPE
+    assert decompress(lib, P=0) == SHAPE
+    assert decompress(lib, H=0) == SHAPE
+    assert decompress(lib, sc=None) == ARG
+    assert decompress(lib, y=None) == ARG
+    assert decompress(lib, pk=None) == ARG
+    assert decompress(lib, ol=None) == ARG
+    assert decompress(lib, y=A + 2) == ALIGN
+    assert decompress(lib, sc=A + 1) == ALIGN
+    assert decompress(lib, T=0, y=None, pk=None, ol=None) == OK

@@ -1,0 +1,155 @@
+"""GPU parity: every HIP step against the CPU oracle, element by element.
+
+Bar: calibration statistics equal by value; parameters, outlier set, maps,
+packed codes and BF16 blocks bitwise; reduced output within
+1e-3*|y| + 1e-2*max_p scale (BF16 feature columns bit-exact).
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_tensor_activation_amd as B
+from oracle import oracle as O
+import workloads as W
+from helpers import (assert_bits_equal, assert_selection_equal, assert_stats_equal, assert_y_close,
+                     oracle_calib, oracle_compress_rows, say, u16)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def run_both(calib_xs, x, k, momentum, *, x_offset=0):
+    """Calibrate, select, compress and decompress on both sides; compare all."""
+    P, T, H = x.shape
+    rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
+    rmax = torch.empty_like(rmin)
+    mn = mx = None
+    for b, xb in enumerate(calib_xs):
+        B.btq_calib_update(xb, rmin, rmax, momentum, first_batch=(b == 0))
+        mn, mx = oracle_calib(u16(xb), mn, mx, momentum, first=(b == 0))
+    torch.cuda.synchronize()
+    assert_stats_equal(rmin, mn, "run_min")
+    assert_stats_equal(rmax, mx, "run_max")
+
+    sel_g = B.btq_select_outliers(rmin, rmax, k)
+    sel_o = O.select_outliers(mn, mx, k)
+    torch.cuda.synchronize()
+    assert_selection_equal(sel_g, sel_o)
+
+    if x_offset:   # misaligned base pointer: same values, shifted storage
+        big = torch.empty(x.numel() + x_offset, dtype=torch.int16, device=DEV)
+        big[x_offset:] = x.reshape(-1)
+        x = big[x_offset:].view(P, T, H)
+    pk, ol = B.btq_compress_pack(x, k, sel_g["rscale"], sel_g["zero_point"],
+                                 sel_g["outlier_idx"], sel_g["cmap"])
+    pk_o, ol_o = oracle_compress_rows(u16(x), sel_o)
+    torch.cuda.synchronize()
+    assert_bits_equal(pk, pk_o, "packed")
+    assert_bits_equal(ol.view(torch.int16), ol_o.view(np.int16), "outliers")
+
+    y = B.btq_decompress_reduce(pk, ol, H, sel_g["scale"], sel_g["zero_point"],
+                                sel_g["outlier_idx"], sel_g["cmap"])
+    y_o = O.decompress_reduce(pk_o, ol_o, sel_o["scale"], sel_o["zero_point"], sel_o["fmap"])
+    torch.cuda.synchronize()
+    assert_y_close(y.cpu().numpy(), y_o, sel_o["scale"], sel_o["idx"])
+    return sel_g, pk, ol, y
+
+
+def test_tiny_workload_end_to_end():
+    w = W.WORKLOADS["tiny"]
+    say("case: tiny workload")
+    calib = [W.batch(w, W.PHASE_CALIB, b, device=DEV) for b in range(w.calib_batches)]
+    x = W.batch(w, W.PHASE_INFER, 0, device=DEV)
+    sel, *_ = run_both(calib, x, w.k, w.momentum)
+    planted = set(W.outlier_columns(w).tolist())
+    assert planted <= set(sel["outlier_idx"].cpu().tolist())
+
+
+# (P, T, H, k, base, outlier columns, note)
+CASES = [
+    (2, 16, 256, 8, "normal", [3, 77, 128, 200], "tiny shape"),
+    (8, 70, 2048, 64, "normal", list(range(5, 2048, 41)), "fast path, 4 tiles, ragged T"),
+    (4, 3, 4104, 8, "laplace", [0, 1, 2, 4103], "H=4104, outliers at both ends"),
+    (3, 33, 1032, 8, "normal", [10, 500, 1031], "P=3"),
+    (5, 9, 1024, 16, "laplace", [7, 8, 9, 10], "P=5"),
+    (6, 12, 520, 8, "normal", [519], "P=6, partial last tile"),
+    (7, 5, 1040, 0, "normal", [], "P=7, k=0"),
+    (1, 40, 512, 0, "normal", [], "P=1, k=0, one full tile"),
+    (2, 9, 256, 256, "normal", [1, 2], "k=H: all BF16"),
+    (9, 17, 512, 16, "laplace", [100, 101], "P=9: general receiver"),
+    (3, 5, 250, 7, "normal", [0, 249, 100], "H not a multiple of 8"),
+    (5, 33, 1032, 13, "normal", [1, 2, 3], "H-k odd: pad nibble, general sender"),
+    (2, 8, 1024, 200, "normal", list(range(100, 300)), "200 clustered BF16 features in one tile"),
+    (4, 6, 2048, 600, "laplace", list(range(0, 2048, 3))[:600], "k=600: wide LDS span"),
+    (1, 1, 8, 3, "normal", [1], "smallest: P=1, T=1, H=8"),
+    (8, 1, 8192, 64, "normal", list(range(3, 8192, 200)), "decode-like T=1"),
+]
+
+
+@pytest.mark.parametrize("P,T,H,k,base,cols,note", CASES, ids=[c[-1] for c in CASES])
+def test_shapes(P, T, H, k, base, cols, note):
+    say(f"case: P={P} T={T} H={H} k={k} ({note})")
+    calib = [W.draw(P, max(T, 4), H, 1000 + b, base=base, cols=cols, outlier_factor=40.0,
+                    device=DEV) for b in range(3)]
+    x = W.draw(P, T, H, 2000, base=base, cols=cols, outlier_factor=40.0, device=DEV)
+    run_both(calib, x, k, 0.9)
+
+
+def test_misaligned_input_pointer():
+    say("case: x base pointer offset by one element")
+    P, T, H, k = 4, 10, 1024, 16
+    calib = [W.draw(P, T, H, 3000 + b, device=DEV) for b in range(2)]
+    x = W.draw(P, T, H, 3100, device=DEV)
+    run_both(calib, x, k, 0.95, x_offset=1)
+
+
+def test_momentum_extremes():
+    say("case: momentum 0 and 1")
+    P, T, H = 2, 8, 64
+    xs = [W.draw(P, T, H, 4000 + b, device=DEV) for b in range(3)]
+    for m in (0.0, 1.0):
+        run_both(xs, xs[-1], 4, m)
+
+
+def test_empty_batch_leaves_outputs_untouched():
+    say("case: T=0")
+    P, H, k = 3, 256, 8
+    xs = [W.draw(P, 4, H, 5000, device=DEV)]
+    rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
+    rmax = torch.empty_like(rmin)
+    B.btq_calib_update(xs[0], rmin, rmax, 0.9, True)
+    sel = B.btq_select_outliers(rmin, rmax, k)
+    x0 = torch.empty((P, 0, H), dtype=torch.int16, device=DEV)
+    pk, ol = B.btq_compress_pack(x0, k, sel["rscale"], sel["zero_point"], sel["outlier_idx"],
+                                 sel["cmap"])
+    assert pk.shape == (P, 0, (H - k + 1) // 2) and ol.shape == (P, 0, k)
+    y = B.btq_decompress_reduce(pk, ol, H, sel["scale"], sel["zero_point"], sel["outlier_idx"],
+                                sel["cmap"])
+    torch.cuda.synchronize()
+    assert y.shape == (0, H)
+
+
+def test_repeatable_bitwise():
+    say("case: repeat runs give identical bytes")
+    w = W.WORKLOADS["tiny"]
+    P, T, H, k = 8, 64, 4096, 64
+    cols = W.outlier_columns(W.WORKLOADS["7b_prefill"])
+    calib = [W.draw(P, T, H, 6000 + b, sigma=0.5, cols=cols, outlier_factor=100.0, device=DEV)
+             for b in range(2)]
+    x = W.draw(P, T, H, 6100, sigma=0.5, cols=cols, outlier_factor=100.0, device=DEV)
+    outs = []
+    for _ in range(2):
+        rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
+        rmax = torch.empty_like(rmin)
+        for b, xb in enumerate(calib):
+            B.btq_calib_update(xb, rmin, rmax, 0.9, b == 0)
+        sel = B.btq_select_outliers(rmin, rmax, k)
+        pk, ol = B.btq_compress_pack(x, k, sel["rscale"], sel["zero_point"], sel["outlier_idx"],
+                                     sel["cmap"])
+        y = B.btq_decompress_reduce(pk, ol, H, sel["scale"], sel["zero_point"],
+                                    sel["outlier_idx"], sel["cmap"])
+        torch.cuda.synchronize()
+        outs.append([t.cpu().clone() for t in (rmin, rmax, sel["scale"], sel["cmap"], pk, ol, y)])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
+                           b.view(torch.uint8) if b.dtype != torch.uint8 else b)
