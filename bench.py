@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Throughput of the hybrid int4/BF16 partial-sum codec on one MI355X.
+
+One step = one pass of the per-batch hot path over one inference batch:
+btq_compress_pack (every shard's sender message) and then
+btq_decompress_reduce (the receiver's fused dequantize and fp32 sum over
+P shards). Calibration and selection run once before the timed region, as
+the method prescribes: they are computed offline on calibration batches.
+They are timed separately and reported under "offline".
+
+Metric: bf16-equivalent GB/s = steps * P*T*H*2 bytes / wall time of the
+timed steps. Inputs are resident in HBM before timing starts. R copies of the
+batch and of every output rotate, so that each step streams from HBM and not
+from the 256 MB last-level cache. The receiver reads the message written two
+steps earlier.
+
+Roofline: the dominant kernel (compress) is HBM-bound. achieved = its
+algorithmic bytes per launch / its mean duration from HIP events recorded on
+the launch stream. traffic = HBM bytes per launch from rocprofv3 counters
+(profiles/), reported only while the kernel source still matches the hash
+those counters were taken at.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 7b_prefill]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
+METRIC = "GB/s (bf16-equiv) of compress+decompress_reduce; % of HBM peak"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["bit_tensor_activation_amd/csrc/compress.hip",
+                  "bit_tensor_activation_amd/csrc/common.hpp"]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per compress launch from the committed counter summary."""
+    path = os.path.join(PROFILES, f"compress_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("source_hash") != source_hash(KERNEL_SOURCES):
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def algorithmic_bytes(P, T, H, k):
+    """Bytes the method must move per launch (inputs once, outputs once)."""
+    Bq = (H - k + 1) // 2
+    params = P * H * 5 + 4 * H               # scale or rscale (4 B) + zero point (1 B); maps
+    message = P * T * (Bq + 2 * k)
+    compress = P * T * H * 2 + message + params
+    decompress = message + T * H * 4 + params
+    return compress, decompress
+
+
+def cpu_baseline(w, T_sample: int, min_seconds: float):
+    """The oracle, as it is, on a bounded sample of the same workload."""
+    import numpy as np
+    import workloads as W
+    from oracle import oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except Exception:   # numpy's elementwise ops are single-threaded anyway
+        limiter = None
+    x = W.to_u16(W.batch(w, W.PHASE_INFER, 0, T=T_sample, device="cpu"))
+    mn, mx = O.batch_min_max(x)
+    sel = O.select_outliers(mn, mx, w.k)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        pk, ol = O.compress_pack(x, sel["rscale"], sel["zero_point"], sel["idx"], sel["cmap"])
+        O.decompress_reduce(pk, ol, sel["scale"], sel["zero_point"], sel["fmap"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    if limiter is not None:
+        limiter.unregister()
+    gbps = reps * x.nbytes / el / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{w.name}: P={w.P} x T={T_sample} of {w.T[0]} tokens x H={w.H}, k={w.k}; "
+                       f"numpy oracle compress_pack + decompress_reduce, {reps} reps in "
+                       f"{el:.1f} s, one thread; parameters from the sample's own min/max")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="7b_prefill")
+    ap.add_argument("--T", type=int, default=None, help="token count (decode sweep)")
+    ap.add_argument("--k", type=int, default=None, help="BF16 feature count (stress sweep)")
+    ap.add_argument("--rotate-mib", type=int, default=1024,
+                    help="minimum MiB streamed between reuses of one buffer set")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-sample-T", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the P shards of one tensor-parallel group share one GPU's HBM). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import bit_tensor_activation_amd as B
+    from bit_tensor_activation_amd import _lib
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    w = W.WORKLOADS[args.workload]
+    T = args.T if args.T is not None else w.T[0]
+    k = args.k if args.k is not None else w.k
+    P, H = w.P, w.H
+    lib = _lib.load()
+    stream = torch.cuda.current_stream(dev)
+    sh = int(stream.cuda_stream)
+
+    # ---- offline: calibration over the calibration set, then selection ----
+    log(f"workload {w.name}: P={P} T={T} H={H} k={k}; calibrating on {w.calib_batches} batches")
+    rmin = torch.empty((P, H), dtype=torch.float32, device=dev)
+    rmax = torch.empty_like(rmin)
+    ws = torch.empty(max(B.btq_calib_workspace_bytes(P, w.calib_T, H), 1), dtype=torch.uint8,
+                     device=dev)
+    calib_ms = 0.0
+    for b in range(w.calib_batches):
+        xb = W.batch(w, W.PHASE_CALIB, b, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        B.btq_calib_update(xb, rmin, rmax, w.momentum, b == 0, workspace=ws)
+        e1.record(stream)
+        e1.synchronize()
+        calib_ms += e0.elapsed_time(e1)
+        del xb
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    B.btq_select_outliers(rmin, rmax, k)     # warm
+    e0.record(stream)
+    sel = B.btq_select_outliers(rmin, rmax, k)
+    e1.record(stream)
+    e1.synchronize()
+    select_ms = e0.elapsed_time(e1)
+
+    # ---- resident inputs and rotated buffer sets ----
+    x0 = W.batch(w, W.PHASE_INFER, 0, T=T, device=dev)
+    Bq = B.btq_packed_row_bytes(H, k)
+    set_bytes = P * T * H * 2 + P * T * (Bq + 2 * k) + T * H * 4
+    R = max(3, -(-args.rotate_mib * 2 ** 20 // set_bytes) + 1)
+    xs = [x0.clone() for _ in range(R)]
+    pks = [torch.empty((P, T, Bq), dtype=torch.uint8, device=dev) for _ in range(R)]
+    ols = [torch.empty((P, T, k), dtype=torch.int16, device=dev) for _ in range(R)]
+    ys = [torch.empty((T, H), dtype=torch.float32, device=dev) for _ in range(R)]
+    del x0
+    p = lambda t: t.data_ptr() if t.numel() else None
+    rs, zp, oi, cm, sc = (p(sel["rscale"]), p(sel["zero_point"]), p(sel["outlier_idx"]),
+                          p(sel["cmap"]), p(sel["scale"]))
+    comp_args = [(p(xs[r]), P, T, H, k, rs, zp, oi, cm, p(pks[r]), p(ols[r]), sh) for r in range(R)]
+    deco_args = [(p(pks[(r - 2) % R]), p(ols[(r - 2) % R]), P, T, H, k, sc, zp, oi, cm, p(ys[r]), sh)
+                 for r in range(R)]
+    compress, decompress = lib.btq_compress_pack, lib.btq_decompress_reduce
+    # first fill every message buffer once, so the receiver always reads a real message
+    for r in range(R):
+        _lib.check(compress(*comp_args[r]), "btq_compress_pack")
+    torch.cuda.synchronize()
+    log(f"{R} rotating buffer sets of {set_bytes / 2**20:.1f} MiB; warmup {args.warmup}, "
+        f"steps {args.steps}")
+
+    def step(i, ev=None):
+        r = i % R
+        if ev is not None:
+            ev[0].record(stream)
+        st = compress(*comp_args[r])
+        if ev is not None:
+            ev[1].record(stream)
+        st |= decompress(*deco_args[r])
+        if ev is not None:
+            ev[2].record(stream)
+        return st
+
+    st = 0
+    for i in range(args.warmup):
+        st |= step(i)
+    torch.cuda.synchronize()
+    _lib.check(st, "warmup")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        st |= step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    _lib.check(st, "timed steps")
+    comp_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    deco_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    comp_mean = sum(comp_ms) / len(comp_ms)
+    deco_mean = sum(deco_ms) / len(deco_ms)
+    med = lambda v: sorted(v)[len(v) // 2]
+
+    copy_probe = None
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * 2 ** 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(5):
+            dst.copy_(src)
+        c1.record(stream)
+        c1.synchronize()
+        copy_probe = {"bytes_per_copy": 2 * n, "GBps": round(5 * 2 * n / (c0.elapsed_time(c1) * 1e-3) / 1e9, 1)}
+        del src, dst
+
+    bf16_bytes = P * T * H * 2
+    comp_bytes, deco_bytes = algorithmic_bytes(P, T, H, k)
+    value = args.steps * bf16_bytes / wall / 1e9
+    achieved = comp_bytes / (comp_mean * 1e-3) / 1e9
+    traffic = read_traffic(w.name) if (T == w.T[0] and k == w.k) else None
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "P": P, "T": T, "H": H, "k": k,
+                   "input": "bf16 partial sums", "message": "int4 packed + bf16 outlier block",
+                   "output": "fp32", "rotating_sets": R},
+        "roofline": {"bound": "hbm", "kernel": "compress_pack", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": comp_bytes},
+        "kernels": {
+            "compress_pack": {"mean_us": round(comp_mean * 1e3, 2), "median_us": round(med(comp_ms) * 1e3, 2),
+                              "algorithmic_bytes": comp_bytes,
+                              "hbm_GBps": round(comp_bytes / (comp_mean * 1e-3) / 1e9, 1),
+                              "bf16_equiv_GBps": round(bf16_bytes / (comp_mean * 1e-3) / 1e9, 1)},
+            "decompress_reduce": {"mean_us": round(deco_mean * 1e3, 2), "median_us": round(med(deco_ms) * 1e3, 2),
+                                  "algorithmic_bytes": deco_bytes,
+                                  "hbm_GBps": round(deco_bytes / (deco_mean * 1e-3) / 1e9, 1),
+                                  "frac": round(deco_bytes / (deco_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                  "bf16_equiv_GBps": round(bf16_bytes / (deco_mean * 1e-3) / 1e9, 1)},
+            "kernel_sum_bf16_equiv_GBps": round(bf16_bytes / ((comp_mean + deco_mean) * 1e-3) / 1e9, 1),
+        },
+        "offline": {"calib_batches": w.calib_batches, "calib_ms_total": round(calib_ms, 3),
+                    "calib_GBps": round(w.calib_batches * P * w.calib_T * H * 2 / (calib_ms * 1e-3) / 1e9, 1),
+                    "select_us": round(select_ms * 1e3, 2)},
+    }
+    if copy_probe:
+        out["copy_probe"] = copy_probe
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for >= {args.cpu_seconds:.0f} s")
+        out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample_T, T), args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

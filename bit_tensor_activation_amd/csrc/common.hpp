@@ -24,6 +24,46 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Raw buffer resources (gfx9 format). A wave builds a descriptor over the
+// part of a tensor it touches, so every offset stays 32-bit. The hardware
+// range check then handles ragged edges: a load at or past num_records
+// returns 0, and a store there is dropped. Lanes that have nothing to do
+// point their offset at kOOB instead of branching. That keeps the memory
+// instructions out of divergent control flow, where the compiler has to
+// wait for all loads in flight at every join. Every descriptor this library
+// builds spans fewer than 2^31 bytes, so any offset >= kOOB is out of range.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // dword3: 32-bit data format, raw (no swizzle)
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+
+// Cache policy for streaming (read-once / write-once) buffer accesses:
+// the non-temporal hint (bit 1 of the gfx94x/gfx950 cache-policy operand).
+constexpr int kStream = 2;
+
+// XCD-aware block order. MI355X deals workgroups round-robin over its 8
+// XCDs, and each XCD has its own L2. A unit is a group of `per_unit`
+// consecutive logical blocks whose writes share cache lines: all tiles of
+// one block of token rows. This mapping runs a whole unit on one XCD, so the
+// partial lines its blocks write merge in one L2 before they reach HBM.
+// Returns false for the padding blocks of the last round.
+constexpr int kXcds = 8;
+__device__ __forceinline__ bool xcd_unit_block(int64_t b, int64_t per_unit, int64_t units,
+                                               int64_t* unit, int64_t* sub) {
+  const int64_t xcd = b % kXcds;
+  const int64_t slot = b / kXcds;
+  *unit = (slot / per_unit) * kXcds + xcd;
+  *sub = slot % per_unit;
+  return *unit < units;
+}
+__host__ __forceinline__ int64_t xcd_grid(int64_t per_unit, int64_t units) {
+  return (units + kXcds - 1) / kXcds * kXcds * per_unit;
+}
+
 // Geometry of one wave-tile of the int4 slot axis. A tile owns the slots
 // [jstart, jend), 8 per lane, so that no two tiles share a packed byte. It
 // also owns every feature h in [hs, he): its int4 features plus the BF16

@@ -7,30 +7,42 @@
 // "Combating Quantization Errors with Tensor Parallelism" (each device
 // quantizes its partial sum before the sum).
 //
-// Fast kernel. One wavefront owns a wave-tile of 512 int4 slots, 8 per lane,
-// so that each lane writes exactly one packed dword per token row. The wave
-// walks a block of token rows of one shard. For each row:
-//  1. Coalesced 16-byte loads bring the tile's feature span [hs, he) of the
-//     bf16 row (plus alignment slack) into a wave-private LDS buffer. The
-//     next rows' loads are issued before the current rows are computed.
-//  2. Each lane gathers its 8 features from LDS. Each feature's offset is
-//     fixed for the whole tile, and its rscale and zero point sit in
-//     registers. The lane quantizes and packs 8 nibbles into one dword, and
-//     the 64 dwords of the wave go out as one coalesced 256-byte store.
-//  3. The lanes that own the tile's BF16 features copy their bf16 bits out
-//     of the same LDS buffer.
-// The LDS layout pads 4 bytes after every 16-byte chunk. Lane l's features
-// then start at dword 5*l, so the 64 gathers of one instruction spread over
-// all banks.
+// Fast kernel. A wave-tile is 512 int4 slots, 8 per lane, so each lane writes
+// exactly one packed dword per token row. A 256-thread block takes one shard
+// and one wave-tile, and its 4 waves walk 4 separate blocks of token rows.
+// All tiles of one row group run on one XCD (see xcd_unit_block): a token
+// row's packed bytes and BF16 block are written in pieces by all its tiles,
+// and the pieces must merge in one L2.
+//  0. Setup, once per block. The block loads the tile's contiguous parameter
+//     span (rscale, zero point for features hs..he) into LDS with coalesced
+//     loads. Each lane then takes its 8 features' parameters from there into
+//     registers. Gathering them straight from global memory would cost more
+//     cache traffic than the activations themselves.
+//  1. Per step of 4 rows, coalesced 16-byte buffer loads bring the tile's
+//     bf16 feature span (plus alignment slack) into a wave-private LDS
+//     buffer. The loads of the next 4 rows are issued before this step's
+//     compute.
+//  2. Each lane gathers its 8 features from LDS at fixed offsets, quantizes
+//     them, packs 8 nibbles into one dword and stores it. The wave's 64
+//     dwords form one coalesced 256-byte store.
+//  3. The lanes that own the tile's BF16 features copy their bf16 bits out of
+//     the same LDS buffer.
+// The staging layout pads 4 bytes after every 16-byte chunk. Lane l's
+// features then start at dword 5*l, so one gather instruction spreads over
+// all banks. All global accesses go through per-wave buffer resources:
+// ragged rows, idle lanes and surplus chunks become clamped or out-of-range
+// offsets, not branches.
 //
-// General kernel. One thread per packed byte and per BF16 value, with
-// 2-byte loads. It serves any H, k, alignment and LDS size.
+// General kernel. One thread per packed byte and per BF16 value. It serves
+// any H, k, alignment and LDS size.
 #include "common.hpp"
 
 namespace btq {
 
-constexpr int kCpWaves = 4;   // independent waves per 256-thread block
+constexpr int kCpWaves = 4;   // waves per 256-thread block, each on its own rows
 constexpr int kCpRows = 4;    // token rows staged per step
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t pad_byte_off(uint32_t e) {   // element offset -> LDS byte
   return (e >> 3) * 20u + (e & 7u) * 2u;
@@ -42,100 +54,337 @@ __device__ __forceinline__ uint32_t quant4(uint32_t bits16, float r, float z) {
   return (uint32_t)q;
 }
 
+// LDS: [param span: rscale fp32 x span_max | zero point u8 x span_max]
+//      [4 waves x kCpRows staging buffers of buf_bytes]
 template <int kMaxChunks>
 __global__ __launch_bounds__(256) void compress_kernel(
     const uint16_t* __restrict__ x, int64_t T, int H, int Hq, int k, int ntiles,
-    int64_t rows_per_wave, int64_t nrowblk, int64_t nwaves, int buf_bytes,
-    const float* __restrict__ rscale, const uint8_t* __restrict__ zp,
+    int rows_per_wave, int64_t nrowblk, int64_t ngroups, int span_max, int buf_bytes,
+    int64_t P, const float* __restrict__ rscale, const uint8_t* __restrict__ zp,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cmap,
-    uint32_t* __restrict__ packed32, uint16_t* __restrict__ outl) {
+    uint8_t* __restrict__ packed, uint16_t* __restrict__ outl) {
   extern __shared__ __align__(16) char smem[];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
-  const int64_t gw = (int64_t)blockIdx.x * kCpWaves + wave;
-  if (gw >= nwaves) return;   // waves never synchronize with each other
-  const int c = (int)(gw % ntiles);
-  const int64_t rest = gw / ntiles;
-  const int64_t rb = rest % nrowblk;
-  const int64_t p = rest / nrowblk;
+  // unit = (shard, row group); its ntiles blocks run on one XCD
+  int64_t unit, sub;
+  if (!xcd_unit_block(blockIdx.x, ntiles, P * ngroups, &unit, &sub)) return;
+  const int c = (int)sub;
+  const int64_t rg = unit % ngroups;
+  const int64_t p = unit / ngroups;
   const TileGeom g = tile_geom(cmap, c, ntiles, Hq, H);
+  const int L = g.he - g.hs;
+  const int lane = threadIdx.x & (kWave - 1);
+  // wave-uniform by construction; readfirstlane lets the compiler keep
+  // everything derived from it (rows, descriptors) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t rb = rg * kCpWaves + wave;
   const int a0 = g.hs & ~7;
   const int nch = (((g.he + 7) & ~7) - a0) >> 3;   // 16-byte chunks in the span
   const int64_t t0 = rb * rows_per_wave;
-  const int64_t t1 = min(T, t0 + rows_per_wave);
-  char* const buf = smem + (size_t)wave * kCpRows * buf_bytes;
-  const int Bq4 = Hq >> 3;
+  // waves past the last row block get no rows: every access of theirs is
+  // out of range, and they leave after the block barrier
+  const int nrows = (rb < nrowblk) ? (int)min(T - t0, (int64_t)rows_per_wave) : 0;
+  const int64_t row0 = p * T + t0;
+  const int Bq = Hq >> 1;
+  char* const buf = smem + (size_t)span_max * 5 + (size_t)wave * kCpRows * buf_bytes;
 
-  // Per-lane constants for the whole tile.
-  const int j0 = g.jstart + kLaneSlots * lane;
-  const bool active = j0 < g.jend;
-  float rs[8], zf[8];
-  uint32_t ad[8];
-  if (active) {
+  // This wave's rows of x, packed and outliers, as buffer resources.
+  const rsrc_t rx = make_rsrc(x + row0 * H, (uint32_t)nrows * (uint32_t)H * 2u);
+  const rsrc_t rp = make_rsrc(packed + row0 * Bq, (uint32_t)nrows * (uint32_t)Bq);
+  const rsrc_t ro = make_rsrc(outl + row0 * k, (uint32_t)nrows * (uint32_t)k * 2u);
+  const rsrc_t rc = make_rsrc(cmap, (uint32_t)Hq * 4u);
+
+  // Chunk m of lane l is span chunk l + 64m. Surplus lanes load out of range
+  // (no memory traffic) and write nothing.
+  uint32_t gx[kMaxChunks], lx[kMaxChunks];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int h = cmap[j0 + e];
-      rs[e] = rscale[p * H + h];
-      zf[e] = (float)zp[p * H + h];
-      ad[e] = pad_byte_off((uint32_t)(h - a0));
-    }
+  for (int m = 0; m < kMaxChunks; ++m) {
+    const int ci = lane + kWave * m;
+    gx[m] = (ci < nch) ? (uint32_t)(a0 + 8 * ci) * 2u : kOOB;
+    lx[m] = (uint32_t)ci * 20u;
   }
-  uint32_t oad = 0;
-  if (lane < g.nout) oad = pad_byte_off((uint32_t)(idx[g.ilo + lane] - a0));
+  const uint32_t rowb = (uint32_t)H * 2u;
 
-  const uint16_t* __restrict__ xs = x + p * T * (int64_t)H + a0;
-  uint4 v[kCpRows][kMaxChunks];
-  auto load_rows = [&](int64_t t) {
+  v4u v[kCpRows][kMaxChunks];
+  // The lane's offset stays in one VGPR per chunk; the row offset is uniform
+  // and rides in the instruction's SGPR offset. No per-row address math, and
+  // no register that a load in flight still owns is rewritten.
+  auto load_rows = [&](int s) {
 #pragma unroll
     for (int r = 0; r < kCpRows; ++r) {
+      const uint32_t ro_ = (uint32_t)min(s + r, nrows - 1) * rowb;
 #pragma unroll
-      for (int m = 0; m < kMaxChunks; ++m) {
-        const int ci = lane + kWave * m;
-        if (t + r < t1 && ci < nch)
-          v[r][m] = *reinterpret_cast<const uint4*>(xs + (t + r) * (int64_t)H + 8 * ci);
-      }
+      for (int m = 0; m < kMaxChunks; ++m)
+        v[r][m] = __builtin_amdgcn_raw_buffer_load_b128(rx, gx[m], ro_, kStream);
     }
   };
+  // The first rows' loads go out before the setup below, so that its latency
+  // (parameter loads, barrier, map loads) overlaps theirs.
+  if (nrows > 0) load_rows(0);
 
-  load_rows(t0);
-  for (int64_t t = t0; t < t1; t += kCpRows) {
+  // 0. parameter span -> LDS (all 4 waves), then one block barrier
+  float* const rs_l = reinterpret_cast<float*>(smem);
+  uint8_t* const zp_l = reinterpret_cast<uint8_t*>(smem + (size_t)span_max * 4);
+  for (int i = threadIdx.x; i < L; i += blockDim.x) {
+    rs_l[i] = rscale[p * H + g.hs + i];
+    zp_l[i] = zp[p * H + g.hs + i];
+  }
+  __syncthreads();
+  if (nrows <= 0) return;   // no block barrier after this point
+
+  // Per-lane constants for the whole tile. Idle lanes (past the end of a
+  // partial last tile) read valid parameters and store out of range.
+  const int j0 = g.jstart + kLaneSlots * lane;
+  const bool active = j0 < g.jend;
+  const int jj = active ? j0 : g.jstart;
+  const v4u hA = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)jj * 4u, 0, 0);
+  const v4u hB = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)jj * 4u + 16u, 0, 0);
+  const int hh[8] = {(int)hA[0], (int)hA[1], (int)hA[2], (int)hA[3],
+                     (int)hB[0], (int)hB[1], (int)hB[2], (int)hB[3]};
+  float rs[8], zf[8];
+  uint32_t ad[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int o = hh[e] - g.hs;
+    rs[e] = rs_l[o];
+    zf[e] = (float)zp_l[o];
+    ad[e] = pad_byte_off((uint32_t)(hh[e] - a0));
+  }
+  const uint32_t st_off = active ? (uint32_t)(j0 >> 1) : kOOB;
+  const int nout_it = (g.nout + kWave - 1) / kWave;   // uniform
+  uint32_t oad = 0;
+  if (g.nout > 0) oad = pad_byte_off((uint32_t)(idx[g.ilo + min(lane, g.nout - 1)] - a0));
+  const uint32_t o_off = (lane < g.nout) ? (uint32_t)(g.ilo + lane) * 2u : kOOB;
+
+  for (int s = 0; s < nrows; s += kCpRows) {
 #pragma unroll
     for (int r = 0; r < kCpRows; ++r) {
 #pragma unroll
       for (int m = 0; m < kMaxChunks; ++m) {
-        const int ci = lane + kWave * m;
-        if (t + r < t1 && ci < nch) {
-          uint32_t* d = reinterpret_cast<uint32_t*>(buf + r * buf_bytes + ci * 20);
-          d[0] = v[r][m].x;
-          d[1] = v[r][m].y;
-          d[2] = v[r][m].z;
-          d[3] = v[r][m].w;
+        // Surplus lanes skip the write: many lanes storing to one LDS address
+        // serialize on its bank.
+        if (lane + kWave * m < nch) {
+          uint32_t* d = reinterpret_cast<uint32_t*>(buf + r * buf_bytes + lx[m]);
+          d[0] = v[r][m][0];
+          d[1] = v[r][m][1];
+          d[2] = v[r][m][2];
+          d[3] = v[r][m][3];
         }
       }
     }
     wave_lds_sync();
-    if (t + kCpRows < t1) load_rows(t + kCpRows);   // in flight during the compute below
+    if (s + kCpRows < nrows) load_rows(s + kCpRows);   // in flight during the compute below
+    // all gathers of the step first, then the math: one LDS round trip, not 32
+    uint32_t u[kCpRows][8];
 #pragma unroll
     for (int r = 0; r < kCpRows; ++r) {
-      const int64_t tt = t + r;
-      if (tt >= t1) break;
-      const char* b = buf + r * buf_bytes;
-      const int64_t row = p * T + tt;
-      if (active) {
-        uint32_t w = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t u = *reinterpret_cast<const uint16_t*>(b + ad[e]);
-          w |= quant4(u, rs[e], zf[e]) << (4 * e);
-        }
-        packed32[row * Bq4 + (j0 >> 3)] = w;
-      }
-      for (int i = lane; i < g.nout; i += kWave) {
-        const uint32_t o = (i < kWave) ? oad : pad_byte_off((uint32_t)(idx[g.ilo + i] - a0));
-        outl[row * k + g.ilo + i] = *reinterpret_cast<const uint16_t*>(b + o);
+      for (int e = 0; e < 8; ++e)
+        u[r][e] = *reinterpret_cast<const uint16_t*>(buf + r * buf_bytes + ad[e]);
+    }
+#pragma unroll
+    for (int r = 0; r < kCpRows; ++r) {
+      const int row = s + r;
+      if (row >= nrows) break;
+      uint32_t w = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w |= quant4(u[r][e], rs[e], zf[e]) << (4 * e);
+      __builtin_amdgcn_raw_buffer_store_b32(w, rp, st_off, (uint32_t)row * (uint32_t)Bq, kStream);
+    }
+    for (int it = 0; it < nout_it; ++it) {
+      const int i = lane + kWave * it;
+      const uint32_t o =
+          (it == 0) ? oad : pad_byte_off((uint32_t)(idx[g.ilo + min(i, g.nout - 1)] - a0));
+      const uint32_t off =
+          (it == 0) ? o_off : ((i < g.nout) ? (uint32_t)(g.ilo + i) * 2u : kOOB);
+#pragma unroll
+      for (int r = 0; r < kCpRows; ++r) {
+        const int row = s + r;
+        if (row >= nrows) break;
+        const uint16_t b16 = *reinterpret_cast<const uint16_t*>(buf + r * buf_bytes + o);
+        __builtin_amdgcn_raw_buffer_store_b16(b16, ro, off, (uint32_t)row * (uint32_t)k * 2u, 0);
       }
     }
     wave_lds_sync();
+  }
+}
+
+// Ring kernel: the same tiles, with a deeper load pipeline. Each wave keeps
+// kRing token rows in flight in registers, and stages kSub of them at a time
+// through a small LDS buffer. A span's first 64 chunks come in one 16-byte
+// load per lane. The few chunks past 64 (BF16 features inside the tile and
+// alignment slack) come in a narrow tail load of kRemDw dwords per lane.
+// Rows past the wave's last row load and store out of range, so every trip
+// of the loop issues the same memory instructions and the compiler can count
+// exactly which loads it must wait for.
+constexpr int kRing = 8;   // token rows in flight per wave
+constexpr int kSub = 2;    // token rows staged in LDS per sub-step
+
+// Staging bytes per row for a tail of kRemDw dwords per lane: 64 + 16*kRemDw
+// chunks of 20 bytes. A compile-time stride lets the row offset ride in the
+// LDS instruction's immediate field.
+template <int kRemDw>
+constexpr int ring_row_bytes() { return (kWave + 16 * kRemDw) * 20; }
+
+template <int kRemDw>
+__global__ __launch_bounds__(256) void compress_ring_kernel(
+    const uint16_t* __restrict__ x, int64_t T, int H, int Hq, int k, int ntiles,
+    int rows_per_wave, int64_t nrowblk, int64_t ngroups, int span_max, int64_t P,
+    const float* __restrict__ rscale, const uint8_t* __restrict__ zp,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ cmap,
+    uint8_t* __restrict__ packed, uint16_t* __restrict__ outl) {
+  constexpr int buf_bytes = ring_row_bytes<kRemDw>();
+  extern __shared__ __align__(16) char smem[];
+  // unit = (shard, row group); its ntiles blocks run on one XCD
+  int64_t unit, sub;
+  if (!xcd_unit_block(blockIdx.x, ntiles, P * ngroups, &unit, &sub)) return;
+  const int c = (int)sub;
+  const int64_t rg = unit % ngroups;
+  const int64_t p = unit / ngroups;
+  const TileGeom g = tile_geom(cmap, c, ntiles, Hq, H);
+  const int L = g.he - g.hs;
+  const int lane = threadIdx.x & (kWave - 1);
+  // wave-uniform by construction; readfirstlane lets the compiler keep
+  // everything derived from it (rows, descriptors) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t rb = rg * kCpWaves + wave;
+  const int a0 = g.hs & ~7;
+  const int nch = (((g.he + 7) & ~7) - a0) >> 3;   // 16-byte chunks in the span
+  const int64_t t0 = rb * rows_per_wave;
+  // waves past the last row block get no rows: every access of theirs is
+  // out of range, and they leave after the block barrier
+  const int nrows = (rb < nrowblk) ? (int)min(T - t0, (int64_t)rows_per_wave) : 0;
+  const int64_t row0 = p * T + t0;
+  const int Bq = Hq >> 1;
+  char* const buf = smem + (size_t)span_max * 5 + (size_t)wave * kSub * buf_bytes;
+
+  const rsrc_t rx = make_rsrc(x + row0 * H, (uint32_t)nrows * (uint32_t)H * 2u);
+  const rsrc_t rp = make_rsrc(packed + row0 * Bq, (uint32_t)nrows * (uint32_t)Bq);
+  const rsrc_t ro = make_rsrc(outl + row0 * k, (uint32_t)nrows * (uint32_t)k * 2u);
+  const rsrc_t rc = make_rsrc(cmap, (uint32_t)Hq * 4u);
+
+  // main chunk: lane l loads span chunk l (zeros past the span)
+  const uint32_t gmain = (lane < nch) ? (uint32_t)(a0 + 8 * lane) * 2u : kOOB;
+  const uint32_t lmain = (uint32_t)lane * 20u;
+  // tail: dwords d = lane*kRemDw + i of the span past chunk 64; the launcher
+  // guarantees they fit (nch - 64 <= 16*kRemDw)
+  const int ntail = max(nch - kWave, 0) * 4;
+  const int d0 = lane * (kRemDw > 0 ? kRemDw : 1);
+  const uint32_t gtail = (d0 < ntail) ? (uint32_t)(a0 + 8 * kWave + 2 * d0) * 2u : kOOB;
+  const uint32_t rowb = (uint32_t)H * 2u;
+
+  constexpr int kT = kRemDw > 0 ? kRemDw : 1;
+  v4u vm[kRing];
+  uint32_t vt[kRing][kT];
+  auto load = [&](int q, int row) {
+    const bool ok = row < nrows;   // uniform
+    const uint32_t so = (uint32_t)min(row, nrows - 1) * rowb;
+    vm[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? gmain : kOOB, so, kStream);
+    if constexpr (kRemDw == 1) {
+      vt[q][0] = __builtin_amdgcn_raw_buffer_load_b32(rx, ok ? gtail : kOOB, so, kStream);
+    } else if constexpr (kRemDw == 2) {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b64(rx, ok ? gtail : kOOB, so, kStream);
+      vt[q][0] = t[0];
+      vt[q][1] = t[1];
+    } else if constexpr (kRemDw == 4) {
+      const v4u t = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? gtail : kOOB, so, kStream);
+      vt[q][0] = t[0];
+      vt[q][1] = t[1];
+      vt[q][2] = t[2];
+      vt[q][3] = t[3];
+    }
+  };
+  // The first rows' loads go out before the setup below, so that its latency
+  // (parameter loads, barrier, map loads) overlaps theirs.
+#pragma unroll
+  for (int q = 0; q < kRing; ++q) load(q, q);
+
+  // parameter span -> LDS (all 4 waves), then one block barrier
+  float* const rs_l = reinterpret_cast<float*>(smem);
+  uint8_t* const zp_l = reinterpret_cast<uint8_t*>(smem + (size_t)span_max * 4);
+  for (int i = threadIdx.x; i < L; i += blockDim.x) {
+    rs_l[i] = rscale[p * H + g.hs + i];
+    zp_l[i] = zp[p * H + g.hs + i];
+  }
+  __syncthreads();
+  if (nrows <= 0) return;   // no block barrier after this point
+
+  const int j0 = g.jstart + kLaneSlots * lane;
+  const bool active = j0 < g.jend;
+  const int jj = active ? j0 : g.jstart;
+  const v4u hA = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)jj * 4u, 0, 0);
+  const v4u hB = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)jj * 4u + 16u, 0, 0);
+  const int hh[8] = {(int)hA[0], (int)hA[1], (int)hA[2], (int)hA[3],
+                     (int)hB[0], (int)hB[1], (int)hB[2], (int)hB[3]};
+  float rs[8], zf[8];
+  uint32_t ad[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int o = hh[e] - g.hs;
+    rs[e] = rs_l[o];
+    zf[e] = (float)zp_l[o];
+    ad[e] = pad_byte_off((uint32_t)(hh[e] - a0));
+  }
+  const uint32_t st_off = active ? (uint32_t)(j0 >> 1) : kOOB;
+  uint32_t oad = 0;
+  if (g.nout > 0) oad = pad_byte_off((uint32_t)(idx[g.ilo + min(lane, g.nout - 1)] - a0));
+  const uint32_t o_off = (lane < g.nout) ? (uint32_t)(g.ilo + lane) * 2u : kOOB;
+
+  for (int base = 0; base < nrows; base += kRing) {
+#pragma unroll
+    for (int sb = 0; sb < kRing / kSub; ++sb) {
+      // stage kSub rows (the main chunk of lanes past the span lands in
+      // unused chunk slots of the buffer; tail dwords past the span skip)
+#pragma unroll
+      for (int r = 0; r < kSub; ++r) {
+        const int q = sb * kSub + r;
+        char* b = buf + r * buf_bytes;
+        uint32_t* dm = reinterpret_cast<uint32_t*>(b + lmain);
+        dm[0] = vm[q][0];
+        dm[1] = vm[q][1];
+        dm[2] = vm[q][2];
+        dm[3] = vm[q][3];
+        if constexpr (kRemDw > 0) {
+#pragma unroll
+          for (int i = 0; i < kRemDw; ++i) {
+            const int d = d0 + i;
+            if (d < ntail)
+              *reinterpret_cast<uint32_t*>(b + (kWave + (d >> 2)) * 20 + (d & 3) * 4) = vt[q][i];
+          }
+        }
+      }
+      wave_lds_sync();
+      // refill the staged slots with the rows kRing ahead
+#pragma unroll
+      for (int r = 0; r < kSub; ++r) load(sb * kSub + r, base + kRing + sb * kSub + r);
+      uint32_t u[kSub][8];
+#pragma unroll
+      for (int r = 0; r < kSub; ++r) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          u[r][e] = *reinterpret_cast<const uint16_t*>(buf + r * buf_bytes + ad[e]);
+      }
+#pragma unroll
+      for (int r = 0; r < kSub; ++r) {
+        const int row = base + sb * kSub + r;
+        const bool ok = row < nrows;   // uniform
+        const uint32_t rr = (uint32_t)min(row, nrows - 1);
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w |= quant4(u[r][e], rs[e], zf[e]) << (4 * e);
+        __builtin_amdgcn_raw_buffer_store_b32(w, rp, ok ? st_off : kOOB, rr * (uint32_t)Bq,
+                                              kStream);
+        const uint16_t b16 = *reinterpret_cast<const uint16_t*>(buf + r * buf_bytes + oad);
+        __builtin_amdgcn_raw_buffer_store_b16(b16, ro, ok ? o_off : kOOB, rr * (uint32_t)k * 2u, 0);
+        // tiles holding more than 64 BF16 features (uniform, rare)
+        for (int i = lane + kWave; i - lane < g.nout; i += kWave) {
+          const uint32_t o = pad_byte_off((uint32_t)(idx[g.ilo + min(i, g.nout - 1)] - a0));
+          const uint16_t v16 = *reinterpret_cast<const uint16_t*>(buf + r * buf_bytes + o);
+          const uint32_t off = (ok && i < g.nout) ? (uint32_t)(g.ilo + i) * 2u : kOOB;
+          __builtin_amdgcn_raw_buffer_store_b16(v16, ro, off, rr * (uint32_t)k * 2u, 0);
+        }
+      }
+      wave_lds_sync();
+    }
   }
 }
 
@@ -167,13 +416,14 @@ __global__ __launch_bounds__(256) void compress_general_kernel(
   }
 }
 
-static int64_t pick_rows_per_wave(int64_t slots_waves, int64_t T) {
-  // ~8192 waves over the chip, a multiple of the staging depth, 4..64 rows.
-  int64_t rpw = (slots_waves * T + 8191) / 8192;
+// Rows per wave: about 8192 waves over the chip (32 per CU), a multiple of
+// the staging depth, 4..64 rows.
+static int pick_rows_per_wave(int64_t tile_waves, int64_t T) {
+  int64_t rpw = (tile_waves * T + 8191) / 8192;
   rpw = (rpw + kCpRows - 1) / kCpRows * kCpRows;
   if (rpw < kCpRows) rpw = kCpRows;
   if (rpw > 64) rpw = 64;
-  return rpw;
+  return (int)rpw;
 }
 
 hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
@@ -181,28 +431,62 @@ hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, i
                            const int32_t* cmap, uint8_t* packed, uint16_t* outl, hipStream_t s) {
   const int64_t Hq = H - k;
   const int64_t Bq = (Hq + 1) / 2;
-  // The span of one tile holds its 512 slots plus the BF16 features between
-  // them, at most min(H, 512 + k) features, plus 14 of alignment slack.
-  const int64_t span = (H < kTileSlots + k ? H : kTileSlots + k) + 16;
-  const int64_t nch_max = (span + 7) / 8;
+  // A tile's feature span holds its 512 slots plus the BF16 features between
+  // them: at most min(H, 512 + k) features. Staging adds 14 of alignment slack.
+  const int64_t span = (H < kTileSlots + k ? H : kTileSlots + k);
+  const int64_t nch_max = (span + 16 + 7) / 8;
   const int buf_bytes = (int)((nch_max * 20 + 15) / 16 * 16);
-  const size_t lds = (size_t)kCpWaves * kCpRows * buf_bytes;
-  const bool fast = Hq > 0 && H % 8 == 0 && Hq % 8 == 0 && (uintptr_t)x % 16 == 0 &&
-                    (uintptr_t)packed % 4 == 0 && nch_max <= 4 * kWave && lds <= 65536;
+  const int span_max = (int)((span + 15) / 16 * 16);
+  const size_t lds = (size_t)span_max * 5 + (size_t)kCpWaves * kCpRows * buf_bytes;
+  // The per-wave buffer resources span at most 64 rows of H bf16 values:
+  // H < 2^24 keeps them below 2^31 bytes.
+  const bool fast = Hq > 0 && H % 8 == 0 && Hq % 8 == 0 && H < (int64_t(1) << 24) &&
+                    (uintptr_t)x % 16 == 0 && (uintptr_t)packed % 4 == 0 &&
+                    nch_max <= 4 * kWave && lds <= 65536;
+  // Ring kernel: span chunks past 64 must fit the tail load (16 chunks per
+  // tail dword per lane).
+  const int64_t tail = nch_max > kWave ? nch_max - kWave : 0;
+  const int rem_dw = tail == 0 ? 0 : tail <= 16 ? 1 : tail <= 32 ? 2 : tail <= 64 ? 4 : -1;
+  const int ring_buf = (kWave + 16 * (rem_dw > 0 ? rem_dw : 0)) * 20;
+  const size_t ring_lds = (size_t)span_max * 5 + (size_t)kCpWaves * kSub * ring_buf;
+  if (fast && rem_dw >= 0 && ring_lds <= 65536) {
+    const int ntiles = (int)((Hq + kTileSlots - 1) / kTileSlots);
+    // about 4096 waves (16 per CU), a multiple of the ring depth, 8..64 rows
+    int64_t rpw64 = (P * ntiles * T + 4095) / 4096;
+    rpw64 = (rpw64 + kRing - 1) / kRing * kRing;
+    if (rpw64 < kRing) rpw64 = kRing;
+    if (rpw64 > 64) rpw64 = 64;
+    const int rpw = (int)rpw64;
+    const int64_t nrowblk = (T + rpw - 1) / rpw;
+    const int64_t ngroups = (nrowblk + kCpWaves - 1) / kCpWaves;
+    const unsigned blocks = (unsigned)xcd_grid(ntiles, P * ngroups);
+#define BTQ_RING(n)                                                                               \
+  compress_ring_kernel<n><<<blocks, 256, ring_lds, s>>>(x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, \
+                                                        nrowblk, ngroups, span_max, P,              \
+                                                        rscale, zp, idx, cmap, packed, outl)
+    switch (rem_dw) {
+      case 0: BTQ_RING(0); break;
+      case 1: BTQ_RING(1); break;
+      case 2: BTQ_RING(2); break;
+      default: BTQ_RING(4); break;
+    }
+#undef BTQ_RING
+    return hipGetLastError();
+  }
   if (fast) {
     const int ntiles = (int)((Hq + kTileSlots - 1) / kTileSlots);
-    const int64_t rpw = pick_rows_per_wave(P * ntiles, T);
+    const int rpw = pick_rows_per_wave(P * ntiles, T);
     const int64_t nrowblk = (T + rpw - 1) / rpw;
-    const int64_t nwaves = P * nrowblk * ntiles;
-    const unsigned blocks = (unsigned)((nwaves + kCpWaves - 1) / kCpWaves);
+    const int64_t ngroups = (nrowblk + kCpWaves - 1) / kCpWaves;
+    const int64_t blocks = xcd_grid(ntiles, P * ngroups);
     if (nch_max <= 2 * kWave)
-      compress_kernel<2><<<blocks, 256, lds, s>>>(x, T, (int)H, (int)Hq, (int)k, ntiles, rpw,
-                                                  nrowblk, nwaves, buf_bytes, rscale, zp, idx,
-                                                  cmap, (uint32_t*)packed, outl);
+      compress_kernel<2><<<(unsigned)blocks, 256, lds, s>>>(
+          x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, ngroups, span_max, buf_bytes, P,
+          rscale, zp, idx, cmap, packed, outl);
     else
-      compress_kernel<4><<<blocks, 256, lds, s>>>(x, T, (int)H, (int)Hq, (int)k, ntiles, rpw,
-                                                  nrowblk, nwaves, buf_bytes, rscale, zp, idx,
-                                                  cmap, (uint32_t*)packed, outl);
+      compress_kernel<4><<<(unsigned)blocks, 256, lds, s>>>(
+          x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, ngroups, span_max, buf_bytes, P,
+          rscale, zp, idx, cmap, packed, outl);
     return hipGetLastError();
   }
   const int64_t n = P * T * (Bq + k);
