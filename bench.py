@@ -74,10 +74,11 @@ def read_traffic(workload: str):
 def algorithmic_bytes(P, T, H, k):
     """Bytes the method must move per launch (inputs once, outputs once)."""
     Bq = (H - k + 1) // 2
-    params = P * H * 5 + 4 * H               # scale or rscale (4 B) + zero point (1 B); maps
+    Hq = H - k
+    maps = 4 * H                             # cmap and outlier_idx
     message = P * T * (Bq + 2 * k)
-    compress = P * T * H * 2 + message + params
-    decompress = message + T * H * 4 + params
+    compress = P * T * H * 2 + message + P * Hq * 8 + maps           # + (rscale, zero point) table
+    decompress = message + T * H * 4 + (P + 1) * Hq * 4 + maps       # + scale rows, constant row
     return compress, decompress
 
 
@@ -187,10 +188,9 @@ def main() -> int:
     ys = [torch.empty((T, H), dtype=torch.float32, device=dev) for _ in range(R)]
     del x0
     p = lambda t: t.data_ptr() if t.numel() else None
-    rs, zp, oi, cm, sc = (p(sel["rscale"]), p(sel["zero_point"]), p(sel["outlier_idx"]),
-                          p(sel["cmap"]), p(sel["scale"]))
-    comp_args = [(p(xs[r]), P, T, H, k, rs, zp, oi, cm, p(pks[r]), p(ols[r]), sh) for r in range(R)]
-    deco_args = [(p(pks[(r - 2) % R]), p(ols[(r - 2) % R]), P, T, H, k, sc, zp, oi, cm, p(ys[r]), sh)
+    enc, dec, oi, cm = p(sel["enc"]), p(sel["dec"]), p(sel["outlier_idx"]), p(sel["cmap"])
+    comp_args = [(p(xs[r]), P, T, H, k, enc, oi, cm, p(pks[r]), p(ols[r]), sh) for r in range(R)]
+    deco_args = [(p(pks[(r - 2) % R]), p(ols[(r - 2) % R]), P, T, H, k, dec, oi, cm, p(ys[r]), sh)
                  for r in range(R)]
     compress, decompress = lib.btq_compress_pack, lib.btq_decompress_reduce
     # first fill every message buffer once, so the receiver always reads a real message

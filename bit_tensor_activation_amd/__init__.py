@@ -8,7 +8,9 @@ from .api import (  # noqa: F401
     btq_calib_update,
     btq_calib_workspace_bytes,
     btq_compress_pack,
+    btq_dec_table_floats,
     btq_decompress_reduce,
+    btq_enc_table_floats,
     btq_packed_row_bytes,
     btq_select_outliers,
     btq_select_workspace_bytes,

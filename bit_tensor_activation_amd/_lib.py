@@ -18,10 +18,13 @@ _P, _I64, _I, _F, _SZ = _c.c_void_p, _c.c_int64, _c.c_int, _c.c_float, _c.c_size
 SIGNATURES = {
     "btq_calib_update": (_I, [_P, _I64, _I64, _I64, _F, _I, _P, _P, _P, _SZ, _P]),
     "btq_calib_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
-    "btq_select_outliers": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "btq_select_outliers": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 _SZ, _P]),
     "btq_select_workspace_bytes": (_SZ, [_I64, _I64]),
-    "btq_compress_pack": (_I, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
-    "btq_decompress_reduce": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
+    "btq_enc_table_floats": (_I64, [_I64, _I64, _I64]),
+    "btq_dec_table_floats": (_I64, [_I64, _I64, _I64]),
+    "btq_compress_pack": (_I, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
+    "btq_decompress_reduce": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "btq_packed_row_bytes": (_I64, [_I64, _I64]),
     "btq_status_str": (_c.c_char_p, [_I]),
     "btq_version": (_c.c_char_p, []),

@@ -11,6 +11,8 @@ Layouts (contiguous, row-major, last index fastest):
   run_min/max float32 [P,H]
   scale, rscale float32 [P,H];  zero_point uint8 [P,H]
   outlier_idx int32 [k];  fmap int32 [H];  cmap int32 [H-k]
+  enc_table   float32 [P,H-k,2]  (rscale, zero point) per int4 slot
+  dec_table   float32 [2P+1,H-k] scale rows, zero-point rows, constant row
   packed      uint8 [P,T,ceil((H-k)/2)];  outliers int16 [P,T,k]
   y           float32 [T,H]
 """
@@ -72,6 +74,14 @@ def btq_select_workspace_bytes(P: int, H: int) -> int:
     return int(_lib.load().btq_select_workspace_bytes(P, H))
 
 
+def btq_enc_table_floats(P: int, H: int, k: int) -> int:
+    return int(_lib.load().btq_enc_table_floats(P, H, k))
+
+
+def btq_dec_table_floats(P: int, H: int, k: int) -> int:
+    return int(_lib.load().btq_dec_table_floats(P, H, k))
+
+
 def btq_calib_update(x: torch.Tensor, run_min: torch.Tensor, run_max: torch.Tensor,
                      momentum: float, first_batch: bool,
                      workspace: Optional[torch.Tensor] = None, stream=None) -> None:
@@ -95,7 +105,8 @@ def btq_select_outliers(run_min: torch.Tensor, run_max: torch.Tensor, k: int, ou
                         workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
     """Parameters and the BF16 feature set from the running extremes.
 
-    Returns a dict with scale, rscale, zero_point, outlier_idx, fmap, cmap.
+    Returns a dict with scale, rscale, zero_point, outlier_idx, fmap, cmap,
+    enc (the encoder table) and dec (the decoder table).
     """
     dev = _device(run_min)
     P, H = run_min.shape
@@ -110,9 +121,13 @@ def btq_select_outliers(run_min: torch.Tensor, run_max: torch.Tensor, k: int, ou
     o.setdefault("outlier_idx", torch.empty((k,), dtype=torch.int32, device=dev))
     o.setdefault("fmap", torch.empty((H,), dtype=torch.int32, device=dev))
     o.setdefault("cmap", torch.empty((H - k,), dtype=torch.int32, device=dev))
+    o.setdefault("enc", torch.empty((P, H - k, 2), dtype=torch.float32, device=dev))
+    o.setdefault("dec", torch.empty((2 * P + 1, H - k), dtype=torch.float32, device=dev))
     for name, dt, shp in (("scale", torch.float32, (P, H)), ("rscale", torch.float32, (P, H)),
                           ("zero_point", torch.uint8, (P, H)), ("outlier_idx", torch.int32, (k,)),
-                          ("fmap", torch.int32, (H,)), ("cmap", torch.int32, (H - k,))):
+                          ("fmap", torch.int32, (H,)), ("cmap", torch.int32, (H - k,)),
+                          ("enc", torch.float32, (P, H - k, 2)),
+                          ("dec", torch.float32, (2 * P + 1, H - k))):
         _need(o[name], name, (dt,), shp, dev)
     need = btq_select_workspace_bytes(P, H)
     if workspace is None:
@@ -120,14 +135,15 @@ def btq_select_outliers(run_min: torch.Tensor, run_max: torch.Tensor, k: int, ou
     lib = _lib.load()
     st = lib.btq_select_outliers(_ptr(run_min), _ptr(run_max), P, H, k, _ptr(o["scale"]),
                                  _ptr(o["rscale"]), _ptr(o["zero_point"]), _ptr(o["outlier_idx"]),
-                                 _ptr(o["fmap"]), _ptr(o["cmap"]), _ptr(workspace),
+                                 _ptr(o["fmap"]), _ptr(o["cmap"]), _ptr(o["enc"]),
+                                 _ptr(o["dec"]), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(),
                                  _stream(dev, stream))
     _lib.check(st, "btq_select_outliers")
     return o
 
 
-def btq_compress_pack(x: torch.Tensor, k: int, rscale: torch.Tensor, zero_point: torch.Tensor,
+def btq_compress_pack(x: torch.Tensor, k: int, enc_table: torch.Tensor,
                       outlier_idx: torch.Tensor, cmap: torch.Tensor,
                       packed: Optional[torch.Tensor] = None,
                       outliers: Optional[torch.Tensor] = None, stream=None):
@@ -136,8 +152,7 @@ def btq_compress_pack(x: torch.Tensor, k: int, rscale: torch.Tensor, zero_point:
     P, T, H = x.shape
     _need(x, "x", _BF16, (P, T, H), dev)
     Bq = btq_packed_row_bytes(H, k)
-    _need(rscale, "rscale", (torch.float32,), (P, H), dev)
-    _need(zero_point, "zero_point", (torch.uint8,), (P, H), dev)
+    _need(enc_table, "enc_table", (torch.float32,), (P, H - k, 2), dev)
     _need(outlier_idx, "outlier_idx", (torch.int32,), (k,), dev)
     _need(cmap, "cmap", (torch.int32,), (H - k,), dev)
     if packed is None:
@@ -147,16 +162,15 @@ def btq_compress_pack(x: torch.Tensor, k: int, rscale: torch.Tensor, zero_point:
     _need(packed, "packed", (torch.uint8,), (P, T, Bq), dev)
     _need(outliers, "outliers", _BF16, (P, T, k), dev)
     lib = _lib.load()
-    st = lib.btq_compress_pack(_ptr(_bits(x)), P, T, H, k, _ptr(rscale), _ptr(zero_point),
-                               _ptr(outlier_idx), _ptr(cmap), _ptr(packed), _ptr(_bits(outliers)),
+    st = lib.btq_compress_pack(_ptr(_bits(x)), P, T, H, k, _ptr(enc_table), _ptr(outlier_idx),
+                               _ptr(cmap), _ptr(packed), _ptr(_bits(outliers)),
                                _stream(dev, stream))
     _lib.check(st, "btq_compress_pack")
     return packed, outliers
 
 
 def btq_decompress_reduce(packed: torch.Tensor, outliers: torch.Tensor, H: int,
-                          scale: torch.Tensor, zero_point: torch.Tensor,
-                          outlier_idx: torch.Tensor, cmap: torch.Tensor,
+                          dec_table: torch.Tensor, outlier_idx: torch.Tensor, cmap: torch.Tensor,
                           y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Receiver: y float32 [T,H] = sum over shards of the dequantized messages."""
     dev = _device(packed)
@@ -166,16 +180,15 @@ def btq_decompress_reduce(packed: torch.Tensor, outliers: torch.Tensor, H: int,
         raise ValueError(f"packed rows of {Bq} bytes do not match H={H}, k={k}")
     _need(packed, "packed", (torch.uint8,), (P, T, Bq), dev)
     _need(outliers, "outliers", _BF16, (P, T, k), dev)
-    _need(scale, "scale", (torch.float32,), (P, H), dev)
-    _need(zero_point, "zero_point", (torch.uint8,), (P, H), dev)
+    _need(dec_table, "dec_table", (torch.float32,), (2 * P + 1, H - k), dev)
     _need(outlier_idx, "outlier_idx", (torch.int32,), (k,), dev)
     _need(cmap, "cmap", (torch.int32,), (H - k,), dev)
     if y is None:
         y = torch.empty((T, H), dtype=torch.float32, device=dev)
     _need(y, "y", (torch.float32,), (T, H), dev)
     lib = _lib.load()
-    st = lib.btq_decompress_reduce(_ptr(packed), _ptr(_bits(outliers)), P, T, H, k, _ptr(scale),
-                                   _ptr(zero_point), _ptr(outlier_idx), _ptr(cmap), _ptr(y),
+    st = lib.btq_decompress_reduce(_ptr(packed), _ptr(_bits(outliers)), P, T, H, k,
+                                   _ptr(dec_table), _ptr(outlier_idx), _ptr(cmap), _ptr(y),
                                    _stream(dev, stream))
     _lib.check(st, "btq_decompress_reduce")
     return y

@@ -45,6 +45,16 @@ size_t btq_select_workspace_bytes(int64_t P, int64_t H) {
   return (size_t)H * sizeof(float);
 }
 
+int64_t btq_enc_table_floats(int64_t P, int64_t H, int64_t k) {
+  if (P < 1 || P > kMaxP || H < 1 || H > kMaxH || check_k(H, k) != BTQ_OK) return -1;
+  return 2 * P * (H - k);
+}
+
+int64_t btq_dec_table_floats(int64_t P, int64_t H, int64_t k) {
+  if (P < 1 || P > kMaxP || H < 1 || H > kMaxH || check_k(H, k) != BTQ_OK) return -1;
+  return (2 * P + 1) * (H - k);
+}
+
 int btq_calib_update(const uint16_t* x, int64_t P, int64_t T, int64_t H, float momentum,
                      int first_batch, float* run_min, float* run_max, void* workspace,
                      size_t workspace_bytes, void* stream) {
@@ -65,61 +75,61 @@ int btq_calib_update(const uint16_t* x, int64_t P, int64_t T, int64_t H, float m
 
 int btq_select_outliers(const float* run_min, const float* run_max, int64_t P, int64_t H,
                         int64_t k, float* scale, float* rscale, uint8_t* zero_point,
-                        int32_t* outlier_idx, int32_t* fmap, int32_t* cmap, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        int32_t* outlier_idx, int32_t* fmap, int32_t* cmap, float* enc_table,
+                        float* dec_table, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   if (P < 1 || P > kMaxP || H < 1 || H > kMaxH) return BTQ_ERR_SHAPE;
   int st = check_k(H, k);
   if (st != BTQ_OK) return st;
   if (!run_min || !run_max || !scale || !rscale || !zero_point || !fmap) return BTQ_ERR_ARG;
-  if ((k > 0 && !outlier_idx) || (k < H && !cmap)) return BTQ_ERR_ARG;
+  if ((k > 0 && !outlier_idx) || (k < H && (!cmap || !enc_table || !dec_table)))
+    return BTQ_ERR_ARG;
   if (!aligned(run_min, 4) || !aligned(run_max, 4) || !aligned(scale, 4) ||
-      !aligned(rscale, 4) || !aligned(outlier_idx, 4) || !aligned(fmap, 4) || !aligned(cmap, 4))
+      !aligned(rscale, 4) || !aligned(outlier_idx, 4) || !aligned(fmap, 4) || !aligned(cmap, 4) ||
+      !aligned(enc_table, 4) || !aligned(dec_table, 4))
     return BTQ_ERR_ALIGN;
   const size_t need = btq_select_workspace_bytes(P, H);
   if (!workspace) return BTQ_ERR_ARG;
   if (workspace_bytes < need) return BTQ_ERR_WORKSPACE;
   if (!aligned(workspace, 4)) return BTQ_ERR_ALIGN;
   return hip_status(btq::launch_select(run_min, run_max, P, H, k, scale, rscale, zero_point,
-                                       outlier_idx, fmap, cmap, (float*)workspace,
-                                       (hipStream_t)stream));
+                                       outlier_idx, fmap, cmap, enc_table, dec_table,
+                                       (float*)workspace, (hipStream_t)stream));
 }
 
 int btq_compress_pack(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
-                      const float* rscale, const uint8_t* zero_point,
-                      const int32_t* outlier_idx, const int32_t* cmap, uint8_t* packed,
-                      uint16_t* outliers, void* stream) {
+                      const float* enc_table, const int32_t* outlier_idx, const int32_t* cmap,
+                      uint8_t* packed, uint16_t* outliers, void* stream) {
   int st = check_dims(P, T, H, 0);
   if (st != BTQ_OK) return st;
   st = check_k(H, k);
   if (st != BTQ_OK) return st;
-  if (!rscale || !zero_point) return BTQ_ERR_ARG;
-  if ((k > 0 && !outlier_idx) || (k < H && !cmap)) return BTQ_ERR_ARG;
+  if ((k > 0 && !outlier_idx) || (k < H && (!cmap || !enc_table))) return BTQ_ERR_ARG;
   if (T > 0 && (!x || (k < H && !packed) || (k > 0 && !outliers))) return BTQ_ERR_ARG;
-  if (!aligned(x, 2) || !aligned(rscale, 4) || !aligned(outlier_idx, 4) || !aligned(cmap, 4) ||
-      !aligned(outliers, 2))
+  if (!aligned(x, 2) || !aligned(enc_table, 4) || !aligned(outlier_idx, 4) ||
+      !aligned(cmap, 4) || !aligned(outliers, 2))
     return BTQ_ERR_ALIGN;
   if (T == 0) return BTQ_OK;
-  return hip_status(btq::launch_compress(x, P, T, H, k, rscale, zero_point, outlier_idx, cmap,
-                                         packed, outliers, (hipStream_t)stream));
+  return hip_status(btq::launch_compress(x, P, T, H, k, enc_table, outlier_idx, cmap, packed,
+                                         outliers, (hipStream_t)stream));
 }
 
 int btq_decompress_reduce(const uint8_t* packed, const uint16_t* outliers, int64_t P, int64_t T,
-                          int64_t H, int64_t k, const float* scale, const uint8_t* zero_point,
+                          int64_t H, int64_t k, const float* dec_table,
                           const int32_t* outlier_idx, const int32_t* cmap, float* y,
                           void* stream) {
   int st = check_dims(P, T, H, 0);
   if (st != BTQ_OK) return st;
   st = check_k(H, k);
   if (st != BTQ_OK) return st;
-  if (!scale || !zero_point) return BTQ_ERR_ARG;
-  if ((k > 0 && !outlier_idx) || (k < H && !cmap)) return BTQ_ERR_ARG;
+  if ((k > 0 && !outlier_idx) || (k < H && (!cmap || !dec_table))) return BTQ_ERR_ARG;
   if (T > 0 && (!y || (k < H && !packed) || (k > 0 && !outliers))) return BTQ_ERR_ARG;
-  if (!aligned(outliers, 2) || !aligned(scale, 4) || !aligned(outlier_idx, 4) ||
+  if (!aligned(outliers, 2) || !aligned(dec_table, 4) || !aligned(outlier_idx, 4) ||
       !aligned(cmap, 4) || !aligned(y, 4))
     return BTQ_ERR_ALIGN;
   if (T == 0) return BTQ_OK;
-  return hip_status(btq::launch_decompress(packed, outliers, P, T, H, k, scale, zero_point,
-                                           outlier_idx, cmap, y, (hipStream_t)stream));
+  return hip_status(btq::launch_decompress(packed, outliers, P, T, H, k, dec_table, outlier_idx,
+                                           cmap, y, (hipStream_t)stream));
 }
 
 const char* btq_status_str(int status) {

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void calib_partial_kernel(
       smax[wave][lane + kWave * e] = mx[e];
     }
   }
-  __syncthreads();
+  lds_barrier();
   for (int col = threadIdx.x; col < kCalCols; col += blockDim.x) {
     const int64_t h = h0 + col;
     if (h >= H) continue;

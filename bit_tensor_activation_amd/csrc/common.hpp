@@ -19,9 +19,18 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
 // LDS accesses across this point. The hardware runs one wave's LDS
 // instructions in issue order.
 __device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Block barrier that orders LDS only. __syncthreads() also orders global
+// memory, which makes every wave wait for all of its loads in flight
+// (vmcnt(0)) before the barrier, also where only LDS needs ordering.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Raw buffer resources (gfx9 format). A wave builds a descriptor over the
@@ -102,14 +111,15 @@ hipError_t launch_calib(const uint16_t* x, int64_t P, int64_t T, int64_t H, floa
 
 hipError_t launch_select(const float* run_min, const float* run_max, int64_t P, int64_t H,
                          int64_t k, float* scale, float* rscale, uint8_t* zp, int32_t* idx,
-                         int32_t* fmap, int32_t* cmap, float* ws_score, hipStream_t s);
+                         int32_t* fmap, int32_t* cmap, float* enc, float* dec, float* ws_score,
+                         hipStream_t s);
 
 hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
-                           const float* rscale, const uint8_t* zp, const int32_t* idx,
-                           const int32_t* cmap, uint8_t* packed, uint16_t* outl, hipStream_t s);
+                           const float* enc, const int32_t* idx, const int32_t* cmap,
+                           uint8_t* packed, uint16_t* outl, hipStream_t s);
 
 hipError_t launch_decompress(const uint8_t* packed, const uint16_t* outl, int64_t P, int64_t T,
-                             int64_t H, int64_t k, const float* scale, const uint8_t* zp,
-                             const int32_t* idx, const int32_t* cmap, float* y, hipStream_t s);
+                             int64_t H, int64_t k, const float* dec, const int32_t* idx,
+                             const int32_t* cmap, float* y, hipStream_t s);
 
 }  // namespace btq

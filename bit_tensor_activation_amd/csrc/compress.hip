@@ -13,11 +13,11 @@
 // All tiles of one row group run on one XCD (see xcd_unit_block): a token
 // row's packed bytes and BF16 block are written in pieces by all its tiles,
 // and the pieces must merge in one L2.
-//  0. Setup, once per block. The block loads the tile's contiguous parameter
-//     span (rscale, zero point for features hs..he) into LDS with coalesced
-//     loads. Each lane then takes its 8 features' parameters from there into
-//     registers. Gathering them straight from global memory would cost more
-//     cache traffic than the activations themselves.
+//  0. Setup, once per wave. Each lane loads its 8 slots' (rscale, zero point)
+//     pairs from the encoder table, which selection wrote in slot order: 64
+//     contiguous bytes per lane, so a wave reads one contiguous 4 KB block.
+//     No LDS staging and no block barrier: the waves of a block never wait
+//     for each other.
 //  1. Per step of 4 rows, coalesced 16-byte buffer loads bring the tile's
 //     bf16 feature span (plus alignment slack) into a wave-private LDS
 //     buffer. The loads of the next 4 rows are issued before this step's
@@ -54,13 +54,27 @@ __device__ __forceinline__ uint32_t quant4(uint32_t bits16, float r, float z) {
   return (uint32_t)q;
 }
 
-// LDS: [param span: rscale fp32 x span_max | zero point u8 x span_max]
-//      [4 waves x kCpRows staging buffers of buf_bytes]
+// The lane's 8 slot parameters from the encoder table [P, Hq, 2]: `re` spans
+// the tile's slots of one shard. Lanes past the tile read zeros.
+__device__ __forceinline__ void load_enc(rsrc_t re, bool active, int lane, float rs[8],
+                                         float zf[8]) {
+  const uint32_t o = active ? (uint32_t)lane * 64u : kOOB;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const v4u t = __builtin_amdgcn_raw_buffer_load_b128(re, o + 16u * m, 0, 0);
+    rs[2 * m] = __uint_as_float(t[0]);
+    zf[2 * m] = __uint_as_float(t[1]);
+    rs[2 * m + 1] = __uint_as_float(t[2]);
+    zf[2 * m + 1] = __uint_as_float(t[3]);
+  }
+}
+
+// LDS: 4 waves x kCpRows staging buffers of buf_bytes
 template <int kMaxChunks>
 __global__ __launch_bounds__(256) void compress_kernel(
     const uint16_t* __restrict__ x, int64_t T, int H, int Hq, int k, int ntiles,
-    int rows_per_wave, int64_t nrowblk, int64_t ngroups, int span_max, int buf_bytes,
-    int64_t P, const float* __restrict__ rscale, const uint8_t* __restrict__ zp,
+    int rows_per_wave, int64_t nrowblk, int64_t ngroups, int buf_bytes,
+    int64_t P, const float* __restrict__ enc,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cmap,
     uint8_t* __restrict__ packed, uint16_t* __restrict__ outl) {
   extern __shared__ __align__(16) char smem[];
@@ -71,21 +85,19 @@ __global__ __launch_bounds__(256) void compress_kernel(
   const int64_t rg = unit % ngroups;
   const int64_t p = unit / ngroups;
   const TileGeom g = tile_geom(cmap, c, ntiles, Hq, H);
-  const int L = g.he - g.hs;
   const int lane = threadIdx.x & (kWave - 1);
   // wave-uniform by construction; readfirstlane lets the compiler keep
   // everything derived from it (rows, descriptors) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t rb = rg * kCpWaves + wave;
+  if (rb >= nrowblk) return;   // no rows for this wave (no block barrier below)
   const int a0 = g.hs & ~7;
   const int nch = (((g.he + 7) & ~7) - a0) >> 3;   // 16-byte chunks in the span
   const int64_t t0 = rb * rows_per_wave;
-  // waves past the last row block get no rows: every access of theirs is
-  // out of range, and they leave after the block barrier
-  const int nrows = (rb < nrowblk) ? (int)min(T - t0, (int64_t)rows_per_wave) : 0;
+  const int nrows = (int)min(T - t0, (int64_t)rows_per_wave);
   const int64_t row0 = p * T + t0;
   const int Bq = Hq >> 1;
-  char* const buf = smem + (size_t)span_max * 5 + (size_t)wave * kCpRows * buf_bytes;
+  char* const buf = smem + (size_t)wave * kCpRows * buf_bytes;
 
   // This wave's rows of x, packed and outliers, as buffer resources.
   const rsrc_t rx = make_rsrc(x + row0 * H, (uint32_t)nrows * (uint32_t)H * 2u);
@@ -117,38 +129,23 @@ __global__ __launch_bounds__(256) void compress_kernel(
         v[r][m] = __builtin_amdgcn_raw_buffer_load_b128(rx, gx[m], ro_, kStream);
     }
   };
-  // The first rows' loads go out before the setup below, so that its latency
-  // (parameter loads, barrier, map loads) overlaps theirs.
-  if (nrows > 0) load_rows(0);
-
-  // 0. parameter span -> LDS (all 4 waves), then one block barrier
-  float* const rs_l = reinterpret_cast<float*>(smem);
-  uint8_t* const zp_l = reinterpret_cast<uint8_t*>(smem + (size_t)span_max * 4);
-  for (int i = threadIdx.x; i < L; i += blockDim.x) {
-    rs_l[i] = rscale[p * H + g.hs + i];
-    zp_l[i] = zp[p * H + g.hs + i];
-  }
-  __syncthreads();
-  if (nrows <= 0) return;   // no block barrier after this point
-
-  // Per-lane constants for the whole tile. Idle lanes (past the end of a
-  // partial last tile) read valid parameters and store out of range.
+  // Per-lane constants for the whole tile, loaded before the first rows
+  // (the vector-memory counter retires in order). Idle lanes (past the end
+  // of a partial last tile) read valid indices and store out of range.
   const int j0 = g.jstart + kLaneSlots * lane;
   const bool active = j0 < g.jend;
   const int jj = active ? j0 : g.jstart;
   const v4u hA = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)jj * 4u, 0, 0);
   const v4u hB = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)jj * 4u + 16u, 0, 0);
+  float rs[8], zf[8];
+  load_enc(make_rsrc(enc + (p * Hq + g.jstart) * 2, (uint32_t)(g.jend - g.jstart) * 8u), active,
+           lane, rs, zf);
+  load_rows(0);
   const int hh[8] = {(int)hA[0], (int)hA[1], (int)hA[2], (int)hA[3],
                      (int)hB[0], (int)hB[1], (int)hB[2], (int)hB[3]};
-  float rs[8], zf[8];
   uint32_t ad[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int o = hh[e] - g.hs;
-    rs[e] = rs_l[o];
-    zf[e] = (float)zp_l[o];
-    ad[e] = pad_byte_off((uint32_t)(hh[e] - a0));
-  }
+  for (int e = 0; e < 8; ++e) ad[e] = pad_byte_off((uint32_t)(hh[e] - a0));
   const uint32_t st_off = active ? (uint32_t)(j0 >> 1) : kOOB;
   const int nout_it = (g.nout + kWave - 1) / kWave;   // uniform
   uint32_t oad = 0;
@@ -228,10 +225,10 @@ constexpr int ring_row_bytes() { return (kWave + 16 * kRemDw) * 20; }
 template <int kRemDw>
 __global__ __launch_bounds__(256) void compress_ring_kernel(
     const uint16_t* __restrict__ x, int64_t T, int H, int Hq, int k, int ntiles,
-    int rows_per_wave, int64_t nrowblk, int64_t ngroups, int span_max, int64_t P,
-    const float* __restrict__ rscale, const uint8_t* __restrict__ zp,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ cmap,
-    uint8_t* __restrict__ packed, uint16_t* __restrict__ outl) {
+    int rows_per_wave, int64_t nrowblk, int64_t ngroups, int64_t P,
+    const float* __restrict__ enc, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ cmap, uint8_t* __restrict__ packed,
+    uint16_t* __restrict__ outl) {
   constexpr int buf_bytes = ring_row_bytes<kRemDw>();
   extern __shared__ __align__(16) char smem[];
   // unit = (shard, row group); its ntiles blocks run on one XCD
@@ -241,21 +238,19 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
   const int64_t rg = unit % ngroups;
   const int64_t p = unit / ngroups;
   const TileGeom g = tile_geom(cmap, c, ntiles, Hq, H);
-  const int L = g.he - g.hs;
   const int lane = threadIdx.x & (kWave - 1);
   // wave-uniform by construction; readfirstlane lets the compiler keep
   // everything derived from it (rows, descriptors) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t rb = rg * kCpWaves + wave;
+  if (rb >= nrowblk) return;   // no rows for this wave (no block barrier below)
   const int a0 = g.hs & ~7;
   const int nch = (((g.he + 7) & ~7) - a0) >> 3;   // 16-byte chunks in the span
   const int64_t t0 = rb * rows_per_wave;
-  // waves past the last row block get no rows: every access of theirs is
-  // out of range, and they leave after the block barrier
-  const int nrows = (rb < nrowblk) ? (int)min(T - t0, (int64_t)rows_per_wave) : 0;
+  const int nrows = (int)min(T - t0, (int64_t)rows_per_wave);
   const int64_t row0 = p * T + t0;
   const int Bq = Hq >> 1;
-  char* const buf = smem + (size_t)span_max * 5 + (size_t)wave * kSub * buf_bytes;
+  char* const buf = smem + (size_t)wave * kSub * buf_bytes;
 
   const rsrc_t rx = make_rsrc(x + row0 * H, (uint32_t)nrows * (uint32_t)H * 2u);
   const rsrc_t rp = make_rsrc(packed + row0 * Bq, (uint32_t)nrows * (uint32_t)Bq);
@@ -293,40 +288,35 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
       vt[q][3] = t[3];
     }
   };
-  // The first rows' loads go out before the setup below, so that its latency
-  // (parameter loads, barrier, map loads) overlaps theirs.
-#pragma unroll
-  for (int q = 0; q < kRing; ++q) load(q, q);
 
-  // parameter span -> LDS (all 4 waves), then one block barrier
-  float* const rs_l = reinterpret_cast<float*>(smem);
-  uint8_t* const zp_l = reinterpret_cast<uint8_t*>(smem + (size_t)span_max * 4);
-  for (int i = threadIdx.x; i < L; i += blockDim.x) {
-    rs_l[i] = rscale[p * H + g.hs + i];
-    zp_l[i] = zp[p * H + g.hs + i];
-  }
-  __syncthreads();
-  if (nrows <= 0) return;   // no block barrier after this point
-
+  // Setup loads first, ring loads second: the vector-memory counter retires
+  // in order, so waiting for a setup load never waits for the ring.
+  // (a) the lane's 8 feature indices and its BF16 feature index
   const int j0 = g.jstart + kLaneSlots * lane;
   const bool active = j0 < g.jend;
   const int jj = active ? j0 : g.jstart;
   const v4u hA = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)jj * 4u, 0, 0);
   const v4u hB = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)jj * 4u + 16u, 0, 0);
+  const rsrc_t ri_ = make_rsrc(idx, (uint32_t)k * 4u);
+  const uint32_t oh = __builtin_amdgcn_raw_buffer_load_b32(
+      ri_, (g.nout > 0) ? (uint32_t)(g.ilo + min(lane, g.nout - 1)) * 4u : kOOB, 0, 0);
+  // (b) the lane's 8 slot parameters (4 x 16 contiguous bytes)
+  float rs[8], zf[8];
+  load_enc(make_rsrc(enc + (p * Hq + g.jstart) * 2, (uint32_t)(g.jend - g.jstart) * 8u), active,
+           lane, rs, zf);
+  // (c) the ring: the first kRing rows. Unconditional: a branch around it
+  // would make the compiler assume at the join that these loads might not
+  // exist, and wait for the ring when it waits for the setup loads.
+#pragma unroll
+  for (int q = 0; q < kRing; ++q) load(q, q);
+
   const int hh[8] = {(int)hA[0], (int)hA[1], (int)hA[2], (int)hA[3],
                      (int)hB[0], (int)hB[1], (int)hB[2], (int)hB[3]};
-  float rs[8], zf[8];
   uint32_t ad[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int o = hh[e] - g.hs;
-    rs[e] = rs_l[o];
-    zf[e] = (float)zp_l[o];
-    ad[e] = pad_byte_off((uint32_t)(hh[e] - a0));
-  }
+  for (int e = 0; e < 8; ++e) ad[e] = pad_byte_off((uint32_t)(hh[e] - a0));
   const uint32_t st_off = active ? (uint32_t)(j0 >> 1) : kOOB;
-  uint32_t oad = 0;
-  if (g.nout > 0) oad = pad_byte_off((uint32_t)(idx[g.ilo + min(lane, g.nout - 1)] - a0));
+  const uint32_t oad = (g.nout > 0) ? pad_byte_off((uint32_t)((int)oh - a0)) : 0u;
   const uint32_t o_off = (lane < g.nout) ? (uint32_t)(g.ilo + lane) * 2u : kOOB;
 
   for (int base = 0; base < nrows; base += kRing) {
@@ -390,9 +380,9 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
 
 __global__ __launch_bounds__(256) void compress_general_kernel(
     const uint16_t* __restrict__ x, int64_t P, int64_t T, int64_t H, int64_t k, int64_t Hq,
-    int64_t Bq, const float* __restrict__ rscale, const uint8_t* __restrict__ zp,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ cmap,
-    uint8_t* __restrict__ packed, uint16_t* __restrict__ outl) {
+    int64_t Bq, const float* __restrict__ enc, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ cmap, uint8_t* __restrict__ packed,
+    uint16_t* __restrict__ outl) {
   const int64_t n1 = P * T * Bq;
   const int64_t n2 = P * T * k;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -401,12 +391,9 @@ __global__ __launch_bounds__(256) void compress_general_kernel(
       const int64_t row = i / Bq, byte = i % Bq;
       const int64_t p = row / T;
       const int64_t j = 2 * byte;
-      const int64_t h0 = cmap[j];
-      uint32_t q = quant4(x[row * H + h0], rscale[p * H + h0], (float)zp[p * H + h0]);
-      if (j + 1 < Hq) {
-        const int64_t h1 = cmap[j + 1];
-        q |= quant4(x[row * H + h1], rscale[p * H + h1], (float)zp[p * H + h1]) << 4;
-      }
+      const float* e = enc + (p * Hq + j) * 2;   // (rscale, zero point) of slot j
+      uint32_t q = quant4(x[row * H + cmap[j]], e[0], e[1]);
+      if (j + 1 < Hq) q |= quant4(x[row * H + cmap[j + 1]], e[2], e[3]) << 4;
       packed[i] = (uint8_t)q;
     } else {
       const int64_t ii = i - n1;
@@ -427,8 +414,8 @@ static int pick_rows_per_wave(int64_t tile_waves, int64_t T) {
 }
 
 hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
-                           const float* rscale, const uint8_t* zp, const int32_t* idx,
-                           const int32_t* cmap, uint8_t* packed, uint16_t* outl, hipStream_t s) {
+                           const float* enc, const int32_t* idx, const int32_t* cmap,
+                           uint8_t* packed, uint16_t* outl, hipStream_t s) {
   const int64_t Hq = H - k;
   const int64_t Bq = (Hq + 1) / 2;
   // A tile's feature span holds its 512 slots plus the BF16 features between
@@ -436,19 +423,18 @@ hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, i
   const int64_t span = (H < kTileSlots + k ? H : kTileSlots + k);
   const int64_t nch_max = (span + 16 + 7) / 8;
   const int buf_bytes = (int)((nch_max * 20 + 15) / 16 * 16);
-  const int span_max = (int)((span + 15) / 16 * 16);
-  const size_t lds = (size_t)span_max * 5 + (size_t)kCpWaves * kCpRows * buf_bytes;
+  const size_t lds = (size_t)kCpWaves * kCpRows * buf_bytes;
   // The per-wave buffer resources span at most 64 rows of H bf16 values:
   // H < 2^24 keeps them below 2^31 bytes.
   const bool fast = Hq > 0 && H % 8 == 0 && Hq % 8 == 0 && H < (int64_t(1) << 24) &&
                     (uintptr_t)x % 16 == 0 && (uintptr_t)packed % 4 == 0 &&
-                    nch_max <= 4 * kWave && lds <= 65536;
+                    (uintptr_t)enc % 16 == 0 && nch_max <= 4 * kWave && lds <= 65536;
   // Ring kernel: span chunks past 64 must fit the tail load (16 chunks per
   // tail dword per lane).
   const int64_t tail = nch_max > kWave ? nch_max - kWave : 0;
   const int rem_dw = tail == 0 ? 0 : tail <= 16 ? 1 : tail <= 32 ? 2 : tail <= 64 ? 4 : -1;
   const int ring_buf = (kWave + 16 * (rem_dw > 0 ? rem_dw : 0)) * 20;
-  const size_t ring_lds = (size_t)span_max * 5 + (size_t)kCpWaves * kSub * ring_buf;
+  const size_t ring_lds = (size_t)kCpWaves * kSub * ring_buf;
   if (fast && rem_dw >= 0 && ring_lds <= 65536) {
     const int ntiles = (int)((Hq + kTileSlots - 1) / kTileSlots);
     // about 4096 waves (16 per CU), a multiple of the ring depth, 8..64 rows
@@ -462,8 +448,8 @@ hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, i
     const unsigned blocks = (unsigned)xcd_grid(ntiles, P * ngroups);
 #define BTQ_RING(n)                                                                               \
   compress_ring_kernel<n><<<blocks, 256, ring_lds, s>>>(x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, \
-                                                        nrowblk, ngroups, span_max, P,              \
-                                                        rscale, zp, idx, cmap, packed, outl)
+                                                        nrowblk, ngroups, P, enc, idx, cmap,        \
+                                                        packed, outl)
     switch (rem_dw) {
       case 0: BTQ_RING(0); break;
       case 1: BTQ_RING(1); break;
@@ -481,20 +467,20 @@ hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, i
     const int64_t blocks = xcd_grid(ntiles, P * ngroups);
     if (nch_max <= 2 * kWave)
       compress_kernel<2><<<(unsigned)blocks, 256, lds, s>>>(
-          x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, ngroups, span_max, buf_bytes, P,
-          rscale, zp, idx, cmap, packed, outl);
+          x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, ngroups, buf_bytes, P, enc, idx,
+          cmap, packed, outl);
     else
       compress_kernel<4><<<(unsigned)blocks, 256, lds, s>>>(
-          x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, ngroups, span_max, buf_bytes, P,
-          rscale, zp, idx, cmap, packed, outl);
+          x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, ngroups, buf_bytes, P, enc, idx,
+          cmap, packed, outl);
     return hipGetLastError();
   }
   const int64_t n = P * T * (Bq + k);
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  compress_general_kernel<<<(unsigned)blocks, 256, 0, s>>>(x, P, T, H, k, Hq, Bq, rscale, zp, idx,
-                                                           cmap, packed, outl);
+  compress_general_kernel<<<(unsigned)blocks, 256, 0, s>>>(x, P, T, H, k, Hq, Bq, enc, idx, cmap,
+                                                           packed, outl);
   return hipGetLastError();
 }
 

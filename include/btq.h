@@ -106,16 +106,34 @@ size_t btq_calib_workspace_bytes(int64_t P, int64_t T, int64_t H);
  *   fmap              i32  [H]    out, fmap[h] = j (the int4 slot of h), or
  *                                 -1-i when h = outlier_idx[i]
  *   cmap              i32  [H-k]  out, cmap[j] = h of int4 slot j (ascending)
+ *   enc_table   fp32 [P, H-k, 2]  out: (rscale, zero_point) of slot j's
+ *                                 feature cmap[j], per shard: the sender's
+ *                                 parameters in message order
+ *   dec_table   fp32 [2P+1, H-k]  out: rows 0..P-1 scale, rows P..2P-1
+ *                                 zero_point, row 2P the per-slot constant
+ *                                 -sum_p zero_point*scale (fp32 steps in
+ *                                 shard order): the receiver's parameters in
+ *                                 message order
  *   workspace  at least btq_select_workspace_bytes(P,H) bytes of scratch.
- * Pointers for zero-length outputs (k == 0, or k == H for cmap) may be NULL.
+ * The two tables only reorder the per-feature parameters (and add one
+ * derived sum), so the hot kernels read them with contiguous vector loads.
+ * Pointers for zero-length outputs (k == 0, or k == H for cmap and the
+ * tables) may be NULL. The tables should be 16-byte aligned (other
+ * alignments run on the general path).
  */
 int btq_select_outliers(const float *run_min, const float *run_max,
                         int64_t P, int64_t H, int64_t k,
                         float *scale, float *rscale, uint8_t *zero_point,
                         int32_t *outlier_idx, int32_t *fmap, int32_t *cmap,
+                        float *enc_table, float *dec_table,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 size_t btq_select_workspace_bytes(int64_t P, int64_t H);
+
+/* Floats in enc_table (2*P*(H-k)) and dec_table ((2P+1)*(H-k)); -1 for
+ * invalid sizes. */
+int64_t btq_enc_table_floats(int64_t P, int64_t H, int64_t k);
+int64_t btq_dec_table_floats(int64_t P, int64_t H, int64_t k);
 
 /*
  * Sender side of inference -- "The Hybrid Quantization Algorithm", Inference
@@ -123,12 +141,13 @@ size_t btq_select_workspace_bytes(int64_t P, int64_t H);
  * with Tensor Parallelism".
  *
  * For each token row (p,t), the int4 slots j = 0..H-k-1 take feature
- * h = cmap[j]:  q = clamp(rint_half_even(fl(x*rscale[p,h])) + zero_point[p,h], 0, 15)
- * and are packed two per byte: slot 2b in the low nibble of byte b, slot
- * 2b+1 in the high nibble. An odd H-k leaves the last high nibble 0. The BF16
- * features are copied bit for bit: outliers[p,t,i] = x[p,t,outlier_idx[i]].
+ * h = cmap[j]:  q = clamp(rint_half_even(fl(x*rscale)) + zero_point, 0, 15),
+ * with (rscale, zero_point) = enc_table[p,j]. Codes are packed two per byte:
+ * slot 2b in the low nibble of byte b, slot 2b+1 in the high nibble. An odd
+ * H-k leaves the last high nibble 0. The BF16 features are copied bit for
+ * bit: outliers[p,t,i] = x[p,t,outlier_idx[i]].
  *   x          bf16 [P,T,H]                       in
- *   rscale     fp32 [P,H], zero_point u8 [P,H]    in (from btq_select_outliers)
+ *   enc_table  fp32 [P,H-k,2]                     in (from btq_select_outliers)
  *   outlier_idx i32 [k], cmap i32 [H-k]           in (from btq_select_outliers)
  *   packed     u8   [P,T,btq_packed_row_bytes(H,k)]  out (rows are unpadded)
  *   outliers   bf16 [P,T,k]                       out
@@ -136,31 +155,30 @@ size_t btq_select_workspace_bytes(int64_t P, int64_t H);
  * ascending order, as btq_select_outliers writes them.
  */
 int btq_compress_pack(const uint16_t *x, int64_t P, int64_t T, int64_t H, int64_t k,
-                      const float *rscale, const uint8_t *zero_point,
-                      const int32_t *outlier_idx, const int32_t *cmap,
-                      uint8_t *packed, uint16_t *outliers, void *stream);
+                      const float *enc_table, const int32_t *outlier_idx,
+                      const int32_t *cmap, uint8_t *packed, uint16_t *outliers, void *stream);
 
 /*
  * Receiver side of inference -- "The Hybrid Quantization Algorithm",
  * Inference bullet (convert back, sum across devices).
  *
  * y[t,h] = sum over p = 0..P-1 of term_p, in fp32, where
- *   int4 feature h = cmap[j]:       term_p = (q_p - zero_point[p,h]) * scale[p,h]
- *                                   (q_p = nibble j of packed row (p,t))
+ *   int4 feature h = cmap[j]:       term_p = (q_p - zero_point) * scale
+ *                                   (q_p = nibble j of packed row (p,t);
+ *                                   scale, zero_point from dec_table[.,j])
  *   BF16 feature h = outlier_idx[i]: term_p = the bf16 value outliers[p,t,i]
  * BF16 features are summed in p order starting from 0, so they match a
  * sequential fp32 sum bit for bit. int4 features may be evaluated as
- * fma(q_p, scale, acc) plus a per-feature constant -sum_p zero_point*scale,
- * which stays within 1e-3*|y| + 1e-2*max_p scale[p,h] of the sequential sum.
+ * fma(q_p, scale, acc) seeded with the table's per-slot constant, which
+ * stays within 1e-3*|y| + 1e-2*max_p scale of the sequential sum.
  *   packed, outliers  as written by btq_compress_pack (P shards)  in
- *   scale fp32 [P,H], zero_point u8 [P,H], outlier_idx [k], cmap [H-k]  in
+ *   dec_table fp32 [2P+1,H-k], outlier_idx [k], cmap [H-k]        in
  *   y    fp32 [T,H]  out
  */
 int btq_decompress_reduce(const uint8_t *packed, const uint16_t *outliers,
                           int64_t P, int64_t T, int64_t H, int64_t k,
-                          const float *scale, const uint8_t *zero_point,
-                          const int32_t *outlier_idx, const int32_t *cmap,
-                          float *y, void *stream);
+                          const float *dec_table, const int32_t *outlier_idx,
+                          const int32_t *cmap, float *y, void *stream);
 
 /* Bytes per packed row: ceil((H-k)/2); -1 if H < 1 or k is outside [0,H]. */
 int64_t btq_packed_row_bytes(int64_t H, int64_t k);

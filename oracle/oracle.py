@@ -147,13 +147,40 @@ def top_k_features(score: np.ndarray, k: int):
     return idx, fmap, cmap
 
 
+def codec_tables(scale, rscale, zero_point, cmap):
+    """The parameters in message order, as the selection step hands them on.
+
+    Slot j of the int4 message carries feature h = cmap[j]. The sender's
+    table holds (rscale, zero_point) of that feature for each shard. The
+    receiver's table holds scale and zero_point per shard and slot, plus
+    one constant per slot, bias[j] = -(z_0*s_0 + z_1*s_1 + ...). The bias
+    is evaluated as fp32 steps b = fl(b - fl(z_p*s_p)) in shard order from
+    0. These are the same numbers as the per-feature arrays, reordered;
+    the bias is a derived sum. Returns
+      enc  float32 [P, H-k, 2]   (rscale, zero_point)
+      dec  float32 [2P+1, H-k]   rows 0..P-1 scale, P..2P-1 zero_point, 2P bias
+    """
+    cmap = np.asarray(cmap, np.int64)
+    s = np.asarray(scale, F32)[:, cmap]
+    r = np.asarray(rscale, F32)[:, cmap]
+    z = np.asarray(zero_point).astype(F32)[:, cmap]
+    enc = np.stack([r, z], axis=-1).astype(F32)
+    bias = np.zeros(cmap.shape[0], F32)
+    for p in range(s.shape[0]):
+        bias = bias - (z[p] * s[p])
+    dec = np.concatenate([s, z, bias[None, :]], axis=0).astype(F32)
+    return enc, dec
+
+
 def select_outliers(run_min, run_max, k: int) -> dict:
-    """[Selection] after [Calibration]: parameters, scores, BF16 set, maps."""
+    """[Selection] after [Calibration]: parameters, scores, BF16 set, maps,
+    and the same parameters in message order."""
     scale, rscale, zp, width = quant_params(run_min, run_max)
     score = range_score(width)
     idx, fmap, cmap = top_k_features(score, k)
+    enc, dec = codec_tables(scale, rscale, zp, cmap)
     return dict(scale=scale, rscale=rscale, zero_point=zp, width=width,
-                score=score, idx=idx, fmap=fmap, cmap=cmap)
+                score=score, idx=idx, fmap=fmap, cmap=cmap, enc=enc, dec=dec)
 
 
 # ------------------------------------------------- inference, sender ----

@@ -82,6 +82,8 @@ def assert_selection_equal(sel_gpu: dict, sel_orc: dict) -> None:
     assert_bits_equal(sel_gpu["outlier_idx"], sel_orc["idx"].astype(np.int32), "outlier_idx")
     assert_bits_equal(sel_gpu["fmap"], sel_orc["fmap"].astype(np.int32), "fmap")
     assert_bits_equal(sel_gpu["cmap"], sel_orc["cmap"].astype(np.int32), "cmap")
+    assert_bits_equal(sel_gpu["enc"], sel_orc["enc"], "enc_table")
+    assert_bits_equal(sel_gpu["dec"], sel_orc["dec"], "dec_table")
 
 
 def assert_y_close(y_gpu: np.ndarray, y_orc: np.ndarray, scale: np.ndarray, idx) -> None:

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -56,6 +56,12 @@ def test_size_helpers(lib):
     n = lib.btq_calib_workspace_bytes(8, 2048, 4096)
     assert n > 0 and n % (2 * 8 * 4096 * 4) == 0
     assert lib.btq_calib_workspace_bytes(8, 0, 4096) == 0
+    assert lib.btq_enc_table_floats(8, 4096, 64) == 2 * 8 * 4032
+    assert lib.btq_dec_table_floats(8, 4096, 64) == 17 * 4032
+    assert lib.btq_enc_table_floats(3, 16, 16) == 0
+    assert lib.btq_dec_table_floats(3, 16, 16) == 0
+    assert lib.btq_enc_table_floats(0, 16, 4) == -1
+    assert lib.btq_dec_table_floats(2, 16, 17) == -1
 
 
 def calib(lib, x=A, P=2, T=4, H=16, m=0.9, rmin=A, rmax=A, ws=A, wsb=BIG):
@@ -81,9 +87,10 @@ def test_calib_validation(lib):
     assert calib(lib, ws=A + 2) == ALIGN
 
 
-def select(lib, rmin=A, rmax=A, P=2, H=16, k=4, sc=A, rs=A, zp=A, idx=A, fmap=A, cmap=A, ws=A,
-           wsb=BIG):
-    return lib.btq_select_outliers(rmin, rmax, P, H, k, sc, rs, zp, idx, fmap, cmap, ws, wsb, None)
+def select(lib, rmin=A, rmax=A, P=2, H=16, k=4, sc=A, rs=A, zp=A, idx=A, fmap=A, cmap=A, enc=A,
+           dec=A, ws=A, wsb=BIG):
+    return lib.btq_select_outliers(rmin, rmax, P, H, k, sc, rs, zp, idx, fmap, cmap, enc, dec, ws,
+                                   wsb, None)
 
 
 def test_select_validation(lib):
@@ -94,6 +101,10 @@ def test_select_validation(lib):
     assert select(lib, fmap=None) == ARG
     assert select(lib, idx=None) == ARG
     assert select(lib, cmap=None) == ARG
+    assert select(lib, enc=None) == ARG
+    assert select(lib, dec=None) == ARG
+    assert select(lib, enc=A + 2) == ALIGN
+    assert select(lib, dec=A + 1) == ALIGN
     assert select(lib, ws=None) == ARG
     assert select(lib, wsb=4) == WS
     assert select(lib, sc=A + 1) == ALIGN
@@ -102,42 +113,44 @@ def test_select_validation(lib):
     # called here (they would launch).
 
 
-def compress(lib, x=A, P=2, T=4, H=16, k=4, rs=A, zp=A, idx=A, cmap=A, pk=A, ol=A):
-    return lib.btq_compress_pack(x, P, T, H, k, rs, zp, idx, cmap, pk, ol, None)
+def compress(lib, x=A, P=2, T=4, H=16, k=4, enc=A, idx=A, cmap=A, pk=A, ol=A):
+    return lib.btq_compress_pack(x, P, T, H, k, enc, idx, cmap, pk, ol, None)
 
 
 def test_compress_validation(lib):
     assert compress(lib, k=17) == SHAPE
     assert compress(lib, T=-1) == SHAPE
     assert compress(lib, P=0) == SHAPE
-    assert compress(lib, rs=None) == ARG
+    assert compress(lib, enc=None) == ARG
     assert compress(lib, idx=None) == ARG
     assert compress(lib, cmap=None) == ARG
     assert compress(lib, x=None) == ARG
     assert compress(lib, pk=None) == ARG
     assert compress(lib, ol=None) == ARG
     assert compress(lib, x=A + 1) == ALIGN
-    assert compress(lib, rs=A + 2) == ALIGN
+    assert compress(lib, enc=A + 2) == ALIGN
     assert compress(lib, ol=A + 1) == ALIGN
     # T == 0 is an empty batch: valid, nothing enqueued
     assert compress(lib, T=0, x=None, pk=None, ol=None) == OK
     # zero-length maps may be NULL
     assert compress(lib, T=0, k=0, idx=None) == OK
-    assert compress(lib, T=0, k=16, cmap=None) == OK
+    assert compress(lib, T=0, k=16, cmap=None, enc=None) == OK
 
 
-def decompress(lib, pk=A, ol=A, P=2, T=4, H=16, k=4, sc=A, zp=A, idx=A, cmap=A, y=A):
-    return lib.btq_decompress_reduce(pk, ol, P, T, H, k, sc, zp, idx, cmap, y, None)
+def decompress(lib, pk=A, ol=A, P=2, T=4, H=16, k=4, dec=A, idx=A, cmap=A, y=A):
+    return lib.btq_decompress_reduce(pk, ol, P, T, H, k, dec, idx, cmap, y, None)
 
 
 def test_decompress_validation(lib):
     assert decompress(lib, k=17) == SHAPE
     assert decompress(lib, P=0) == SHAPE
     assert decompress(lib, H=0) == SHAPE
-    assert decompress(lib, sc=None) == ARG
+    assert decompress(lib, dec=None) == ARG
+    assert decompress(lib, cmap=None) == ARG
     assert decompress(lib, y=None) == ARG
     assert decompress(lib, pk=None) == ARG
     assert decompress(lib, ol=None) == ARG
     assert decompress(lib, y=A + 2) == ALIGN
-    assert decompress(lib, sc=A + 1) == ALIGN
+    assert decompress(lib, dec=A + 1) == ALIGN
     assert decompress(lib, T=0, y=None, pk=None, ol=None) == OK
+    assert decompress(lib, T=0, k=16, cmap=None, dec=None) == OK

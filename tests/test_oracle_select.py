@@ -91,3 +91,24 @@ def test_zero_inclusion_holds_on_tiny_workload():
         x = W.to_u16(W.batch(w, W.PHASE_CALIB, b))
         mn, mx = O.calib_update(x, mn, mx, w.momentum, first=(b == 0))
     assert np.all(mn < 0) and np.all(mx > 0)
+
+
+def test_codec_tables_are_the_parameters_in_message_order():
+    # Brute force: walk the slots and read the per-feature arrays directly.
+    rng = np.random.default_rng(9)
+    P, H, k = 3, 40, 6
+    mn = -np.abs(rng.standard_normal((P, H))).astype(np.float32) * 3
+    mx = np.abs(rng.standard_normal((P, H))).astype(np.float32) * 3
+    sel = O.select_outliers(mn, mx, k)
+    enc, dec = sel["enc"], sel["dec"]
+    assert enc.shape == (P, H - k, 2) and dec.shape == (2 * P + 1, H - k)
+    for j, h in enumerate(sel["cmap"]):
+        exact = 0.0
+        for p in range(P):
+            assert enc[p, j, 0] == sel["rscale"][p, h]
+            assert enc[p, j, 1] == float(sel["zero_point"][p, h])
+            assert dec[p, j] == sel["scale"][p, h]
+            assert dec[P + p, j] == float(sel["zero_point"][p, h])
+            exact -= float(sel["zero_point"][p, h]) * float(sel["scale"][p, h])
+        # the fp32 bias is the exact sum up to P roundings
+        assert abs(dec[2 * P, j] - exact) <= 2 * P * 2.0 ** -24 * (abs(exact) + 15 * P * sel["scale"][:, h].max())

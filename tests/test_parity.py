@@ -18,7 +18,14 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
-def run_both(calib_xs, x, k, momentum, *, x_offset=0):
+def _shifted(t: torch.Tensor, off: int) -> torch.Tensor:
+    """Same values in storage that starts `off` elements past an allocation."""
+    big = torch.empty(t.numel() + off, dtype=t.dtype, device=t.device)
+    big[off:] = t.reshape(-1)
+    return big[off:].view(t.shape)
+
+
+def run_both(calib_xs, x, k, momentum, *, x_offset=0, table_offset=0):
     """Calibrate, select, compress and decompress on both sides; compare all."""
     P, T, H = x.shape
     rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
@@ -37,18 +44,17 @@ def run_both(calib_xs, x, k, momentum, *, x_offset=0):
     assert_selection_equal(sel_g, sel_o)
 
     if x_offset:   # misaligned base pointer: same values, shifted storage
-        big = torch.empty(x.numel() + x_offset, dtype=torch.int16, device=DEV)
-        big[x_offset:] = x.reshape(-1)
-        x = big[x_offset:].view(P, T, H)
-    pk, ol = B.btq_compress_pack(x, k, sel_g["rscale"], sel_g["zero_point"],
-                                 sel_g["outlier_idx"], sel_g["cmap"])
+        x = _shifted(x, x_offset)
+    enc, dec = sel_g["enc"], sel_g["dec"]
+    if table_offset:   # tables aligned to 4 bytes but not to 16
+        enc, dec = _shifted(enc, table_offset), _shifted(dec, table_offset)
+    pk, ol = B.btq_compress_pack(x, k, enc, sel_g["outlier_idx"], sel_g["cmap"])
     pk_o, ol_o = oracle_compress_rows(u16(x), sel_o)
     torch.cuda.synchronize()
     assert_bits_equal(pk, pk_o, "packed")
     assert_bits_equal(ol.view(torch.int16), ol_o.view(np.int16), "outliers")
 
-    y = B.btq_decompress_reduce(pk, ol, H, sel_g["scale"], sel_g["zero_point"],
-                                sel_g["outlier_idx"], sel_g["cmap"])
+    y = B.btq_decompress_reduce(pk, ol, H, dec, sel_g["outlier_idx"], sel_g["cmap"])
     y_o = O.decompress_reduce(pk_o, ol_o, sel_o["scale"], sel_o["zero_point"], sel_o["fmap"])
     torch.cuda.synchronize()
     assert_y_close(y.cpu().numpy(), y_o, sel_o["scale"], sel_o["idx"])
@@ -103,6 +109,14 @@ def test_misaligned_input_pointer():
     run_both(calib, x, k, 0.95, x_offset=1)
 
 
+def test_misaligned_tables():
+    say("case: codec tables offset by one float")
+    P, T, H, k = 3, 12, 1024, 8
+    calib = [W.draw(P, T, H, 3200 + b, device=DEV) for b in range(2)]
+    x = W.draw(P, T, H, 3300, device=DEV)
+    run_both(calib, x, k, 0.9, table_offset=1)
+
+
 def test_momentum_extremes():
     say("case: momentum 0 and 1")
     P, T, H = 2, 8, 64
@@ -120,11 +134,9 @@ def test_empty_batch_leaves_outputs_untouched():
     B.btq_calib_update(xs[0], rmin, rmax, 0.9, True)
     sel = B.btq_select_outliers(rmin, rmax, k)
     x0 = torch.empty((P, 0, H), dtype=torch.int16, device=DEV)
-    pk, ol = B.btq_compress_pack(x0, k, sel["rscale"], sel["zero_point"], sel["outlier_idx"],
-                                 sel["cmap"])
+    pk, ol = B.btq_compress_pack(x0, k, sel["enc"], sel["outlier_idx"], sel["cmap"])
     assert pk.shape == (P, 0, (H - k + 1) // 2) and ol.shape == (P, 0, k)
-    y = B.btq_decompress_reduce(pk, ol, H, sel["scale"], sel["zero_point"], sel["outlier_idx"],
-                                sel["cmap"])
+    y = B.btq_decompress_reduce(pk, ol, H, sel["dec"], sel["outlier_idx"], sel["cmap"])
     torch.cuda.synchronize()
     assert y.shape == (0, H)
 
@@ -144,10 +156,8 @@ def test_repeatable_bitwise():
         for b, xb in enumerate(calib):
             B.btq_calib_update(xb, rmin, rmax, 0.9, b == 0)
         sel = B.btq_select_outliers(rmin, rmax, k)
-        pk, ol = B.btq_compress_pack(x, k, sel["rscale"], sel["zero_point"], sel["outlier_idx"],
-                                     sel["cmap"])
-        y = B.btq_decompress_reduce(pk, ol, H, sel["scale"], sel["zero_point"],
-                                    sel["outlier_idx"], sel["cmap"])
+        pk, ol = B.btq_compress_pack(x, k, sel["enc"], sel["outlier_idx"], sel["cmap"])
+        y = B.btq_decompress_reduce(pk, ol, H, sel["dec"], sel["outlier_idx"], sel["cmap"])
         torch.cuda.synchronize()
         outs.append([t.cpu().clone() for t in (rmin, rmax, sel["scale"], sel["cmap"], pk, ol, y)])
     for a, b in zip(*outs):
