@@ -179,19 +179,20 @@ def main() -> int:
 
     # ---- resident inputs and rotated buffer sets ----
     x0 = W.batch(w, W.PHASE_INFER, 0, T=T, device=dev)
-    Bq = B.btq_packed_row_bytes(H, k)
-    set_bytes = P * T * H * 2 + P * T * (Bq + 2 * k) + T * H * 4
+    pitch = B.btq_packed_pitch(H, k)
+    set_bytes = P * T * H * 2 + P * T * (pitch + 2 * k) + T * H * 4
     R = max(3, -(-args.rotate_mib * 2 ** 20 // set_bytes) + 1)
     xs = [x0.clone() for _ in range(R)]
-    pks = [torch.empty((P, T, Bq), dtype=torch.uint8, device=dev) for _ in range(R)]
+    pks = [torch.empty((P, T, pitch), dtype=torch.uint8, device=dev) for _ in range(R)]
     ols = [torch.empty((P, T, k), dtype=torch.int16, device=dev) for _ in range(R)]
     ys = [torch.empty((T, H), dtype=torch.float32, device=dev) for _ in range(R)]
     del x0
     p = lambda t: t.data_ptr() if t.numel() else None
     enc, dec, oi, cm = p(sel["enc"]), p(sel["dec"]), p(sel["outlier_idx"]), p(sel["cmap"])
-    comp_args = [(p(xs[r]), P, T, H, k, enc, oi, cm, p(pks[r]), p(ols[r]), sh) for r in range(R)]
-    deco_args = [(p(pks[(r - 2) % R]), p(ols[(r - 2) % R]), P, T, H, k, dec, oi, cm, p(ys[r]), sh)
+    comp_args = [(p(xs[r]), P, T, H, k, enc, oi, cm, p(pks[r]), pitch, p(ols[r]), sh)
                  for r in range(R)]
+    deco_args = [(p(pks[(r - 2) % R]), pitch, p(ols[(r - 2) % R]), P, T, H, k, dec, oi, cm,
+                  p(ys[r]), sh) for r in range(R)]
     compress, decompress = lib.btq_compress_pack, lib.btq_decompress_reduce
     # first fill every message buffer once, so the receiver always reads a real message
     for r in range(R):

@@ -11,6 +11,7 @@ from .api import (  # noqa: F401
     btq_dec_table_floats,
     btq_decompress_reduce,
     btq_enc_table_floats,
+    btq_packed_pitch,
     btq_packed_row_bytes,
     btq_select_outliers,
     btq_select_workspace_bytes,

@@ -23,9 +23,10 @@ SIGNATURES = {
     "btq_select_workspace_bytes": (_SZ, [_I64, _I64]),
     "btq_enc_table_floats": (_I64, [_I64, _I64, _I64]),
     "btq_dec_table_floats": (_I64, [_I64, _I64, _I64]),
-    "btq_compress_pack": (_I, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
-    "btq_decompress_reduce": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "btq_compress_pack": (_I, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _P, _P]),
+    "btq_decompress_reduce": (_I, [_P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "btq_packed_row_bytes": (_I64, [_I64, _I64]),
+    "btq_packed_pitch": (_I64, [_I64, _I64]),
     "btq_status_str": (_c.c_char_p, [_I]),
     "btq_version": (_c.c_char_p, []),
 }

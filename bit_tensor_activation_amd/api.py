@@ -13,7 +13,9 @@ Layouts (contiguous, row-major, last index fastest):
   outlier_idx int32 [k];  fmap int32 [H];  cmap int32 [H-k]
   enc_table   float32 [P,H-k,2]  (rscale, zero point) per int4 slot
   dec_table   float32 [2P+1,H-k] scale rows, zero-point rows, constant row
-  packed      uint8 [P,T,ceil((H-k)/2)];  outliers int16 [P,T,k]
+  packed      uint8 [P,T,pitch]: ceil((H-k)/2) code bytes per row, then zeros;
+              pitch defaults to btq_packed_pitch(H,k) (a multiple of 128)
+  outliers    int16 [P,T,k]
   y           float32 [T,H]
 """
 from __future__ import annotations
@@ -61,6 +63,13 @@ def _device(x: torch.Tensor) -> torch.device:
 
 def btq_packed_row_bytes(H: int, k: int) -> int:
     n = _lib.load().btq_packed_row_bytes(H, k)
+    if n < 0:
+        raise ValueError(f"invalid H={H}, k={k}")
+    return int(n)
+
+
+def btq_packed_pitch(H: int, k: int) -> int:
+    n = _lib.load().btq_packed_pitch(H, k)
     if n < 0:
         raise ValueError(f"invalid H={H}, k={k}")
     return int(n)
@@ -146,24 +155,32 @@ def btq_select_outliers(run_min: torch.Tensor, run_max: torch.Tensor, k: int, ou
 def btq_compress_pack(x: torch.Tensor, k: int, enc_table: torch.Tensor,
                       outlier_idx: torch.Tensor, cmap: torch.Tensor,
                       packed: Optional[torch.Tensor] = None,
-                      outliers: Optional[torch.Tensor] = None, stream=None):
-    """Sender message of every shard: (packed uint8 [P,T,Bq], outliers int16 [P,T,k])."""
+                      outliers: Optional[torch.Tensor] = None, pitch: Optional[int] = None,
+                      stream=None):
+    """Sender message of every shard: (packed uint8 [P,T,pitch], outliers int16 [P,T,k]).
+
+    The row pitch is packed.shape[2] when `packed` is given, else `pitch`,
+    else btq_packed_pitch(H, k).
+    """
     dev = _device(x)
     P, T, H = x.shape
     _need(x, "x", _BF16, (P, T, H), dev)
-    Bq = btq_packed_row_bytes(H, k)
+    if packed is not None:
+        pitch = packed.shape[2] if packed.dim() == 3 else -1
+    elif pitch is None:
+        pitch = btq_packed_pitch(H, k)
     _need(enc_table, "enc_table", (torch.float32,), (P, H - k, 2), dev)
     _need(outlier_idx, "outlier_idx", (torch.int32,), (k,), dev)
     _need(cmap, "cmap", (torch.int32,), (H - k,), dev)
     if packed is None:
-        packed = torch.empty((P, T, Bq), dtype=torch.uint8, device=dev)
+        packed = torch.empty((P, T, pitch), dtype=torch.uint8, device=dev)
     if outliers is None:
         outliers = torch.empty((P, T, k), dtype=torch.int16, device=dev)
-    _need(packed, "packed", (torch.uint8,), (P, T, Bq), dev)
+    _need(packed, "packed", (torch.uint8,), (P, T, pitch), dev)
     _need(outliers, "outliers", _BF16, (P, T, k), dev)
     lib = _lib.load()
     st = lib.btq_compress_pack(_ptr(_bits(x)), P, T, H, k, _ptr(enc_table), _ptr(outlier_idx),
-                               _ptr(cmap), _ptr(packed), _ptr(_bits(outliers)),
+                               _ptr(cmap), _ptr(packed), pitch, _ptr(_bits(outliers)),
                                _stream(dev, stream))
     _lib.check(st, "btq_compress_pack")
     return packed, outliers
@@ -172,13 +189,17 @@ def btq_compress_pack(x: torch.Tensor, k: int, enc_table: torch.Tensor,
 def btq_decompress_reduce(packed: torch.Tensor, outliers: torch.Tensor, H: int,
                           dec_table: torch.Tensor, outlier_idx: torch.Tensor, cmap: torch.Tensor,
                           y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Receiver: y float32 [T,H] = sum over shards of the dequantized messages."""
+    """Receiver: y float32 [T,H] = sum over shards of the dequantized messages.
+
+    packed is uint8 [P,T,pitch]; its rows' first btq_packed_row_bytes(H,k)
+    bytes are read.
+    """
     dev = _device(packed)
-    P, T, Bq = packed.shape
+    P, T, pitch = packed.shape
     k = outliers.shape[2]
-    if Bq != btq_packed_row_bytes(H, k):
-        raise ValueError(f"packed rows of {Bq} bytes do not match H={H}, k={k}")
-    _need(packed, "packed", (torch.uint8,), (P, T, Bq), dev)
+    if pitch < btq_packed_row_bytes(H, k):
+        raise ValueError(f"packed rows of {pitch} bytes are shorter than H={H}, k={k} needs")
+    _need(packed, "packed", (torch.uint8,), (P, T, pitch), dev)
     _need(outliers, "outliers", _BF16, (P, T, k), dev)
     _need(dec_table, "dec_table", (torch.float32,), (2 * P + 1, H - k), dev)
     _need(outlier_idx, "outlier_idx", (torch.int32,), (k,), dev)
@@ -187,7 +208,7 @@ def btq_decompress_reduce(packed: torch.Tensor, outliers: torch.Tensor, H: int,
         y = torch.empty((T, H), dtype=torch.float32, device=dev)
     _need(y, "y", (torch.float32,), (T, H), dev)
     lib = _lib.load()
-    st = lib.btq_decompress_reduce(_ptr(packed), _ptr(_bits(outliers)), P, T, H, k,
+    st = lib.btq_decompress_reduce(_ptr(packed), pitch, _ptr(_bits(outliers)), P, T, H, k,
                                    _ptr(dec_table), _ptr(outlier_idx), _ptr(cmap), _ptr(y),
                                    _stream(dev, stream))
     _lib.check(st, "btq_decompress_reduce")

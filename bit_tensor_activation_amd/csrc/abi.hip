@@ -25,6 +25,13 @@ int check_k(int64_t H, int64_t k) { return (k < 0 || k > H) ? BTQ_ERR_SHAPE : BT
 
 int hip_status(hipError_t e) { return e == hipSuccess ? BTQ_OK : BTQ_ERR_HIP; }
 
+// Packed row pitch: at least the row's code bytes, and P*T*pitch < 2^62.
+int check_pitch(int64_t P, int64_t T, int64_t H, int64_t k, int64_t pitch) {
+  if (pitch < (H - k + 1) / 2 || pitch > kMaxElems) return BTQ_ERR_SHAPE;
+  if (T > 0 && pitch > 0 && T > kMaxElems / (P * pitch)) return BTQ_ERR_SHAPE;
+  return BTQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -32,6 +39,11 @@ extern "C" {
 int64_t btq_packed_row_bytes(int64_t H, int64_t k) {
   if (H < 1 || k < 0 || k > H) return -1;
   return (H - k + 1) / 2;
+}
+
+int64_t btq_packed_pitch(int64_t H, int64_t k) {
+  const int64_t b = btq_packed_row_bytes(H, k);
+  return b < 0 ? -1 : (b + 127) / 128 * 128;
 }
 
 size_t btq_calib_workspace_bytes(int64_t P, int64_t T, int64_t H) {
@@ -99,10 +111,12 @@ int btq_select_outliers(const float* run_min, const float* run_max, int64_t P, i
 
 int btq_compress_pack(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
                       const float* enc_table, const int32_t* outlier_idx, const int32_t* cmap,
-                      uint8_t* packed, uint16_t* outliers, void* stream) {
+                      uint8_t* packed, int64_t packed_pitch, uint16_t* outliers, void* stream) {
   int st = check_dims(P, T, H, 0);
   if (st != BTQ_OK) return st;
   st = check_k(H, k);
+  if (st != BTQ_OK) return st;
+  st = check_pitch(P, T, H, k, packed_pitch);
   if (st != BTQ_OK) return st;
   if ((k > 0 && !outlier_idx) || (k < H && (!cmap || !enc_table))) return BTQ_ERR_ARG;
   if (T > 0 && (!x || (k < H && !packed) || (k > 0 && !outliers))) return BTQ_ERR_ARG;
@@ -111,16 +125,18 @@ int btq_compress_pack(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_
     return BTQ_ERR_ALIGN;
   if (T == 0) return BTQ_OK;
   return hip_status(btq::launch_compress(x, P, T, H, k, enc_table, outlier_idx, cmap, packed,
-                                         outliers, (hipStream_t)stream));
+                                         packed_pitch, outliers, (hipStream_t)stream));
 }
 
-int btq_decompress_reduce(const uint8_t* packed, const uint16_t* outliers, int64_t P, int64_t T,
-                          int64_t H, int64_t k, const float* dec_table,
+int btq_decompress_reduce(const uint8_t* packed, int64_t packed_pitch, const uint16_t* outliers,
+                          int64_t P, int64_t T, int64_t H, int64_t k, const float* dec_table,
                           const int32_t* outlier_idx, const int32_t* cmap, float* y,
                           void* stream) {
   int st = check_dims(P, T, H, 0);
   if (st != BTQ_OK) return st;
   st = check_k(H, k);
+  if (st != BTQ_OK) return st;
+  st = check_pitch(P, T, H, k, packed_pitch);
   if (st != BTQ_OK) return st;
   if ((k > 0 && !outlier_idx) || (k < H && (!cmap || !dec_table))) return BTQ_ERR_ARG;
   if (T > 0 && (!y || (k < H && !packed) || (k > 0 && !outliers))) return BTQ_ERR_ARG;
@@ -128,8 +144,8 @@ int btq_decompress_reduce(const uint8_t* packed, const uint16_t* outliers, int64
       !aligned(cmap, 4) || !aligned(y, 4))
     return BTQ_ERR_ALIGN;
   if (T == 0) return BTQ_OK;
-  return hip_status(btq::launch_decompress(packed, outliers, P, T, H, k, dec_table, outlier_idx,
-                                           cmap, y, (hipStream_t)stream));
+  return hip_status(btq::launch_decompress(packed, packed_pitch, outliers, P, T, H, k, dec_table,
+                                           outlier_idx, cmap, y, (hipStream_t)stream));
 }
 
 const char* btq_status_str(int status) {

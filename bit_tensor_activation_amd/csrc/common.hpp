@@ -33,6 +33,21 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Keeps the scheduler from moving instructions across this point. The fast
+// kernels issue their setup loads first and their token-row loads second: the
+// vector-memory counter retires in issue order, so a wait for a setup load
+// then never includes the row loads behind it.
+__device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Marks a register as redefined here (an empty asm that reads and writes it).
+// The fast kernels apply it to the per-lane constants that come straight from
+// setup loads, once, before their main loop: the completion wait then happens
+// there, and the loop body never has to wait for a setup load again.
+template <typename V>
+__device__ __forceinline__ void settle(V& v) {
+  asm volatile("" : "+v"(v));
+}
+
 // Raw buffer resources (gfx9 format). A wave builds a descriptor over the
 // part of a tensor it touches, so every offset stays 32-bit. The hardware
 // range check then handles ragged edges: a load at or past num_records
@@ -116,10 +131,10 @@ hipError_t launch_select(const float* run_min, const float* run_max, int64_t P, 
 
 hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
                            const float* enc, const int32_t* idx, const int32_t* cmap,
-                           uint8_t* packed, uint16_t* outl, hipStream_t s);
+                           uint8_t* packed, int64_t pitch, uint16_t* outl, hipStream_t s);
 
-hipError_t launch_decompress(const uint8_t* packed, const uint16_t* outl, int64_t P, int64_t T,
-                             int64_t H, int64_t k, const float* dec, const int32_t* idx,
+hipError_t launch_decompress(const uint8_t* packed, int64_t pitch, const uint16_t* outl, int64_t P,
+                             int64_t T, int64_t H, int64_t k, const float* dec, const int32_t* idx,
                              const int32_t* cmap, float* y, hipStream_t s);
 
 }  // namespace btq

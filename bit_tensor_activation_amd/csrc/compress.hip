@@ -7,34 +7,42 @@
 // "Combating Quantization Errors with Tensor Parallelism" (each device
 // quantizes its partial sum before the sum).
 //
-// Fast kernel. A wave-tile is 512 int4 slots, 8 per lane, so each lane writes
-// exactly one packed dword per token row. A 256-thread block takes one shard
-// and one wave-tile, and its 4 waves walk 4 separate blocks of token rows.
-// All tiles of one row group run on one XCD (see xcd_unit_block): a token
-// row's packed bytes and BF16 block are written in pieces by all its tiles,
-// and the pieces must merge in one L2.
-//  0. Setup, once per wave. Each lane loads its 8 slots' (rscale, zero point)
-//     pairs from the encoder table, which selection wrote in slot order: 64
-//     contiguous bytes per lane, so a wave reads one contiguous 4 KB block.
-//     No LDS staging and no block barrier: the waves of a block never wait
-//     for each other.
-//  1. Per step of 4 rows, coalesced 16-byte buffer loads bring the tile's
-//     bf16 feature span (plus alignment slack) into a wave-private LDS
-//     buffer. The loads of the next 4 rows are issued before this step's
-//     compute.
+// Tiles. A wave-tile is 512 int4 slots, 8 per lane, so each lane writes
+// exactly one packed dword per token row. The tile also owns the BF16
+// features that fall between its slots (TileGeom). Packed rows sit `pitch`
+// bytes apart; with a pitch that is a multiple of 128 every tile's 256-byte
+// row piece covers whole cache lines, and the lanes past the last slot write
+// the row's zero padding.
+//
+// Ring kernel (the fast path). A 256-thread block takes 4 adjacent tiles of
+// one shard's block of token rows, one wave per tile, so the block reads
+// about 4 KB of each row in one go. All blocks of a row block run on one XCD
+// (xcd_unit_block).
+//  0. Setup, once per wave: the lane's 8 feature indices, its 8 (rscale,
+//     zero point) pairs from the encoder table (64 contiguous bytes, in slot
+//     order) and its BF16 feature index. Then the first kRing token rows are
+//     issued, and only then does the wave wait for the setup values. No LDS
+//     staging of parameters and no block barrier.
+//  1. Each ring row arrives as one 16-byte load per lane (the span's first
+//     64 chunks) plus a narrow tail load for the chunks past 64 (BF16
+//     features and alignment slack). kSub rows at a time are staged in a
+//     wave-private LDS buffer and their slots refilled kRing rows ahead.
 //  2. Each lane gathers its 8 features from LDS at fixed offsets, quantizes
-//     them, packs 8 nibbles into one dword and stores it. The wave's 64
-//     dwords form one coalesced 256-byte store.
+//     them, packs 8 nibbles into one dword and stores it: one coalesced
+//     256-byte store per wave and row.
 //  3. The lanes that own the tile's BF16 features copy their bf16 bits out of
 //     the same LDS buffer.
-// The staging layout pads 4 bytes after every 16-byte chunk. Lane l's
-// features then start at dword 5*l, so one gather instruction spreads over
-// all banks. All global accesses go through per-wave buffer resources:
-// ragged rows, idle lanes and surplus chunks become clamped or out-of-range
-// offsets, not branches.
+// The staging layout pads 4 bytes after every 16-byte chunk, so lane l's
+// features start at dword 5*l and one gather spreads over all banks. All
+// global accesses go through per-wave buffer resources: ragged rows, idle
+// lanes and surplus chunks become clamped or out-of-range offsets, not
+// branches.
+//
+// Staged kernel: the same tiles for spans too wide for the ring's tail load
+// (many BF16 features per tile). A block takes one tile and 4 row blocks.
 //
 // General kernel. One thread per packed byte and per BF16 value. It serves
-// any H, k, alignment and LDS size.
+// any H, k, pitch, alignment and LDS size.
 #include "common.hpp"
 
 namespace btq {
@@ -69,14 +77,14 @@ __device__ __forceinline__ void load_enc(rsrc_t re, bool active, int lane, float
   }
 }
 
-// LDS: 4 waves x kCpRows staging buffers of buf_bytes
+// Staged kernel. LDS: 4 waves x kCpRows staging buffers of buf_bytes.
 template <int kMaxChunks>
 __global__ __launch_bounds__(256) void compress_kernel(
     const uint16_t* __restrict__ x, int64_t T, int H, int Hq, int k, int ntiles,
     int rows_per_wave, int64_t nrowblk, int64_t ngroups, int buf_bytes,
     int64_t P, const float* __restrict__ enc,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cmap,
-    uint8_t* __restrict__ packed, uint16_t* __restrict__ outl) {
+    uint8_t* __restrict__ packed, int pitch, uint16_t* __restrict__ outl) {
   extern __shared__ __align__(16) char smem[];
   // unit = (shard, row group); its ntiles blocks run on one XCD
   int64_t unit, sub;
@@ -96,12 +104,11 @@ __global__ __launch_bounds__(256) void compress_kernel(
   const int64_t t0 = rb * rows_per_wave;
   const int nrows = (int)min(T - t0, (int64_t)rows_per_wave);
   const int64_t row0 = p * T + t0;
-  const int Bq = Hq >> 1;
   char* const buf = smem + (size_t)wave * kCpRows * buf_bytes;
 
   // This wave's rows of x, packed and outliers, as buffer resources.
   const rsrc_t rx = make_rsrc(x + row0 * H, (uint32_t)nrows * (uint32_t)H * 2u);
-  const rsrc_t rp = make_rsrc(packed + row0 * Bq, (uint32_t)nrows * (uint32_t)Bq);
+  const rsrc_t rp = make_rsrc(packed + row0 * pitch, (uint32_t)nrows * (uint32_t)pitch);
   const rsrc_t ro = make_rsrc(outl + row0 * k, (uint32_t)nrows * (uint32_t)k * 2u);
   const rsrc_t rc = make_rsrc(cmap, (uint32_t)Hq * 4u);
 
@@ -146,7 +153,8 @@ __global__ __launch_bounds__(256) void compress_kernel(
   uint32_t ad[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) ad[e] = pad_byte_off((uint32_t)(hh[e] - a0));
-  const uint32_t st_off = active ? (uint32_t)(j0 >> 1) : kOOB;
+  // (lanes past the last slot write the row's zero padding, up to the pitch)
+  const uint32_t st_off = ((j0 >> 1) + 4 <= pitch) ? (uint32_t)(j0 >> 1) : kOOB;
   const int nout_it = (g.nout + kWave - 1) / kWave;   // uniform
   uint32_t oad = 0;
   if (g.nout > 0) oad = pad_byte_off((uint32_t)(idx[g.ilo + min(lane, g.nout - 1)] - a0));
@@ -185,7 +193,8 @@ __global__ __launch_bounds__(256) void compress_kernel(
       uint32_t w = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) w |= quant4(u[r][e], rs[e], zf[e]) << (4 * e);
-      __builtin_amdgcn_raw_buffer_store_b32(w, rp, st_off, (uint32_t)row * (uint32_t)Bq, kStream);
+      w = active ? w : 0u;   // past the last slot: the row's zero padding
+      __builtin_amdgcn_raw_buffer_store_b32(w, rp, st_off, (uint32_t)row * (uint32_t)pitch, kStream);
     }
     for (int it = 0; it < nout_it; ++it) {
       const int i = lane + kWave * it;
@@ -205,14 +214,11 @@ __global__ __launch_bounds__(256) void compress_kernel(
   }
 }
 
-// Ring kernel: the same tiles, with a deeper load pipeline. Each wave keeps
-// kRing token rows in flight in registers, and stages kSub of them at a time
-// through a small LDS buffer. A span's first 64 chunks come in one 16-byte
-// load per lane. The few chunks past 64 (BF16 features inside the tile and
-// alignment slack) come in a narrow tail load of kRemDw dwords per lane.
-// Rows past the wave's last row load and store out of range, so every trip
-// of the loop issues the same memory instructions and the compiler can count
-// exactly which loads it must wait for.
+// Ring kernel. Each wave keeps kRing token rows in flight in registers and
+// stages kSub of them at a time through a small LDS buffer. Rows past the
+// wave's last row load and store out of range, so every trip of the loop
+// issues the same memory instructions and the compiler can count exactly
+// which loads it must wait for.
 constexpr int kRing = 8;   // token rows in flight per wave
 constexpr int kSub = 2;    // token rows staged in LDS per sub-step
 
@@ -225,35 +231,34 @@ constexpr int ring_row_bytes() { return (kWave + 16 * kRemDw) * 20; }
 template <int kRemDw>
 __global__ __launch_bounds__(256) void compress_ring_kernel(
     const uint16_t* __restrict__ x, int64_t T, int H, int Hq, int k, int ntiles,
-    int rows_per_wave, int64_t nrowblk, int64_t ngroups, int64_t P,
+    int rows_per_wave, int64_t nrowblk, int ntgrp, int64_t P,
     const float* __restrict__ enc, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ cmap, uint8_t* __restrict__ packed,
+    const int32_t* __restrict__ cmap, uint8_t* __restrict__ packed, int pitch,
     uint16_t* __restrict__ outl) {
   constexpr int buf_bytes = ring_row_bytes<kRemDw>();
   extern __shared__ __align__(16) char smem[];
-  // unit = (shard, row group); its ntiles blocks run on one XCD
+  // unit = (shard, row block); its ntgrp blocks of 4 adjacent tiles run on
+  // one XCD
   int64_t unit, sub;
-  if (!xcd_unit_block(blockIdx.x, ntiles, P * ngroups, &unit, &sub)) return;
-  const int c = (int)sub;
-  const int64_t rg = unit % ngroups;
-  const int64_t p = unit / ngroups;
-  const TileGeom g = tile_geom(cmap, c, ntiles, Hq, H);
+  if (!xcd_unit_block(blockIdx.x, ntgrp, P * nrowblk, &unit, &sub)) return;
+  const int64_t rb = unit % nrowblk;
+  const int64_t p = unit / nrowblk;
   const int lane = threadIdx.x & (kWave - 1);
   // wave-uniform by construction; readfirstlane lets the compiler keep
   // everything derived from it (rows, descriptors) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t rb = rg * kCpWaves + wave;
-  if (rb >= nrowblk) return;   // no rows for this wave (no block barrier below)
+  const int c = (int)sub * kCpWaves + wave;
+  if (c >= ntiles) return;   // past the last tile (no block barrier below)
+  const TileGeom g = tile_geom(cmap, c, ntiles, Hq, H);
   const int a0 = g.hs & ~7;
   const int nch = (((g.he + 7) & ~7) - a0) >> 3;   // 16-byte chunks in the span
   const int64_t t0 = rb * rows_per_wave;
   const int nrows = (int)min(T - t0, (int64_t)rows_per_wave);
   const int64_t row0 = p * T + t0;
-  const int Bq = Hq >> 1;
   char* const buf = smem + (size_t)wave * kSub * buf_bytes;
 
   const rsrc_t rx = make_rsrc(x + row0 * H, (uint32_t)nrows * (uint32_t)H * 2u);
-  const rsrc_t rp = make_rsrc(packed + row0 * Bq, (uint32_t)nrows * (uint32_t)Bq);
+  const rsrc_t rp = make_rsrc(packed + row0 * pitch, (uint32_t)nrows * (uint32_t)pitch);
   const rsrc_t ro = make_rsrc(outl + row0 * k, (uint32_t)nrows * (uint32_t)k * 2u);
   const rsrc_t rc = make_rsrc(cmap, (uint32_t)Hq * 4u);
 
@@ -307,19 +312,37 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
   // (c) the ring: the first kRing rows. Unconditional: a branch around it
   // would make the compiler assume at the join that these loads might not
   // exist, and wait for the ring when it waits for the setup loads.
+  // (one fence per row keeps the rows in issue order: the loop consumes
+  // them oldest first)
+  issue_fence();
 #pragma unroll
-  for (int q = 0; q < kRing; ++q) load(q, q);
+  for (int q = 0; q < kRing; ++q) {
+    load(q, q);
+    issue_fence();
+  }
 
   const int hh[8] = {(int)hA[0], (int)hA[1], (int)hA[2], (int)hA[3],
                      (int)hB[0], (int)hB[1], (int)hB[2], (int)hB[3]};
   uint32_t ad[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ad[e] = pad_byte_off((uint32_t)(hh[e] - a0));
-  const uint32_t st_off = active ? (uint32_t)(j0 >> 1) : kOOB;
-  const uint32_t oad = (g.nout > 0) ? pad_byte_off((uint32_t)((int)oh - a0)) : 0u;
+  for (int e = 0; e < 8; ++e) {
+    ad[e] = pad_byte_off((uint32_t)(hh[e] - a0));
+    settle(rs[e]);
+    settle(zf[e]);
+  }
+  // (lanes past the last slot write the row's zero padding, up to the pitch)
+  const uint32_t st_off = ((j0 >> 1) + 4 <= pitch) ? (uint32_t)(j0 >> 1) : kOOB;
+  // (used unconditionally: a load whose only use sits under a branch gets
+  // sunk below the ring prologue, and its wait would then drain the ring;
+  // with no BF16 feature oh reads 0 and the clamp keeps the offset in range)
+  const uint32_t oad = pad_byte_off((uint32_t)max((int)oh - a0, 0));
   const uint32_t o_off = (lane < g.nout) ? (uint32_t)(g.ilo + lane) * 2u : kOOB;
 
-  for (int base = 0; base < nrows; base += kRing) {
+  // nrows >= 1 here. The do-while has no entry guard: a guarded loop lets the
+  // compiler sink the prologue loads below the guard, past the point where
+  // the setup registers settle.
+  int base = 0;
+  do {
 #pragma unroll
     for (int sb = 0; sb < kRing / kSub; ++sb) {
       // stage kSub rows (the main chunk of lanes past the span lands in
@@ -361,7 +384,8 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
         uint32_t w = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) w |= quant4(u[r][e], rs[e], zf[e]) << (4 * e);
-        __builtin_amdgcn_raw_buffer_store_b32(w, rp, ok ? st_off : kOOB, rr * (uint32_t)Bq,
+        w = active ? w : 0u;   // past the last slot: the row's zero padding
+        __builtin_amdgcn_raw_buffer_store_b32(w, rp, ok ? st_off : kOOB, rr * (uint32_t)pitch,
                                               kStream);
         const uint16_t b16 = *reinterpret_cast<const uint16_t*>(buf + r * buf_bytes + oad);
         __builtin_amdgcn_raw_buffer_store_b16(b16, ro, ok ? o_off : kOOB, rr * (uint32_t)k * 2u, 0);
@@ -375,25 +399,29 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
       }
       wave_lds_sync();
     }
-  }
+    base += kRing;
+  } while (base < nrows);
 }
 
 __global__ __launch_bounds__(256) void compress_general_kernel(
     const uint16_t* __restrict__ x, int64_t P, int64_t T, int64_t H, int64_t k, int64_t Hq,
     int64_t Bq, const float* __restrict__ enc, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ cmap, uint8_t* __restrict__ packed,
+    const int32_t* __restrict__ cmap, uint8_t* __restrict__ packed, int64_t pitch,
     uint16_t* __restrict__ outl) {
-  const int64_t n1 = P * T * Bq;
+  const int64_t n1 = P * T * pitch;
   const int64_t n2 = P * T * k;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n1 + n2; i += stride) {
     if (i < n1) {
-      const int64_t row = i / Bq, byte = i % Bq;
+      const int64_t row = i / pitch, byte = i % pitch;
       const int64_t p = row / T;
       const int64_t j = 2 * byte;
-      const float* e = enc + (p * Hq + j) * 2;   // (rscale, zero point) of slot j
-      uint32_t q = quant4(x[row * H + cmap[j]], e[0], e[1]);
-      if (j + 1 < Hq) q |= quant4(x[row * H + cmap[j + 1]], e[2], e[3]) << 4;
+      uint32_t q = 0;   // padding bytes past the codes stay zero
+      if (byte < Bq) {
+        const float* e = enc + (p * Hq + j) * 2;   // (rscale, zero point) of slot j
+        q = quant4(x[row * H + cmap[j]], e[0], e[1]);
+        if (j + 1 < Hq) q |= quant4(x[row * H + cmap[j + 1]], e[2], e[3]) << 4;
+      }
       packed[i] = (uint8_t)q;
     } else {
       const int64_t ii = i - n1;
@@ -415,9 +443,10 @@ static int pick_rows_per_wave(int64_t tile_waves, int64_t T) {
 
 hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
                            const float* enc, const int32_t* idx, const int32_t* cmap,
-                           uint8_t* packed, uint16_t* outl, hipStream_t s) {
+                           uint8_t* packed, int64_t pitch, uint16_t* outl, hipStream_t s) {
   const int64_t Hq = H - k;
   const int64_t Bq = (Hq + 1) / 2;
+  const int64_t ntiles64 = (Hq + kTileSlots - 1) / kTileSlots;
   // A tile's feature span holds its 512 slots plus the BF16 features between
   // them: at most min(H, 512 + k) features. Staging adds 14 of alignment slack.
   const int64_t span = (H < kTileSlots + k ? H : kTileSlots + k);
@@ -428,7 +457,10 @@ hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, i
   // H < 2^24 keeps them below 2^31 bytes.
   const bool fast = Hq > 0 && H % 8 == 0 && Hq % 8 == 0 && H < (int64_t(1) << 24) &&
                     (uintptr_t)x % 16 == 0 && (uintptr_t)packed % 4 == 0 &&
-                    (uintptr_t)enc % 16 == 0 && nch_max <= 4 * kWave && lds <= 65536;
+                    (uintptr_t)enc % 16 == 0 && nch_max <= 4 * kWave && lds <= 65536 &&
+                    // the pitch: dword stores, and the lanes of the last
+                    // tile reach every padding byte
+                    pitch % 4 == 0 && pitch <= ntiles64 * (kTileSlots / 2);
   // Ring kernel: span chunks past 64 must fit the tail load (16 chunks per
   // tail dword per lane).
   const int64_t tail = nch_max > kWave ? nch_max - kWave : 0;
@@ -444,12 +476,12 @@ hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, i
     if (rpw64 > 64) rpw64 = 64;
     const int rpw = (int)rpw64;
     const int64_t nrowblk = (T + rpw - 1) / rpw;
-    const int64_t ngroups = (nrowblk + kCpWaves - 1) / kCpWaves;
-    const unsigned blocks = (unsigned)xcd_grid(ntiles, P * ngroups);
+    const int ntgrp = (ntiles + kCpWaves - 1) / kCpWaves;
+    const unsigned blocks = (unsigned)xcd_grid(ntgrp, P * nrowblk);
 #define BTQ_RING(n)                                                                               \
   compress_ring_kernel<n><<<blocks, 256, ring_lds, s>>>(x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, \
-                                                        nrowblk, ngroups, P, enc, idx, cmap,        \
-                                                        packed, outl)
+                                                        nrowblk, ntgrp, P, enc, idx, cmap, packed,  \
+                                                        (int)pitch, outl)
     switch (rem_dw) {
       case 0: BTQ_RING(0); break;
       case 1: BTQ_RING(1); break;
@@ -468,19 +500,19 @@ hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, i
     if (nch_max <= 2 * kWave)
       compress_kernel<2><<<(unsigned)blocks, 256, lds, s>>>(
           x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, ngroups, buf_bytes, P, enc, idx,
-          cmap, packed, outl);
+          cmap, packed, (int)pitch, outl);
     else
       compress_kernel<4><<<(unsigned)blocks, 256, lds, s>>>(
           x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, ngroups, buf_bytes, P, enc, idx,
-          cmap, packed, outl);
+          cmap, packed, (int)pitch, outl);
     return hipGetLastError();
   }
-  const int64_t n = P * T * (Bq + k);
+  const int64_t n = P * T * (pitch + k);
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
   compress_general_kernel<<<(unsigned)blocks, 256, 0, s>>>(x, P, T, H, k, Hq, Bq, enc, idx, cmap,
-                                                           packed, outl);
+                                                           packed, pitch, outl);
   return hipGetLastError();
 }
 

@@ -6,33 +6,37 @@
 // devices' values are summed).
 //
 // Fast kernel, specialised on the shard count (1..8). A wave-tile is the
-// sender's 512 int4 slots, 8 per lane. A 256-thread block takes one tile,
-// and its 4 waves walk 4 separate blocks of token rows. All tiles of one row
-// group run on one XCD, so the partial cache lines of y written at tile
-// boundaries merge in one L2.
-//  0. Setup, once per wave. Each lane loads its 8 slots' scales for every
-//     shard and their constant -sum_p z*s, which seeds the accumulator, from
-//     the decoder table that selection wrote in slot order (32 contiguous
-//     bytes per row of the table). Then it issues its first kDqRing token
-//     rows. No LDS staging and no block barrier.
+// sender's 512 int4 slots, 8 per lane. A 256-thread block takes 4 adjacent
+// tiles of one block of token rows, one wave per tile; all blocks of a row
+// block run on one XCD, so the partial cache lines of y at tile boundaries
+// merge in one L2.
+//  0. Setup, once per wave: the lane's 8 slots' scales for every shard and
+//     their constant -sum_p z*s (which seeds the accumulator) from the
+//     decoder table, in slot order (32 contiguous bytes per table row); the
+//     lane's 8 feature indices; its BF16 feature index. Then the first
+//     kDqRing rows are issued, and only then does the wave wait for the setup
+//     values. No LDS staging of parameters and no block barrier.
 //  1. Per token row, each lane holds one packed dword per shard, so each
 //     packed byte is read from HBM exactly once, in coalesced 256-byte wave
-//     loads. The tile's BF16 values of all shards fill one or two registers
-//     across the wave, one lane per (shard, feature). A ring of kDqRing rows
-//     stays in flight, and consumed slots reload kDqRing rows ahead.
+//     loads. The tile's BF16 values of all shards fill kOR registers across
+//     the wave, one lane per (shard, feature). A ring of kDqRing rows stays
+//     in flight, and consumed slots reload kDqRing rows ahead.
 //  2. A low nibble converts with one byte-to-float instruction. A high nibble
 //     is masked in place (16*q) and meets a scale pre-divided by 16, which is
 //     exact. Each term is one fma. For a BF16 feature, the lane that owns it
 //     fetches its shards' values across lanes (ds_bpermute) and adds them in
-//     shard order from 0.
+//     shard order from 0. A tile with more BF16 values than kOR registers
+//     hold sums them after the row loop instead.
 //  3. The outputs scatter to their feature positions in a wave-private LDS
-//     row, padded one dword per 8 so the scatter avoids bank conflicts. The
-//     wave then writes the tile's contiguous y span with coalesced stores.
+//     row. The wave then writes the tile's span of y with 16-byte stores
+//     (whole aligned chunks) and one dword store for the at most 6 ragged
+//     features at its ends.
 //
 // General kernel: one thread per (token, slot) and per (token, BF16 feature).
 // It evaluates term = fl(q - z) * s and adds the terms in shard order, for
-// any P, H, k and alignment. Both read the decoder table [2P+1, Hq]: rows
-// 0..P-1 scale, rows P..2P-1 zero point, row 2P the per-slot constant.
+// any P, H, k, pitch and alignment. Both kernels read the decoder table
+// [2P+1, Hq]: rows 0..P-1 scale, rows P..2P-1 zero point, row 2P the
+// per-slot constant.
 #include "common.hpp"
 
 namespace btq {
@@ -40,53 +44,66 @@ namespace btq {
 constexpr int kDqWaves = 4;
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint32_t pad_dword(uint32_t i) { return i + (i >> 3); }
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kDqRing = 8;   // token rows in flight per wave
 constexpr int kDqSub = 2;    // token rows per sub-step (LDS y rows)
-constexpr int kOutRegs = 2;  // BF16-block registers per row: covers P*nout <= 128
 
-// LDS: 4 waves x kDqSub y rows of buf_dwords
-template <int NP>
+// LDS y row: position i of the row's span (relative to the 16-byte aligned
+// feature a4 <= hs) lives at dword cpad(i). Four dwords of padding per 32
+// keep each 16-byte chunk contiguous and aligned for the wide reads, and
+// spread the lanes' stride-8 scatter over 8 banks per element.
+__device__ __forceinline__ uint32_t cpad(uint32_t i) { return i + ((i >> 5) << 2); }
+
+// Dwords per LDS y row for spans of up to `span` features: the padded span
+// plus one private dummy dword per lane (idle lanes write there, so no two
+// lanes ever store to one address).
+__host__ __device__ constexpr int dq_row_dwords(int span) {
+  return ((span + 3 + 31) / 32 * 32) * 9 / 8 + kWave;
+}
+
+// LDS: 4 waves x kDqSub y rows of buf_dwords.
+// NP: shards. kOR: BF16 registers per row; a tile whose NP*nout BF16 values
+// fit in kOR*64 lanes sums them in the ring, a wider tile in a pass after it.
+template <int NP, int kOR>
 __global__ __launch_bounds__(256) void decompress_kernel(
-    const uint8_t* __restrict__ packed, const uint16_t* __restrict__ outl, int64_t T, int H,
-    int Hq, int k, int ntiles, int rows_per_wave, int64_t nrowblk, int buf_dwords,
+    const uint8_t* __restrict__ packed, int pitch, const uint16_t* __restrict__ outl, int64_t T,
+    int H, int Hq, int k, int ntiles, int rows_per_wave, int64_t nrowblk, int buf_dwords,
     const float* __restrict__ dec, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ cmap, float* __restrict__ y) {
   extern __shared__ __align__(16) char smem[];
-  // unit = row group; its ntiles blocks run on one XCD
-  int64_t rg, sub;
-  if (!xcd_unit_block(blockIdx.x, ntiles, (nrowblk + kDqWaves - 1) / kDqWaves, &rg, &sub)) return;
-  const int c = (int)sub;
-  const TileGeom g = tile_geom(cmap, c, ntiles, Hq, H);
-  const int L = g.he - g.hs;
+  // unit = row block; its blocks of 4 adjacent tiles run on one XCD
+  int64_t rb, sub;
+  const int ntgrp = (ntiles + kDqWaves - 1) / kDqWaves;
+  if (!xcd_unit_block(blockIdx.x, ntgrp, nrowblk, &rb, &sub)) return;
   const int lane = threadIdx.x & (kWave - 1);
   // wave-uniform by construction; readfirstlane lets the compiler keep
   // everything derived from it (rows, descriptors) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t rb = rg * kDqWaves + wave;
-  if (rb >= nrowblk) return;   // no rows for this wave (no block barrier below)
+  const int c = (int)sub * kDqWaves + wave;
+  if (c >= ntiles) return;   // past the last tile (no block barrier below)
+  const TileGeom g = tile_geom(cmap, c, ntiles, Hq, H);
   const int64_t t0 = rb * rows_per_wave;
-  const int nrows = (int)min(T - t0, (int64_t)rows_per_wave);
-  const int Bq = Hq >> 1;
+  const int nrows = (int)min(T - t0, (int64_t)rows_per_wave);   // >= 1
   float* const buf = reinterpret_cast<float*>(smem) + (size_t)wave * kDqSub * buf_dwords;
+  const uint32_t dummy = (uint32_t)(buf_dwords - kWave + lane);
 
   // Whole message tensors (the launcher checks they span < 2^31 bytes), and
   // this wave's rows of y.
-  const rsrc_t rp = make_rsrc(packed, (uint32_t)(NP * T * (int64_t)Bq));
+  const rsrc_t rp = make_rsrc(packed, (uint32_t)(NP * T * (int64_t)pitch));
   const rsrc_t ro = make_rsrc(outl, (uint32_t)(NP * T * (int64_t)k * 2));
   const rsrc_t ry = make_rsrc(y + t0 * H, (uint32_t)nrows * (uint32_t)H * 4u);
   const rsrc_t rc = make_rsrc(cmap, (uint32_t)Hq * 4u);
+  const rsrc_t ri = make_rsrc(idx, (uint32_t)k * 4u);
 
   const int j0 = g.jstart + kLaneSlots * lane;
   const bool active = j0 < g.jend;
   const uint32_t pk_off = active ? (uint32_t)(j0 >> 1) : kOOB;
   // BF16 block: entry e = r*64 + lane holds shard e / nout, feature e % nout
-  const bool compact = NP * g.nout <= kOutRegs * kWave;   // uniform
-  uint32_t o_off[kOutRegs];
+  const bool compact = NP * g.nout <= kOR * kWave;   // uniform
+  uint32_t o_off[kOR];
 #pragma unroll
-  for (int r = 0; r < kOutRegs; ++r) {
+  for (int r = 0; r < kOR; ++r) {
     const int e = r * kWave + lane;
     o_off[r] = kOOB;
     if (g.nout > 0 && compact && e < NP * g.nout) {
@@ -95,7 +112,7 @@ __global__ __launch_bounds__(256) void decompress_kernel(
     }
   }
 
-  uint32_t w[kDqRing][NP], ov[kDqRing][kOutRegs];
+  uint32_t w[kDqRing][NP], ov[kDqRing][kOR];
   // The lane's offsets stay in fixed VGPRs; the (shard, row) offset is
   // uniform and rides in the instruction's SGPR offset.
   auto load = [&](int q, int row) {
@@ -103,10 +120,10 @@ __global__ __launch_bounds__(256) void decompress_kernel(
     const int64_t rowg = t0 + min(row, nrows - 1);
 #pragma unroll
     for (int p = 0; p < NP; ++p)
-      w[q][p] = __builtin_amdgcn_raw_buffer_load_b32(rp, ok ? pk_off : kOOB,
-                                                     (uint32_t)(((int64_t)p * T + rowg) * Bq), kStream);
+      w[q][p] = __builtin_amdgcn_raw_buffer_load_b32(
+          rp, ok ? pk_off : kOOB, (uint32_t)(((int64_t)p * T + rowg) * pitch), kStream);
 #pragma unroll
-    for (int r = 0; r < kOutRegs; ++r)
+    for (int r = 0; r < kOR; ++r)
       ov[q][r] = __builtin_amdgcn_raw_buffer_load_b16(ro, ok ? o_off[r] : kOOB,
                                                       (uint32_t)(rowg * k * 2), 0);
   };
@@ -129,44 +146,71 @@ __global__ __launch_bounds__(256) void decompress_kernel(
   const int jj = active ? j0 : g.jstart;
   const v4u hA = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)jj * 4u, 0, 0);
   const v4u hB = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)jj * 4u + 16u, 0, 0);
-  const rsrc_t ri_ = make_rsrc(idx, (uint32_t)k * 4u);
   const bool own_out = lane < g.nout;
-  const uint32_t oh = __builtin_amdgcn_raw_buffer_load_b32(
-      ri_, own_out ? (uint32_t)(g.ilo + lane) * 4u : kOOB, 0, 0);
+  const uint32_t oh =
+      __builtin_amdgcn_raw_buffer_load_b32(ri, own_out ? (uint32_t)(g.ilo + lane) * 4u : kOOB, 0, 0);
   // (c) the ring: the first kDqRing rows. Unconditional: a branch around it
   // would make the compiler assume at the join that these loads might not
   // exist, and wait for the ring when it waits for the setup loads.
+  // (one fence per row keeps the rows in issue order: the loop consumes
+  // them oldest first)
+  issue_fence();
 #pragma unroll
-  for (int q = 0; q < kDqRing; ++q) load(q, q);
+  for (int q = 0; q < kDqRing; ++q) {
+    load(q, q);
+    issue_fence();
+  }
 
+  // Per-lane constants, settled once (their loads are older than the ring).
+  const int a4 = g.hs & ~3;   // first feature of the span's first 16-byte chunk of y
   const int hh[8] = {(int)hA[0], (int)hA[1], (int)hA[2], (int)hA[3],
                      (int)hB[0], (int)hB[1], (int)hB[2], (int)hB[3]};
   float sc[NP][8], bias[8];
   uint32_t ya[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    ya[e] = pad_dword((uint32_t)(hh[e] - g.hs));
+    ya[e] = active ? cpad((uint32_t)(hh[e] - a4)) : dummy;
     bias[e] = __uint_as_float(bv[e >> 2][e & 3]);
+    settle(bias[e]);
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const float s = __uint_as_float(sv[p][e >> 2][e & 3]);
       sc[p][e] = (e & 1) ? s * 0.0625f : s;   // high nibbles arrive as 16*q
+      settle(sc[p][e]);
     }
   }
-  const uint32_t oa = own_out ? pad_dword((uint32_t)((int)oh - g.hs)) : 0u;
+  // (a lane that owns no BF16 feature reads oh = 0; the clamp keeps its
+  // unused address in range, and its write goes to its dummy dword)
+  const uint32_t oa = own_out ? cpad((uint32_t)max((int)oh - a4, 0)) : dummy;
   // Lane i < nout owns BF16 feature ilo+i: its shard p value sits in entry
   // p*nout + i, i.e. register (entry / 64) of lane (entry % 64).
-  int src_addr[NP];
-  bool src_hi[NP];
+  int src_addr[NP], src_reg[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int e = p * g.nout + (own_out ? lane : 0);
     src_addr[p] = (e & (kWave - 1)) * 4;
-    src_hi[p] = e >= kWave;
+    src_reg[p] = min(e >> 6, kOR - 1);
   }
-  const int st_it = (L + kWave - 1) / kWave;   // uniform
+  // y stores: whole 16-byte chunks q_lo..q_hi-1 of the span, plus at most 3
+  // ragged features at each end (lanes 0-2 and 3-5), one dword each.
+  const int q_lo = (g.hs - a4 + 3) >> 2;
+  const int q_hi = max((g.he - a4) >> 2, q_lo);
+  const int st_it = (q_hi - q_lo + kWave - 1) / kWave;   // uniform
+  int bpos = -1;
+  if (lane < 3) {
+    const int h = g.hs + lane;
+    if (h < min(a4 + 4 * q_lo, g.he)) bpos = h;
+  } else if (lane < 6) {
+    const int h = a4 + 4 * q_hi + (lane - 3);
+    if (h < g.he) bpos = h;
+  }
+  const uint32_t b_lds = cpad((uint32_t)(max(bpos, g.hs) - a4));
+  const uint32_t b_off = bpos >= 0 ? (uint32_t)bpos * 4u : kOOB;
 
-  for (int base = 0; base < nrows; base += kDqRing) {
+  // nrows >= 1: a do-while has no entry guard that the ring loads could be
+  // sunk below.
+  int base = 0;
+  do {
 #pragma unroll
     for (int sb = 0; sb < kDqRing / kDqSub; ++sb) {
 #pragma unroll
@@ -187,35 +231,21 @@ __global__ __launch_bounds__(256) void decompress_kernel(
                 fmaf((float)((hi >> (8 * bb)) & 0xFFu), sc[p][2 * bb + 1], acc[2 * bb + 1]);
           }
         }
-        // idle lanes skip their LDS writes: many lanes storing to one address
-        // serialize on its bank
-        if (active) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) b[ya[e]] = acc[e];
-        }
-        if (g.nout > 0) {   // uniform
-          const int row = base + q;
-          if (compact) {
-            float o = 0.0f;
+        for (int e = 0; e < 8; ++e) b[ya[e]] = acc[e];
+        if (compact && g.nout > 0) {   // uniform
+          float o = 0.0f;
 #pragma unroll
-            for (int p = 0; p < NP; ++p) {
-              const int v0 = __builtin_amdgcn_ds_bpermute(src_addr[p], (int)ov[q][0]);
-              const int v1 = __builtin_amdgcn_ds_bpermute(src_addr[p], (int)ov[q][1]);
-              o = __fadd_rn(o, bf16_to_f32((uint32_t)(src_hi[p] ? v1 : v0) & 0xFFFFu));
+          for (int p = 0; p < NP; ++p) {
+            int v = 0;
+#pragma unroll
+            for (int rr = 0; rr < kOR; ++rr) {
+              const int t = __builtin_amdgcn_ds_bpermute(src_addr[p], (int)ov[q][rr]);
+              v = (src_reg[p] == rr) ? t : v;
             }
-            if (own_out) b[oa] = o;
-          } else {
-            // many BF16 features in this tile: sum them straight from memory
-            const int64_t rowg = t0 + min(row, nrows - 1);
-            for (int i = lane; i < g.nout; i += kWave) {
-              float o = 0.0f;
-              for (int p = 0; p < NP; ++p)
-                o = __fadd_rn(o, bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
-                                     ro, (uint32_t)(((int64_t)p * T * k + g.ilo + i) * 2),
-                                     (uint32_t)(rowg * k * 2), 0)));
-              b[pad_dword((uint32_t)(idx[g.ilo + i] - g.hs))] = o;
-            }
+            o = __fadd_rn(o, bf16_to_f32((uint32_t)v & 0xFFFFu));
           }
+          b[oa] = o;
         }
       }
       // refill the consumed slots with the rows kDqRing ahead
@@ -228,28 +258,49 @@ __global__ __launch_bounds__(256) void decompress_kernel(
         const bool ok = row < nrows;   // uniform
         const float* b = buf + r * buf_dwords;
         const uint32_t rowoff = (uint32_t)min(row, nrows - 1) * (uint32_t)H * 4u;
-        // batches of 4: LDS reads first, then the stores
-        for (int it0 = 0; it0 < st_it; it0 += 4) {
-          float v[4];
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq)
-            v[qq] = b[pad_dword((uint32_t)min(lane + kWave * (it0 + qq), L - 1))];
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const int i = lane + kWave * (it0 + qq);
-            const uint32_t off = (ok && i < L) ? (uint32_t)(g.hs + i) * 4u : kOOB;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[qq]), ry, off, rowoff, kStream);
-          }
+        for (int it = 0; it < st_it; ++it) {
+          const int qc = q_lo + lane + kWave * it;
+          const v4f v = *reinterpret_cast<const v4f*>(b + cpad((uint32_t)(4 * min(qc, q_hi - 1))));
+          const uint32_t off = (ok && qc < q_hi) ? (uint32_t)(a4 + 4 * qc) * 4u : kOOB;
+          __builtin_amdgcn_raw_buffer_store_b128(
+              v4u{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                  __float_as_uint(v[3])},
+              ry, off, rowoff, kStream);
         }
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(b[b_lds]), ry, ok ? b_off : kOOB,
+                                              rowoff, kStream);
       }
       wave_lds_sync();
+    }
+    base += kDqRing;
+  } while (base < nrows);
+
+  if (!compact) {   // uniform
+    // More BF16 values than the ring's registers hold: the loop stored stale
+    // LDS values at these features. Wait until those stores are complete, then
+    // write the sums over the shards, in shard order from 0.
+    __builtin_amdgcn_s_waitcnt(0);
+    const int n = nrows * g.nout;
+    for (int e0 = 0; e0 < n; e0 += kWave) {
+      const int e = min(e0 + lane, n - 1);
+      const int r = e / g.nout, i = e - r * g.nout;
+      const bool ok = e0 + lane < n;
+      const uint32_t h = __builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)(g.ilo + i) * 4u, 0, 0);
+      float o = 0.0f;
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+        o = __fadd_rn(o, bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
+                             ro, (uint32_t)(((int64_t)p * T * k + g.ilo + i) * 2),
+                             (uint32_t)((t0 + r) * k * 2), 0)));
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), ry, ok ? h * 4u : kOOB,
+                                            (uint32_t)r * (uint32_t)H * 4u, 0);
     }
   }
 }
 
 __global__ __launch_bounds__(256) void decompress_general_kernel(
-    const uint8_t* __restrict__ packed, const uint16_t* __restrict__ outl, int64_t P, int64_t T,
-    int64_t H, int64_t k, int64_t Hq, int64_t Bq, const float* __restrict__ dec,
+    const uint8_t* __restrict__ packed, int64_t pitch, const uint16_t* __restrict__ outl, int64_t P,
+    int64_t T, int64_t H, int64_t k, int64_t Hq, const float* __restrict__ dec,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cmap, float* __restrict__ y) {
   const int64_t n1 = T * Hq;
   const int64_t n2 = T * k;
@@ -260,7 +311,7 @@ __global__ __launch_bounds__(256) void decompress_general_kernel(
       const int64_t t = i / Hq, j = i % Hq;
       const int64_t h = cmap[j];
       for (int64_t p = 0; p < P; ++p) {
-        const uint32_t byte = packed[(p * T + t) * Bq + (j >> 1)];
+        const uint32_t byte = packed[(p * T + t) * pitch + (j >> 1)];
         const int q = (int)((j & 1) ? (byte >> 4) : (byte & 0xFu));
         const float d = __fsub_rn((float)q, dec[(P + p) * Hq + j]);   // exact
         acc = __fadd_rn(acc, __fmul_rn(d, dec[p * Hq + j]));
@@ -275,31 +326,34 @@ __global__ __launch_bounds__(256) void decompress_general_kernel(
   }
 }
 
-template <int NP>
-static void launch_fast(const uint8_t* packed, const uint16_t* outl, int64_t T, int64_t H,
+template <int NP, int kOR>
+static void launch_fast(const uint8_t* packed, int64_t pitch, const uint16_t* outl, int64_t T,
+                        int64_t H,
                         int64_t k, int64_t Hq, int ntiles, int rpw, int64_t nrowblk,
                         int buf_dwords, const float* dec, const int32_t* idx,
                         const int32_t* cmap, float* y, hipStream_t s) {
-  const int64_t ngroups = (nrowblk + kDqWaves - 1) / kDqWaves;
+  const int64_t ntgrp = (ntiles + kDqWaves - 1) / kDqWaves;
   const size_t lds = (size_t)kDqWaves * kDqSub * buf_dwords * 4;
-  decompress_kernel<NP><<<(unsigned)xcd_grid(ntiles, ngroups), 256, lds, s>>>(
-      packed, outl, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, buf_dwords, dec, idx, cmap,
-      y);
+  decompress_kernel<NP, kOR><<<(unsigned)xcd_grid(ntgrp, nrowblk), 256, lds, s>>>(
+      packed, (int)pitch, outl, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, buf_dwords, dec,
+      idx, cmap, y);
 }
 
-hipError_t launch_decompress(const uint8_t* packed, const uint16_t* outl, int64_t P, int64_t T,
-                             int64_t H, int64_t k, const float* dec, const int32_t* idx,
+hipError_t launch_decompress(const uint8_t* packed, int64_t pitch, const uint16_t* outl, int64_t P,
+                             int64_t T, int64_t H, int64_t k, const float* dec, const int32_t* idx,
                              const int32_t* cmap, float* y, hipStream_t s) {
   const int64_t Hq = H - k;
-  const int64_t Bq = (Hq + 1) / 2;
   const int64_t span = (H < kTileSlots + k ? H : kTileSlots + k);
-  const int buf_dwords = (int)((span + span / 8 + 8 + 3) / 4 * 4);
+  const int buf_dwords = span < 65536 ? dq_row_dwords((int)span) : (1 << 30);
   const size_t lds = (size_t)kDqWaves * kDqSub * buf_dwords * 4;
   // Buffer resources: the whole message, the decoder table and one wave's
-  // rows of y must each span fewer than 2^31 bytes.
+  // rows of y must each span fewer than 2^31 bytes. y rows take 16-byte
+  // stores: H a multiple of 4 and y 16-byte aligned.
   const int64_t lim = int64_t(1) << 31;
-  const bool fast = Hq > 0 && P <= 8 && Hq % 8 == 0 && (uintptr_t)packed % 4 == 0 &&
-                    (uintptr_t)dec % 16 == 0 && lds <= 65536 && P * T * Bq < lim &&
+  const bool fast = Hq > 0 && P <= 8 && Hq % 8 == 0 && H % 4 == 0 &&
+                    (uintptr_t)packed % 4 == 0 && (uintptr_t)dec % 16 == 0 &&
+                    (uintptr_t)y % 16 == 0 && lds <= 65536 && pitch % 4 == 0 &&
+                    P * T * pitch < lim &&
                     P * T * k * 2 < lim && (2 * P + 1) * Hq * 4 < lim && 64 * H * 4 < lim;
   if (fast) {
     const int ntiles = (int)((Hq + kTileSlots - 1) / kTileSlots);
@@ -310,11 +364,17 @@ hipError_t launch_decompress(const uint8_t* packed, const uint16_t* outl, int64_
     if (rpw64 > 64) rpw64 = 64;
     const int rpw = (int)rpw64;
     const int64_t nrowblk = (T + rpw - 1) / rpw;
+    // BF16 registers per row: enough for every tile when P*k <= 128.
+    const bool wide = P * k > 2 * kWave;
     switch (P) {
-#define BTQ_DQ_CASE(n)                                                                         \
-  case n:                                                                                      \
-    launch_fast<n>(packed, outl, T, H, k, Hq, ntiles, rpw, nrowblk, buf_dwords, dec, idx, cmap, \
-                   y, s);                                                                      \
+#define BTQ_DQ_CASE(n)                                                                           \
+  case n:                                                                                        \
+    if (wide)                                                                                    \
+      launch_fast<n, 4>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk, buf_dwords, dec, \
+                        idx, cmap, y, s);                                                        \
+    else                                                                                         \
+      launch_fast<n, 2>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk, buf_dwords, dec, \
+                        idx, cmap, y, s);                                                        \
     break;
       BTQ_DQ_CASE(1)
       BTQ_DQ_CASE(2)
@@ -332,8 +392,8 @@ hipError_t launch_decompress(const uint8_t* packed, const uint16_t* outl, int64_
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  decompress_general_kernel<<<(unsigned)blocks, 256, 0, s>>>(packed, outl, P, T, H, k, Hq, Bq, dec,
-                                                             idx, cmap, y);
+  decompress_general_kernel<<<(unsigned)blocks, 256, 0, s>>>(packed, pitch, outl, P, T, H, k, Hq,
+                                                             dec, idx, cmap, y);
   return hipGetLastError();
 }
 

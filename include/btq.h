@@ -149,14 +149,20 @@ int64_t btq_dec_table_floats(int64_t P, int64_t H, int64_t k);
  *   x          bf16 [P,T,H]                       in
  *   enc_table  fp32 [P,H-k,2]                     in (from btq_select_outliers)
  *   outlier_idx i32 [k], cmap i32 [H-k]           in (from btq_select_outliers)
- *   packed     u8   [P,T,btq_packed_row_bytes(H,k)]  out (rows are unpadded)
+ *   packed     u8   [P,T,packed_pitch]            out: row (p,t) holds its
+ *              Bq = btq_packed_row_bytes(H,k) code bytes, then packed_pitch-Bq
+ *              zero bytes
+ *   packed_pitch  bytes per packed row, >= Bq. btq_packed_pitch(H,k) (Bq
+ *              rounded up to 128) lets every row start on a cache line, so
+ *              the kernels write whole lines; Bq gives the densest message.
  *   outliers   bf16 [P,T,k]                       out
  * The maps are trusted: outlier_idx and cmap must partition 0..H-1, each in
  * ascending order, as btq_select_outliers writes them.
  */
 int btq_compress_pack(const uint16_t *x, int64_t P, int64_t T, int64_t H, int64_t k,
                       const float *enc_table, const int32_t *outlier_idx,
-                      const int32_t *cmap, uint8_t *packed, uint16_t *outliers, void *stream);
+                      const int32_t *cmap, uint8_t *packed, int64_t packed_pitch,
+                      uint16_t *outliers, void *stream);
 
 /*
  * Receiver side of inference -- "The Hybrid Quantization Algorithm",
@@ -172,16 +178,22 @@ int btq_compress_pack(const uint16_t *x, int64_t P, int64_t T, int64_t H, int64_
  * fma(q_p, scale, acc) seeded with the table's per-slot constant, which
  * stays within 1e-3*|y| + 1e-2*max_p scale of the sequential sum.
  *   packed, outliers  as written by btq_compress_pack (P shards)  in
+ *   packed_pitch      bytes per packed row, >= btq_packed_row_bytes(H,k);
+ *                     only the code bytes of a row are read
  *   dec_table fp32 [2P+1,H-k], outlier_idx [k], cmap [H-k]        in
  *   y    fp32 [T,H]  out
  */
-int btq_decompress_reduce(const uint8_t *packed, const uint16_t *outliers,
-                          int64_t P, int64_t T, int64_t H, int64_t k,
-                          const float *dec_table, const int32_t *outlier_idx,
+int btq_decompress_reduce(const uint8_t *packed, int64_t packed_pitch,
+                          const uint16_t *outliers, int64_t P, int64_t T, int64_t H,
+                          int64_t k, const float *dec_table, const int32_t *outlier_idx,
                           const int32_t *cmap, float *y, void *stream);
 
-/* Bytes per packed row: ceil((H-k)/2); -1 if H < 1 or k is outside [0,H]. */
+/* Code bytes per packed row: ceil((H-k)/2); -1 if H < 1 or k is outside [0,H]. */
 int64_t btq_packed_row_bytes(int64_t H, int64_t k);
+
+/* Recommended packed row pitch: the code bytes rounded up to a multiple of
+ * 128; -1 for invalid sizes. */
+int64_t btq_packed_pitch(int64_t H, int64_t k);
 
 /* Static text for a btq_status value (never NULL). */
 const char *btq_status_str(int status);

@@ -220,7 +220,22 @@ def unpack_nibbles(b: np.ndarray, n: int) -> np.ndarray:
     return q[..., :n]
 
 
-def compress_pack(x, rscale, zero_point, idx, cmap):
+def pad_rows(b: np.ndarray, pitch: int) -> np.ndarray:
+    """Rows of bytes widened to `pitch` bytes with zeros (layout only).
+
+    The packed message may carry its rows at a pitch larger than the code
+    bytes; the extra bytes of a row are zero and carry nothing.
+    """
+    b = np.asarray(b, np.uint8)
+    n = b.shape[-1]
+    if pitch < n:
+        raise ValueError(f"pitch {pitch} below the row's {n} bytes")
+    out = np.zeros(b.shape[:-1] + (pitch,), np.uint8)
+    out[..., :n] = b
+    return out
+
+
+def compress_pack(x, rscale, zero_point, idx, cmap, pitch=None):
     """Sender side of [Inference]: the message each device sends.
 
     The BF16 features stay BF16. Every other feature is quantized to 4
@@ -228,7 +243,8 @@ def compress_pack(x, rscale, zero_point, idx, cmap):
     errors]). The message holds only the int4 features, in ascending h,
     packed two per byte, plus the BF16 features as a separate block.
     x: uint16 [P,T,H]. rscale, zero_point: [P,H]. idx [k], cmap [H-k].
-    Returns packed uint8 [P,T,ceil((H-k)/2)] and outliers uint16 [P,T,k].
+    Returns packed uint8 [P,T,pitch] (pitch defaults to the ceil((H-k)/2)
+    code bytes; extra bytes are zero) and outliers uint16 [P,T,k].
     """
     x = np.asarray(x, np.uint16)
     cmap = np.asarray(cmap, np.int64)
@@ -236,7 +252,10 @@ def compress_pack(x, rscale, zero_point, idx, cmap):
     f = bf16_to_f32(x[:, :, cmap])
     q = quantize(f, np.asarray(rscale, F32)[:, None, cmap],
                  np.asarray(zero_point, np.uint8)[:, None, cmap])
-    return pack_nibbles(q), x[:, :, idx].copy()
+    packed = pack_nibbles(q)
+    if pitch is not None:
+        packed = pad_rows(packed, pitch)
+    return packed, x[:, :, idx].copy()
 
 
 # ----------------------------------------------- inference, receiver ----
@@ -270,6 +289,8 @@ def decompress_reduce(packed, outliers, scale, zero_point, fmap) -> np.ndarray:
     devices. The reading here: each term is an fp32 value (dequantized
     int4, or the exact BF16 value), and the sum runs in fp32 over
     p = 0, 1, ..., P-1, starting from 0. The output is fp32 [T,H].
+    A packed row may be wider than its code bytes (a pitch); only the first
+    ceil((H-k)/2) bytes are read.
     """
     packed = np.asarray(packed, np.uint8)
     outliers = np.asarray(outliers, np.uint16)

@@ -44,7 +44,7 @@ def oracle_calib(x: np.ndarray, mn, mx, momentum: float, first: bool):
     return (np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res]))
 
 
-def oracle_compress_rows(x: np.ndarray, sel: dict, rows=None):
+def oracle_compress_rows(x: np.ndarray, sel: dict, rows=None, pitch=None):
     """Oracle message for token rows `rows` (all if None), shard-parallel."""
     if rows is not None:
         x = x[:, rows, :]
@@ -52,7 +52,7 @@ def oracle_compress_rows(x: np.ndarray, sel: dict, rows=None):
 
     def one(p):
         return O.compress_pack(x[p:p + 1], sel["rscale"][p:p + 1], sel["zero_point"][p:p + 1],
-                               sel["idx"], sel["cmap"])
+                               sel["idx"], sel["cmap"], pitch=pitch)
 
     res = list(POOL.map(one, range(P)))
     return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -51,6 +51,11 @@ def test_size_helpers(lib):
     assert lib.btq_packed_row_bytes(8, 8) == 0
     assert lib.btq_packed_row_bytes(8, 9) == -1
     assert lib.btq_packed_row_bytes(0, 0) == -1
+    assert lib.btq_packed_pitch(4096, 64) == 2048
+    assert lib.btq_packed_pitch(8192, 256) == 3968
+    assert lib.btq_packed_pitch(5, 2) == 128
+    assert lib.btq_packed_pitch(8, 8) == 0
+    assert lib.btq_packed_pitch(8, 9) == -1
     assert lib.btq_select_workspace_bytes(8, 4096) == 4096 * 4
     assert lib.btq_select_workspace_bytes(0, 4096) == 0
     n = lib.btq_calib_workspace_bytes(8, 2048, 4096)
@@ -113,8 +118,8 @@ def test_select_validation(lib):
     # called here (they would launch).
 
 
-def compress(lib, x=A, P=2, T=4, H=16, k=4, enc=A, idx=A, cmap=A, pk=A, ol=A):
-    return lib.btq_compress_pack(x, P, T, H, k, enc, idx, cmap, pk, ol, None)
+def compress(lib, x=A, P=2, T=4, H=16, k=4, enc=A, idx=A, cmap=A, pk=A, pitch=128, ol=A):
+    return lib.btq_compress_pack(x, P, T, H, k, enc, idx, cmap, pk, pitch, ol, None)
 
 
 def test_compress_validation(lib):
@@ -127,6 +132,9 @@ def test_compress_validation(lib):
     assert compress(lib, x=None) == ARG
     assert compress(lib, pk=None) == ARG
     assert compress(lib, ol=None) == ARG
+    assert compress(lib, pitch=5) == SHAPE       # below the 6 code bytes of a row
+    assert compress(lib, pitch=-1) == SHAPE
+    assert compress(lib, T=1 << 40, P=1, H=16, pitch=1 << 30) == SHAPE   # P*T*pitch overflow
     assert compress(lib, x=A + 1) == ALIGN
     assert compress(lib, enc=A + 2) == ALIGN
     assert compress(lib, ol=A + 1) == ALIGN
@@ -137,8 +145,8 @@ def test_compress_validation(lib):
     assert compress(lib, T=0, k=16, cmap=None, enc=None) == OK
 
 
-def decompress(lib, pk=A, ol=A, P=2, T=4, H=16, k=4, dec=A, idx=A, cmap=A, y=A):
-    return lib.btq_decompress_reduce(pk, ol, P, T, H, k, dec, idx, cmap, y, None)
+def decompress(lib, pk=A, pitch=128, ol=A, P=2, T=4, H=16, k=4, dec=A, idx=A, cmap=A, y=A):
+    return lib.btq_decompress_reduce(pk, pitch, ol, P, T, H, k, dec, idx, cmap, y, None)
 
 
 def test_decompress_validation(lib):
@@ -147,6 +155,7 @@ def test_decompress_validation(lib):
     assert decompress(lib, H=0) == SHAPE
     assert decompress(lib, dec=None) == ARG
     assert decompress(lib, cmap=None) == ARG
+    assert decompress(lib, pitch=5) == SHAPE
     assert decompress(lib, y=None) == ARG
     assert decompress(lib, pk=None) == ARG
     assert decompress(lib, ol=None) == ARG

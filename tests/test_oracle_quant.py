@@ -149,3 +149,30 @@ def test_compress_outlier_block_is_column_copy():
         for t in range(4):
             for i, h in enumerate(idx):
                 assert outl[p, t, i] == x[p, t, h]
+
+
+def test_pitch_pads_rows_with_zeros_and_receiver_ignores_them():
+    # The row pitch is layout only: the code bytes are unchanged, the extra
+    # bytes are zero, and the reduced output is the same for any pitch.
+    x = W.to_u16(W.draw(2, 3, 24, 11))
+    idx = np.array([4, 17])
+    cmap = np.setdiff1d(np.arange(24), idx)
+    rng = np.random.default_rng(12)
+    r = (rng.random((2, 24)) + 0.5).astype(np.float32)
+    z = rng.integers(0, 16, (2, 24)).astype(np.uint8)
+    s = (np.float32(1) / r).astype(np.float32)
+    fmap = np.empty(24, np.int64)
+    fmap[cmap] = np.arange(cmap.size)
+    fmap[idx] = -1 - np.arange(idx.size)
+    base, outl = O.compress_pack(x, r, z, idx, cmap)
+    assert base.shape == (2, 3, 11)
+    y0 = O.decompress_reduce(base, outl, s, z, fmap)
+    for pitch in (11, 12, 16, 128):
+        pk, ol = O.compress_pack(x, r, z, idx, cmap, pitch=pitch)
+        assert pk.shape == (2, 3, pitch)
+        assert np.array_equal(pk[..., :11], base) and not pk[..., 11:].any()
+        assert np.array_equal(ol, outl)
+        y = O.decompress_reduce(pk, ol, s, z, fmap)
+        assert np.array_equal(y.view(np.uint32), y0.view(np.uint32))
+    with pytest.raises(ValueError):
+        O.compress_pack(x, r, z, idx, cmap, pitch=10)

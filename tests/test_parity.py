@@ -25,7 +25,7 @@ def _shifted(t: torch.Tensor, off: int) -> torch.Tensor:
     return big[off:].view(t.shape)
 
 
-def run_both(calib_xs, x, k, momentum, *, x_offset=0, table_offset=0):
+def run_both(calib_xs, x, k, momentum, *, x_offset=0, table_offset=0, pitch=None):
     """Calibrate, select, compress and decompress on both sides; compare all."""
     P, T, H = x.shape
     rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
@@ -48,8 +48,10 @@ def run_both(calib_xs, x, k, momentum, *, x_offset=0, table_offset=0):
     enc, dec = sel_g["enc"], sel_g["dec"]
     if table_offset:   # tables aligned to 4 bytes but not to 16
         enc, dec = _shifted(enc, table_offset), _shifted(dec, table_offset)
-    pk, ol = B.btq_compress_pack(x, k, enc, sel_g["outlier_idx"], sel_g["cmap"])
-    pk_o, ol_o = oracle_compress_rows(u16(x), sel_o)
+    if pitch is None:
+        pitch = B.btq_packed_pitch(H, k)
+    pk, ol = B.btq_compress_pack(x, k, enc, sel_g["outlier_idx"], sel_g["cmap"], pitch=pitch)
+    pk_o, ol_o = oracle_compress_rows(u16(x), sel_o, pitch=pitch)
     torch.cuda.synchronize()
     assert_bits_equal(pk, pk_o, "packed")
     assert_bits_equal(ol.view(torch.int16), ol_o.view(np.int16), "outliers")
@@ -109,6 +111,16 @@ def test_misaligned_input_pointer():
     run_both(calib, x, k, 0.95, x_offset=1)
 
 
+@pytest.mark.parametrize("pitch_extra", [0, 4, 130])
+def test_packed_pitch(pitch_extra):
+    # pitch = code bytes (densest), a few bytes more, and more than one line
+    P, T, H, k = 3, 20, 2048, 64
+    say(f"case: packed pitch = code bytes + {pitch_extra}")
+    calib = [W.draw(P, T, H, 3400 + b, device=DEV) for b in range(2)]
+    x = W.draw(P, T, H, 3500, device=DEV)
+    run_both(calib, x, k, 0.9, pitch=B.btq_packed_row_bytes(H, k) + pitch_extra)
+
+
 def test_misaligned_tables():
     say("case: codec tables offset by one float")
     P, T, H, k = 3, 12, 1024, 8
@@ -135,7 +147,7 @@ def test_empty_batch_leaves_outputs_untouched():
     sel = B.btq_select_outliers(rmin, rmax, k)
     x0 = torch.empty((P, 0, H), dtype=torch.int16, device=DEV)
     pk, ol = B.btq_compress_pack(x0, k, sel["enc"], sel["outlier_idx"], sel["cmap"])
-    assert pk.shape == (P, 0, (H - k + 1) // 2) and ol.shape == (P, 0, k)
+    assert pk.shape == (P, 0, B.btq_packed_pitch(H, k)) and ol.shape == (P, 0, k)
     y = B.btq_decompress_reduce(pk, ol, H, sel["dec"], sel["outlier_idx"], sel["cmap"])
     torch.cuda.synchronize()
     assert y.shape == (0, H)
