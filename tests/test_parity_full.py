@@ -1,0 +1,114 @@
+"""GPU parity at the workloads' full sizes, through the same calls and
+launch configuration that the benchmark times (default stream, default
+packed pitch).
+
+Every workload runs at its real [P,T,H] and k. Its calibration uses the
+workload's batch shape, but fewer batches than the full recipe, so that the
+oracle's exact statistics over all of H stay cheap. The kernels' launch
+shape depends on (P,T,H) only, not on the number of batches.
+
+Checked on every case:
+  * running min/max over all (p,h): equal by value;
+  * parameters, outlier set, maps and codec tables: bitwise;
+  * packed rows and BF16 blocks of sampled token rows: bitwise against the
+    oracle's message for those rows (the rows include both ends, the
+    benchmark's row-block boundaries and random rows);
+  * y on the same rows: within 1e-3*|y| + 1e-2*max_p scale, BF16 columns
+    bit-exact;
+  * properties over the whole tensors: every padding byte of the packed
+    rows is zero and y is finite.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_tensor_activation_amd as B
+from oracle import oracle as O
+import workloads as W
+from helpers import (assert_bits_equal, assert_selection_equal, assert_stats_equal, assert_y_close,
+                     oracle_calib, oracle_compress_rows, say, u16)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+# (workload, inference T, k, calibration batches used here)
+CASES = [
+    ("7b_prefill", 2048, 64, 4),
+    ("decode", 1, 64, 3),
+    ("decode", 8, 64, 3),
+    ("decode", 32, 64, 3),
+    ("decode", 64, 64, 3),
+    ("large_prefill", 8192, 128, 3),
+    ("stress", 16384, 0, 2),
+    ("stress", 16384, 32, 2),
+    ("stress", 16384, 256, 2),
+]
+
+_calib_cache = {}
+
+
+def calibrated(name: str, nb: int):
+    """GPU and oracle running stats after `nb` calibration batches (cached)."""
+    key = (name, nb)
+    if key not in _calib_cache:
+        _calib_cache.clear()
+        w = W.WORKLOADS[name]
+        rmin = torch.empty((w.P, w.H), dtype=torch.float32, device=DEV)
+        rmax = torch.empty_like(rmin)
+        mn = mx = None
+        for b in range(nb):
+            xb = W.batch(w, W.PHASE_CALIB, b, device=DEV)
+            B.btq_calib_update(xb, rmin, rmax, w.momentum, first_batch=(b == 0))
+            mn, mx = oracle_calib(u16(xb), mn, mx, w.momentum, first=(b == 0))
+            del xb
+        torch.cuda.synchronize()
+        _calib_cache[key] = (rmin, rmax, mn, mx)
+    return _calib_cache[key]
+
+
+def sample_rows(T: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 7, 8, 15, 16, 31, 32, 63, 64, T // 2, T - 2, T - 1]
+    rows = set(r for r in fixed if 0 <= r < T)
+    rows |= set(rng.integers(0, T, size=min(T, 24)).tolist())
+    return np.array(sorted(rows), np.int64)
+
+
+@pytest.mark.parametrize("name,T,k,nb", CASES, ids=[f"{c[0]}-T{c[1]}-k{c[2]}" for c in CASES])
+def test_full_size(name, T, k, nb):
+    w = W.WORKLOADS[name]
+    P, H = w.P, w.H
+    say(f"case: {name} P={P} T={T} H={H} k={k} ({nb} calibration batches)")
+    rmin, rmax, mn, mx = calibrated(name, nb)
+    assert_stats_equal(rmin, mn, "run_min")
+    assert_stats_equal(rmax, mx, "run_max")
+
+    sel_g = B.btq_select_outliers(rmin, rmax, k)
+    sel_o = O.select_outliers(mn, mx, k)
+    torch.cuda.synchronize()
+    assert_selection_equal(sel_g, sel_o)
+
+    b = w.T.index(T) if T in w.T else 0
+    x = W.batch(w, W.PHASE_INFER, b, T=T, device=DEV)
+    pk, ol = B.btq_compress_pack(x, k, sel_g["enc"], sel_g["outlier_idx"], sel_g["cmap"])
+    y = B.btq_decompress_reduce(pk, ol, H, sel_g["dec"], sel_g["outlier_idx"], sel_g["cmap"])
+    torch.cuda.synchronize()
+    pitch = pk.shape[2]
+    assert pitch == B.btq_packed_pitch(H, k)
+    Bq = B.btq_packed_row_bytes(H, k)
+
+    # whole-tensor properties
+    assert not bool(pk[:, :, Bq:].any()), "packed padding bytes must be zero"
+    assert bool(torch.isfinite(y).all()), "y must be finite"
+
+    rows = sample_rows(T, seed=T * 131 + k)
+    xs = u16(x[:, torch.as_tensor(rows, device=DEV), :])
+    pk_o, ol_o = oracle_compress_rows(xs, sel_o, pitch=pitch)
+    ridx = torch.as_tensor(rows, device=DEV)
+    assert_bits_equal(pk[:, ridx, :], pk_o, "packed (sampled rows)")
+    assert_bits_equal(ol[:, ridx, :].view(torch.int16), ol_o.view(np.int16),
+                      "outliers (sampled rows)")
+    y_o = O.decompress_reduce(pk_o, ol_o, sel_o["scale"], sel_o["zero_point"], sel_o["fmap"])
+    assert_y_close(y[ridx].cpu().numpy(), y_o, sel_o["scale"], sel_o["idx"])
+    del x, pk, ol, y
+    torch.cuda.empty_cache()
