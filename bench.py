@@ -16,7 +16,8 @@ steps earlier.
 
 Roofline: the dominant kernel (compress) is HBM-bound. achieved = its
 algorithmic bytes per launch / its mean duration from HIP events recorded on
-the launch stream. traffic = HBM bytes per launch from rocprofv3 counters
+the launch stream around every launch of the timed steps (events without the
+system-scope fence, so recording them flushes no cache). traffic = HBM bytes per launch from rocprofv3 counters
 (profiles/), reported only while the kernel source still matches the hash
 those counters were taken at.
 
@@ -69,6 +70,134 @@ def read_traffic(workload: str):
         return float(kv["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+class HipEvents:
+    """Timing events of the HIP runtime that torch has loaded (one runtime per
+    process: libbtq links the same soname).
+
+    They are created with hipEventDisableSystemFence: recording them does
+    not write back and invalidate the caches, so a kernel bracketed by two
+    of them runs as it would without them. Every elapsed time is read only
+    after a device synchronization.
+    """
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self.c = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pool = []
+
+    def new(self):
+        e = self.c.c_void_p()
+        if self.hip.hipEventCreateWithFlags(self.c.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.pool.append(e)
+        return e
+
+    def record(self, e, stream: int) -> None:
+        if self.hip.hipEventRecord(e, self.c.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b) -> float:
+        t = self.c.c_float()
+        if self.hip.hipEventElapsedTime(self.c.byref(t), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return t.value
+
+    def close(self) -> None:
+        for e in self.pool:
+            self.hip.hipEventDestroy(e)
+        self.pool = []
+
+
+def _csv_rows(d: str, suffix: str):
+    import csv
+    import glob
+    for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(f) as fh:
+            yield from csv.DictReader(fh)
+
+
+def _kernel_class(name: str):
+    if "btq::" in name and "decompress" in name:
+        return "decompress_reduce"
+    if "btq::" in name and "compress" in name:
+        return "compress_pack"
+    if "copyBuffer" in name:
+        return "copy"
+    return None
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
+                       note: str) -> str:
+    """Traffic summary from two rocprofv3 --pmc runs of this script.
+
+    The runs count FETCH_SIZE and then WRITE_SIZE (KiB per dispatch) over
+    `python bench.py ... --copy-probe-mib N`. The last 5 copy dispatches are
+    that probe's plain device copies of N MiB: their readings give the scale
+    of each counter. The compress and decompress readings are medians over
+    the timed dispatches, divided by that scale.
+    """
+    import statistics
+    import workloads as W
+    med, copies = {}, {}
+    for d, ctr in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        per = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] != ctr:
+                continue
+            c = _kernel_class(r["Kernel_Name"])
+            if c:
+                per.setdefault(c, []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+        for c, v in per.items():
+            v.sort()
+            if c == "copy":
+                copies[ctr] = [x for _, x in v[-5:]]
+            else:
+                med[(c, ctr)] = statistics.median(x for _, x in v)
+    kib = copy_mib * 1024.0
+    fscale = statistics.median(copies["FETCH_SIZE"]) / kib
+    wscale = statistics.median(copies["WRITE_SIZE"]) / kib
+    w = W.WORKLOADS[workload]
+    comp_alg, deco_alg = algorithmic_bytes(w.P, w.T[0], w.H, w.k)
+    lines = [f"# HBM traffic per launch, workload {workload} (P={w.P}, T={w.T[0]}, H={w.H}, k={w.k})",
+             "# " + note.replace("\n", "\n# "),
+             f"source_hash={source_hash(KERNEL_SOURCES)}",
+             f"workload={workload}",
+             f"copy_probe_bytes={copy_mib * 2 ** 20}",
+             f"copy_fetch_kib={statistics.median(copies['FETCH_SIZE']):.1f}",
+             f"copy_write_kib={statistics.median(copies['WRITE_SIZE']):.1f}",
+             f"fetch_scale={fscale:.4f}",
+             f"write_scale={wscale:.4f}"]
+    for name, alg in (("compress_pack", comp_alg), ("decompress_reduce", deco_alg)):
+        f_kib, w_kib = med[(name, "FETCH_SIZE")], med[(name, "WRITE_SIZE")]
+        traffic = f_kib / fscale * 1024 + w_kib / wscale * 1024
+        tag = "" if name == "compress_pack" else name + "_"
+        lines += [f"{name}_fetch_kib_median={f_kib:.1f}",
+                  f"{name}_write_kib_median={w_kib:.1f}",
+                  f"{tag}traffic_bytes_per_launch={traffic:.0f}",
+                  f"{name}_algorithmic_bytes={alg}",
+                  f"{name}_traffic_over_algorithmic={traffic / alg:.4f}"]
+    return "\n".join(lines) + "\n"
+
+
+def summarize_trace(trace_dir: str, note: str) -> str:
+    """The libbtq rows of a rocprofv3 --kernel-trace --stats run."""
+    lines = ["# " + note.replace("\n", "\n# "),
+             "# kernel | calls | average ns | min ns | max ns | share of GPU time %"]
+    for r in _csv_rows(trace_dir, "kernel_stats.csv"):
+        if "btq::" in r["Name"]:
+            name = r["Name"].split("(")[0].replace("void ", "")
+            lines.append(f"{name} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+                         f"{r['MaxNs']} | {float(r['Percentage']):.2f}")
+    return "\n".join(lines) + "\n"
 
 
 def algorithmic_bytes(P, T, H, k):
@@ -127,7 +256,19 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter scaling)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="print the libbtq rows of a rocprofv3 --stats run and exit")
+    ap.add_argument("--note", default="", help="header text for the summaries")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters, args.workload, args.copy_probe_mib,
+                                 args.note), end="")
+        return 0
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.note), end="")
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -152,6 +293,7 @@ def main() -> int:
     lib = _lib.load()
     stream = torch.cuda.current_stream(dev)
     sh = int(stream.cuda_stream)
+    hev = HipEvents()
 
     # ---- offline: calibration over the calibration set, then selection ----
     log(f"workload {w.name}: P={P} T={T} H={H} k={k}; calibrating on {w.calib_batches} batches")
@@ -162,20 +304,20 @@ def main() -> int:
     calib_ms = 0.0
     for b in range(w.calib_batches):
         xb = W.batch(w, W.PHASE_CALIB, b, device=dev)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        e0, e1 = hev.new(), hev.new()
+        hev.record(e0, sh)
         B.btq_calib_update(xb, rmin, rmax, w.momentum, b == 0, workspace=ws)
-        e1.record(stream)
-        e1.synchronize()
-        calib_ms += e0.elapsed_time(e1)
+        hev.record(e1, sh)
+        torch.cuda.synchronize()
+        calib_ms += hev.ms(e0, e1)
         del xb
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = hev.new(), hev.new()
     B.btq_select_outliers(rmin, rmax, k)     # warm
-    e0.record(stream)
+    hev.record(e0, sh)
     sel = B.btq_select_outliers(rmin, rmax, k)
-    e1.record(stream)
-    e1.synchronize()
-    select_ms = e0.elapsed_time(e1)
+    hev.record(e1, sh)
+    torch.cuda.synchronize()
+    select_ms = hev.ms(e0, e1)
 
     # ---- resident inputs and rotated buffer sets ----
     x0 = W.batch(w, W.PHASE_INFER, 0, T=T, device=dev)
@@ -204,13 +346,13 @@ def main() -> int:
     def step(i, ev=None):
         r = i % R
         if ev is not None:
-            ev[0].record(stream)
+            hev.record(ev[0], sh)
         st = compress(*comp_args[r])
         if ev is not None:
-            ev[1].record(stream)
+            hev.record(ev[1], sh)
         st |= decompress(*deco_args[r])
         if ev is not None:
-            ev[2].record(stream)
+            hev.record(ev[2], sh)
         return st
 
     st = 0
@@ -218,7 +360,7 @@ def main() -> int:
         st |= step(i)
     torch.cuda.synchronize()
     _lib.check(st, "warmup")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[hev.new() for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -226,8 +368,8 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     _lib.check(st, "timed steps")
-    comp_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    deco_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    comp_ms = [hev.ms(e[0], e[1]) for e in evs]
+    deco_ms = [hev.ms(e[1], e[2]) for e in evs]
     comp_mean = sum(comp_ms) / len(comp_ms)
     deco_mean = sum(deco_ms) / len(deco_ms)
     med = lambda v: sorted(v)[len(v) // 2]
@@ -238,13 +380,13 @@ def main() -> int:
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
+        c0, c1 = hev.new(), hev.new()
+        hev.record(c0, sh)
         for _ in range(5):
             dst.copy_(src)
-        c1.record(stream)
-        c1.synchronize()
-        copy_probe = {"bytes_per_copy": 2 * n, "GBps": round(5 * 2 * n / (c0.elapsed_time(c1) * 1e-3) / 1e9, 1)}
+        hev.record(c1, sh)
+        torch.cuda.synchronize()
+        copy_probe = {"bytes_per_copy": 2 * n, "GBps": round(5 * 2 * n / (hev.ms(c0, c1) * 1e-3) / 1e9, 1)}
         del src, dst
 
     bf16_bytes = P * T * H * 2
@@ -292,6 +434,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for >= {args.cpu_seconds:.0f} s")
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample_T, T), args.cpu_seconds)
+    hev.close()
     print(json.dumps(out), flush=True)
     return 0
 
