@@ -219,8 +219,9 @@ __global__ __launch_bounds__(256) void compress_kernel(
 // wave's last row load and store out of range, so every trip of the loop
 // issues the same memory instructions and the compiler can count exactly
 // which loads it must wait for.
-constexpr int kRing = 8;   // token rows in flight per wave
-constexpr int kSub = 2;    // token rows staged in LDS per sub-step
+constexpr int kRing = 8;        // token rows in flight per wave
+constexpr int kRingSmall = 2;   // the same for short batches (decode): more, shorter waves
+constexpr int kSub = 2;         // token rows staged in LDS per sub-step
 
 // Staging bytes per row for a tail of kRemDw dwords per lane: 64 + 16*kRemDw
 // chunks of 20 bytes. A compile-time stride lets the row offset ride in the
@@ -228,7 +229,7 @@ constexpr int kSub = 2;    // token rows staged in LDS per sub-step
 template <int kRemDw>
 constexpr int ring_row_bytes() { return (kWave + 16 * kRemDw) * 20; }
 
-template <int kRemDw>
+template <int kRemDw, int kR>
 __global__ __launch_bounds__(256) void compress_ring_kernel(
     const uint16_t* __restrict__ x, int64_t T, int H, int Hq, int k, int ntiles,
     int rows_per_wave, int64_t nrowblk, int ntgrp, int64_t P,
@@ -273,8 +274,8 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
   const uint32_t rowb = (uint32_t)H * 2u;
 
   constexpr int kT = kRemDw > 0 ? kRemDw : 1;
-  v4u vm[kRing];
-  uint32_t vt[kRing][kT];
+  v4u vm[kR];
+  uint32_t vt[kR][kT];
   auto load = [&](int q, int row) {
     const bool ok = row < nrows;   // uniform
     const uint32_t so = (uint32_t)min(row, nrows - 1) * rowb;
@@ -309,14 +310,14 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
   float rs[8], zf[8];
   load_enc(make_rsrc(enc + (p * Hq + g.jstart) * 2, (uint32_t)(g.jend - g.jstart) * 8u), active,
            lane, rs, zf);
-  // (c) the ring: the first kRing rows. Unconditional: a branch around it
+  // (c) the ring: the first kR rows. Unconditional: a branch around it
   // would make the compiler assume at the join that these loads might not
   // exist, and wait for the ring when it waits for the setup loads.
   // (one fence per row keeps the rows in issue order: the loop consumes
   // them oldest first)
   issue_fence();
 #pragma unroll
-  for (int q = 0; q < kRing; ++q) {
+  for (int q = 0; q < kR; ++q) {
     load(q, q);
     issue_fence();
   }
@@ -344,7 +345,7 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
   int base = 0;
   do {
 #pragma unroll
-    for (int sb = 0; sb < kRing / kSub; ++sb) {
+    for (int sb = 0; sb < kR / kSub; ++sb) {
       // stage kSub rows (the main chunk of lanes past the span lands in
       // unused chunk slots of the buffer; tail dwords past the span skip)
 #pragma unroll
@@ -366,9 +367,9 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
         }
       }
       wave_lds_sync();
-      // refill the staged slots with the rows kRing ahead
+      // refill the staged slots with the rows kR ahead
 #pragma unroll
-      for (int r = 0; r < kSub; ++r) load(sb * kSub + r, base + kRing + sb * kSub + r);
+      for (int r = 0; r < kSub; ++r) load(sb * kSub + r, base + kR + sb * kSub + r);
       uint32_t u[kSub][8];
 #pragma unroll
       for (int r = 0; r < kSub; ++r) {
@@ -399,7 +400,7 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
       }
       wave_lds_sync();
     }
-    base += kRing;
+    base += kR;
   } while (base < nrows);
 }
 
@@ -469,25 +470,31 @@ hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, i
   const size_t ring_lds = (size_t)kCpWaves * kSub * ring_buf;
   if (fast && rem_dw >= 0 && ring_lds <= 65536) {
     const int ntiles = (int)((Hq + kTileSlots - 1) / kTileSlots);
-    // about 4096 waves (16 per CU), a multiple of the ring depth, 8..64 rows
+    // about 4096 waves (16 per CU), a multiple of the ring depth, up to 64
+    // rows; batches too short to give every wave a full 8-row ring take the
+    // 2-row ring
     int64_t rpw64 = (P * ntiles * T + 4095) / 4096;
-    rpw64 = (rpw64 + kRing - 1) / kRing * kRing;
-    if (rpw64 < kRing) rpw64 = kRing;
+    const int ring = rpw64 < kRing ? kRingSmall : kRing;
+    rpw64 = (rpw64 + ring - 1) / ring * ring;
+    if (rpw64 < ring) rpw64 = ring;
     if (rpw64 > 64) rpw64 = 64;
     const int rpw = (int)rpw64;
     const int64_t nrowblk = (T + rpw - 1) / rpw;
     const int ntgrp = (ntiles + kCpWaves - 1) / kCpWaves;
     const unsigned blocks = (unsigned)xcd_grid(ntgrp, P * nrowblk);
-#define BTQ_RING(n)                                                                               \
-  compress_ring_kernel<n><<<blocks, 256, ring_lds, s>>>(x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, \
-                                                        nrowblk, ntgrp, P, enc, idx, cmap, packed,  \
-                                                        (int)pitch, outl)
+#define BTQ_RING(n, r)                                                                    \
+  compress_ring_kernel<n, r><<<blocks, 256, ring_lds, s>>>(x, T, (int)H, (int)Hq, (int)k, ntiles, \
+                                                           rpw, nrowblk, ntgrp, P, enc, idx, cmap, \
+                                                           packed, (int)pitch, outl)
+#define BTQ_RING_R(n) \
+  if (ring == kRing) BTQ_RING(n, kRing); else BTQ_RING(n, kRingSmall);
     switch (rem_dw) {
-      case 0: BTQ_RING(0); break;
-      case 1: BTQ_RING(1); break;
-      case 2: BTQ_RING(2); break;
-      default: BTQ_RING(4); break;
+      case 0: BTQ_RING_R(0); break;
+      case 1: BTQ_RING_R(1); break;
+      case 2: BTQ_RING_R(2); break;
+      default: BTQ_RING_R(4); break;
     }
+#undef BTQ_RING_R
 #undef BTQ_RING
     return hipGetLastError();
   }

@@ -37,6 +37,8 @@
 // any P, H, k, pitch and alignment. Both kernels read the decoder table
 // [2P+1, Hq]: rows 0..P-1 scale, rows P..2P-1 zero point, row 2P the
 // per-slot constant.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace btq {
@@ -46,7 +48,8 @@ constexpr int kDqWaves = 4;
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kDqRing = 8;   // token rows in flight per wave
+constexpr int kDqRing = 8;        // token rows in flight per wave
+constexpr int kDqRingSmall = 2;   // the same for short batches (decode): more, shorter waves
 constexpr int kDqSub = 2;    // token rows per sub-step (LDS y rows)
 
 // LDS y row: position i of the row's span (relative to the 16-byte aligned
@@ -65,7 +68,7 @@ __host__ __device__ constexpr int dq_row_dwords(int span) {
 // LDS: 4 waves x kDqSub y rows of buf_dwords.
 // NP: shards. kOR: BF16 registers per row; a tile whose NP*nout BF16 values
 // fit in kOR*64 lanes sums them in the ring, a wider tile in a pass after it.
-template <int NP, int kOR>
+template <int NP, int kOR, int kR>
 __global__ __launch_bounds__(256) void decompress_kernel(
     const uint8_t* __restrict__ packed, int pitch, const uint16_t* __restrict__ outl, int64_t T,
     int H, int Hq, int k, int ntiles, int rows_per_wave, int64_t nrowblk, int buf_dwords,
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(256) void decompress_kernel(
     }
   }
 
-  uint32_t w[kDqRing][NP], ov[kDqRing][kOR];
+  uint32_t w[kR][NP], ov[kR][kOR];
   // The lane's offsets stay in fixed VGPRs; the (shard, row) offset is
   // uniform and rides in the instruction's SGPR offset.
   auto load = [&](int q, int row) {
@@ -149,14 +152,14 @@ __global__ __launch_bounds__(256) void decompress_kernel(
   const bool own_out = lane < g.nout;
   const uint32_t oh =
       __builtin_amdgcn_raw_buffer_load_b32(ri, own_out ? (uint32_t)(g.ilo + lane) * 4u : kOOB, 0, 0);
-  // (c) the ring: the first kDqRing rows. Unconditional: a branch around it
+  // (c) the ring: the first kR rows. Unconditional: a branch around it
   // would make the compiler assume at the join that these loads might not
   // exist, and wait for the ring when it waits for the setup loads.
   // (one fence per row keeps the rows in issue order: the loop consumes
   // them oldest first)
   issue_fence();
 #pragma unroll
-  for (int q = 0; q < kDqRing; ++q) {
+  for (int q = 0; q < kR; ++q) {
     load(q, q);
     issue_fence();
   }
@@ -191,6 +194,7 @@ __global__ __launch_bounds__(256) void decompress_kernel(
     src_addr[p] = (e & (kWave - 1)) * 4;
     src_reg[p] = min(e >> 6, kOR - 1);
   }
+  const int nreg = (NP * g.nout + kWave - 1) / kWave;   // BF16 registers this tile uses
   // y stores: whole 16-byte chunks q_lo..q_hi-1 of the span, plus at most 3
   // ragged features at each end (lanes 0-2 and 3-5), one dword each.
   const int q_lo = (g.hs - a4 + 3) >> 2;
@@ -212,7 +216,7 @@ __global__ __launch_bounds__(256) void decompress_kernel(
   int base = 0;
   do {
 #pragma unroll
-    for (int sb = 0; sb < kDqRing / kDqSub; ++sb) {
+    for (int sb = 0; sb < kR / kDqSub; ++sb) {
 #pragma unroll
       for (int r = 0; r < kDqSub; ++r) {
         const int q = sb * kDqSub + r;
@@ -234,23 +238,36 @@ __global__ __launch_bounds__(256) void decompress_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) b[ya[e]] = acc[e];
         if (compact && g.nout > 0) {   // uniform
-          float o = 0.0f;
+          // The sum reads only the registers the tile fills; one body per
+          // register count keeps its cross-lane reads back to back.
+          auto bf16_sum = [&](auto regs) {
+            constexpr int nr = decltype(regs)::value;
+            float o = 0.0f;
 #pragma unroll
-          for (int p = 0; p < NP; ++p) {
-            int v = 0;
+            for (int p = 0; p < NP; ++p) {
+              int v = 0;
 #pragma unroll
-            for (int rr = 0; rr < kOR; ++rr) {
-              const int t = __builtin_amdgcn_ds_bpermute(src_addr[p], (int)ov[q][rr]);
-              v = (src_reg[p] == rr) ? t : v;
+              for (int rr = 0; rr < nr; ++rr) {
+                const int t = __builtin_amdgcn_ds_bpermute(src_addr[p], (int)ov[q][rr]);
+                v = (src_reg[p] == rr) ? t : v;
+              }
+              o = __fadd_rn(o, bf16_to_f32((uint32_t)v & 0xFFFFu));
             }
-            o = __fadd_rn(o, bf16_to_f32((uint32_t)v & 0xFFFFu));
-          }
+            return o;
+          };
+          float o;
+          if (nreg <= 1)   // uniform
+            o = bf16_sum(std::integral_constant<int, 1>{});
+          else if (nreg <= 2)
+            o = bf16_sum(std::integral_constant<int, 2>{});
+          else
+            o = bf16_sum(std::integral_constant<int, kOR>{});
           b[oa] = o;
         }
       }
-      // refill the consumed slots with the rows kDqRing ahead
+      // refill the consumed slots with the rows kR ahead
 #pragma unroll
-      for (int r = 0; r < kDqSub; ++r) load(sb * kDqSub + r, base + kDqRing + sb * kDqSub + r);
+      for (int r = 0; r < kDqSub; ++r) load(sb * kDqSub + r, base + kR + sb * kDqSub + r);
       wave_lds_sync();
 #pragma unroll
       for (int r = 0; r < kDqSub; ++r) {
@@ -272,7 +289,7 @@ __global__ __launch_bounds__(256) void decompress_kernel(
       }
       wave_lds_sync();
     }
-    base += kDqRing;
+    base += kR;
   } while (base < nrows);
 
   if (!compact) {   // uniform
@@ -326,7 +343,7 @@ __global__ __launch_bounds__(256) void decompress_general_kernel(
   }
 }
 
-template <int NP, int kOR>
+template <int NP, int kOR, int kR>
 static void launch_fast(const uint8_t* packed, int64_t pitch, const uint16_t* outl, int64_t T,
                         int64_t H,
                         int64_t k, int64_t Hq, int ntiles, int rpw, int64_t nrowblk,
@@ -334,7 +351,7 @@ static void launch_fast(const uint8_t* packed, int64_t pitch, const uint16_t* ou
                         const int32_t* cmap, float* y, hipStream_t s) {
   const int64_t ntgrp = (ntiles + kDqWaves - 1) / kDqWaves;
   const size_t lds = (size_t)kDqWaves * kDqSub * buf_dwords * 4;
-  decompress_kernel<NP, kOR><<<(unsigned)xcd_grid(ntgrp, nrowblk), 256, lds, s>>>(
+  decompress_kernel<NP, kOR, kR><<<(unsigned)xcd_grid(ntgrp, nrowblk), 256, lds, s>>>(
       packed, (int)pitch, outl, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, buf_dwords, dec,
       idx, cmap, y);
 }
@@ -357,10 +374,14 @@ hipError_t launch_decompress(const uint8_t* packed, int64_t pitch, const uint16_
                     P * T * k * 2 < lim && (2 * P + 1) * Hq * 4 < lim && 64 * H * 4 < lim;
   if (fast) {
     const int ntiles = (int)((Hq + kTileSlots - 1) / kTileSlots);
-    // about 2048 waves (8 per CU), a multiple of the ring depth, 8..64 rows
+    // about 2048 waves (8 per CU), a multiple of the ring depth, up to 64
+    // rows; batches too short to give every wave a full 8-row ring take the
+    // 2-row ring
     int64_t rpw64 = (ntiles * T + 2047) / 2048;
-    rpw64 = (rpw64 + kDqRing - 1) / kDqRing * kDqRing;
-    if (rpw64 < kDqRing) rpw64 = kDqRing;
+    const bool small = rpw64 < kDqRing;
+    const int ring = small ? kDqRingSmall : kDqRing;
+    rpw64 = (rpw64 + ring - 1) / ring * ring;
+    if (rpw64 < ring) rpw64 = ring;
     if (rpw64 > 64) rpw64 = 64;
     const int rpw = (int)rpw64;
     const int64_t nrowblk = (T + rpw - 1) / rpw;
@@ -369,12 +390,18 @@ hipError_t launch_decompress(const uint8_t* packed, int64_t pitch, const uint16_
     switch (P) {
 #define BTQ_DQ_CASE(n)                                                                           \
   case n:                                                                                        \
-    if (wide)                                                                                    \
-      launch_fast<n, 4>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk, buf_dwords, dec, \
-                        idx, cmap, y, s);                                                        \
+    if (wide && !small)                                                                          \
+      launch_fast<n, 4, kDqRing>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk,         \
+                                 buf_dwords, dec, idx, cmap, y, s);                              \
+    else if (wide)                                                                               \
+      launch_fast<n, 4, kDqRingSmall>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk,    \
+                                      buf_dwords, dec, idx, cmap, y, s);                         \
+    else if (!small)                                                                             \
+      launch_fast<n, 2, kDqRing>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk,         \
+                                 buf_dwords, dec, idx, cmap, y, s);                              \
     else                                                                                         \
-      launch_fast<n, 2>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk, buf_dwords, dec, \
-                        idx, cmap, y, s);                                                        \
+      launch_fast<n, 2, kDqRingSmall>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk,    \
+                                      buf_dwords, dec, idx, cmap, y, s);                         \
     break;
       BTQ_DQ_CASE(1)
       BTQ_DQ_CASE(2)

@@ -91,6 +91,9 @@ CASES = [
     (4, 6, 2048, 600, "laplace", list(range(0, 2048, 3))[:600], "k=600: wide LDS span"),
     (1, 1, 8, 3, "normal", [1], "smallest: P=1, T=1, H=8"),
     (8, 1, 8192, 64, "normal", list(range(3, 8192, 200)), "decode-like T=1"),
+    (8, 24, 2048, 96, "normal", list(range(600, 624)), "P=8, 24 clustered BF16: 3-4 registers"),
+    (8, 20, 2048, 64, "normal", list(range(700, 745)), "P=8, 45 clustered BF16: post-loop sums"),
+    (8, 40, 4096, 64, "laplace", list(range(5, 4096, 64)), "P=8, T=40: 2-row ring"),
 ]
 
 
