@@ -55,7 +55,7 @@ def test_kernel_sources_include_only_their_own_headers():
             for name in inc.findall(open(os.path.join(dp, f)).read()):
                 assert "oracle" not in name, (f, name)
                 assert name in {"common.hpp", "btq.h", "hip/hip_runtime.h", "stdint.h",
-                                "stddef.h", "float.h", "math.h"}, (f, name)
+                                "stddef.h", "float.h", "math.h", "type_traits"}, (f, name)
 
 
 def test_input_generator_is_independent_and_holds_no_codec_arithmetic():
