@@ -470,14 +470,16 @@ hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, i
   const size_t ring_lds = (size_t)kCpWaves * kSub * ring_buf;
   if (fast && rem_dw >= 0 && ring_lds <= 65536) {
     const int ntiles = (int)((Hq + kTileSlots - 1) / kTileSlots);
-    // about 4096 waves (16 per CU), a multiple of the ring depth, up to 64
-    // rows; batches too short to give every wave a full 8-row ring take the
-    // 2-row ring
+    // Rows per wave: enough for about 4096 waves (16 per CU, one resident
+    // generation) up to 32 rows; larger batches run several generations of
+    // 16-row waves, whose short lifetimes keep the end of the launch
+    // balanced. A multiple of the ring depth; batches too short to give every
+    // wave a full 8-row ring take the 2-row ring.
     int64_t rpw64 = (P * ntiles * T + 4095) / 4096;
+    if (rpw64 > 32) rpw64 = 16;
     const int ring = rpw64 < kRing ? kRingSmall : kRing;
     rpw64 = (rpw64 + ring - 1) / ring * ring;
     if (rpw64 < ring) rpw64 = ring;
-    if (rpw64 > 64) rpw64 = 64;
     const int rpw = (int)rpw64;
     const int64_t nrowblk = (T + rpw - 1) / rpw;
     const int ntgrp = (ntiles + kCpWaves - 1) / kCpWaves;

@@ -374,10 +374,11 @@ hipError_t launch_decompress(const uint8_t* packed, int64_t pitch, const uint16_
                     P * T * k * 2 < lim && (2 * P + 1) * Hq * 4 < lim && 64 * H * 4 < lim;
   if (fast) {
     const int ntiles = (int)((Hq + kTileSlots - 1) / kTileSlots);
-    // about 2048 waves (8 per CU), a multiple of the ring depth, up to 64
-    // rows; batches too short to give every wave a full 8-row ring take the
-    // 2-row ring
-    int64_t rpw64 = (ntiles * T + 2047) / 2048;
+    // about 1024 waves (4 per CU: each wave's table loads then serve at
+    // least 16 rows where the batch allows), a multiple of the ring depth,
+    // up to 64 rows; batches too short to give every wave a full 8-row ring
+    // take the 2-row ring
+    int64_t rpw64 = (ntiles * T + 1023) / 1024;
     const bool small = rpw64 < kDqRing;
     const int ring = small ? kDqRingSmall : kDqRing;
     rpw64 = (rpw64 + ring - 1) / ring * ring;
