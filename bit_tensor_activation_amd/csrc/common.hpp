@@ -48,6 +48,14 @@ __device__ __forceinline__ void settle(V& v) {
   asm volatile("" : "+v"(v));
 }
 
+// Hides a value's origin from the optimizer (an empty asm that reads and
+// writes it, with no side effects), so it cannot rewrite the computation of
+// the value's uses in terms of that origin.
+template <typename V>
+__device__ __forceinline__ void opaque(V& v) {
+  asm("" : "+v"(v));
+}
+
 // Raw buffer resources (gfx9 format). A wave builds a descriptor over the
 // part of a tensor it touches, so every offset stays 32-bit. The hardware
 // range check then handles ragged edges: a load at or past num_records

@@ -226,8 +226,13 @@ __global__ __launch_bounds__(256) void decompress_kernel(
         for (int e = 0; e < 8; ++e) acc[e] = bias[e];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-          const uint32_t lo = w[q][p] & 0x0F0F0F0Fu;
-          const uint32_t hi = w[q][p] & 0xF0F0F0F0u;
+          uint32_t lo = w[q][p] & 0x0F0F0F0Fu;
+          uint32_t hi = w[q][p] & 0xF0F0F0F0u;
+          // Opaque to the optimizer: otherwise it folds each mask into a
+          // per-byte extract, one more instruction per code. Kept whole, each
+          // byte converts directly (v_cvt_f32_ubyte0..3).
+          opaque(lo);
+          opaque(hi);
 #pragma unroll
           for (int bb = 0; bb < 4; ++bb) {
             acc[2 * bb] = fmaf((float)((lo >> (8 * bb)) & 0xFFu), sc[p][2 * bb], acc[2 * bb]);
@@ -297,20 +302,32 @@ __global__ __launch_bounds__(256) void decompress_kernel(
     // LDS values at these features. Wait until those stores are complete, then
     // write the sums over the shards, in shard order from 0.
     __builtin_amdgcn_s_waitcnt(0);
+    // 4 entries per lane per trip, all their loads in flight together
+    constexpr int kPer = 4;
     const int n = nrows * g.nout;
-    for (int e0 = 0; e0 < n; e0 += kWave) {
-      const int e = min(e0 + lane, n - 1);
-      const int r = e / g.nout, i = e - r * g.nout;
-      const bool ok = e0 + lane < n;
-      const uint32_t h = __builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)(g.ilo + i) * 4u, 0, 0);
-      float o = 0.0f;
+    for (int e0 = 0; e0 < n; e0 += kPer * kWave) {
+      uint32_t hv[kPer], v[kPer][NP], yo[kPer];
 #pragma unroll
-      for (int p = 0; p < NP; ++p)
-        o = __fadd_rn(o, bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
-                             ro, (uint32_t)(((int64_t)p * T * k + g.ilo + i) * 2),
-                             (uint32_t)((t0 + r) * k * 2), 0)));
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), ry, ok ? h * 4u : kOOB,
-                                            (uint32_t)r * (uint32_t)H * 4u, 0);
+      for (int u = 0; u < kPer; ++u) {
+        const int eu = e0 + u * kWave + lane;
+        const int e = min(eu, n - 1);
+        const int r = e / g.nout, i = e - r * g.nout;
+        hv[u] = __builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)(g.ilo + i) * 4u, 0, 0);
+        yo[u] = eu < n ? (uint32_t)r * (uint32_t)H * 4u : kOOB;
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+          v[u][p] = __builtin_amdgcn_raw_buffer_load_b16(
+              ro, (uint32_t)(((int64_t)p * T * k + g.ilo + i) * 2), (uint32_t)((t0 + r) * k * 2), 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        float o = 0.0f;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) o = __fadd_rn(o, bf16_to_f32(v[u][p]));
+        // (an entry past the end stores out of range)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), ry,
+                                              yo[u] == kOOB ? kOOB : yo[u] + hv[u] * 4u, 0, 0);
+      }
     }
   }
 }
@@ -386,8 +403,10 @@ hipError_t launch_decompress(const uint8_t* packed, int64_t pitch, const uint16_
     if (rpw64 > 64) rpw64 = 64;
     const int rpw = (int)rpw64;
     const int64_t nrowblk = (T + rpw - 1) / rpw;
-    // BF16 registers per row: enough for every tile when P*k <= 128.
-    const bool wide = P * k > 2 * kWave;
+    // BF16 registers per row: 2 (128 shard x feature values per tile) while a
+    // tile holds at most 64 of them on average, else 4. A tile beyond its
+    // registers sums its BF16 features after the row loop.
+    const bool wide = P * k > int64_t(kWave) * ntiles;
     switch (P) {
 #define BTQ_DQ_CASE(n)                                                                           \
   case n:                                                                                        \
