@@ -244,19 +244,27 @@ __global__ __launch_bounds__(256) void decompress_kernel(
         for (int e = 0; e < 8; ++e) b[ya[e]] = acc[e];
         if (compact && g.nout > 0) {   // uniform
           // The sum reads only the registers the tile fills; one body per
-          // register count keeps its cross-lane reads back to back.
+          // register count. All cross-lane reads of the row are issued
+          // before the first is used (the fence keeps the scheduler from
+          // interleaving them with the sum, one round trip each).
           auto bf16_sum = [&](auto regs) {
             constexpr int nr = decltype(regs)::value;
+            int t[NP][nr];
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+#pragma unroll
+              for (int rr = 0; rr < nr; ++rr)
+                t[p][rr] = __builtin_amdgcn_ds_bpermute(src_addr[p], (int)ov[q][rr]);
+            }
+            issue_fence();
             float o = 0.0f;
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-              int v = 0;
+              int v = t[p][0];
 #pragma unroll
-              for (int rr = 0; rr < nr; ++rr) {
-                const int t = __builtin_amdgcn_ds_bpermute(src_addr[p], (int)ov[q][rr]);
-                v = (src_reg[p] == rr) ? t : v;
-              }
-              o = __fadd_rn(o, bf16_to_f32((uint32_t)v & 0xFFFFu));
+              for (int rr = 1; rr < nr; ++rr) v = (src_reg[p] == rr) ? t[p][rr] : v;
+              // (the loads zero-extend the 16 bf16 bits)
+              o = __fadd_rn(o, bf16_to_f32((uint32_t)v));
             }
             return o;
           };
