@@ -48,7 +48,10 @@ constexpr int kDqWaves = 4;
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kDqRing = 8;        // token rows in flight per wave
+// Token rows in flight per wave. A row costs NP + kOR loads and about 4
+// stores, and the vector-memory counter holds at most 63 operations: with 8
+// shards a 4-row ring is the deepest whose waits stay exact.
+constexpr int kDqRing = 4;
 constexpr int kDqRingSmall = 2;   // the same for short batches (decode): more, shorter waves
 constexpr int kDqSub = 2;    // token rows per sub-step (LDS y rows)
 
