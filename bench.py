@@ -200,14 +200,15 @@ def summarize_trace(trace_dir: str, note: str) -> str:
     return "\n".join(lines) + "\n"
 
 
-def algorithmic_bytes(P, T, H, k):
-    """Bytes the method must move per launch (inputs once, outputs once)."""
+def algorithmic_bytes(P, T, H, k, y_bytes=4):
+    """Bytes the method must move per launch (inputs once, outputs once);
+    y_bytes is 4 for the fp32 receiver, 2 for the bf16 one."""
     Bq = (H - k + 1) // 2
     Hq = H - k
     maps = 4 * H                             # cmap and outlier_idx
     message = P * T * (Bq + 2 * k)
     compress = P * T * H * 2 + message + P * Hq * 8 + maps           # + (rscale, zero point) table
-    decompress = message + T * H * 4 + (P + 1) * Hq * 4 + maps       # + scale rows, constant row
+    decompress = message + T * H * y_bytes + (P + 1) * Hq * 4 + maps  # + scale rows, constant row
     return compress, decompress
 
 
@@ -374,6 +375,26 @@ def main() -> int:
     deco_mean = sum(deco_ms) / len(deco_ms)
     med = lambda v: sorted(v)[len(v) // 2]
 
+    # The bf16-output receiver, timed on its own after the steps (it is not
+    # part of a step: the step's receiver writes fp32).
+    y16 = [torch.empty((T, H), dtype=torch.int16, device=dev) for _ in range(2)]
+    d16_args = [(a[0], a[1], a[2], P, T, H, k, dec, oi, cm, p(y16[r % 2]), sh)
+                for r, a in enumerate(deco_args)]
+    n16 = max(20, min(args.steps, 200))
+    for i in range(5):
+        st |= lib.btq_decompress_reduce_bf16(*d16_args[i % R])
+    e16 = [(hev.new(), hev.new()) for _ in range(n16)]
+    torch.cuda.synchronize()
+    for i in range(n16):
+        hev.record(e16[i][0], sh)
+        st |= lib.btq_decompress_reduce_bf16(*d16_args[i % R])
+        hev.record(e16[i][1], sh)
+    torch.cuda.synchronize()
+    _lib.check(st, "bf16-output receiver")
+    d16_mean = sum(hev.ms(a, b) for a, b in e16) / n16
+    d16_bytes = algorithmic_bytes(P, T, H, k, y_bytes=2)[1]
+    del y16
+
     copy_probe = None
     if args.copy_probe_mib:
         n = args.copy_probe_mib * 2 ** 20
@@ -424,6 +445,11 @@ def main() -> int:
                                   "frac": round(deco_bytes / (deco_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                                   "bf16_equiv_GBps": round(bf16_bytes / (deco_mean * 1e-3) / 1e9, 1)},
             "kernel_sum_bf16_equiv_GBps": round(bf16_bytes / ((comp_mean + deco_mean) * 1e-3) / 1e9, 1),
+            "decompress_reduce_bf16": {"mean_us": round(d16_mean * 1e3, 2), "algorithmic_bytes": d16_bytes,
+                                       "hbm_GBps": round(d16_bytes / (d16_mean * 1e-3) / 1e9, 1),
+                                       "frac": round(d16_bytes / (d16_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                       "note": "bf16 output (one rounding of the fp32 sum); "
+                                               "timed separately, not part of value"},
         },
         "offline": {"calib_batches": w.calib_batches, "calib_ms_total": round(calib_ms, 3),
                     "calib_GBps": round(w.calib_batches * P * w.calib_T * H * 2 / (calib_ms * 1e-3) / 1e9, 1),

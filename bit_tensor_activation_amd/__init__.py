@@ -10,6 +10,7 @@ from .api import (  # noqa: F401
     btq_compress_pack,
     btq_dec_table_floats,
     btq_decompress_reduce,
+    btq_decompress_reduce_bf16,
     btq_enc_table_floats,
     btq_packed_pitch,
     btq_packed_row_bytes,

@@ -25,6 +25,7 @@ SIGNATURES = {
     "btq_dec_table_floats": (_I64, [_I64, _I64, _I64]),
     "btq_compress_pack": (_I, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _P, _P]),
     "btq_decompress_reduce": (_I, [_P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "btq_decompress_reduce_bf16": (_I, [_P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "btq_packed_row_bytes": (_I64, [_I64, _I64]),
     "btq_packed_pitch": (_I64, [_I64, _I64]),
     "btq_status_str": (_c.c_char_p, [_I]),

@@ -16,7 +16,7 @@ Layouts (contiguous, row-major, last index fastest):
   packed      uint8 [P,T,pitch]: ceil((H-k)/2) code bytes per row, then zeros;
               pitch defaults to btq_packed_pitch(H,k) (a multiple of 128)
   outliers    int16 [P,T,k]
-  y           float32 [T,H]
+  y           float32 [T,H]  (bf16 [T,H] from btq_decompress_reduce_bf16)
 """
 from __future__ import annotations
 
@@ -186,14 +186,9 @@ def btq_compress_pack(x: torch.Tensor, k: int, enc_table: torch.Tensor,
     return packed, outliers
 
 
-def btq_decompress_reduce(packed: torch.Tensor, outliers: torch.Tensor, H: int,
-                          dec_table: torch.Tensor, outlier_idx: torch.Tensor, cmap: torch.Tensor,
-                          y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Receiver: y float32 [T,H] = sum over shards of the dequantized messages.
-
-    packed is uint8 [P,T,pitch]; its rows' first btq_packed_row_bytes(H,k)
-    bytes are read.
-    """
+def _decompress(entry: str, packed: torch.Tensor, outliers: torch.Tensor, H: int,
+                dec_table: torch.Tensor, outlier_idx: torch.Tensor, cmap: torch.Tensor,
+                y: Optional[torch.Tensor], ydtypes, ynew, stream) -> torch.Tensor:
     dev = _device(packed)
     P, T, pitch = packed.shape
     k = outliers.shape[2]
@@ -205,14 +200,38 @@ def btq_decompress_reduce(packed: torch.Tensor, outliers: torch.Tensor, H: int,
     _need(outlier_idx, "outlier_idx", (torch.int32,), (k,), dev)
     _need(cmap, "cmap", (torch.int32,), (H - k,), dev)
     if y is None:
-        y = torch.empty((T, H), dtype=torch.float32, device=dev)
-    _need(y, "y", (torch.float32,), (T, H), dev)
+        y = torch.empty((T, H), dtype=ynew, device=dev)
+    _need(y, "y", ydtypes, (T, H), dev)
     lib = _lib.load()
-    st = lib.btq_decompress_reduce(_ptr(packed), pitch, _ptr(_bits(outliers)), P, T, H, k,
-                                   _ptr(dec_table), _ptr(outlier_idx), _ptr(cmap), _ptr(y),
-                                   _stream(dev, stream))
-    _lib.check(st, "btq_decompress_reduce")
+    st = getattr(lib, entry)(_ptr(packed), pitch, _ptr(_bits(outliers)), P, T, H, k,
+                             _ptr(dec_table), _ptr(outlier_idx), _ptr(cmap), _ptr(_bits(y)),
+                             _stream(dev, stream))
+    _lib.check(st, entry)
     return y
+
+
+def btq_decompress_reduce(packed: torch.Tensor, outliers: torch.Tensor, H: int,
+                          dec_table: torch.Tensor, outlier_idx: torch.Tensor, cmap: torch.Tensor,
+                          y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Receiver: y float32 [T,H] = sum over shards of the dequantized messages.
+
+    packed is uint8 [P,T,pitch]; its rows' first btq_packed_row_bytes(H,k)
+    bytes are read.
+    """
+    return _decompress("btq_decompress_reduce", packed, outliers, H, dec_table, outlier_idx, cmap,
+                       y, (torch.float32,), torch.float32, stream)
+
+
+def btq_decompress_reduce_bf16(packed: torch.Tensor, outliers: torch.Tensor, H: int,
+                               dec_table: torch.Tensor, outlier_idx: torch.Tensor,
+                               cmap: torch.Tensor, y: Optional[torch.Tensor] = None,
+                               stream=None) -> torch.Tensor:
+    """Receiver with bf16 output: the fp32 sum rounded once to bf16.
+
+    Returns int16 [T,H] bf16 bits (torch.bfloat16 is also accepted for y).
+    """
+    return _decompress("btq_decompress_reduce_bf16", packed, outliers, H, dec_table, outlier_idx,
+                       cmap, y, _BF16, torch.int16, stream)
 
 
 def btq_status_str(status: int) -> str:

@@ -128,10 +128,12 @@ int btq_compress_pack(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_
                                          packed_pitch, outliers, (hipStream_t)stream));
 }
 
-int btq_decompress_reduce(const uint8_t* packed, int64_t packed_pitch, const uint16_t* outliers,
-                          int64_t P, int64_t T, int64_t H, int64_t k, const float* dec_table,
-                          const int32_t* outlier_idx, const int32_t* cmap, float* y,
-                          void* stream) {
+namespace {
+
+int decompress_common(const uint8_t* packed, int64_t packed_pitch, const uint16_t* outliers,
+                      int64_t P, int64_t T, int64_t H, int64_t k, const float* dec_table,
+                      const int32_t* outlier_idx, const int32_t* cmap, void* y, bool bf16,
+                      void* stream) {
   int st = check_dims(P, T, H, 0);
   if (st != BTQ_OK) return st;
   st = check_k(H, k);
@@ -141,11 +143,29 @@ int btq_decompress_reduce(const uint8_t* packed, int64_t packed_pitch, const uin
   if ((k > 0 && !outlier_idx) || (k < H && (!cmap || !dec_table))) return BTQ_ERR_ARG;
   if (T > 0 && (!y || (k < H && !packed) || (k > 0 && !outliers))) return BTQ_ERR_ARG;
   if (!aligned(outliers, 2) || !aligned(dec_table, 4) || !aligned(outlier_idx, 4) ||
-      !aligned(cmap, 4) || !aligned(y, 4))
+      !aligned(cmap, 4) || !aligned(y, bf16 ? 2 : 4))
     return BTQ_ERR_ALIGN;
   if (T == 0) return BTQ_OK;
   return hip_status(btq::launch_decompress(packed, packed_pitch, outliers, P, T, H, k, dec_table,
-                                           outlier_idx, cmap, y, (hipStream_t)stream));
+                                           outlier_idx, cmap, y, bf16, (hipStream_t)stream));
+}
+
+}  // namespace
+
+int btq_decompress_reduce(const uint8_t* packed, int64_t packed_pitch, const uint16_t* outliers,
+                          int64_t P, int64_t T, int64_t H, int64_t k, const float* dec_table,
+                          const int32_t* outlier_idx, const int32_t* cmap, float* y,
+                          void* stream) {
+  return decompress_common(packed, packed_pitch, outliers, P, T, H, k, dec_table, outlier_idx,
+                           cmap, y, false, stream);
+}
+
+int btq_decompress_reduce_bf16(const uint8_t* packed, int64_t packed_pitch,
+                               const uint16_t* outliers, int64_t P, int64_t T, int64_t H,
+                               int64_t k, const float* dec_table, const int32_t* outlier_idx,
+                               const int32_t* cmap, uint16_t* y, void* stream) {
+  return decompress_common(packed, packed_pitch, outliers, P, T, H, k, dec_table, outlier_idx,
+                           cmap, y, true, stream);
 }
 
 const char* btq_status_str(int status) {

@@ -143,6 +143,6 @@ hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, i
 
 hipError_t launch_decompress(const uint8_t* packed, int64_t pitch, const uint16_t* outl, int64_t P,
                              int64_t T, int64_t H, int64_t k, const float* dec, const int32_t* idx,
-                             const int32_t* cmap, float* y, hipStream_t s);
+                             const int32_t* cmap, void* y, bool bf16, hipStream_t s);
 
 }  // namespace btq

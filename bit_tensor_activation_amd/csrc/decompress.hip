@@ -55,6 +55,16 @@ constexpr int kDqRing = 4;
 constexpr int kDqRingSmall = 2;   // the same for short batches (decode): more, shorter waves
 constexpr int kDqSub = 2;    // token rows per sub-step (LDS y rows)
 
+// fp32 -> bf16, round to nearest even: the one rounding of the bf16-output
+// receiver. Two values per instruction (v_cvt_pk_bf16_f32): a in the low
+// half, b in the high half.
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{a, b}, v2bf));
+}
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) { return bf16_pair(f, 0.0f) & 0xFFFFu; }
+
 // LDS y row: position i of the row's span (relative to the 16-byte aligned
 // feature a4 <= hs) lives at dword cpad(i). Four dwords of padding per 32
 // keep each 16-byte chunk contiguous and aligned for the wide reads, and
@@ -71,12 +81,15 @@ __host__ __device__ constexpr int dq_row_dwords(int span) {
 // LDS: 4 waves x kDqSub y rows of buf_dwords.
 // NP: shards. kOR: BF16 registers per row; a tile whose NP*nout BF16 values
 // fit in kOR*64 lanes sums them in the ring, a wider tile in a pass after it.
-template <int NP, int kOR, int kR>
+// kR: ring depth. kBf: y is bf16 (one rounding of the fp32 sum) instead of
+// fp32.
+template <int NP, int kOR, int kR, bool kBf>
 __global__ __launch_bounds__(256) void decompress_kernel(
     const uint8_t* __restrict__ packed, int pitch, const uint16_t* __restrict__ outl, int64_t T,
     int H, int Hq, int k, int ntiles, int rows_per_wave, int64_t nrowblk, int buf_dwords,
     const float* __restrict__ dec, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ cmap, float* __restrict__ y) {
+    const int32_t* __restrict__ cmap, void* __restrict__ y) {
+  constexpr uint32_t kYB = kBf ? 2u : 4u;   // bytes per y value
   extern __shared__ __align__(16) char smem[];
   // unit = row block; its blocks of 4 adjacent tiles run on one XCD
   int64_t rb, sub;
@@ -98,7 +111,7 @@ __global__ __launch_bounds__(256) void decompress_kernel(
   // this wave's rows of y.
   const rsrc_t rp = make_rsrc(packed, (uint32_t)(NP * T * (int64_t)pitch));
   const rsrc_t ro = make_rsrc(outl, (uint32_t)(NP * T * (int64_t)k * 2));
-  const rsrc_t ry = make_rsrc(y + t0 * H, (uint32_t)nrows * (uint32_t)H * 4u);
+  const rsrc_t ry = make_rsrc(static_cast<char*>(y) + t0 * H * kYB, (uint32_t)nrows * (uint32_t)H * kYB);
   const rsrc_t rc = make_rsrc(cmap, (uint32_t)Hq * 4u);
   const rsrc_t ri = make_rsrc(idx, (uint32_t)k * 4u);
 
@@ -212,7 +225,7 @@ __global__ __launch_bounds__(256) void decompress_kernel(
     if (h < g.he) bpos = h;
   }
   const uint32_t b_lds = cpad((uint32_t)(max(bpos, g.hs) - a4));
-  const uint32_t b_off = bpos >= 0 ? (uint32_t)bpos * 4u : kOOB;
+  const uint32_t b_off = bpos >= 0 ? (uint32_t)bpos * kYB : kOOB;
 
   // nrows >= 1: a do-while has no entry guard that the ring loads could be
   // sunk below.
@@ -290,18 +303,28 @@ __global__ __launch_bounds__(256) void decompress_kernel(
         const int row = base + sb * kDqSub + r;
         const bool ok = row < nrows;   // uniform
         const float* b = buf + r * buf_dwords;
-        const uint32_t rowoff = (uint32_t)min(row, nrows - 1) * (uint32_t)H * 4u;
+        const uint32_t rowoff = (uint32_t)min(row, nrows - 1) * (uint32_t)H * kYB;
         for (int it = 0; it < st_it; ++it) {
           const int qc = q_lo + lane + kWave * it;
           const v4f v = *reinterpret_cast<const v4f*>(b + cpad((uint32_t)(4 * min(qc, q_hi - 1))));
-          const uint32_t off = (ok && qc < q_hi) ? (uint32_t)(a4 + 4 * qc) * 4u : kOOB;
-          __builtin_amdgcn_raw_buffer_store_b128(
-              v4u{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                  __float_as_uint(v[3])},
-              ry, off, rowoff, kStream);
+          const uint32_t off = (ok && qc < q_hi) ? (uint32_t)(a4 + 4 * qc) * kYB : kOOB;
+          if constexpr (kBf) {
+            typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+            __builtin_amdgcn_raw_buffer_store_b64(v2u{bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3])},
+                                                  ry, off, rowoff, kStream);
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b128(
+                v4u{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                    __float_as_uint(v[3])},
+                ry, off, rowoff, kStream);
+          }
         }
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(b[b_lds]), ry, ok ? b_off : kOOB,
-                                              rowoff, kStream);
+        if constexpr (kBf)
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bf16_bits_rne(b[b_lds]), ry,
+                                                ok ? b_off : kOOB, rowoff, kStream);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(b[b_lds]), ry, ok ? b_off : kOOB,
+                                                rowoff, kStream);
       }
       wave_lds_sync();
     }
@@ -324,7 +347,7 @@ __global__ __launch_bounds__(256) void decompress_kernel(
         const int e = min(eu, n - 1);
         const int r = e / g.nout, i = e - r * g.nout;
         hv[u] = __builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)(g.ilo + i) * 4u, 0, 0);
-        yo[u] = eu < n ? (uint32_t)r * (uint32_t)H * 4u : kOOB;
+        yo[u] = eu < n ? (uint32_t)r * (uint32_t)H * kYB : kOOB;
 #pragma unroll
         for (int p = 0; p < NP; ++p)
           v[u][p] = __builtin_amdgcn_raw_buffer_load_b16(
@@ -336,17 +359,27 @@ __global__ __launch_bounds__(256) void decompress_kernel(
 #pragma unroll
         for (int p = 0; p < NP; ++p) o = __fadd_rn(o, bf16_to_f32(v[u][p]));
         // (an entry past the end stores out of range)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), ry,
-                                              yo[u] == kOOB ? kOOB : yo[u] + hv[u] * 4u, 0, 0);
+        const uint32_t off = yo[u] == kOOB ? kOOB : yo[u] + hv[u] * kYB;
+        if constexpr (kBf)
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bf16_bits_rne(o), ry, off, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o), ry, off, 0, 0);
       }
     }
   }
 }
 
+template <bool kBf>
 __global__ __launch_bounds__(256) void decompress_general_kernel(
     const uint8_t* __restrict__ packed, int64_t pitch, const uint16_t* __restrict__ outl, int64_t P,
     int64_t T, int64_t H, int64_t k, int64_t Hq, const float* __restrict__ dec,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ cmap, float* __restrict__ y) {
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ cmap, void* __restrict__ y) {
+  auto put = [&](int64_t i, float v) {
+    if constexpr (kBf)
+      static_cast<uint16_t*>(y)[i] = (uint16_t)bf16_bits_rne(v);
+    else
+      static_cast<float*>(y)[i] = v;
+  };
   const int64_t n1 = T * Hq;
   const int64_t n2 = T * k;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -361,45 +394,80 @@ __global__ __launch_bounds__(256) void decompress_general_kernel(
         const float d = __fsub_rn((float)q, dec[(P + p) * Hq + j]);   // exact
         acc = __fadd_rn(acc, __fmul_rn(d, dec[p * Hq + j]));
       }
-      y[t * H + h] = acc;
+      put(t * H + h, acc);
     } else {
       const int64_t ii = i - n1;
       const int64_t t = ii / k, o = ii % k;
       for (int64_t p = 0; p < P; ++p) acc = __fadd_rn(acc, bf16_to_f32(outl[(p * T + t) * k + o]));
-      y[t * H + idx[o]] = acc;
+      put(t * H + idx[o], acc);
     }
   }
 }
 
-template <int NP, int kOR, int kR>
+template <int NP, int kOR, int kR, bool kBf>
 static void launch_fast(const uint8_t* packed, int64_t pitch, const uint16_t* outl, int64_t T,
                         int64_t H,
                         int64_t k, int64_t Hq, int ntiles, int rpw, int64_t nrowblk,
                         int buf_dwords, const float* dec, const int32_t* idx,
-                        const int32_t* cmap, float* y, hipStream_t s) {
+                        const int32_t* cmap, void* y, hipStream_t s) {
   const int64_t ntgrp = (ntiles + kDqWaves - 1) / kDqWaves;
   const size_t lds = (size_t)kDqWaves * kDqSub * buf_dwords * 4;
-  decompress_kernel<NP, kOR, kR><<<(unsigned)xcd_grid(ntgrp, nrowblk), 256, lds, s>>>(
+  decompress_kernel<NP, kOR, kR, kBf><<<(unsigned)xcd_grid(ntgrp, nrowblk), 256, lds, s>>>(
       packed, (int)pitch, outl, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, buf_dwords, dec,
       idx, cmap, y);
 }
 
+template <bool kBf>
+static void dispatch_fast(int64_t P, bool wide, bool small, const uint8_t* packed, int64_t pitch,
+                          const uint16_t* outl, int64_t T, int64_t H, int64_t k, int64_t Hq,
+                          int ntiles, int rpw, int64_t nrowblk, int buf_dwords, const float* dec,
+                          const int32_t* idx, const int32_t* cmap, void* y, hipStream_t s) {
+  switch (P) {
+#define BTQ_DQ_CASE(n)                                                                          \
+  case n:                                                                                       \
+    if (wide && !small)                                                                         \
+      launch_fast<n, 4, kDqRing, kBf>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk,   \
+                                      buf_dwords, dec, idx, cmap, y, s);                        \
+    else if (wide)                                                                              \
+      launch_fast<n, 4, kDqRingSmall, kBf>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw,       \
+                                           nrowblk, buf_dwords, dec, idx, cmap, y, s);          \
+    else if (!small)                                                                            \
+      launch_fast<n, 2, kDqRing, kBf>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk,   \
+                                      buf_dwords, dec, idx, cmap, y, s);                        \
+    else                                                                                        \
+      launch_fast<n, 2, kDqRingSmall, kBf>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw,       \
+                                           nrowblk, buf_dwords, dec, idx, cmap, y, s);          \
+    break;
+    BTQ_DQ_CASE(1)
+    BTQ_DQ_CASE(2)
+    BTQ_DQ_CASE(3)
+    BTQ_DQ_CASE(4)
+    BTQ_DQ_CASE(5)
+    BTQ_DQ_CASE(6)
+    BTQ_DQ_CASE(7)
+    BTQ_DQ_CASE(8)
+#undef BTQ_DQ_CASE
+  }
+}
+
 hipError_t launch_decompress(const uint8_t* packed, int64_t pitch, const uint16_t* outl, int64_t P,
                              int64_t T, int64_t H, int64_t k, const float* dec, const int32_t* idx,
-                             const int32_t* cmap, float* y, hipStream_t s) {
+                             const int32_t* cmap, void* y, bool bf16, hipStream_t s) {
+  const int64_t yb = bf16 ? 2 : 4;   // bytes per y value
   const int64_t Hq = H - k;
   const int64_t span = (H < kTileSlots + k ? H : kTileSlots + k);
   const int buf_dwords = span < 65536 ? dq_row_dwords((int)span) : (1 << 30);
   const size_t lds = (size_t)kDqWaves * kDqSub * buf_dwords * 4;
   // Buffer resources: the whole message, the decoder table and one wave's
-  // rows of y must each span fewer than 2^31 bytes. y rows take 16-byte
-  // stores: H a multiple of 4 and y 16-byte aligned.
+  // rows of y must each span fewer than 2^31 bytes. y rows take stores of 4
+  // values (16 bytes fp32, 8 bytes bf16): H a multiple of 4 and y aligned to
+  // one such store.
   const int64_t lim = int64_t(1) << 31;
   const bool fast = Hq > 0 && P <= 8 && Hq % 8 == 0 && H % 4 == 0 &&
                     (uintptr_t)packed % 4 == 0 && (uintptr_t)dec % 16 == 0 &&
-                    (uintptr_t)y % 16 == 0 && lds <= 65536 && pitch % 4 == 0 &&
+                    (uintptr_t)y % (4 * yb) == 0 && lds <= 65536 && pitch % 4 == 0 &&
                     P * T * pitch < lim &&
-                    P * T * k * 2 < lim && (2 * P + 1) * Hq * 4 < lim && 64 * H * 4 < lim;
+                    P * T * k * 2 < lim && (2 * P + 1) * Hq * 4 < lim && 64 * H * yb < lim;
   if (fast) {
     const int ntiles = (int)((Hq + kTileSlots - 1) / kTileSlots);
     // about 1024 waves (4 per CU: each wave's table loads then serve at
@@ -418,40 +486,24 @@ hipError_t launch_decompress(const uint8_t* packed, int64_t pitch, const uint16_
     // tile holds at most 64 of them on average, else 4. A tile beyond its
     // registers sums its BF16 features after the row loop.
     const bool wide = P * k > int64_t(kWave) * ntiles;
-    switch (P) {
-#define BTQ_DQ_CASE(n)                                                                           \
-  case n:                                                                                        \
-    if (wide && !small)                                                                          \
-      launch_fast<n, 4, kDqRing>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk,         \
-                                 buf_dwords, dec, idx, cmap, y, s);                              \
-    else if (wide)                                                                               \
-      launch_fast<n, 4, kDqRingSmall>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk,    \
-                                      buf_dwords, dec, idx, cmap, y, s);                         \
-    else if (!small)                                                                             \
-      launch_fast<n, 2, kDqRing>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk,         \
-                                 buf_dwords, dec, idx, cmap, y, s);                              \
-    else                                                                                         \
-      launch_fast<n, 2, kDqRingSmall>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk,    \
-                                      buf_dwords, dec, idx, cmap, y, s);                         \
-    break;
-      BTQ_DQ_CASE(1)
-      BTQ_DQ_CASE(2)
-      BTQ_DQ_CASE(3)
-      BTQ_DQ_CASE(4)
-      BTQ_DQ_CASE(5)
-      BTQ_DQ_CASE(6)
-      BTQ_DQ_CASE(7)
-      BTQ_DQ_CASE(8)
-#undef BTQ_DQ_CASE
-    }
+    if (bf16)
+      dispatch_fast<true>(P, wide, small, packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk,
+                          buf_dwords, dec, idx, cmap, y, s);
+    else
+      dispatch_fast<false>(P, wide, small, packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk,
+                           buf_dwords, dec, idx, cmap, y, s);
     return hipGetLastError();
   }
   const int64_t n = T * H;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  decompress_general_kernel<<<(unsigned)blocks, 256, 0, s>>>(packed, pitch, outl, P, T, H, k, Hq,
-                                                             dec, idx, cmap, y);
+  if (bf16)
+    decompress_general_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(packed, pitch, outl, P, T, H,
+                                                                     k, Hq, dec, idx, cmap, y);
+  else
+    decompress_general_kernel<false><<<(unsigned)blocks, 256, 0, s>>>(packed, pitch, outl, P, T, H,
+                                                                      k, Hq, dec, idx, cmap, y);
   return hipGetLastError();
 }
 

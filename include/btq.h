@@ -188,6 +188,24 @@ int btq_decompress_reduce(const uint8_t *packed, int64_t packed_pitch,
                           int64_t k, const float *dec_table, const int32_t *outlier_idx,
                           const int32_t *cmap, float *y, void *stream);
 
+/*
+ * Receiver with bf16 output -- "The Hybrid Quantization Algorithm",
+ * Inference bullet (after communication the tensors convert back to BF16).
+ *
+ * The same sum as btq_decompress_reduce, rounded once from fp32 to bf16
+ * (round to nearest even): y[t,h] = bf16(fp32 sum). Arguments, layouts and
+ * errors as for btq_decompress_reduce, except:
+ *   y    bf16 [T,H] (uint16 bits)  out, 2-byte aligned (8-byte aligned for
+ *        the fast path)
+ * For BF16 features the result is the bf16 rounding of the exact sequential
+ * fp32 sum. For int4 features it is the bf16 rounding of the value that
+ * btq_decompress_reduce writes.
+ */
+int btq_decompress_reduce_bf16(const uint8_t *packed, int64_t packed_pitch,
+                               const uint16_t *outliers, int64_t P, int64_t T, int64_t H,
+                               int64_t k, const float *dec_table, const int32_t *outlier_idx,
+                               const int32_t *cmap, uint16_t *y, void *stream);
+
 /* Code bytes per packed row: ceil((H-k)/2); -1 if H < 1 or k is outside [0,H]. */
 int64_t btq_packed_row_bytes(int64_t H, int64_t k);
 

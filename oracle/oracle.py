@@ -309,7 +309,23 @@ def decompress_reduce(packed, outliers, scale, zero_point, fmap) -> np.ndarray:
 
 
 def f32_to_bf16(y: np.ndarray) -> np.ndarray:
-    """fp32 -> bf16 bits, round to nearest even (finite inputs)."""
+    """fp32 -> bf16 bits, round to nearest even (finite inputs).
+
+    The bf16-output receiver of [Inference] (every tensor converts back to
+    BF16) rounds its fp32 sum once with this.
+    """
     u = np.asarray(y, F32).view(np.uint32).astype(np.uint64)
     lsb = (u >> np.uint64(16)) & np.uint64(1)
     return ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+
+
+def decompress_reduce_bf16(packed, outliers, scale, zero_point, fmap) -> np.ndarray:
+    """The receiver with bf16 output: the fp32 sum of decompress_reduce,
+    rounded once to bf16 (round to nearest even). Returns uint16 bits [T,H].
+
+    Page section "The Hybrid Quantization Algorithm", Inference bullet: after
+    communication the tensors are converted back to BF16. Here the terms are
+    summed in fp32 first and the sum is converted once, so the BF16 output
+    carries a single rounding.
+    """
+    return f32_to_bf16(decompress_reduce(packed, outliers, scale, zero_point, fmap))

@@ -86,6 +86,23 @@ def assert_selection_equal(sel_gpu: dict, sel_orc: dict) -> None:
     assert_bits_equal(sel_gpu["dec"], sel_orc["dec"], "dec_table")
 
 
+def assert_y_bf16_close(y_gpu_bits: np.ndarray, y_orc: np.ndarray, scale: np.ndarray, idx) -> None:
+    """bf16 output: within the fp32 tolerance plus half a bf16 ulp (<= 2^-8 |y|)
+    of the oracle's fp32 sum; BF16 columns equal the oracle's rounding exactly."""
+    g = (np.asarray(y_gpu_bits).view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    tol = TOL_REL * np.abs(y_orc) + TOL_ABS_SCALE * scale.max(0)[None, :] + \
+        np.abs(y_orc.astype(np.float64)) * 2.0 ** -8
+    err = np.abs(g.astype(np.float64) - y_orc.astype(np.float64))
+    bad = ~(err <= tol)
+    assert not bad.any(), (f"y bf16: {int(bad.sum())} outside tolerance; worst excess "
+                           f"{float(np.max(err - tol))} at {np.argwhere(bad)[0]}")
+    idx = np.asarray(idx, np.int64)
+    if idx.size:
+        want = O.f32_to_bf16(y_orc[:, idx])
+        assert np.array_equal(np.asarray(y_gpu_bits).view(np.uint16)[:, idx], want), \
+            "y bf16: BF16 feature columns differ from the oracle's rounding"
+
+
 def assert_y_close(y_gpu: np.ndarray, y_orc: np.ndarray, scale: np.ndarray, idx) -> None:
     tol = TOL_REL * np.abs(y_orc) + TOL_ABS_SCALE * scale.max(0)[None, :]
     err = np.abs(y_gpu.astype(np.float64) - y_orc.astype(np.float64))

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -163,3 +163,17 @@ def test_decompress_validation(lib):
     assert decompress(lib, dec=A + 1) == ALIGN
     assert decompress(lib, T=0, y=None, pk=None, ol=None) == OK
     assert decompress(lib, T=0, k=16, cmap=None, dec=None) == OK
+
+
+def decompress_bf16(lib, pk=A, pitch=128, ol=A, P=2, T=4, H=16, k=4, dec=A, idx=A, cmap=A, y=A):
+    return lib.btq_decompress_reduce_bf16(pk, pitch, ol, P, T, H, k, dec, idx, cmap, y, None)
+
+
+def test_decompress_bf16_validation(lib):
+    assert decompress_bf16(lib, k=17) == SHAPE
+    assert decompress_bf16(lib, pitch=5) == SHAPE
+    assert decompress_bf16(lib, dec=None) == ARG
+    assert decompress_bf16(lib, y=None) == ARG
+    assert decompress_bf16(lib, y=A + 1) == ALIGN      # bf16 y: 2-byte alignment
+    assert decompress_bf16(lib, dec=A + 2) == ALIGN
+    assert decompress_bf16(lib, T=0, y=None, pk=None, ol=None) == OK

@@ -141,3 +141,33 @@ def test_range_ranked_beats_random_selection():
                    for i in range(8)])
     assert ranked < 0.1 * rnd
     assert rnd > 0.5 * none
+
+
+def test_f32_to_bf16_matches_torch_round_to_nearest_even():
+    # Library routine: torch's fp32 -> bf16 conversion rounds to nearest even.
+    rng = np.random.default_rng(21)
+    u = rng.integers(0, 2 ** 32, 1 << 20, dtype=np.uint64).astype(np.uint32)
+    u = u[(u & 0x7F800000) != 0x7F800000]                      # finite only
+    ties = (rng.integers(0, 2 ** 16, 4096).astype(np.uint32) << 16) | 0x8000   # exact halves
+    ties = ties[(ties & 0x7F800000) != 0x7F800000]
+    special = np.array([0, 0x80000000, 0x00000001, 0x7F7FFFFF, 0x3F808000, 0x3F818000,
+                        0x3F7FFFFF, 0xBF808000], np.uint32)
+    f = np.concatenate([u, ties, special]).view(np.float32)
+    ours = O.f32_to_bf16(f)
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    # ties go to the even neighbour: 1 + 2^-8 exactly halfway between 1 and 1 + 2^-7
+    assert O.f32_to_bf16(np.array([1.0 + 2.0 ** -8], np.float32))[0] == 0x3F80
+    assert O.f32_to_bf16(np.array([1.0 + 3 * 2.0 ** -8], np.float32))[0] == 0x3F82
+
+
+def test_bf16_output_is_one_rounding_of_the_fp32_sum():
+    rng = np.random.default_rng(22)
+    x = W.to_u16(W.draw(4, 16, 96, 31, cols=[5, 50], outlier_factor=30.0))
+    sel, packed, outl, y32 = _pipeline(x, 6)
+    y16 = O.decompress_reduce_bf16(packed, outl, sel["scale"], sel["zero_point"], sel["fmap"])
+    assert y16.dtype == np.uint16 and y16.shape == y32.shape
+    back = (y16.astype(np.uint32) << 16).view(np.float32)
+    # half a bf16 ulp (8 significant bits) is at most 2^-8 |y|
+    assert np.all(np.abs(back.astype(np.float64) - y32) <= np.abs(y32.astype(np.float64)) * 2.0 ** -8)
+    assert np.array_equal(y16, O.f32_to_bf16(y32))

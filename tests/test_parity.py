@@ -1,8 +1,10 @@
 """GPU parity: every HIP step against the CPU oracle, element by element.
 
 Bar: calibration statistics equal by value; parameters, outlier set, maps,
-packed codes and BF16 blocks bitwise; reduced output within
-1e-3*|y| + 1e-2*max_p scale (BF16 feature columns bit-exact).
+codec tables, packed codes and BF16 blocks bitwise; reduced output within
+1e-3*|y| + 1e-2*max_p scale (BF16 feature columns bit-exact). The bf16-output
+receiver: within that bound plus half a bf16 ulp, BF16 columns equal to the
+oracle's rounding, and bit-identical to rounding the fp32 receiver's output.
 """
 import numpy as np
 import pytest
@@ -12,7 +14,7 @@ import bit_tensor_activation_amd as B
 from oracle import oracle as O
 import workloads as W
 from helpers import (assert_bits_equal, assert_selection_equal, assert_stats_equal, assert_y_close,
-                     oracle_calib, oracle_compress_rows, say, u16)
+                     assert_y_bf16_close, oracle_calib, oracle_compress_rows, say, u16)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -57,9 +59,13 @@ def run_both(calib_xs, x, k, momentum, *, x_offset=0, table_offset=0, pitch=None
     assert_bits_equal(ol.view(torch.int16), ol_o.view(np.int16), "outliers")
 
     y = B.btq_decompress_reduce(pk, ol, H, dec, sel_g["outlier_idx"], sel_g["cmap"])
+    y16 = B.btq_decompress_reduce_bf16(pk, ol, H, dec, sel_g["outlier_idx"], sel_g["cmap"])
     y_o = O.decompress_reduce(pk_o, ol_o, sel_o["scale"], sel_o["zero_point"], sel_o["fmap"])
     torch.cuda.synchronize()
     assert_y_close(y.cpu().numpy(), y_o, sel_o["scale"], sel_o["idx"])
+    assert_y_bf16_close(y16.cpu().numpy(), y_o, sel_o["scale"], sel_o["idx"])
+    # the bf16 output is one round-to-nearest-even of the fp32 output
+    assert torch.equal(y16, y.to(torch.bfloat16).view(torch.int16))
     return sel_g, pk, ol, y
 
 

@@ -14,7 +14,9 @@ Checked on every case:
     oracle's message for those rows (the rows include both ends, the
     benchmark's row-block boundaries and random rows);
   * y on the same rows: within 1e-3*|y| + 1e-2*max_p scale, BF16 columns
-    bit-exact;
+    bit-exact; the bf16-output receiver within that plus half a bf16 ulp,
+    its BF16 columns equal to the oracle's rounding, and over the whole
+    tensor bit-identical to rounding the fp32 receiver's output;
   * properties over the whole tensors: every padding byte of the packed
     rows is zero and y is finite.
 """
@@ -26,7 +28,7 @@ import bit_tensor_activation_amd as B
 from oracle import oracle as O
 import workloads as W
 from helpers import (assert_bits_equal, assert_selection_equal, assert_stats_equal, assert_y_close,
-                     oracle_calib, oracle_compress_rows, say, u16)
+                     assert_y_bf16_close, oracle_calib, oracle_compress_rows, say, u16)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -92,7 +94,10 @@ def test_full_size(name, T, k, nb):
     x = W.batch(w, W.PHASE_INFER, b, T=T, device=DEV)
     pk, ol = B.btq_compress_pack(x, k, sel_g["enc"], sel_g["outlier_idx"], sel_g["cmap"])
     y = B.btq_decompress_reduce(pk, ol, H, sel_g["dec"], sel_g["outlier_idx"], sel_g["cmap"])
+    y16 = B.btq_decompress_reduce_bf16(pk, ol, H, sel_g["dec"], sel_g["outlier_idx"],
+                                       sel_g["cmap"])
     torch.cuda.synchronize()
+    assert torch.equal(y16, y.to(torch.bfloat16).view(torch.int16)), "bf16 y is not RNE(fp32 y)"
     pitch = pk.shape[2]
     assert pitch == B.btq_packed_pitch(H, k)
     Bq = B.btq_packed_row_bytes(H, k)
@@ -110,5 +115,6 @@ def test_full_size(name, T, k, nb):
                       "outliers (sampled rows)")
     y_o = O.decompress_reduce(pk_o, ol_o, sel_o["scale"], sel_o["zero_point"], sel_o["fmap"])
     assert_y_close(y[ridx].cpu().numpy(), y_o, sel_o["scale"], sel_o["idx"])
-    del x, pk, ol, y
+    assert_y_bf16_close(y16[ridx].cpu().numpy(), y_o, sel_o["scale"], sel_o["idx"])
+    del x, pk, ol, y, y16
     torch.cuda.empty_cache()
