@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     btq_enc_table_floats,
     btq_packed_pitch,
     btq_packed_row_bytes,
+    btq_select_features,
     btq_select_outliers,
     btq_select_workspace_bytes,
     btq_status_str,

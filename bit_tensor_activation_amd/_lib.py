@@ -21,6 +21,8 @@ SIGNATURES = {
     "btq_select_outliers": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _SZ, _P]),
     "btq_select_workspace_bytes": (_SZ, [_I64, _I64]),
+    "btq_select_features": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 _P]),
     "btq_enc_table_floats": (_I64, [_I64, _I64, _I64]),
     "btq_dec_table_floats": (_I64, [_I64, _I64, _I64]),
     "btq_compress_pack": (_I, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _P, _P]),

@@ -119,6 +119,52 @@ def btq_select_outliers(run_min: torch.Tensor, run_max: torch.Tensor, k: int, ou
     """
     dev = _device(run_min)
     P, H = run_min.shape
+    o = _select_outputs(run_min, run_max, k, out)
+    need = btq_select_workspace_bytes(P, H)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    lib = _lib.load()
+    st = lib.btq_select_outliers(_ptr(run_min), _ptr(run_max), P, H, k, _ptr(o["scale"]),
+                                 _ptr(o["rscale"]), _ptr(o["zero_point"]), _ptr(o["outlier_idx"]),
+                                 _ptr(o["fmap"]), _ptr(o["cmap"]), _ptr(o["enc"]),
+                                 _ptr(o["dec"]), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(),
+                                 _stream(dev, stream))
+    _lib.check(st, "btq_select_outliers")
+    return o
+
+
+def btq_select_features(run_min: torch.Tensor, run_max: torch.Tensor, features, out: dict = None,
+                        stream=None) -> dict:
+    """Parameters, maps and tables for a BF16 set chosen by the caller.
+
+    features: the k BF16 features (any int sequence, array or tensor), distinct
+    and ascending. Returns the same dict as btq_select_outliers. The call
+    waits for its stream, because the set travels from host memory.
+    """
+    dev = _device(run_min)
+    P, H = run_min.shape
+    feat = torch.as_tensor(features).to(device="cpu", dtype=torch.int32).contiguous().reshape(-1)
+    k = feat.numel()
+    o = _select_outputs(run_min, run_max, k, out)
+    lib = _lib.load()
+    st = lib.btq_select_features(_ptr(run_min), _ptr(run_max), P, H, k, _ptr(feat),
+                                 _ptr(o["scale"]), _ptr(o["rscale"]), _ptr(o["zero_point"]),
+                                 _ptr(o["outlier_idx"]), _ptr(o["fmap"]), _ptr(o["cmap"]),
+                                 _ptr(o["enc"]), _ptr(o["dec"]), _stream(dev, stream))
+    _lib.check(st, "btq_select_features")
+    if stream is None:
+        torch.cuda.current_stream(dev).synchronize()
+    elif hasattr(stream, "synchronize"):
+        stream.synchronize()
+    else:
+        torch.cuda.ExternalStream(int(stream), device=dev).synchronize()
+    return o
+
+
+def _select_outputs(run_min: torch.Tensor, run_max: torch.Tensor, k: int, out) -> dict:
+    dev = _device(run_min)
+    P, H = run_min.shape
     _need(run_min, "run_min", (torch.float32,), (P, H), dev)
     _need(run_max, "run_max", (torch.float32,), (P, H), dev)
     if not 0 <= k <= H:
@@ -138,17 +184,6 @@ def btq_select_outliers(run_min: torch.Tensor, run_max: torch.Tensor, k: int, ou
                           ("enc", torch.float32, (P, H - k, 2)),
                           ("dec", torch.float32, (2 * P + 1, H - k))):
         _need(o[name], name, (dt,), shp, dev)
-    need = btq_select_workspace_bytes(P, H)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    lib = _lib.load()
-    st = lib.btq_select_outliers(_ptr(run_min), _ptr(run_max), P, H, k, _ptr(o["scale"]),
-                                 _ptr(o["rscale"]), _ptr(o["zero_point"]), _ptr(o["outlier_idx"]),
-                                 _ptr(o["fmap"]), _ptr(o["cmap"]), _ptr(o["enc"]),
-                                 _ptr(o["dec"]), _ptr(workspace),
-                                 workspace.numel() * workspace.element_size(),
-                                 _stream(dev, stream))
-    _lib.check(st, "btq_select_outliers")
     return o
 
 

@@ -109,6 +109,34 @@ int btq_select_outliers(const float* run_min, const float* run_max, int64_t P, i
                                        (float*)workspace, (hipStream_t)stream));
 }
 
+int btq_select_features(const float* run_min, const float* run_max, int64_t P, int64_t H,
+                        int64_t k, const int32_t* features, float* scale, float* rscale,
+                        uint8_t* zero_point, int32_t* outlier_idx, int32_t* fmap, int32_t* cmap,
+                        float* enc_table, float* dec_table, void* stream) {
+  if (P < 1 || P > kMaxP || H < 1 || H > kMaxH) return BTQ_ERR_SHAPE;
+  int st = check_k(H, k);
+  if (st != BTQ_OK) return st;
+  if (!run_min || !run_max || !scale || !rscale || !zero_point || !fmap) return BTQ_ERR_ARG;
+  if ((k > 0 && (!outlier_idx || !features)) || (k < H && (!cmap || !enc_table || !dec_table)))
+    return BTQ_ERR_ARG;
+  if (!aligned(run_min, 4) || !aligned(run_max, 4) || !aligned(scale, 4) ||
+      !aligned(rscale, 4) || !aligned(outlier_idx, 4) || !aligned(fmap, 4) || !aligned(cmap, 4) ||
+      !aligned(enc_table, 4) || !aligned(dec_table, 4) || !aligned(features, 4))
+    return BTQ_ERR_ALIGN;
+  for (int64_t i = 0; i < k; ++i) {   // distinct, ascending, inside [0, H)
+    const int64_t h = features[i];
+    if (h < 0 || h >= H || (i > 0 && h <= features[i - 1])) return BTQ_ERR_ARG;
+  }
+  const hipStream_t s = (hipStream_t)stream;
+  if (k > 0) {
+    const hipError_t e = hipMemcpyAsync(outlier_idx, features, (size_t)k * sizeof(int32_t),
+                                        hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return BTQ_ERR_HIP;
+  }
+  return hip_status(btq::launch_select_set(run_min, run_max, P, H, k, scale, rscale, zero_point,
+                                           outlier_idx, fmap, cmap, enc_table, dec_table, s));
+}
+
 int btq_compress_pack(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
                       const float* enc_table, const int32_t* outlier_idx, const int32_t* cmap,
                       uint8_t* packed, int64_t packed_pitch, uint16_t* outliers, void* stream) {

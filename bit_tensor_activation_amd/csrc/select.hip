@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void qparams_kernel(
     zp[i] = (uint8_t)z;
     sc = __fadd_rn(sc, w);                      // p ascending, from +0
   }
-  score[h] = sc;
+  if (score) score[h] = sc;
 }
 
 // Scores are sums of non-negative widths, so their bit patterns order like
@@ -56,6 +56,50 @@ __device__ __forceinline__ unsigned long long rank_key(float s, int64_t h) {
 }
 
 constexpr int kSelThreads = 1024;
+
+// Ordered compaction in ascending h, one 1024-thread block: i = number of
+// selected features below h, j = h - i. Selected h gets fmap = -1 - i (and
+// idx[i] = h when idx is given), the others fmap = j and cmap[j] = h. The
+// guards keep every write in bounds even if sel() picks a wrong count.
+template <class Sel>
+__device__ void write_maps(Sel sel, int64_t H, int64_t k, int32_t* __restrict__ idx,
+                           int32_t* __restrict__ fmap, int32_t* __restrict__ cmap,
+                           unsigned* wave_cnt) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int64_t sel_base = 0;
+  for (int64_t base = 0; base < H; base += kSelThreads) {
+    const int64_t h = base + tid;
+    const bool in = h < H;
+    const bool f = in && sel(h);
+    const unsigned long long b = __ballot(f);
+    if (lane == 0) wave_cnt[wave] = (unsigned)__popcll(b);
+    __syncthreads();
+    int64_t wp = 0, tot = 0;
+    for (int w = 0; w < kSelThreads / kWave; ++w) {
+      const unsigned n = wave_cnt[w];
+      if (w < wave) wp += n;
+      tot += n;
+    }
+    if (in) {
+      const int64_t i = sel_base + wp + __popcll(b & below);
+      const int64_t j = h - i;
+      if (f) {
+        if (i < k) {
+          if (idx) idx[i] = (int32_t)h;
+          fmap[h] = (int32_t)(-1 - i);
+        }
+      } else if (j < H - k) {
+        cmap[j] = (int32_t)h;
+        fmap[h] = (int32_t)j;
+      }
+    }
+    sel_base += tot;
+    __syncthreads();
+  }
+}
 
 __global__ __launch_bounds__(kSelThreads) void topk_maps_kernel(
     const float* __restrict__ score, int64_t H, int64_t k, int32_t* __restrict__ idx,
@@ -101,38 +145,28 @@ __global__ __launch_bounds__(kSelThreads) void topk_maps_kernel(
     kth = prefix;   // the k-th largest key itself
   }
 
-  // Ordered compaction in ascending h. i = #selected below h, j = h - i.
-  const int lane = tid & (kWave - 1);
-  const int wave = tid >> 6;
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  int64_t sel_base = 0;
-  for (int64_t base = 0; base < H; base += kSelThreads) {
-    const int64_t h = base + tid;
-    const bool in = h < H;
-    const bool f = in && (all || (!none && rank_key(score[h], h) >= kth));
-    const unsigned long long b = __ballot(f);
-    if (lane == 0) wave_cnt[wave] = (unsigned)__popcll(b);
-    __syncthreads();
-    int64_t wp = 0, tot = 0;
-    for (int w = 0; w < kSelThreads / kWave; ++w) {
-      const unsigned n = wave_cnt[w];
-      if (w < wave) wp += n;
-      tot += n;
-    }
-    if (in) {
-      const int64_t i = sel_base + wp + __popcll(b & below);
-      const int64_t j = h - i;
-      if (f) {
-        idx[i] = (int32_t)h;
-        fmap[h] = (int32_t)(-1 - i);
-      } else {
-        cmap[j] = (int32_t)h;
-        fmap[h] = (int32_t)j;
-      }
-    }
-    sel_base += tot;
-    __syncthreads();
-  }
+  write_maps(
+      [&](int64_t h) { return all || (!none && rank_key(score[h], h) >= kth); }, H, k, idx, fmap,
+      cmap, wave_cnt);
+}
+
+// Maps for a BF16 set given in ascending h (checked on the host): membership
+// by binary search over idx.
+__global__ __launch_bounds__(kSelThreads) void set_maps_kernel(const int32_t* __restrict__ idx,
+                                                               int64_t H, int64_t k,
+                                                               int32_t* __restrict__ fmap,
+                                                               int32_t* __restrict__ cmap) {
+  __shared__ unsigned wave_cnt[kSelThreads / kWave];
+  write_maps(
+      [&](int64_t h) {
+        int64_t lo = 0, hi = k;   // first i with idx[i] >= h
+        while (lo < hi) {
+          const int64_t mid = (lo + hi) >> 1;
+          if (idx[mid] < h) lo = mid + 1; else hi = mid;
+        }
+        return lo < k && idx[lo] == h;
+      },
+      H, k, nullptr, fmap, cmap, wave_cnt);
 }
 
 // enc[p, j] = (rscale, zero point) and dec[p, j] = scale, dec[P+p, j] = zero
@@ -167,6 +201,24 @@ hipError_t launch_select(const float* run_min, const float* run_max, int64_t P, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   topk_maps_kernel<<<1, kSelThreads, 0, s>>>(ws_score, H, k, idx, fmap, cmap);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t Hq = H - k;
+  if (Hq == 0) return hipSuccess;
+  codec_tables_kernel<<<(unsigned)((Hq + 255) / 256), 256, 0, s>>>(scale, rscale, zp, cmap, P, H,
+                                                                    Hq, enc, dec);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_set(const float* run_min, const float* run_max, int64_t P, int64_t H,
+                             int64_t k, float* scale, float* rscale, uint8_t* zp,
+                             const int32_t* idx, int32_t* fmap, int32_t* cmap, float* enc,
+                             float* dec, hipStream_t s) {
+  qparams_kernel<<<(unsigned)((H + 255) / 256), 256, 0, s>>>(run_min, run_max, P, H, scale,
+                                                              rscale, zp, nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  set_maps_kernel<<<1, kSelThreads, 0, s>>>(idx, H, k, fmap, cmap);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t Hq = H - k;

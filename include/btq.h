@@ -130,6 +130,27 @@ int btq_select_outliers(const float *run_min, const float *run_max,
 
 size_t btq_select_workspace_bytes(int64_t P, int64_t H);
 
+/*
+ * Selection with the BF16 set given by the caller -- the comparison in
+ * "Key Observations and Future Directions" (features picked at random
+ * instead of by range), and any other selection rule computed elsewhere.
+ *
+ * Same parameters, maps and tables as btq_select_outliers, with the
+ * ranking replaced by the given set:
+ *   features      i32 [k]  in, HOST memory: k distinct features in
+ *                          ascending order, each in [0, H). Anything else
+ *                          returns BTQ_ERR_ARG and enqueues nothing.
+ *   outlier_idx   i32 [k]  out (device): a copy of features, made by a
+ *                          host-to-device copy on `stream`. Keep `features`
+ *                          unchanged until the stream has passed this call.
+ * Every other argument is as in btq_select_outliers. No workspace is needed.
+ */
+int btq_select_features(const float *run_min, const float *run_max,
+                        int64_t P, int64_t H, int64_t k, const int32_t *features,
+                        float *scale, float *rscale, uint8_t *zero_point,
+                        int32_t *outlier_idx, int32_t *fmap, int32_t *cmap,
+                        float *enc_table, float *dec_table, void *stream);
+
 /* Floats in enc_table (2*P*(H-k)) and dec_table ((2P+1)*(H-k)); -1 for
  * invalid sizes. */
 int64_t btq_enc_table_floats(int64_t P, int64_t H, int64_t k);
@@ -147,8 +168,8 @@ int64_t btq_dec_table_floats(int64_t P, int64_t H, int64_t k);
  * H-k leaves the last high nibble 0. The BF16 features are copied bit for
  * bit: outliers[p,t,i] = x[p,t,outlier_idx[i]].
  *   x          bf16 [P,T,H]                       in
- *   enc_table  fp32 [P,H-k,2]                     in (from btq_select_outliers)
- *   outlier_idx i32 [k], cmap i32 [H-k]           in (from btq_select_outliers)
+ *   enc_table  fp32 [P,H-k,2]                     in (from a selection call)
+ *   outlier_idx i32 [k], cmap i32 [H-k]           in (from a selection call)
  *   packed     u8   [P,T,packed_pitch]            out: row (p,t) holds its
  *              Bq = btq_packed_row_bytes(H,k) code bytes, then packed_pitch-Bq
  *              zero bytes
@@ -157,7 +178,7 @@ int64_t btq_dec_table_floats(int64_t P, int64_t H, int64_t k);
  *              the kernels write whole lines; Bq gives the densest message.
  *   outliers   bf16 [P,T,k]                       out
  * The maps are trusted: outlier_idx and cmap must partition 0..H-1, each in
- * ascending order, as btq_select_outliers writes them.
+ * ascending order, as the selection calls write them.
  */
 int btq_compress_pack(const uint16_t *x, int64_t P, int64_t T, int64_t H, int64_t k,
                       const float *enc_table, const int32_t *outlier_idx,

@@ -137,14 +137,26 @@ def top_k_features(score: np.ndarray, k: int):
         raise ValueError("k must lie in [0, H]")
     h = np.arange(H)
     order = np.lexsort((h, -score))           # score descending, then h ascending
-    idx = np.sort(order[:k]).astype(np.int32)
+    return maps_for_set(np.sort(order[:k]), H)
+
+
+def maps_for_set(idx, H: int):
+    """Maps for a BF16 set given as k distinct features in ascending h.
+
+    Returns (idx, fmap, cmap) as top_k_features does: the int4 slots are the
+    other features in ascending h.
+    """
+    idx = np.asarray(idx, np.int64)
+    k = idx.shape[0]
+    if k and (np.any(np.diff(idx) <= 0) or idx[0] < 0 or idx[-1] >= H):
+        raise ValueError("the BF16 set must be distinct features in [0, H), ascending")
     keep = np.ones(H, bool)
     keep[idx] = False
     cmap = np.nonzero(keep)[0].astype(np.int32)
     fmap = np.empty(H, np.int32)
     fmap[cmap] = np.arange(H - k, dtype=np.int32)
     fmap[idx] = -1 - np.arange(k, dtype=np.int32)
-    return idx, fmap, cmap
+    return idx.astype(np.int32), fmap, cmap
 
 
 def codec_tables(scale, rscale, zero_point, cmap):
@@ -178,6 +190,19 @@ def select_outliers(run_min, run_max, k: int) -> dict:
     scale, rscale, zp, width = quant_params(run_min, run_max)
     score = range_score(width)
     idx, fmap, cmap = top_k_features(score, k)
+    enc, dec = codec_tables(scale, rscale, zp, cmap)
+    return dict(scale=scale, rscale=rscale, zero_point=zp, width=width,
+                score=score, idx=idx, fmap=fmap, cmap=cmap, enc=enc, dec=dec)
+
+
+def select_features(run_min, run_max, idx) -> dict:
+    """[Calibration] parameters with a BF16 set chosen by the caller instead
+    of the range ranking of [Selection] (for instance random features, the
+    baseline that [Future] compares against). Same outputs as
+    select_outliers."""
+    scale, rscale, zp, width = quant_params(run_min, run_max)
+    score = range_score(width)
+    idx, fmap, cmap = maps_for_set(idx, scale.shape[1])
     enc, dec = codec_tables(scale, rscale, zp, cmap)
     return dict(scale=scale, rscale=rscale, zero_point=zp, width=width,
                 score=score, idx=idx, fmap=fmap, cmap=cmap, enc=enc, dec=dec)

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -116,6 +116,38 @@ def test_select_validation(lib):
     assert select(lib, cmap=A + 2) == ALIGN
     # zero-length outputs may be NULL; these pass validation, so they are not
     # called here (they would launch).
+
+
+def host_set(*h):
+    arr = (ctypes.c_int32 * max(len(h), 1))(*h)
+    return arr, ctypes.addressof(arr)
+
+
+GOOD_SET = host_set(1, 5, 9, 15)
+
+
+def select_set(lib, rmin=A, rmax=A, P=2, H=16, k=4, feat=GOOD_SET[1], sc=A, rs=A, zp=A, idx=A,
+               fmap=A, cmap=A, enc=A, dec=A):
+    return lib.btq_select_features(rmin, rmax, P, H, k, feat, sc, rs, zp, idx, fmap, cmap, enc,
+                                   dec, None)
+
+
+def test_select_features_validation(lib):
+    assert select_set(lib, k=-1) == SHAPE
+    assert select_set(lib, k=17) == SHAPE
+    assert select_set(lib, H=0) == SHAPE
+    assert select_set(lib, feat=None) == ARG
+    assert select_set(lib, idx=None) == ARG
+    assert select_set(lib, cmap=None) == ARG
+    assert select_set(lib, enc=None) == ARG
+    assert select_set(lib, zp=None) == ARG
+    assert select_set(lib, feat=GOOD_SET[1] + 2) == ALIGN
+    assert select_set(lib, dec=A + 1) == ALIGN
+    # sets that are not k distinct ascending features of [0, H): rejected on
+    # the host before anything is enqueued
+    for bad in ((1, 5, 5, 9), (5, 1, 9, 15), (-1, 5, 9, 15), (1, 5, 9, 16), (0, 1, 2, 99)):
+        arr, ptr = host_set(*bad)
+        assert select_set(lib, feat=ptr) == ARG, bad
 
 
 def compress(lib, x=A, P=2, T=4, H=16, k=4, enc=A, idx=A, cmap=A, pk=A, pitch=128, ol=A):

@@ -112,3 +112,36 @@ def test_codec_tables_are_the_parameters_in_message_order():
             exact -= float(sel["zero_point"][p, h]) * float(sel["scale"][p, h])
         # the fp32 bias is the exact sum up to P roundings
         assert abs(dec[2 * P, j] - exact) <= 2 * P * 2.0 ** -24 * (abs(exact) + 15 * P * sel["scale"][:, h].max())
+
+
+@pytest.mark.parametrize("H,k,seed", [(1, 0, 0), (1, 1, 1), (40, 7, 2), (300, 0, 3), (300, 300, 4),
+                                      (517, 64, 5)])
+def test_maps_for_a_given_set_brute_force(H, k, seed):
+    rng = np.random.default_rng(seed)
+    want = np.sort(rng.choice(H, k, replace=False))
+    idx, fmap, cmap = O.maps_for_set(want, H)
+    assert idx.tolist() == want.tolist()
+    _check_maps(idx, fmap, cmap, H, k)
+
+
+def test_maps_for_a_given_set_rejects_bad_sets():
+    for bad in ([3, 2], [1, 1], [-1, 2], [0, 10]):
+        with pytest.raises(ValueError):
+            O.maps_for_set(np.array(bad), 10)
+
+
+def test_given_set_selection_matches_ranked_selection_on_its_set():
+    rng = np.random.default_rng(13)
+    mn = -np.abs(rng.standard_normal((4, 70))).astype(np.float32) * 2
+    mx = np.abs(rng.standard_normal((4, 70))).astype(np.float32) * 2
+    ranked = O.select_outliers(mn, mx, 9)
+    given = O.select_features(mn, mx, ranked["idx"])
+    for key in ("scale", "rscale", "zero_point", "score", "idx", "fmap", "cmap", "enc", "dec"):
+        assert np.array_equal(np.ascontiguousarray(given[key]).view(np.uint8),
+                              np.ascontiguousarray(ranked[key]).view(np.uint8)), key
+    # a random set: maps and tables follow the set, parameters do not change
+    other = np.sort(rng.choice(70, 9, replace=False))
+    g2 = O.select_features(mn, mx, other)
+    assert g2["idx"].tolist() == other.tolist()
+    assert np.array_equal(g2["scale"], ranked["scale"])
+    _check_maps(g2["idx"], g2["fmap"], g2["cmap"], 70, 9)

@@ -27,8 +27,11 @@ def _shifted(t: torch.Tensor, off: int) -> torch.Tensor:
     return big[off:].view(t.shape)
 
 
-def run_both(calib_xs, x, k, momentum, *, x_offset=0, table_offset=0, pitch=None):
-    """Calibrate, select, compress and decompress on both sides; compare all."""
+def run_both(calib_xs, x, k, momentum, *, x_offset=0, table_offset=0, pitch=None,
+             features=None):
+    """Calibrate, select, compress and decompress on both sides; compare all.
+
+    features: a BF16 set given to both sides in place of the range ranking."""
     P, T, H = x.shape
     rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
     rmax = torch.empty_like(rmin)
@@ -40,8 +43,12 @@ def run_both(calib_xs, x, k, momentum, *, x_offset=0, table_offset=0, pitch=None
     assert_stats_equal(rmin, mn, "run_min")
     assert_stats_equal(rmax, mx, "run_max")
 
-    sel_g = B.btq_select_outliers(rmin, rmax, k)
-    sel_o = O.select_outliers(mn, mx, k)
+    if features is None:
+        sel_g = B.btq_select_outliers(rmin, rmax, k)
+        sel_o = O.select_outliers(mn, mx, k)
+    else:
+        sel_g = B.btq_select_features(rmin, rmax, features)
+        sel_o = O.select_features(mn, mx, features)
     torch.cuda.synchronize()
     assert_selection_equal(sel_g, sel_o)
 
@@ -110,6 +117,51 @@ def test_shapes(P, T, H, k, base, cols, note):
                     device=DEV) for b in range(3)]
     x = W.draw(P, T, H, 2000, base=base, cols=cols, outlier_factor=40.0, device=DEV)
     run_both(calib, x, k, 0.9)
+
+
+# (P, T, H, k, note): a seeded random BF16 set of size k
+SET_CASES = [
+    (2, 16, 256, 8, "tiny shape"),
+    (8, 70, 2048, 64, "fast path, 4 tiles"),
+    (4, 9, 4104, 5, "partial last tile"),
+    (3, 5, 250, 0, "empty set"),
+    (2, 4, 256, 256, "every feature"),
+    (9, 17, 512, 16, "P=9: general receiver"),
+    (5, 3, 3000, 1500, "half the features"),
+]
+
+
+@pytest.mark.parametrize("P,T,H,k,note", SET_CASES, ids=[c[-1] for c in SET_CASES])
+def test_given_feature_set(P, T, H, k, note):
+    say(f"case: given set P={P} T={T} H={H} k={k} ({note})")
+    cols = [H // 3, H - 1]
+    calib = [W.draw(P, 8, H, 3000 + b, cols=cols, outlier_factor=40.0, device=DEV)
+             for b in range(2)]
+    x = W.draw(P, T, H, 3100, cols=cols, outlier_factor=40.0, device=DEV)
+    feats = np.sort(np.random.default_rng(H * 7 + k).choice(H, k, replace=False))
+    sel, *_ = run_both(calib, x, k, 0.9, features=feats)
+    assert sel["outlier_idx"].cpu().numpy().tolist() == feats.tolist()
+
+
+def test_given_set_reproduces_the_ranked_selection():
+    say("case: select_features(top-k set) == select_outliers")
+    P, H, k = 8, 4104, 64
+    x = W.draw(P, 16, H, 3200, cols=list(range(7, H, 67)), outlier_factor=40.0, device=DEV)
+    rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
+    rmax = torch.empty_like(rmin)
+    B.btq_calib_update(x, rmin, rmax, 0.9, first_batch=True)
+    ranked = B.btq_select_outliers(rmin, rmax, k)
+    given = B.btq_select_features(rmin, rmax, ranked["outlier_idx"].cpu())
+    torch.cuda.synchronize()
+    for key in ranked:
+        assert torch.equal(given[key], ranked[key]), key
+
+
+def test_given_set_rejects_bad_sets():
+    rmin = torch.zeros((2, 16), dtype=torch.float32, device=DEV)
+    for bad in ([3, 2], [1, 1], [-1, 4], [0, 16]):
+        with pytest.raises(RuntimeError):
+            B.btq_select_features(rmin, rmin, bad)
 
 
 def test_misaligned_input_pointer():
