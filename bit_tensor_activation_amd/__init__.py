@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     btq_packed_row_bytes,
     btq_select_features,
     btq_select_outliers,
+    btq_select_outliers_rule,
     btq_select_workspace_bytes,
     btq_status_str,
     btq_version,

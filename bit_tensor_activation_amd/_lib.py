@@ -20,6 +20,8 @@ SIGNATURES = {
     "btq_calib_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "btq_select_outliers": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _SZ, _P]),
+    "btq_select_outliers_rule": (_I, [_P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P,
+                                      _P, _P, _SZ, _P]),
     "btq_select_workspace_bytes": (_SZ, [_I64, _I64]),
     "btq_select_features": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _P]),
@@ -40,6 +42,9 @@ BTQ_ERR_SHAPE = -2
 BTQ_ERR_ALIGN = -3
 BTQ_ERR_WORKSPACE = -4
 BTQ_ERR_HIP = -5
+
+BTQ_SCORE_SUM = 0
+BTQ_SCORE_MAX = 1
 
 _lock = threading.Lock()
 _lib = None

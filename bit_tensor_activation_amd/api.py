@@ -117,6 +117,25 @@ def btq_select_outliers(run_min: torch.Tensor, run_max: torch.Tensor, k: int, ou
     Returns a dict with scale, rscale, zero_point, outlier_idx, fmap, cmap,
     enc (the encoder table) and dec (the decoder table).
     """
+    return _select_ranked("btq_select_outliers", run_min, run_max, k, None, out, workspace,
+                          stream)
+
+
+_RULES = {"sum": _lib.BTQ_SCORE_SUM, "max": _lib.BTQ_SCORE_MAX}
+
+
+def btq_select_outliers_rule(run_min: torch.Tensor, run_max: torch.Tensor, k: int, rule: str,
+                             out: dict = None, workspace: Optional[torch.Tensor] = None,
+                             stream=None) -> dict:
+    """btq_select_outliers with the rank score chosen by `rule`: "sum" (the
+    per-shard ranges added) or "max" (the widest shard's range)."""
+    if rule not in _RULES:
+        raise ValueError(f"rule must be one of {sorted(_RULES)}")
+    return _select_ranked("btq_select_outliers_rule", run_min, run_max, k, _RULES[rule], out,
+                          workspace, stream)
+
+
+def _select_ranked(name, run_min, run_max, k, rule, out, workspace, stream) -> dict:
     dev = _device(run_min)
     P, H = run_min.shape
     o = _select_outputs(run_min, run_max, k, out)
@@ -124,13 +143,12 @@ def btq_select_outliers(run_min: torch.Tensor, run_max: torch.Tensor, k: int, ou
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     lib = _lib.load()
-    st = lib.btq_select_outliers(_ptr(run_min), _ptr(run_max), P, H, k, _ptr(o["scale"]),
-                                 _ptr(o["rscale"]), _ptr(o["zero_point"]), _ptr(o["outlier_idx"]),
-                                 _ptr(o["fmap"]), _ptr(o["cmap"]), _ptr(o["enc"]),
-                                 _ptr(o["dec"]), _ptr(workspace),
-                                 workspace.numel() * workspace.element_size(),
-                                 _stream(dev, stream))
-    _lib.check(st, "btq_select_outliers")
+    head = [_ptr(run_min), _ptr(run_max), P, H, k] + ([] if rule is None else [rule])
+    st = getattr(lib, name)(*head, _ptr(o["scale"]), _ptr(o["rscale"]), _ptr(o["zero_point"]),
+                            _ptr(o["outlier_idx"]), _ptr(o["fmap"]), _ptr(o["cmap"]),
+                            _ptr(o["enc"]), _ptr(o["dec"]), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(dev, stream))
+    _lib.check(st, name)
     return o
 
 

@@ -90,7 +90,18 @@ int btq_select_outliers(const float* run_min, const float* run_max, int64_t P, i
                         int32_t* outlier_idx, int32_t* fmap, int32_t* cmap, float* enc_table,
                         float* dec_table, void* workspace, size_t workspace_bytes,
                         void* stream) {
+  return btq_select_outliers_rule(run_min, run_max, P, H, k, BTQ_SCORE_SUM, scale, rscale,
+                                  zero_point, outlier_idx, fmap, cmap, enc_table, dec_table,
+                                  workspace, workspace_bytes, stream);
+}
+
+int btq_select_outliers_rule(const float* run_min, const float* run_max, int64_t P, int64_t H,
+                             int64_t k, int score_rule, float* scale, float* rscale,
+                             uint8_t* zero_point, int32_t* outlier_idx, int32_t* fmap,
+                             int32_t* cmap, float* enc_table, float* dec_table, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   if (P < 1 || P > kMaxP || H < 1 || H > kMaxH) return BTQ_ERR_SHAPE;
+  if (score_rule != BTQ_SCORE_SUM && score_rule != BTQ_SCORE_MAX) return BTQ_ERR_ARG;
   int st = check_k(H, k);
   if (st != BTQ_OK) return st;
   if (!run_min || !run_max || !scale || !rscale || !zero_point || !fmap) return BTQ_ERR_ARG;
@@ -106,7 +117,8 @@ int btq_select_outliers(const float* run_min, const float* run_max, int64_t P, i
   if (!aligned(workspace, 4)) return BTQ_ERR_ALIGN;
   return hip_status(btq::launch_select(run_min, run_max, P, H, k, scale, rscale, zero_point,
                                        outlier_idx, fmap, cmap, enc_table, dec_table,
-                                       (float*)workspace, (hipStream_t)stream));
+                                       (float*)workspace, score_rule == BTQ_SCORE_MAX,
+                                       (hipStream_t)stream));
 }
 
 int btq_select_features(const float* run_min, const float* run_max, int64_t P, int64_t H,

@@ -135,7 +135,7 @@ hipError_t launch_calib(const uint16_t* x, int64_t P, int64_t T, int64_t H, floa
 hipError_t launch_select(const float* run_min, const float* run_max, int64_t P, int64_t H,
                          int64_t k, float* scale, float* rscale, uint8_t* zp, int32_t* idx,
                          int32_t* fmap, int32_t* cmap, float* enc, float* dec, float* ws_score,
-                         hipStream_t s);
+                         bool score_max, hipStream_t s);
 // The same outputs for a given BF16 set: idx is a device copy of k distinct
 // features in ascending order.
 hipError_t launch_select_set(const float* run_min, const float* run_max, int64_t P, int64_t H,

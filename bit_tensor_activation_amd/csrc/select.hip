@@ -26,7 +26,7 @@ namespace btq {
 __global__ __launch_bounds__(256) void qparams_kernel(
     const float* __restrict__ run_min, const float* __restrict__ run_max, int64_t P, int64_t H,
     float* __restrict__ scale, float* __restrict__ rscale, uint8_t* __restrict__ zp,
-    float* __restrict__ score) {
+    float* __restrict__ score, bool score_max) {
   const int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (h >= H) return;
   float sc = 0.0f;
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void qparams_kernel(
     scale[i] = s;
     rscale[i] = r;
     zp[i] = (uint8_t)z;
-    sc = __fadd_rn(sc, w);                      // p ascending, from +0
+    sc = score_max ? fmaxf(sc, w) : __fadd_rn(sc, w);   // p ascending, from +0
   }
   if (score) score[h] = sc;
 }
@@ -195,9 +195,9 @@ __global__ __launch_bounds__(256) void codec_tables_kernel(
 hipError_t launch_select(const float* run_min, const float* run_max, int64_t P, int64_t H,
                          int64_t k, float* scale, float* rscale, uint8_t* zp, int32_t* idx,
                          int32_t* fmap, int32_t* cmap, float* enc, float* dec, float* ws_score,
-                         hipStream_t s) {
+                         bool score_max, hipStream_t s) {
   qparams_kernel<<<(unsigned)((H + 255) / 256), 256, 0, s>>>(run_min, run_max, P, H, scale,
-                                                              rscale, zp, ws_score);
+                                                              rscale, zp, ws_score, score_max);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   topk_maps_kernel<<<1, kSelThreads, 0, s>>>(ws_score, H, k, idx, fmap, cmap);
@@ -215,7 +215,7 @@ hipError_t launch_select_set(const float* run_min, const float* run_max, int64_t
                              const int32_t* idx, int32_t* fmap, int32_t* cmap, float* enc,
                              float* dec, hipStream_t s) {
   qparams_kernel<<<(unsigned)((H + 255) / 256), 256, 0, s>>>(run_min, run_max, P, H, scale,
-                                                              rscale, zp, nullptr);
+                                                              rscale, zp, nullptr, false);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   set_maps_kernel<<<1, kSelThreads, 0, s>>>(idx, H, k, fmap, cmap);

@@ -130,6 +130,29 @@ int btq_select_outliers(const float *run_min, const float *run_max,
 
 size_t btq_select_workspace_bytes(int64_t P, int64_t H);
 
+/* How a feature's P per-shard ranges become its rank score. */
+typedef enum {
+  BTQ_SCORE_SUM = 0,   /* width[0,h] + width[1,h] + ... (fp32, p ascending)    */
+  BTQ_SCORE_MAX = 1    /* max over p of width[p,h] (exact)                     */
+} btq_score_rule;
+
+/*
+ * btq_select_outliers with a choice of rank score -- "The Hybrid
+ * Quantization Algorithm", Selection bullet: features are ranked by their
+ * quantization ranges, which are per device, and the page does not say how
+ * one feature's ranges on the P devices combine. BTQ_SCORE_SUM is the
+ * reading btq_select_outliers uses; BTQ_SCORE_MAX ranks a feature by its
+ * widest shard. Only the score (and so the set, maps and tables) changes;
+ * every other output and argument is as in btq_select_outliers. Any other
+ * score_rule returns BTQ_ERR_ARG.
+ */
+int btq_select_outliers_rule(const float *run_min, const float *run_max,
+                             int64_t P, int64_t H, int64_t k, int score_rule,
+                             float *scale, float *rscale, uint8_t *zero_point,
+                             int32_t *outlier_idx, int32_t *fmap, int32_t *cmap,
+                             float *enc_table, float *dec_table,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
 /*
  * Selection with the BF16 set given by the caller -- the comparison in
  * "Key Observations and Future Directions" (features picked at random

@@ -105,20 +105,27 @@ def quant_params(run_min: np.ndarray, run_max: np.ndarray):
     return scale, rscale, zp, width
 
 
-def range_score(width: np.ndarray) -> np.ndarray:
-    """Rank score of each feature: its quantization range summed over shards.
+SCORE_RULES = ("sum", "max")
+
+
+def range_score(width: np.ndarray, rule: str = "sum") -> np.ndarray:
+    """Rank score of each feature from its per-shard quantization ranges.
 
     [Selection] ranks features by their quantization ranges, and ranges
     are per device ([Calibration]). The receiver has to know which
-    features every sender kept in BF16, so one set serves all shards. The
-    reading here adds each feature's ranges over the P shards in fp32,
-    folding p = 0, 1, ... from 0. That sum over 30 bounds the rounding
-    error of the summed output.
+    features every sender kept in BF16, so one set serves all shards, and
+    the P ranges of a feature must become one score. The page does not say
+    how. The main reading ("sum") adds them in fp32, folding p = 0, 1, ...
+    from 0: that sum over 30 bounds the rounding error of the summed
+    output. The alternative reading ("max") takes the widest shard's range,
+    which is exact.
     """
     width = np.asarray(width, F32)
+    if rule not in SCORE_RULES:
+        raise ValueError(f"unknown score rule {rule!r}")
     score = np.zeros(width.shape[1], F32)
     for p in range(width.shape[0]):
-        score = score + width[p]
+        score = score + width[p] if rule == "sum" else np.maximum(score, width[p])
     return score
 
 
@@ -184,11 +191,11 @@ def codec_tables(scale, rscale, zero_point, cmap):
     return enc, dec
 
 
-def select_outliers(run_min, run_max, k: int) -> dict:
+def select_outliers(run_min, run_max, k: int, rule: str = "sum") -> dict:
     """[Selection] after [Calibration]: parameters, scores, BF16 set, maps,
-    and the same parameters in message order."""
+    and the same parameters in message order. rule: see range_score."""
     scale, rscale, zp, width = quant_params(run_min, run_max)
-    score = range_score(width)
+    score = range_score(width, rule)
     idx, fmap, cmap = top_k_features(score, k)
     enc, dec = codec_tables(scale, rscale, zp, cmap)
     return dict(scale=scale, rscale=rscale, zero_point=zp, width=width,

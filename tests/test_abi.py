@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -116,6 +116,15 @@ def test_select_validation(lib):
     assert select(lib, cmap=A + 2) == ALIGN
     # zero-length outputs may be NULL; these pass validation, so they are not
     # called here (they would launch).
+
+
+def test_select_rule_validation(lib):
+    def call(rule, k=4):
+        return lib.btq_select_outliers_rule(A, A, 2, 16, k, rule, A, A, A, A, A, A, A, A, A, BIG,
+                                            None)
+    assert call(2) == ARG
+    assert call(-1) == ARG
+    assert call(_lib.BTQ_SCORE_MAX, k=17) == SHAPE
 
 
 def host_set(*h):

@@ -145,3 +145,43 @@ def test_given_set_selection_matches_ranked_selection_on_its_set():
     assert g2["idx"].tolist() == other.tolist()
     assert np.array_equal(g2["scale"], ranked["scale"])
     _check_maps(g2["idx"], g2["fmap"], g2["cmap"], 70, 9)
+
+
+def test_score_rules_worked_example():
+    # widths [P=4, H=3]: feature 1 is wide on one shard only, feature 2 on
+    # every shard a little. Sum: [4, 7, 5] -> feature 1 first; max: [1, 4, 5]
+    # -> feature 2 first.
+    w = np.array([[1, 1, 5], [1, 1, 0], [1, 1, 0], [1, 4, 0]], np.float32)
+    assert O.range_score(w, "sum").tolist() == [4.0, 7.0, 5.0]
+    assert O.range_score(w, "max").tolist() == [1.0, 4.0, 5.0]
+    assert O.top_k_features(O.range_score(w, "sum"), 1)[0].tolist() == [1]
+    assert O.top_k_features(O.range_score(w, "max"), 1)[0].tolist() == [2]
+    with pytest.raises(ValueError):
+        O.range_score(w, "mean")
+
+
+def test_max_score_is_an_attained_upper_bound():
+    rng = np.random.default_rng(8)
+    w = np.abs(rng.standard_normal((7, 400))).astype(np.float32) * 3
+    s = O.range_score(w, "max")
+    assert np.all(s[None, :] >= w)
+    assert np.all((w == s[None, :]).any(axis=0))
+    # one shard: both rules give the shard's own ranges
+    assert np.array_equal(O.range_score(w[:1], "max"), w[0])
+    assert np.array_equal(O.range_score(w[:1], "sum"), w[0])
+
+
+def test_select_outliers_rule_changes_only_score_and_set():
+    rng = np.random.default_rng(14)
+    mn = -np.abs(rng.standard_normal((4, 90))).astype(np.float32)
+    mx = np.abs(rng.standard_normal((4, 90))).astype(np.float32)
+    mx[2, 10] = 50.0                      # wide on one shard only
+    mx[:, 20] += 20.0                     # moderately wide on every shard
+    a = O.select_outliers(mn, mx, 1, "sum")
+    b = O.select_outliers(mn, mx, 1, "max")
+    assert a["idx"].tolist() == [20] and b["idx"].tolist() == [10]
+    for key in ("scale", "rscale", "zero_point"):
+        assert np.array_equal(a[key], b[key])
+    c = O.select_features(mn, mx, b["idx"])
+    for key in ("fmap", "cmap", "enc", "dec"):
+        assert np.array_equal(b[key], c[key])

@@ -28,10 +28,11 @@ def _shifted(t: torch.Tensor, off: int) -> torch.Tensor:
 
 
 def run_both(calib_xs, x, k, momentum, *, x_offset=0, table_offset=0, pitch=None,
-             features=None):
+             features=None, rule=None):
     """Calibrate, select, compress and decompress on both sides; compare all.
 
-    features: a BF16 set given to both sides in place of the range ranking."""
+    features: a BF16 set given to both sides in place of the range ranking.
+    rule: the rank score ("sum" or "max") through btq_select_outliers_rule."""
     P, T, H = x.shape
     rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
     rmax = torch.empty_like(rmin)
@@ -43,9 +44,12 @@ def run_both(calib_xs, x, k, momentum, *, x_offset=0, table_offset=0, pitch=None
     assert_stats_equal(rmin, mn, "run_min")
     assert_stats_equal(rmax, mx, "run_max")
 
-    if features is None:
+    if features is None and rule is None:
         sel_g = B.btq_select_outliers(rmin, rmax, k)
         sel_o = O.select_outliers(mn, mx, k)
+    elif features is None:
+        sel_g = B.btq_select_outliers_rule(rmin, rmax, k, rule)
+        sel_o = O.select_outliers(mn, mx, k, rule)
     else:
         sel_g = B.btq_select_features(rmin, rmax, features)
         sel_o = O.select_features(mn, mx, features)
@@ -155,6 +159,39 @@ def test_given_set_reproduces_the_ranked_selection():
     torch.cuda.synchronize()
     for key in ranked:
         assert torch.equal(given[key], ranked[key]), key
+
+
+def _shard_local(x: torch.Tensor, cols_by_shard: dict, factor: float) -> torch.Tensor:
+    """x with the listed columns widened on one shard each."""
+    xb = x.view(torch.bfloat16).clone()
+    for p, cols in cols_by_shard.items():
+        xb[p][:, cols] *= factor
+    return xb.view(torch.int16)
+
+
+# (P, T, H, k, rule, note)
+RULE_CASES = [
+    (4, 12, 1024, 8, "max", "max rule, shard-local outliers"),
+    (8, 70, 2048, 64, "max", "max rule, fast path"),
+    (3, 5, 250, 7, "max", "max rule, general paths"),
+    (4, 12, 1024, 8, "sum", "sum rule through the rule entry"),
+]
+
+
+@pytest.mark.parametrize("P,T,H,k,rule,note", RULE_CASES, ids=[c[-1] for c in RULE_CASES])
+def test_score_rule(P, T, H, k, rule, note):
+    say(f"case: rule={rule} P={P} T={T} H={H} k={k} ({note})")
+    everywhere = [H // 5, H // 2]
+    local = {p: [(37 * p + 11) % H, (53 * p + 101) % H] for p in range(P)}
+
+    def make(T_, seed):
+        x = W.draw(P, T_, H, seed, cols=everywhere, outlier_factor=8.0, device=DEV)
+        return _shard_local(x, local, 30.0)
+    calib = [make(8, 3300 + b) for b in range(2)]
+    sel, *_ = run_both(calib, make(T, 3400), k, 0.9, rule=rule)
+    got = set(sel["outlier_idx"].cpu().tolist())
+    if rule == "max" and k >= 2 * P:   # every shard-local column outranks the shared ones
+        assert {c for cs in local.values() for c in cs} <= got
 
 
 def test_given_set_rejects_bad_sets():

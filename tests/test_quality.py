@@ -1,0 +1,61 @@
+"""The page's two testable claims about the codec's error, measured on the
+GPU path with the synthetic workloads (shapes of the benchmark, fewer
+calibration batches).
+
+  * "Key Observations and Future Directions": random BF16 features help
+    little over pure int4, and ranking features by range is what matters.
+  * "Combating Quantization Errors with Tensor Parallelism": the summed
+    error of the quantized partial sums clusters around zero like an
+    Irwin-Hall sum (mean 0, variance sum_p s_p^2/12, excess kurtosis
+    -1.2 sum_p s_p^4 / (sum_p s_p^2)^2).
+
+Plus two properties of the codec itself: the error cannot grow with k (each
+feature's int4 parameters do not depend on k, and the ranked sets are
+nested), and outlier columns that move after calibration hurt.
+"""
+import pytest
+
+import quality as Q
+from helpers import say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_range_ranked_beats_random_selection():
+    say("case: selection rules, 7b_prefill k=64")
+    recs = {r["rule"]: r for r in Q.selection_rules("7b_prefill", 64, n_random=3,
+                                                      calib_batches=4)}
+    for r in recs.values():
+        say(f"  {r['rule']}: nmse {r['nmse']:.3e}")
+    assert recs["range_sum"]["nmse"] < 0.1 * recs["random"]["nmse"]
+    assert recs["range_max"]["nmse"] < 0.1 * recs["random"]["nmse"]
+    assert recs["random"]["nmse"] > 0.5 * recs["int4_only"]["nmse"]
+
+
+def test_error_never_grows_with_k():
+    say("case: error vs k, 7b_prefill")
+    recs = Q.error_vs_k("7b_prefill", [0, 8, 32, 41, 64, 256], calib_batches=4)
+    for a, b in zip(recs, recs[1:]):
+        assert b["nmse"] <= a["nmse"], (a["k"], b["k"])
+    by_k = {r["k"]: r for r in recs}
+    assert by_k[41]["planted_kept"] == by_k[41]["planted"]
+    assert by_k[41]["nmse"] < 0.01 * by_k[0]["nmse"]
+
+
+@pytest.mark.parametrize("P", [2, 8])
+def test_summed_error_is_irwin_hall_like(P):
+    say(f"case: Irwin-Hall statistics, P={P}")
+    r = Q.irwin_hall([P], T=512, H=2048, calib_batches=2)[0]
+    say(f"  {r}")
+    assert r["frac_in_range"] > 0.9
+    assert abs(r["mean_z"]) < r["mean_z_tolerance"]
+    assert abs(r["var_z"] - 1.0) < 0.05
+    assert abs(r["excess_kurtosis"] - r["predicted_excess_kurtosis"]) < 0.1
+
+
+def test_drifting_outliers_hurt():
+    say("case: drift, stress workload k=32")
+    recs = Q.drift("stress", [32], calib_batches=2)
+    by = {r["inference"]: r for r in recs}
+    assert by["drifted"]["nmse"] > 2.0 * by["no_drift"]["nmse"]
+    assert by["drifted"]["nmse_moved_columns"] > 10.0 * by["no_drift"]["nmse_moved_columns"]
