@@ -127,7 +127,9 @@ def _csv_rows(d: str, suffix: str):
 
 def _kernel_class(name: str):
     if "btq::" in name and "decompress" in name:
-        return "decompress_reduce"
+        # the receiver's template flag selects bf16 output
+        bf16 = name.split("(")[0].rstrip().endswith("true>")
+        return "decompress_reduce_bf16" if bf16 else "decompress_reduce"
     if "btq::" in name and "compress" in name:
         return "compress_pack"
     if "copyBuffer" in name:
@@ -167,6 +169,7 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, copy_mib: 
     wscale = statistics.median(copies["WRITE_SIZE"]) / kib
     w = W.WORKLOADS[workload]
     comp_alg, deco_alg = algorithmic_bytes(w.P, w.T[0], w.H, w.k)
+    deco16_alg = algorithmic_bytes(w.P, w.T[0], w.H, w.k, y_bytes=2)[1]
     lines = [f"# HBM traffic per launch, workload {workload} (P={w.P}, T={w.T[0]}, H={w.H}, k={w.k})",
              "# " + note.replace("\n", "\n# "),
              f"source_hash={source_hash(KERNEL_SOURCES)}",
@@ -176,7 +179,10 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, copy_mib: 
              f"copy_write_kib={statistics.median(copies['WRITE_SIZE']):.1f}",
              f"fetch_scale={fscale:.4f}",
              f"write_scale={wscale:.4f}"]
-    for name, alg in (("compress_pack", comp_alg), ("decompress_reduce", deco_alg)):
+    for name, alg in (("compress_pack", comp_alg), ("decompress_reduce", deco_alg),
+                      ("decompress_reduce_bf16", deco16_alg)):
+        if (name, "FETCH_SIZE") not in med or (name, "WRITE_SIZE") not in med:
+            continue
         f_kib, w_kib = med[(name, "FETCH_SIZE")], med[(name, "WRITE_SIZE")]
         traffic = f_kib / fscale * 1024 + w_kib / wscale * 1024
         tag = "" if name == "compress_pack" else name + "_"
