@@ -215,6 +215,33 @@ def select_features(run_min, run_max, idx) -> dict:
                 score=score, idx=idx, fmap=fmap, cmap=cmap, enc=enc, dec=dec)
 
 
+def select_outliers_per_shard(run_min, run_max, k: int) -> dict:
+    """A second reading of [Selection]: every shard keeps its own k widest
+    features in BF16, ranked by that shard's own quantization range (ties:
+    lower h first).
+
+    The message stays k BF16 values and H-k codes per row, but its layout
+    now differs between shards, so the receiver needs every shard's map.
+    Returns scale, rscale, zero_point, width, and per shard idx [P,k],
+    fmap [P,H], cmap [P,H-k] and the sender's table enc [P,H-k,2] with
+    enc[p,j] = (rscale, zero_point) of feature cmap[p,j] on shard p.
+    """
+    scale, rscale, zp, width = quant_params(run_min, run_max)
+    P, H = width.shape
+    if not 0 <= k <= H:
+        raise ValueError("k must lie in [0, H]")
+    idx = np.empty((P, k), np.int32)
+    fmap = np.empty((P, H), np.int32)
+    cmap = np.empty((P, H - k), np.int32)
+    enc = np.empty((P, H - k, 2), F32)
+    for p in range(P):
+        idx[p], fmap[p], cmap[p] = top_k_features(width[p], k)
+        enc[p, :, 0] = rscale[p, cmap[p]]
+        enc[p, :, 1] = zp[p, cmap[p]].astype(F32)
+    return dict(scale=scale, rscale=rscale, zero_point=zp, width=width, idx=idx, fmap=fmap,
+                cmap=cmap, enc=enc)
+
+
 # ------------------------------------------------- inference, sender ----
 def quantize(f: np.ndarray, rscale: np.ndarray, zero_point: np.ndarray) -> np.ndarray:
     """Codes q = clamp(round_half_even(f * rscale) + zero_point, 0, 15).
@@ -274,20 +301,31 @@ def compress_pack(x, rscale, zero_point, idx, cmap, pitch=None):
     bits with its own shard's parameters (quantized before the sum, [TP
     errors]). The message holds only the int4 features, in ascending h,
     packed two per byte, plus the BF16 features as a separate block.
-    x: uint16 [P,T,H]. rscale, zero_point: [P,H]. idx [k], cmap [H-k].
+    x: uint16 [P,T,H]. rscale, zero_point: [P,H]. idx [k], cmap [H-k]
+    shared by all shards, or idx [P,k], cmap [P,H-k] with one set per shard
+    (select_outliers_per_shard).
     Returns packed uint8 [P,T,pitch] (pitch defaults to the ceil((H-k)/2)
     code bytes; extra bytes are zero) and outliers uint16 [P,T,k].
     """
     x = np.asarray(x, np.uint16)
+    P = x.shape[0]
     cmap = np.asarray(cmap, np.int64)
     idx = np.asarray(idx, np.int64)
-    f = bf16_to_f32(x[:, :, cmap])
-    q = quantize(f, np.asarray(rscale, F32)[:, None, cmap],
-                 np.asarray(zero_point, np.uint8)[:, None, cmap])
-    packed = pack_nibbles(q)
+    if cmap.ndim == 1:
+        cmap = np.broadcast_to(cmap, (P,) + cmap.shape)
+        idx = np.broadcast_to(idx, (P,) + idx.shape)
+    rscale = np.asarray(rscale, F32)
+    zero_point = np.asarray(zero_point, np.uint8)
+    packed, outl = [], []
+    for p in range(P):
+        f = bf16_to_f32(x[p][:, cmap[p]])
+        q = quantize(f, rscale[p, cmap[p]][None, :], zero_point[p, cmap[p]][None, :])
+        packed.append(pack_nibbles(q))
+        outl.append(x[p][:, idx[p]])
+    packed = np.stack(packed)
     if pitch is not None:
         packed = pad_rows(packed, pitch)
-    return packed, x[:, :, idx].copy()
+    return packed, np.stack(outl).astype(np.uint16)
 
 
 # ----------------------------------------------- inference, receiver ----
@@ -322,18 +360,22 @@ def decompress_reduce(packed, outliers, scale, zero_point, fmap) -> np.ndarray:
     int4, or the exact BF16 value), and the sum runs in fp32 over
     p = 0, 1, ..., P-1, starting from 0. The output is fp32 [T,H].
     A packed row may be wider than its code bytes (a pitch); only the first
-    ceil((H-k)/2) bytes are read.
+    ceil((H-k)/2) bytes are read. fmap [H] is shared by all shards; fmap
+    [P,H] gives every shard its own map (select_outliers_per_shard).
     """
     packed = np.asarray(packed, np.uint8)
     outliers = np.asarray(outliers, np.uint16)
     P, T = packed.shape[:2]
-    idx, cmap = maps_from_fmap(fmap)
-    H = cmap.shape[0] + idx.shape[0]
-    q = unpack_nibbles(packed, cmap.shape[0])
+    fmap = np.asarray(fmap)
+    if fmap.ndim == 1:
+        fmap = np.broadcast_to(fmap, (P,) + fmap.shape)
+    H = fmap.shape[1]
     y = np.zeros((T, H), F32)
     for p in range(P):
+        idx, cmap = maps_from_fmap(fmap[p])
+        q = unpack_nibbles(packed[p], cmap.shape[0])
         term = np.empty((T, H), F32)
-        term[:, cmap] = dequantize(q[p], np.asarray(scale, F32)[p, cmap],
+        term[:, cmap] = dequantize(q, np.asarray(scale, F32)[p, cmap],
                                    np.asarray(zero_point, np.uint8)[p, cmap])
         term[:, idx] = bf16_to_f32(outliers[p])
         y = y + term

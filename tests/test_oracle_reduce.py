@@ -171,3 +171,35 @@ def test_bf16_output_is_one_rounding_of_the_fp32_sum():
     # half a bf16 ulp (8 significant bits) is at most 2^-8 |y|
     assert np.all(np.abs(back.astype(np.float64) - y32) <= np.abs(y32.astype(np.float64)) * 2.0 ** -8)
     assert np.array_equal(y16, O.f32_to_bf16(y32))
+
+
+@pytest.mark.parametrize("P,T,H,k", [(3, 4, 9, 2), (2, 3, 8, 0), (4, 2, 6, 6), (2, 5, 11, 4)])
+def test_per_shard_sets_brute_force(P, T, H, k):
+    # Element by element: shard p sends feature h as its bf16 value when h is
+    # in its own set, else as a 4-bit code with its own parameters; the
+    # receiver adds the P fp32 terms in shard order from 0.
+    rng = np.random.default_rng(P * 1000 + T * 100 + H + k)
+    x = W.to_u16(W.draw(P, T, H, P + H, cols=[1], outlier_factor=20.0))
+    mn, mx = O.batch_min_max(x)
+    mx = mx.copy()
+    mx[rng.integers(0, P), rng.integers(0, H)] += 30.0     # a shard-local wide range
+    sel = O.select_outliers_per_shard(mn, mx, k)
+    pk, ol = O.compress_pack(x, sel["rscale"], sel["zero_point"], sel["idx"], sel["cmap"],
+                             pitch=(H - k + 1) // 2 + 3)
+    y = O.decompress_reduce(pk, ol, sel["scale"], sel["zero_point"], sel["fmap"])
+    f = O.bf16_to_f32(x)
+    for t in range(T):
+        for h in range(H):
+            acc = np.float32(0)
+            for p in range(P):
+                if h in set(sel["idx"][p].tolist()):
+                    term = f[p, t, h]
+                else:
+                    r, z, s = sel["rscale"][p, h], sel["zero_point"][p, h], sel["scale"][p, h]
+                    q = O.quantize(np.float32(f[p, t, h]), r, z)
+                    term = O.dequantize(q, s, z)
+                acc = np.float32(acc + np.float32(term))
+            assert y[t, h].view(np.uint32) == acc.view(np.uint32), (t, h)
+    # the message itself: shard p's outlier block is its own columns
+    for p in range(P):
+        assert np.array_equal(ol[p], x[p][:, sel["idx"][p]])

@@ -185,3 +185,49 @@ def test_select_outliers_rule_changes_only_score_and_set():
     c = O.select_features(mn, mx, b["idx"])
     for key in ("fmap", "cmap", "enc", "dec"):
         assert np.array_equal(b[key], c[key])
+
+
+def test_per_shard_selection_worked_example():
+    # widths shard 0 = [1, 5, 2, 3], shard 1 = [4, 1, 1, 1] (run_min 0, so
+    # width = run_max exactly); k = 1: shard 0 keeps feature 1, shard 1
+    # feature 0.
+    mx = np.array([[1, 5, 2, 3], [4, 1, 1, 1]], np.float32)
+    sel = O.select_outliers_per_shard(np.zeros_like(mx), mx, 1)
+    assert sel["idx"].tolist() == [[1], [0]]
+    assert sel["fmap"].tolist() == [[0, -1, 1, 2], [-1, 0, 1, 2]]
+    assert sel["cmap"].tolist() == [[0, 2, 3], [1, 2, 3]]
+    # enc[p, j] = (1/scale, zero point) of feature cmap[p, j]; scale = w/15
+    assert sel["enc"][0, :, 1].tolist() == [0.0, 0.0, 0.0]
+    assert np.array_equal(sel["enc"][1, :, 0], sel["rscale"][1, [1, 2, 3]])
+
+
+def test_per_shard_selection_of_equal_shards_is_the_shared_one():
+    # Two equal shards: the summed score is exactly twice each shard's width,
+    # so every shard's own ranking equals the shared ranking.
+    rng = np.random.default_rng(31)
+    mn = -np.abs(rng.standard_normal((1, 300))).astype(np.float32)
+    mx = np.abs(rng.standard_normal((1, 300))).astype(np.float32)
+    mn2, mx2 = np.repeat(mn, 2, 0), np.repeat(mx, 2, 0)
+    shared = O.select_outliers(mn2, mx2, 17)
+    per = O.select_outliers_per_shard(mn2, mx2, 17)
+    for p in range(2):
+        assert per["idx"][p].tolist() == shared["idx"].tolist()
+        assert per["cmap"][p].tolist() == shared["cmap"].tolist()
+        assert np.array_equal(per["enc"][p], shared["enc"][p])
+
+
+@pytest.mark.parametrize("P,H,k", [(3, 50, 0), (3, 50, 7), (4, 64, 64), (5, 33, 32)])
+def test_per_shard_selection_invariants(P, H, k):
+    rng = np.random.default_rng(P * 100 + H + k)
+    mn = -np.abs(rng.standard_normal((P, H))).astype(np.float32)
+    mx = np.abs(rng.standard_normal((P, H))).astype(np.float32)
+    sel = O.select_outliers_per_shard(mn, mx, k)
+    for p in range(P):
+        _check_maps(sel["idx"][p], sel["fmap"][p], sel["cmap"][p], H, k)
+        chosen = sel["width"][p, sel["idx"][p]]
+        rest = sel["width"][p, sel["cmap"][p]]
+        if k and k < H:
+            assert chosen.min() >= rest.max()
+        for j, h in enumerate(sel["cmap"][p]):
+            assert sel["enc"][p, j, 0] == sel["rscale"][p, h]
+            assert sel["enc"][p, j, 1] == float(sel["zero_point"][p, h])
