@@ -126,6 +126,12 @@ def _csv_rows(d: str, suffix: str):
 
 
 def _kernel_class(name: str):
+    head = name.split("(")[0].rstrip()
+    if "btq::" in name and "decompress_sets" in name:
+        return "decompress_reduce_per_shard"
+    if "btq::" in name and "compress" in name and "decompress" not in name and \
+            head.endswith("true>"):
+        return "compress_pack_per_shard"   # the sender's per-shard template flag
     if "btq::" in name and "decompress" in name:
         # the receiver's template flag selects bf16 output
         bf16 = name.split("(")[0].rstrip().endswith("true>")
@@ -215,6 +221,16 @@ def algorithmic_bytes(P, T, H, k, y_bytes=4):
     message = P * T * (Bq + 2 * k)
     compress = P * T * H * 2 + message + P * Hq * 8 + maps           # + (rscale, zero point) table
     decompress = message + T * H * y_bytes + (P + 1) * Hq * 4 + maps  # + scale rows, constant row
+    return compress, decompress
+
+
+def algorithmic_bytes_per_shard(P, T, H, k):
+    """The same for per-shard BF16 sets: per-shard maps; the receiver reads
+    scale, zero point and fmap by feature (9 bytes per (p,h))."""
+    Bq = (H - k + 1) // 2
+    message = P * T * (Bq + 2 * k)
+    compress = P * T * H * 2 + message + P * (H - k) * 8 + 4 * P * H
+    decompress = message + T * H * 4 + 9 * P * H
     return compress, decompress
 
 
@@ -401,6 +417,35 @@ def main() -> int:
     d16_bytes = algorithmic_bytes(P, T, H, k, y_bytes=2)[1]
     del y16
 
+    # Per-shard BF16 sets (every shard keeps its own k features), timed on
+    # their own in the same rotation: another selection reading, not part of
+    # a step.
+    def time_calls(fn, args_list, n, what):
+        for i in range(5):
+            _lib.check(fn(*args_list[i % len(args_list)]), what)
+        ev = [(hev.new(), hev.new()) for _ in range(n)]
+        torch.cuda.synchronize()
+        s_ = 0
+        for i in range(n):
+            hev.record(ev[i][0], sh)
+            s_ |= fn(*args_list[i % len(args_list)])
+            hev.record(ev[i][1], sh)
+        torch.cuda.synchronize()
+        _lib.check(s_, what)
+        return sum(hev.ms(a, b) for a, b in ev) / n
+
+    sps = B.btq_select_outliers_per_shard(rmin, rmax, k)
+    cps_args = [(p(xs[r]), P, T, H, k, p(sps["enc"]), p(sps["outlier_idx"]), p(sps["cmap"]),
+                 p(pks[r]), pitch, p(ols[r]), sh) for r in range(R)]
+    dps_args = [(p(pks[(r - 2) % R]), pitch, p(ols[(r - 2) % R]), P, T, H, k, p(sps["scale"]),
+                 p(sps["zero_point"]), p(sps["fmap"]), p(ys[r]), sh) for r in range(R)]
+    for r in range(R):
+        _lib.check(lib.btq_compress_pack_per_shard(*cps_args[r]), "per-shard sender")
+    cps_mean = time_calls(lib.btq_compress_pack_per_shard, cps_args, n16, "per-shard sender")
+    dps_mean = time_calls(lib.btq_decompress_reduce_per_shard, dps_args, n16,
+                          "per-shard receiver")
+    cps_bytes, dps_bytes = algorithmic_bytes_per_shard(P, T, H, k)
+
     copy_probe = None
     if args.copy_probe_mib:
         n = args.copy_probe_mib * 2 ** 20
@@ -456,6 +501,16 @@ def main() -> int:
                                        "frac": round(d16_bytes / (d16_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                                        "note": "bf16 output (one rounding of the fp32 sum); "
                                                "timed separately, not part of value"},
+            "compress_pack_per_shard": {
+                "mean_us": round(cps_mean * 1e3, 2), "algorithmic_bytes": cps_bytes,
+                "hbm_GBps": round(cps_bytes / (cps_mean * 1e-3) / 1e9, 1),
+                "frac": round(cps_bytes / (cps_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "note": "one BF16 set per shard; timed separately, not part of value"},
+            "decompress_reduce_per_shard": {
+                "mean_us": round(dps_mean * 1e3, 2), "algorithmic_bytes": dps_bytes,
+                "hbm_GBps": round(dps_bytes / (dps_mean * 1e-3) / 1e9, 1),
+                "frac": round(dps_bytes / (dps_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "note": "one BF16 set per shard; timed separately, not part of value"},
         },
         "offline": {"calib_batches": w.calib_batches, "calib_ms_total": round(calib_ms, 3),
                     "calib_GBps": round(w.calib_batches * P * w.calib_T * H * 2 / (calib_ms * 1e-3) / 1e9, 1),

@@ -8,14 +8,17 @@ from .api import (  # noqa: F401
     btq_calib_update,
     btq_calib_workspace_bytes,
     btq_compress_pack,
+    btq_compress_pack_per_shard,
     btq_dec_table_floats,
     btq_decompress_reduce,
     btq_decompress_reduce_bf16,
+    btq_decompress_reduce_per_shard,
     btq_enc_table_floats,
     btq_packed_pitch,
     btq_packed_row_bytes,
     btq_select_features,
     btq_select_outliers,
+    btq_select_outliers_per_shard,
     btq_select_outliers_rule,
     btq_select_workspace_bytes,
     btq_status_str,

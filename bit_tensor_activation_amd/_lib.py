@@ -23,6 +23,12 @@ SIGNATURES = {
     "btq_select_outliers_rule": (_I, [_P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P,
                                       _P, _P, _SZ, _P]),
     "btq_select_workspace_bytes": (_SZ, [_I64, _I64]),
+    "btq_select_outliers_per_shard": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _SZ, _P]),
+    "btq_compress_pack_per_shard": (_I, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _P,
+                                         _P]),
+    "btq_decompress_reduce_per_shard": (_I, [_P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, _P,
+                                             _P, _P]),
     "btq_select_features": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _P]),
     "btq_enc_table_floats": (_I64, [_I64, _I64, _I64]),

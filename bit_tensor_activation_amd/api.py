@@ -215,6 +215,22 @@ def btq_compress_pack(x: torch.Tensor, k: int, enc_table: torch.Tensor,
     The row pitch is packed.shape[2] when `packed` is given, else `pitch`,
     else btq_packed_pitch(H, k).
     """
+    return _compress("btq_compress_pack", x, k, enc_table, outlier_idx, cmap, packed, outliers,
+                     pitch, stream)
+
+
+def btq_compress_pack_per_shard(x: torch.Tensor, k: int, enc_table: torch.Tensor,
+                                outlier_idx: torch.Tensor, cmap: torch.Tensor,
+                                packed: Optional[torch.Tensor] = None,
+                                outliers: Optional[torch.Tensor] = None,
+                                pitch: Optional[int] = None, stream=None):
+    """btq_compress_pack with one BF16 set per shard: outlier_idx [P,k] and
+    cmap [P,H-k] from btq_select_outliers_per_shard."""
+    return _compress("btq_compress_pack_per_shard", x, k, enc_table, outlier_idx, cmap, packed,
+                     outliers, pitch, stream)
+
+
+def _compress(entry, x, k, enc_table, outlier_idx, cmap, packed, outliers, pitch, stream):
     dev = _device(x)
     P, T, H = x.shape
     _need(x, "x", _BF16, (P, T, H), dev)
@@ -223,8 +239,9 @@ def btq_compress_pack(x: torch.Tensor, k: int, enc_table: torch.Tensor,
     elif pitch is None:
         pitch = btq_packed_pitch(H, k)
     _need(enc_table, "enc_table", (torch.float32,), (P, H - k, 2), dev)
-    _need(outlier_idx, "outlier_idx", (torch.int32,), (k,), dev)
-    _need(cmap, "cmap", (torch.int32,), (H - k,), dev)
+    per = entry.endswith("_per_shard")
+    _need(outlier_idx, "outlier_idx", (torch.int32,), (P, k) if per else (k,), dev)
+    _need(cmap, "cmap", (torch.int32,), (P, H - k) if per else (H - k,), dev)
     if packed is None:
         packed = torch.empty((P, T, pitch), dtype=torch.uint8, device=dev)
     if outliers is None:
@@ -232,11 +249,72 @@ def btq_compress_pack(x: torch.Tensor, k: int, enc_table: torch.Tensor,
     _need(packed, "packed", (torch.uint8,), (P, T, pitch), dev)
     _need(outliers, "outliers", _BF16, (P, T, k), dev)
     lib = _lib.load()
-    st = lib.btq_compress_pack(_ptr(_bits(x)), P, T, H, k, _ptr(enc_table), _ptr(outlier_idx),
-                               _ptr(cmap), _ptr(packed), pitch, _ptr(_bits(outliers)),
-                               _stream(dev, stream))
-    _lib.check(st, "btq_compress_pack")
+    st = getattr(lib, entry)(_ptr(_bits(x)), P, T, H, k, _ptr(enc_table), _ptr(outlier_idx),
+                             _ptr(cmap), _ptr(packed), pitch, _ptr(_bits(outliers)),
+                             _stream(dev, stream))
+    _lib.check(st, entry)
     return packed, outliers
+
+
+def btq_decompress_reduce_per_shard(packed: torch.Tensor, outliers: torch.Tensor, H: int,
+                                    scale: torch.Tensor, zero_point: torch.Tensor,
+                                    fmap: torch.Tensor, y: Optional[torch.Tensor] = None,
+                                    stream=None) -> torch.Tensor:
+    """Reduced fp32 y [T,H] from per-shard-set messages: scale [P,H],
+    zero_point [P,H] and fmap [P,H] from btq_select_outliers_per_shard."""
+    dev = _device(packed)
+    P, T, pitch = packed.shape
+    k = outliers.shape[2]
+    if pitch < btq_packed_row_bytes(H, k):
+        raise ValueError(f"packed rows of {pitch} bytes are shorter than H={H}, k={k} needs")
+    _need(packed, "packed", (torch.uint8,), (P, T, pitch), dev)
+    _need(outliers, "outliers", _BF16, (P, T, k), dev)
+    _need(scale, "scale", (torch.float32,), (P, H), dev)
+    _need(zero_point, "zero_point", (torch.uint8,), (P, H), dev)
+    _need(fmap, "fmap", (torch.int32,), (P, H), dev)
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _need(y, "y", (torch.float32,), (T, H), dev)
+    lib = _lib.load()
+    st = lib.btq_decompress_reduce_per_shard(_ptr(packed), pitch, _ptr(_bits(outliers)), P, T, H,
+                                             k, _ptr(scale), _ptr(zero_point), _ptr(fmap),
+                                             _ptr(y), _stream(dev, stream))
+    _lib.check(st, "btq_decompress_reduce_per_shard")
+    return y
+
+
+def btq_select_outliers_per_shard(run_min: torch.Tensor, run_max: torch.Tensor, k: int,
+                                  out: dict = None, workspace: Optional[torch.Tensor] = None,
+                                  stream=None) -> dict:
+    """One BF16 set per shard, ranked by the shard's own ranges. Returns
+    scale, rscale, zero_point [P,H], outlier_idx [P,k], fmap [P,H],
+    cmap [P,H-k] and enc [P,H-k,2]."""
+    dev = _device(run_min)
+    P, H = run_min.shape
+    _need(run_min, "run_min", (torch.float32,), (P, H), dev)
+    _need(run_max, "run_max", (torch.float32,), (P, H), dev)
+    if not 0 <= k <= H:
+        raise ValueError(f"k={k} outside [0, H={H}]")
+    o = dict(out or {})
+    shapes = (("scale", torch.float32, (P, H)), ("rscale", torch.float32, (P, H)),
+              ("zero_point", torch.uint8, (P, H)), ("outlier_idx", torch.int32, (P, k)),
+              ("fmap", torch.int32, (P, H)), ("cmap", torch.int32, (P, H - k)),
+              ("enc", torch.float32, (P, H - k, 2)))
+    for name, dt, shp in shapes:
+        o.setdefault(name, torch.empty(shp, dtype=dt, device=dev))
+        _need(o[name], name, (dt,), shp, dev)
+    if workspace is None:
+        workspace = torch.empty(btq_select_workspace_bytes(P, H), dtype=torch.uint8, device=dev)
+    lib = _lib.load()
+    st = lib.btq_select_outliers_per_shard(_ptr(run_min), _ptr(run_max), P, H, k,
+                                           _ptr(o["scale"]), _ptr(o["rscale"]),
+                                           _ptr(o["zero_point"]), _ptr(o["outlier_idx"]),
+                                           _ptr(o["fmap"]), _ptr(o["cmap"]), _ptr(o["enc"]),
+                                           _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           _stream(dev, stream))
+    _lib.check(st, "btq_select_outliers_per_shard")
+    return o
 
 
 def _decompress(entry: str, packed: torch.Tensor, outliers: torch.Tensor, H: int,

@@ -54,7 +54,7 @@ size_t btq_calib_workspace_bytes(int64_t P, int64_t T, int64_t H) {
 
 size_t btq_select_workspace_bytes(int64_t P, int64_t H) {
   if (P < 1 || P > kMaxP || H < 1 || H > kMaxH) return 0;
-  return (size_t)H * sizeof(float);
+  return (size_t)(P * H) * sizeof(float);   // per-shard widths; the shared score uses H
 }
 
 int64_t btq_enc_table_floats(int64_t P, int64_t H, int64_t k) {
@@ -121,6 +121,28 @@ int btq_select_outliers_rule(const float* run_min, const float* run_max, int64_t
                                        (hipStream_t)stream));
 }
 
+int btq_select_outliers_per_shard(const float* run_min, const float* run_max, int64_t P,
+                                  int64_t H, int64_t k, float* scale, float* rscale,
+                                  uint8_t* zero_point, int32_t* outlier_idx, int32_t* fmap,
+                                  int32_t* cmap, float* enc_table, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (P < 1 || P > kMaxP || H < 1 || H > kMaxH) return BTQ_ERR_SHAPE;
+  int st = check_k(H, k);
+  if (st != BTQ_OK) return st;
+  if (!run_min || !run_max || !scale || !rscale || !zero_point || !fmap) return BTQ_ERR_ARG;
+  if ((k > 0 && !outlier_idx) || (k < H && (!cmap || !enc_table))) return BTQ_ERR_ARG;
+  if (!aligned(run_min, 4) || !aligned(run_max, 4) || !aligned(scale, 4) ||
+      !aligned(rscale, 4) || !aligned(outlier_idx, 4) || !aligned(fmap, 4) || !aligned(cmap, 4) ||
+      !aligned(enc_table, 4))
+    return BTQ_ERR_ALIGN;
+  if (!workspace) return BTQ_ERR_ARG;
+  if (workspace_bytes < btq_select_workspace_bytes(P, H)) return BTQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 4)) return BTQ_ERR_ALIGN;
+  return hip_status(btq::launch_select_per_shard(run_min, run_max, P, H, k, scale, rscale,
+                                                 zero_point, outlier_idx, fmap, cmap, enc_table,
+                                                 (float*)workspace, (hipStream_t)stream));
+}
+
 int btq_select_features(const float* run_min, const float* run_max, int64_t P, int64_t H,
                         int64_t k, const int32_t* features, float* scale, float* rscale,
                         uint8_t* zero_point, int32_t* outlier_idx, int32_t* fmap, int32_t* cmap,
@@ -149,9 +171,12 @@ int btq_select_features(const float* run_min, const float* run_max, int64_t P, i
                                            outlier_idx, fmap, cmap, enc_table, dec_table, s));
 }
 
-int btq_compress_pack(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
-                      const float* enc_table, const int32_t* outlier_idx, const int32_t* cmap,
-                      uint8_t* packed, int64_t packed_pitch, uint16_t* outliers, void* stream) {
+namespace {
+
+int compress_common(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
+                    const float* enc_table, const int32_t* outlier_idx, const int32_t* cmap,
+                    uint8_t* packed, int64_t packed_pitch, uint16_t* outliers, bool per_shard,
+                    void* stream) {
   int st = check_dims(P, T, H, 0);
   if (st != BTQ_OK) return st;
   st = check_k(H, k);
@@ -165,7 +190,25 @@ int btq_compress_pack(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_
     return BTQ_ERR_ALIGN;
   if (T == 0) return BTQ_OK;
   return hip_status(btq::launch_compress(x, P, T, H, k, enc_table, outlier_idx, cmap, packed,
-                                         packed_pitch, outliers, (hipStream_t)stream));
+                                         packed_pitch, outliers, per_shard,
+                                         (hipStream_t)stream));
+}
+
+}  // namespace
+
+int btq_compress_pack(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
+                      const float* enc_table, const int32_t* outlier_idx, const int32_t* cmap,
+                      uint8_t* packed, int64_t packed_pitch, uint16_t* outliers, void* stream) {
+  return compress_common(x, P, T, H, k, enc_table, outlier_idx, cmap, packed, packed_pitch,
+                         outliers, false, stream);
+}
+
+int btq_compress_pack_per_shard(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
+                                const float* enc_table, const int32_t* outlier_idx,
+                                const int32_t* cmap, uint8_t* packed, int64_t packed_pitch,
+                                uint16_t* outliers, void* stream) {
+  return compress_common(x, P, T, H, k, enc_table, outlier_idx, cmap, packed, packed_pitch,
+                         outliers, true, stream);
 }
 
 namespace {
@@ -206,6 +249,25 @@ int btq_decompress_reduce_bf16(const uint8_t* packed, int64_t packed_pitch,
                                const int32_t* cmap, uint16_t* y, void* stream) {
   return decompress_common(packed, packed_pitch, outliers, P, T, H, k, dec_table, outlier_idx,
                            cmap, y, true, stream);
+}
+
+int btq_decompress_reduce_per_shard(const uint8_t* packed, int64_t packed_pitch,
+                                    const uint16_t* outliers, int64_t P, int64_t T, int64_t H,
+                                    int64_t k, const float* scale, const uint8_t* zero_point,
+                                    const int32_t* fmap, float* y, void* stream) {
+  int st = check_dims(P, T, H, 0);
+  if (st != BTQ_OK) return st;
+  st = check_k(H, k);
+  if (st != BTQ_OK) return st;
+  st = check_pitch(P, T, H, k, packed_pitch);
+  if (st != BTQ_OK) return st;
+  if (!scale || !zero_point || !fmap) return BTQ_ERR_ARG;
+  if (T > 0 && (!y || (k < H && !packed) || (k > 0 && !outliers))) return BTQ_ERR_ARG;
+  if (!aligned(outliers, 2) || !aligned(scale, 4) || !aligned(fmap, 4) || !aligned(y, 4))
+    return BTQ_ERR_ALIGN;
+  if (T == 0) return BTQ_OK;
+  return hip_status(btq::launch_decompress_sets(packed, packed_pitch, outliers, P, T, H, k, scale,
+                                                zero_point, fmap, y, (hipStream_t)stream));
 }
 
 const char* btq_status_str(int status) {

@@ -78,7 +78,8 @@ __device__ __forceinline__ void load_enc(rsrc_t re, bool active, int lane, float
 }
 
 // Staged kernel. LDS: 4 waves x kCpRows staging buffers of buf_bytes.
-template <int kMaxChunks>
+// kPs: idx [P,k] and cmap [P,Hq] hold one BF16 set per shard.
+template <int kMaxChunks, bool kPs>
 __global__ __launch_bounds__(256) void compress_kernel(
     const uint16_t* __restrict__ x, int64_t T, int H, int Hq, int k, int ntiles,
     int rows_per_wave, int64_t nrowblk, int64_t ngroups, int buf_bytes,
@@ -92,6 +93,10 @@ __global__ __launch_bounds__(256) void compress_kernel(
   const int c = (int)sub;
   const int64_t rg = unit % ngroups;
   const int64_t p = unit / ngroups;
+  if (kPs) {   // this shard's own set
+    cmap += p * Hq;
+    idx += p * k;
+  }
   const TileGeom g = tile_geom(cmap, c, ntiles, Hq, H);
   const int lane = threadIdx.x & (kWave - 1);
   // wave-uniform by construction; readfirstlane lets the compiler keep
@@ -229,7 +234,7 @@ constexpr int kSub = 2;         // token rows staged in LDS per sub-step
 template <int kRemDw>
 constexpr int ring_row_bytes() { return (kWave + 16 * kRemDw) * 20; }
 
-template <int kRemDw, int kR>
+template <int kRemDw, int kR, bool kPs>
 __global__ __launch_bounds__(256) void compress_ring_kernel(
     const uint16_t* __restrict__ x, int64_t T, int H, int Hq, int k, int ntiles,
     int rows_per_wave, int64_t nrowblk, int ntgrp, int64_t P,
@@ -244,6 +249,10 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
   if (!xcd_unit_block(blockIdx.x, ntgrp, P * nrowblk, &unit, &sub)) return;
   const int64_t rb = unit % nrowblk;
   const int64_t p = unit / nrowblk;
+  if (kPs) {   // this shard's own set
+    cmap += p * Hq;
+    idx += p * k;
+  }
   const int lane = threadIdx.x & (kWave - 1);
   // wave-uniform by construction; readfirstlane lets the compiler keep
   // everything derived from it (rows, descriptors) in scalar registers
@@ -404,6 +413,7 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
   } while (base < nrows);
 }
 
+template <bool kPs>
 __global__ __launch_bounds__(256) void compress_general_kernel(
     const uint16_t* __restrict__ x, int64_t P, int64_t T, int64_t H, int64_t k, int64_t Hq,
     int64_t Bq, const float* __restrict__ enc, const int32_t* __restrict__ idx,
@@ -420,14 +430,15 @@ __global__ __launch_bounds__(256) void compress_general_kernel(
       uint32_t q = 0;   // padding bytes past the codes stay zero
       if (byte < Bq) {
         const float* e = enc + (p * Hq + j) * 2;   // (rscale, zero point) of slot j
-        q = quant4(x[row * H + cmap[j]], e[0], e[1]);
-        if (j + 1 < Hq) q |= quant4(x[row * H + cmap[j + 1]], e[2], e[3]) << 4;
+        const int32_t* cm = cmap + (kPs ? p * Hq : 0);
+        q = quant4(x[row * H + cm[j]], e[0], e[1]);
+        if (j + 1 < Hq) q |= quant4(x[row * H + cm[j + 1]], e[2], e[3]) << 4;
       }
       packed[i] = (uint8_t)q;
     } else {
       const int64_t ii = i - n1;
       const int64_t row = ii / k, o = ii % k;
-      outl[ii] = x[row * H + idx[o]];
+      outl[ii] = x[row * H + idx[(kPs ? (row / T) * k : 0) + o]];
     }
   }
 }
@@ -442,9 +453,11 @@ static int pick_rows_per_wave(int64_t tile_waves, int64_t T) {
   return (int)rpw;
 }
 
-hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
-                           const float* enc, const int32_t* idx, const int32_t* cmap,
-                           uint8_t* packed, int64_t pitch, uint16_t* outl, hipStream_t s) {
+template <bool kPs>
+static hipError_t launch_compress_t(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
+                                    const float* enc, const int32_t* idx, const int32_t* cmap,
+                                    uint8_t* packed, int64_t pitch, uint16_t* outl,
+                                    hipStream_t s) {
   const int64_t Hq = H - k;
   const int64_t Bq = (Hq + 1) / 2;
   const int64_t ntiles64 = (Hq + kTileSlots - 1) / kTileSlots;
@@ -485,9 +498,9 @@ hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, i
     const int ntgrp = (ntiles + kCpWaves - 1) / kCpWaves;
     const unsigned blocks = (unsigned)xcd_grid(ntgrp, P * nrowblk);
 #define BTQ_RING(n, r)                                                                    \
-  compress_ring_kernel<n, r><<<blocks, 256, ring_lds, s>>>(x, T, (int)H, (int)Hq, (int)k, ntiles, \
-                                                           rpw, nrowblk, ntgrp, P, enc, idx, cmap, \
-                                                           packed, (int)pitch, outl)
+  compress_ring_kernel<n, r, kPs><<<blocks, 256, ring_lds, s>>>(                           \
+      x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, ntgrp, P, enc, idx, cmap, packed,  \
+      (int)pitch, outl)
 #define BTQ_RING_R(n) \
   if (ring == kRing) BTQ_RING(n, kRing); else BTQ_RING(n, kRingSmall);
     switch (rem_dw) {
@@ -507,11 +520,11 @@ hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, i
     const int64_t ngroups = (nrowblk + kCpWaves - 1) / kCpWaves;
     const int64_t blocks = xcd_grid(ntiles, P * ngroups);
     if (nch_max <= 2 * kWave)
-      compress_kernel<2><<<(unsigned)blocks, 256, lds, s>>>(
+      compress_kernel<2, kPs><<<(unsigned)blocks, 256, lds, s>>>(
           x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, ngroups, buf_bytes, P, enc, idx,
           cmap, packed, (int)pitch, outl);
     else
-      compress_kernel<4><<<(unsigned)blocks, 256, lds, s>>>(
+      compress_kernel<4, kPs><<<(unsigned)blocks, 256, lds, s>>>(
           x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, ngroups, buf_bytes, P, enc, idx,
           cmap, packed, (int)pitch, outl);
     return hipGetLastError();
@@ -520,9 +533,18 @@ hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, i
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  compress_general_kernel<<<(unsigned)blocks, 256, 0, s>>>(x, P, T, H, k, Hq, Bq, enc, idx, cmap,
-                                                           packed, pitch, outl);
+  compress_general_kernel<kPs><<<(unsigned)blocks, 256, 0, s>>>(x, P, T, H, k, Hq, Bq, enc, idx,
+                                                                cmap, packed, pitch, outl);
   return hipGetLastError();
+}
+
+hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
+                           const float* enc, const int32_t* idx, const int32_t* cmap,
+                           uint8_t* packed, int64_t pitch, uint16_t* outl, bool per_shard,
+                           hipStream_t s) {
+  return per_shard
+             ? launch_compress_t<true>(x, P, T, H, k, enc, idx, cmap, packed, pitch, outl, s)
+             : launch_compress_t<false>(x, P, T, H, k, enc, idx, cmap, packed, pitch, outl, s);
 }
 
 }  // namespace btq

@@ -26,7 +26,7 @@ namespace btq {
 __global__ __launch_bounds__(256) void qparams_kernel(
     const float* __restrict__ run_min, const float* __restrict__ run_max, int64_t P, int64_t H,
     float* __restrict__ scale, float* __restrict__ rscale, uint8_t* __restrict__ zp,
-    float* __restrict__ score, bool score_max) {
+    float* __restrict__ score, bool score_max, float* __restrict__ width) {
   const int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (h >= H) return;
   float sc = 0.0f;
@@ -43,15 +43,17 @@ __global__ __launch_bounds__(256) void qparams_kernel(
     scale[i] = s;
     rscale[i] = r;
     zp[i] = (uint8_t)z;
+    if (width) width[i] = w;
     sc = score_max ? fmaxf(sc, w) : __fadd_rn(sc, w);   // p ascending, from +0
   }
   if (score) score[h] = sc;
 }
 
-// Scores are sums of non-negative widths, so their bit patterns order like
-// their values. The low word ranks lower h higher.
+// Scores are non-negative widths, their sums or their maxima, so their bit
+// patterns order like their values once -0 is made +0 (a width of -0 ranks
+// equal to +0, as its value does). The low word ranks lower h higher.
 __device__ __forceinline__ unsigned long long rank_key(float s, int64_t h) {
-  return ((unsigned long long)__float_as_uint(s) << 32) |
+  return ((unsigned long long)__float_as_uint(__fadd_rn(s, 0.0f)) << 32) |
          (unsigned long long)(0xFFFFFFFFu - (uint32_t)h);
 }
 
@@ -101,9 +103,15 @@ __device__ void write_maps(Sel sel, int64_t H, int64_t k, int32_t* __restrict__ 
   }
 }
 
+// Block b ranks score row b: one block for the shared set, one per shard for
+// per-shard sets (rows of score, idx, fmap and cmap are H, k, H and H-k long).
 __global__ __launch_bounds__(kSelThreads) void topk_maps_kernel(
     const float* __restrict__ score, int64_t H, int64_t k, int32_t* __restrict__ idx,
     int32_t* __restrict__ fmap, int32_t* __restrict__ cmap) {
+  score += (int64_t)blockIdx.x * H;
+  idx += (int64_t)blockIdx.x * k;
+  fmap += (int64_t)blockIdx.x * H;
+  cmap += (int64_t)blockIdx.x * (H - k);
   __shared__ unsigned hist[256];
   __shared__ unsigned long long s_prefix;
   __shared__ unsigned long long s_rem;
@@ -197,7 +205,8 @@ hipError_t launch_select(const float* run_min, const float* run_max, int64_t P, 
                          int32_t* fmap, int32_t* cmap, float* enc, float* dec, float* ws_score,
                          bool score_max, hipStream_t s) {
   qparams_kernel<<<(unsigned)((H + 255) / 256), 256, 0, s>>>(run_min, run_max, P, H, scale,
-                                                              rscale, zp, ws_score, score_max);
+                                                              rscale, zp, ws_score, score_max,
+                                                              nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   topk_maps_kernel<<<1, kSelThreads, 0, s>>>(ws_score, H, k, idx, fmap, cmap);
@@ -210,12 +219,47 @@ hipError_t launch_select(const float* run_min, const float* run_max, int64_t P, 
   return hipGetLastError();
 }
 
+// Sender table of per-shard sets: enc[p, j] = (rscale, zero point) of
+// feature cmap[p, j] on shard p.
+__global__ __launch_bounds__(256) void shard_enc_kernel(const float* __restrict__ rscale,
+                                                        const uint8_t* __restrict__ zp,
+                                                        const int32_t* __restrict__ cmap,
+                                                        int64_t P, int64_t H, int64_t Hq,
+                                                        float* __restrict__ enc) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // p * Hq + j
+  if (i >= P * Hq) return;
+  const int64_t p = i / Hq;
+  const int64_t h = cmap[i];
+  enc[2 * i] = rscale[p * H + h];
+  enc[2 * i + 1] = (float)zp[p * H + h];
+}
+
+hipError_t launch_select_per_shard(const float* run_min, const float* run_max, int64_t P,
+                                   int64_t H, int64_t k, float* scale, float* rscale, uint8_t* zp,
+                                   int32_t* idx, int32_t* fmap, int32_t* cmap, float* enc,
+                                   float* ws_width, hipStream_t s) {
+  qparams_kernel<<<(unsigned)((H + 255) / 256), 256, 0, s>>>(run_min, run_max, P, H, scale,
+                                                              rscale, zp, nullptr, false,
+                                                              ws_width);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  topk_maps_kernel<<<(unsigned)P, kSelThreads, 0, s>>>(ws_width, H, k, idx, fmap, cmap);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = P * (H - k);
+  if (n == 0) return hipSuccess;
+  shard_enc_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(rscale, zp, cmap, P, H, H - k,
+                                                                enc);
+  return hipGetLastError();
+}
+
 hipError_t launch_select_set(const float* run_min, const float* run_max, int64_t P, int64_t H,
                              int64_t k, float* scale, float* rscale, uint8_t* zp,
                              const int32_t* idx, int32_t* fmap, int32_t* cmap, float* enc,
                              float* dec, hipStream_t s) {
   qparams_kernel<<<(unsigned)((H + 255) / 256), 256, 0, s>>>(run_min, run_max, P, H, scale,
-                                                              rscale, zp, nullptr, false);
+                                                              rscale, zp, nullptr, false,
+                                                              nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   set_maps_kernel<<<1, kSelThreads, 0, s>>>(idx, H, k, fmap, cmap);

@@ -128,6 +128,7 @@ int btq_select_outliers(const float *run_min, const float *run_max,
                         float *enc_table, float *dec_table,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* Scratch bytes for the ranked selections: P*H floats (0 for invalid sizes). */
 size_t btq_select_workspace_bytes(int64_t P, int64_t H);
 
 /* How a feature's P per-shard ranges become its rank score. */
@@ -249,6 +250,51 @@ int btq_decompress_reduce_bf16(const uint8_t *packed, int64_t packed_pitch,
                                const uint16_t *outliers, int64_t P, int64_t T, int64_t H,
                                int64_t k, const float *dec_table, const int32_t *outlier_idx,
                                const int32_t *cmap, uint16_t *y, void *stream);
+
+/*
+ * Per-shard BF16 sets -- a second reading of "The Hybrid Quantization
+ * Algorithm", Selection bullet: the ranges that rank features are per
+ * device, so every shard keeps its own k widest features (ranked by its own
+ * range, ties to the lower h) in BF16. The message keeps its size (k BF16
+ * values and H-k codes per row), but each shard lays it out by its own map,
+ * so the receiver reads every shard's map.
+ *
+ * btq_select_outliers_per_shard: parameters as in btq_select_outliers, plus
+ *   outlier_idx  i32 [P,k]      out, shard p's BF16 features, ascending h
+ *   fmap         i32 [P,H]      out, shard p's map (slot j, or -1-i)
+ *   cmap         i32 [P,H-k]    out, shard p's int4 features, ascending h
+ *   enc_table    fp32 [P,H-k,2] out, (rscale, zero_point) of cmap[p,j] on p
+ *   workspace    at least btq_select_workspace_bytes(P,H) bytes.
+ * The receiver reads scale and zero_point by feature, so there is no
+ * decoder table.
+ *
+ * btq_compress_pack_per_shard: btq_compress_pack with outlier_idx [P,k] and
+ *   cmap [P,H-k] from btq_select_outliers_per_shard; row (p,t) is coded with
+ *   shard p's maps. Same packed and outliers layouts.
+ *
+ * btq_decompress_reduce_per_shard: y[t,h] = sum over p = 0,1,... (fp32, from
+ *   +0) of fl(q - zero_point[p,h]) * scale[p,h], q being shard p's code of h
+ *   at slot fmap[p,h], or of the BF16 value outliers[p,t,-1-fmap[p,h]].
+ *   scale fp32 [P,H], zero_point u8 [P,H], fmap i32 [P,H] in; y fp32 [T,H]
+ *   out. The maps are trusted, as in btq_decompress_reduce. A 16-byte
+ *   aligned y, fmap and scale, 8-byte aligned zero_point, H a multiple of 8
+ *   and a pitch that is a multiple of 4 take the vectorized kernel; any
+ *   other case takes a general one.
+ */
+int btq_select_outliers_per_shard(const float *run_min, const float *run_max,
+                                  int64_t P, int64_t H, int64_t k,
+                                  float *scale, float *rscale, uint8_t *zero_point,
+                                  int32_t *outlier_idx, int32_t *fmap, int32_t *cmap,
+                                  float *enc_table, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+int btq_compress_pack_per_shard(const uint16_t *x, int64_t P, int64_t T, int64_t H, int64_t k,
+                                const float *enc_table, const int32_t *outlier_idx,
+                                const int32_t *cmap, uint8_t *packed, int64_t packed_pitch,
+                                uint16_t *outliers, void *stream);
+int btq_decompress_reduce_per_shard(const uint8_t *packed, int64_t packed_pitch,
+                                    const uint16_t *outliers, int64_t P, int64_t T, int64_t H,
+                                    int64_t k, const float *scale, const uint8_t *zero_point,
+                                    const int32_t *fmap, float *y, void *stream);
 
 /* Code bytes per packed row: ceil((H-k)/2); -1 if H < 1 or k is outside [0,H]. */
 int64_t btq_packed_row_bytes(int64_t H, int64_t k);

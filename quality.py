@@ -6,8 +6,9 @@ output y against the exact sum of the unquantized bf16 partial sums,
 sum_p x[p] in float64. It reports four things:
 
   * error vs k: how the error falls as range-ranked BF16 features are added;
-  * selection rules at a workload's k: range-ranked (shard ranges summed, or
-    the widest shard), random sets, and pure int4 (k = 0). The page's section
+  * selection rules at a workload's k: range-ranked (shard ranges summed,
+    the widest shard, or one set per shard), random sets, and pure int4
+    (k = 0), also on a case with shard-local outliers. The page's section
     "Key Observations and Future Directions" reports that random BF16
     features help little over pure int4 and that ranking by range is what
     matters;
@@ -81,8 +82,15 @@ def calibrate(P, H, batches, momentum):
 
 
 def run_codec(x: torch.Tensor, sel: dict) -> torch.Tensor:
-    """y = decompress_reduce(compress_pack(x)) with the selection's tables."""
+    """y = decompress_reduce(compress_pack(x)) with the selection's tables
+    (the per-shard calls when the selection holds one set per shard)."""
     H = x.shape[2]
+    if sel["outlier_idx"].dim() == 2:
+        k = sel["outlier_idx"].shape[1]
+        pk, ol = B.btq_compress_pack_per_shard(x, k, sel["enc"], sel["outlier_idx"],
+                                               sel["cmap"])
+        return B.btq_decompress_reduce_per_shard(pk, ol, H, sel["scale"], sel["zero_point"],
+                                                 sel["fmap"])
     k = sel["outlier_idx"].numel()
     pk, ol = B.btq_compress_pack(x, k, sel["enc"], sel["outlier_idx"], sel["cmap"])
     return B.btq_decompress_reduce(pk, ol, H, sel["dec"], sel["outlier_idx"], sel["cmap"])
@@ -117,18 +125,46 @@ def error_vs_k(name: str, ks, calib_batches=None) -> list:
     return out
 
 
+def shard_local_state(P=8, T=2048, H=4096, n_shared=24, n_local=8, calib_batches=4, seed=57):
+    """Calibrated stats and an inference batch of normal data (sigma 0.5)
+    with n_shared outlier columns wide on every shard (x40) and n_local more
+    per shard, each wide on its own shard only (x80)."""
+    rng = np.random.default_rng(seed)
+    cols = rng.choice(H, n_shared + P * n_local, replace=False)
+    shared, local = cols[:n_shared], cols[n_shared:].reshape(P, n_local)
+
+    def draw(s):
+        x = W.draw(P, T, H, s, sigma=0.5, cols=shared.tolist(), outlier_factor=40.0,
+                   device=DEV).view(torch.bfloat16)
+        for p in range(P):
+            x[p][:, torch.as_tensor(local[p], device=DEV)] *= 80.0
+        return x.view(torch.int16)
+    rmin, rmax = calibrate(P, H, [lambda b=b: draw(seed * 100 + b) for b in range(calib_batches)],
+                           0.9)
+    return rmin, rmax, draw(seed * 100 + 99)
+
+
 def selection_rules(name: str, k: int, n_random: int = 4, calib_batches=None) -> list:
-    """Range-ranked (sum, max), random sets and pure int4 at one k."""
-    w, rmin, rmax, x = workload_state(name, calib_batches)
+    """Range-ranked (sum, max, per-shard sets), random sets and pure int4 at
+    one k. name "shard_local" is the synthetic case of shard_local_state."""
+    if name == "shard_local":
+        rmin, rmax, x = shard_local_state()
+        P, H = rmin.shape
+        wid = 99
+    else:
+        w, rmin, rmax, x = workload_state(name, calib_batches)
+        P, H, wid = w.P, w.H, w.wid
     ex = exact_sum(x)
-    base = dict(report="selection", workload=name, P=w.P, T=x.shape[1], H=w.H)
+    base = dict(report="selection", workload=name, P=P, T=x.shape[1], H=H)
     out = []
     for rule in ("sum", "max"):
         sel = B.btq_select_outliers_rule(rmin, rmax, k, rule)
         out.append(dict(base, rule=f"range_{rule}", k=k, **error_stats(run_codec(x, sel), ex)))
+    sel = B.btq_select_outliers_per_shard(rmin, rmax, k)
+    out.append(dict(base, rule="range_per_shard", k=k, **error_stats(run_codec(x, sel), ex)))
     rnd = []
     for s in range(n_random):
-        feats = np.sort(np.random.default_rng([w.wid, 77, s]).choice(w.H, k, replace=False))
+        feats = np.sort(np.random.default_rng([wid, 77, s]).choice(H, k, replace=False))
         sel = B.btq_select_features(rmin, rmax, feats)
         rnd.append(error_stats(run_codec(x, sel), ex))
     out.append(dict(base, rule="random", k=k, sets=n_random,
@@ -268,6 +304,8 @@ def run(only=None) -> list:
             recs += selection_rules("7b_prefill", 64)
             recs += selection_rules("large_prefill", 128)
             recs += selection_rules("decode", 64)
+            recs += selection_rules("shard_local", 32)
+            recs += selection_rules("shard_local", 64)
         elif rep == "irwin_hall":
             recs += irwin_hall([1, 2, 4, 8, 16])
         elif rep == "drift":

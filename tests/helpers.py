@@ -50,9 +50,13 @@ def oracle_compress_rows(x: np.ndarray, sel: dict, rows=None, pitch=None):
         x = x[:, rows, :]
     P = x.shape[0]
 
+    per_shard = np.asarray(sel["cmap"]).ndim == 2
+
     def one(p):
+        idx = sel["idx"][p:p + 1] if per_shard else sel["idx"]
+        cmap = sel["cmap"][p:p + 1] if per_shard else sel["cmap"]
         return O.compress_pack(x[p:p + 1], sel["rscale"][p:p + 1], sel["zero_point"][p:p + 1],
-                               sel["idx"], sel["cmap"], pitch=pitch)
+                               idx, cmap, pitch=pitch)
 
     res = list(POOL.map(one, range(P)))
     return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -56,7 +56,7 @@ def test_size_helpers(lib):
     assert lib.btq_packed_pitch(5, 2) == 128
     assert lib.btq_packed_pitch(8, 8) == 0
     assert lib.btq_packed_pitch(8, 9) == -1
-    assert lib.btq_select_workspace_bytes(8, 4096) == 4096 * 4
+    assert lib.btq_select_workspace_bytes(8, 4096) == 8 * 4096 * 4
     assert lib.btq_select_workspace_bytes(0, 4096) == 0
     n = lib.btq_calib_workspace_bytes(8, 2048, 4096)
     assert n > 0 and n % (2 * 8 * 4096 * 4) == 0
@@ -125,6 +125,38 @@ def test_select_rule_validation(lib):
     assert call(2) == ARG
     assert call(-1) == ARG
     assert call(_lib.BTQ_SCORE_MAX, k=17) == SHAPE
+
+
+def test_per_shard_validation(lib):
+    def sel(P=2, H=16, k=4, idx=A, cmap=A, enc=A, ws=A, wsb=BIG, fmap=A):
+        return lib.btq_select_outliers_per_shard(A, A, P, H, k, A, A, A, idx, fmap, cmap, enc, ws,
+                                                 wsb, None)
+    assert sel(k=17) == SHAPE
+    assert sel(P=0) == SHAPE
+    assert sel(idx=None) == ARG
+    assert sel(cmap=None) == ARG
+    assert sel(enc=None) == ARG
+    assert sel(fmap=None) == ARG
+    assert sel(ws=None) == ARG
+    assert sel(wsb=2 * 16 * 4 - 1) == WS
+    assert sel(enc=A + 2) == ALIGN
+
+    def comp(x=A, k=4, idx=A, pitch=128):
+        return lib.btq_compress_pack_per_shard(x, 2, 4, 16, k, A, idx, A, A, pitch, A, None)
+    assert comp(k=17) == SHAPE
+    assert comp(pitch=5) == SHAPE
+    assert comp(idx=None) == ARG
+    assert comp(x=A + 1) == ALIGN
+
+    def dec(y=A, k=4, fmap=A, zp=A, pitch=128, T=4):
+        return lib.btq_decompress_reduce_per_shard(A, pitch, A, 2, T, 16, k, A, zp, fmap, y, None)
+    assert dec(k=-1) == SHAPE
+    assert dec(pitch=5) == SHAPE
+    assert dec(fmap=None) == ARG
+    assert dec(zp=None) == ARG
+    assert dec(y=None) == ARG
+    assert dec(y=A + 2) == ALIGN
+    assert dec(T=0, y=None) == OK      # empty batch: nothing to do, nothing enqueued
 
 
 def host_set(*h):

@@ -1,0 +1,162 @@
+"""GPU parity of per-shard BF16 sets (every shard keeps its own k widest
+features): selection, sender and receiver against the oracle.
+
+Bar: parameters, per-shard sets, maps and sender table bitwise; packed rows
+(with padding) and BF16 blocks bitwise; y within 1e-3*|y| + 1e-2*max_p
+scale, and bit-exact on features that every shard keeps in BF16.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_tensor_activation_amd as B
+from oracle import oracle as O
+import workloads as W
+from helpers import (assert_bits_equal, assert_stats_equal, assert_y_close, oracle_calib,
+                     oracle_compress_rows, say, u16)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def assert_per_shard_selection_equal(g: dict, o: dict) -> None:
+    for key, okey in (("scale", "scale"), ("rscale", "rscale"), ("zero_point", "zero_point"),
+                      ("outlier_idx", "idx"), ("fmap", "fmap"), ("cmap", "cmap"),
+                      ("enc", "enc")):
+        assert_bits_equal(g[key], np.asarray(o[okey]), key)
+
+
+def bf16_everywhere(sel_o: dict) -> np.ndarray:
+    sets = [set(r.tolist()) for r in sel_o["idx"]]
+    return np.array(sorted(set.intersection(*sets)) if sets else [], np.int64)
+
+
+def run_both(calib_xs, x, k, momentum, *, pitch=None):
+    P, T, H = x.shape
+    rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
+    rmax = torch.empty_like(rmin)
+    mn = mx = None
+    for b, xb in enumerate(calib_xs):
+        B.btq_calib_update(xb, rmin, rmax, momentum, first_batch=(b == 0))
+        mn, mx = oracle_calib(u16(xb), mn, mx, momentum, first=(b == 0))
+    torch.cuda.synchronize()
+    assert_stats_equal(rmin, mn, "run_min")
+    assert_stats_equal(rmax, mx, "run_max")
+    sel_g = B.btq_select_outliers_per_shard(rmin, rmax, k)
+    sel_o = O.select_outliers_per_shard(mn, mx, k)
+    torch.cuda.synchronize()
+    assert_per_shard_selection_equal(sel_g, sel_o)
+    if pitch is None:
+        pitch = B.btq_packed_pitch(H, k)
+    pk, ol = B.btq_compress_pack_per_shard(x, k, sel_g["enc"], sel_g["outlier_idx"],
+                                           sel_g["cmap"], pitch=pitch)
+    pk_o, ol_o = oracle_compress_rows(u16(x), sel_o, pitch=pitch)
+    torch.cuda.synchronize()
+    assert_bits_equal(pk, pk_o, "packed")
+    assert_bits_equal(ol.view(torch.int16), ol_o.view(np.int16), "outliers")
+    y = B.btq_decompress_reduce_per_shard(pk, ol, H, sel_g["scale"], sel_g["zero_point"],
+                                          sel_g["fmap"])
+    y_o = O.decompress_reduce(pk_o, ol_o, sel_o["scale"], sel_o["zero_point"], sel_o["fmap"])
+    torch.cuda.synchronize()
+    assert_y_close(y.cpu().numpy(), y_o, sel_o["scale"], bf16_everywhere(sel_o))
+    return sel_g, sel_o
+
+
+def shard_local(P, T, H, seed, factor=30.0):
+    """Normal data, two columns wide everywhere, two more wide on each shard."""
+    x = W.draw(P, T, H, seed, cols=[H // 5, H // 2], outlier_factor=8.0, device=DEV)
+    xb = x.view(torch.bfloat16).clone()
+    for p in range(P):
+        xb[p][:, [(37 * p + 11) % H, (53 * p + 101) % H]] *= factor
+    return xb.view(torch.int16)
+
+
+# (P, T, H, k, pitch extra (None: default pitch), note)
+CASES = [
+    (4, 12, 1024, 8, None, "shard-local outliers"),
+    (8, 70, 2048, 64, None, "fast paths, ragged T"),
+    (3, 5, 250, 7, None, "H not a multiple of 8: general kernels"),
+    (2, 9, 256, 0, None, "k=0"),
+    (2, 9, 256, 256, None, "k=H"),
+    (5, 33, 1032, 13, None, "H-k odd"),
+    (8, 3, 4104, 64, None, "T below the rows per thread, partial feature block"),
+    (4, 6, 2048, 24, 0, "pitch = code bytes (multiple of 4)"),
+    (4, 6, 2048, 23, 0, "pitch = code bytes (odd): general receiver"),
+    (4, 6, 2048, 24, 4, "pitch = code bytes + 4"),
+    (1, 16, 512, 16, None, "one shard"),
+    (4, 6, 2048, 100, None, "k in (64, 128]: two outlier registers"),
+    (8, 5, 4096, 300, None, "k > 128: four outlier registers"),
+    (9, 7, 1024, 16, None, "P=9: shard-loop kernel"),
+    (9, 7, 1020, 16, None, "P=9, H not a multiple of 8: general kernel"),
+    (3, 40, 1028, 9, None, "H a multiple of 4 but not 8, partial last window"),
+    (2, 5, 24, 8, 0, "pitch = 8 bytes: the code window moves back one dword"),
+    (2, 5, 12, 4, 0, "pitch = 4 bytes: general kernel"),
+    (8, 33, 4096, 64, 0, "7B-like rows, pitch = code bytes"),
+]
+
+
+@pytest.mark.parametrize("P,T,H,k,extra,note", CASES, ids=[c[-1] for c in CASES])
+def test_per_shard_sets(P, T, H, k, extra, note):
+    say(f"case: per-shard sets P={P} T={T} H={H} k={k} pitch+{extra} ({note})")
+    calib = [shard_local(P, 8, H, 4000 + b) for b in range(2)]
+    x = shard_local(P, T, H, 4100)
+    pitch = None if extra is None else (H - k + 1) // 2 + extra
+    sel_g, sel_o = run_both(calib, x, k, 0.9, pitch=pitch)
+    if 2 <= k < H:   # each shard keeps its own two wide columns
+        for p in range(P):
+            own = {(37 * p + 11) % H, (53 * p + 101) % H}
+            assert own <= set(sel_o["idx"][p].tolist())
+
+
+def test_signed_zero_ranges_rank_by_feature():
+    # A width of -0 (run_max = -0, run_min = +0) ranks equal to +0: with all
+    # ranges zero the sets are the lowest k features, for every rule.
+    say("case: signed-zero ranges")
+    P, H, k = 3, 64, 5
+    rmin = torch.zeros((P, H), dtype=torch.float32, device=DEV)
+    rmax = torch.zeros((P, H), dtype=torch.float32, device=DEV)
+    rmax[:, 40:50] = -0.0
+    per = B.btq_select_outliers_per_shard(rmin, rmax, k)
+    mx = B.btq_select_outliers_rule(rmin, rmax, k, "max")
+    sm = B.btq_select_outliers(rmin, rmax, k)
+    torch.cuda.synchronize()
+    assert per["outlier_idx"].cpu().tolist() == [list(range(k))] * P
+    assert mx["outlier_idx"].cpu().tolist() == list(range(k))
+    assert sm["outlier_idx"].cpu().tolist() == list(range(k))
+    o = O.select_outliers_per_shard(rmin.cpu().numpy(), rmax.cpu().numpy(), k)
+    assert o["idx"].tolist() == [list(range(k))] * P
+
+
+def test_full_size_7b_sampled_rows():
+    """7b_prefill shape with its calibration batches (4 of them), through the
+    per-shard calls; sampled rows against the oracle."""
+    w = W.WORKLOADS["7b_prefill"]
+    P, H, k, T = w.P, w.H, w.k, w.T[0]
+    say(f"case: per-shard sets at full size P={P} T={T} H={H} k={k}")
+    rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
+    rmax = torch.empty_like(rmin)
+    mn = mx = None
+    for b in range(4):
+        xb = W.batch(w, W.PHASE_CALIB, b, device=DEV)
+        B.btq_calib_update(xb, rmin, rmax, w.momentum, first_batch=(b == 0))
+        mn, mx = oracle_calib(u16(xb), mn, mx, w.momentum, first=(b == 0))
+    sel_g = B.btq_select_outliers_per_shard(rmin, rmax, k)
+    sel_o = O.select_outliers_per_shard(mn, mx, k)
+    torch.cuda.synchronize()
+    assert_per_shard_selection_equal(sel_g, sel_o)
+    x = W.batch(w, W.PHASE_INFER, 0, device=DEV)
+    pk, ol = B.btq_compress_pack_per_shard(x, k, sel_g["enc"], sel_g["outlier_idx"],
+                                           sel_g["cmap"])
+    y = B.btq_decompress_reduce_per_shard(pk, ol, H, sel_g["scale"], sel_g["zero_point"],
+                                          sel_g["fmap"])
+    torch.cuda.synchronize()
+    Bq = B.btq_packed_row_bytes(H, k)
+    assert not bool(pk[:, :, Bq:].any()), "packed padding bytes must be zero"
+    rows = np.array(sorted({0, 1, 3, 4, 511, 1024, T - 2, T - 1} |
+                           set(np.random.default_rng(7).integers(0, T, 20).tolist())))
+    ridx = torch.as_tensor(rows, device=DEV)
+    pk_o, ol_o = oracle_compress_rows(u16(x[:, ridx, :]), sel_o, pitch=pk.shape[2])
+    assert_bits_equal(pk[:, ridx, :], pk_o, "packed (sampled rows)")
+    assert_bits_equal(ol[:, ridx, :].view(torch.int16), ol_o.view(np.int16), "outliers")
+    y_o = O.decompress_reduce(pk_o, ol_o, sel_o["scale"], sel_o["zero_point"], sel_o["fmap"])
+    assert_y_close(y[ridx].cpu().numpy(), y_o, sel_o["scale"], bf16_everywhere(sel_o))

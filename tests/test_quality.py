@@ -29,7 +29,20 @@ def test_range_ranked_beats_random_selection():
         say(f"  {r['rule']}: nmse {r['nmse']:.3e}")
     assert recs["range_sum"]["nmse"] < 0.1 * recs["random"]["nmse"]
     assert recs["range_max"]["nmse"] < 0.1 * recs["random"]["nmse"]
+    assert recs["range_per_shard"]["nmse"] < 0.1 * recs["random"]["nmse"]
     assert recs["random"]["nmse"] > 0.5 * recs["int4_only"]["nmse"]
+
+
+def test_shard_local_outliers_favour_per_shard_sets():
+    # 24 columns wide on every shard plus 8 per shard wide on that shard only
+    # (88 in all). At k = 32 one shared set cannot keep them all; every shard
+    # keeping its own 32 widest can (24 + 8).
+    say("case: selection rules with shard-local outliers, k=32")
+    recs = {r["rule"]: r for r in Q.selection_rules("shard_local", 32, n_random=2)}
+    for r in recs.values():
+        say(f"  {r['rule']}: nmse {r['nmse']:.3e}")
+    assert recs["range_per_shard"]["nmse"] < 0.5 * recs["range_sum"]["nmse"]
+    assert recs["range_per_shard"]["nmse"] < 0.1 * recs["int4_only"]["nmse"]
 
 
 def test_error_never_grows_with_k():
