@@ -176,6 +176,7 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, copy_mib: 
     w = W.WORKLOADS[workload]
     comp_alg, deco_alg = algorithmic_bytes(w.P, w.T[0], w.H, w.k)
     deco16_alg = algorithmic_bytes(w.P, w.T[0], w.H, w.k, y_bytes=2)[1]
+    comp_ps_alg, deco_ps_alg = algorithmic_bytes_per_shard(w.P, w.T[0], w.H, w.k)
     lines = [f"# HBM traffic per launch, workload {workload} (P={w.P}, T={w.T[0]}, H={w.H}, k={w.k})",
              "# " + note.replace("\n", "\n# "),
              f"source_hash={source_hash(KERNEL_SOURCES)}",
@@ -186,7 +187,9 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, copy_mib: 
              f"fetch_scale={fscale:.4f}",
              f"write_scale={wscale:.4f}"]
     for name, alg in (("compress_pack", comp_alg), ("decompress_reduce", deco_alg),
-                      ("decompress_reduce_bf16", deco16_alg)):
+                      ("decompress_reduce_bf16", deco16_alg),
+                      ("compress_pack_per_shard", comp_ps_alg),
+                      ("decompress_reduce_per_shard", deco_ps_alg)):
         if (name, "FETCH_SIZE") not in med or (name, "WRITE_SIZE") not in med:
             continue
         f_kib, w_kib = med[(name, "FETCH_SIZE")], med[(name, "WRITE_SIZE")]
