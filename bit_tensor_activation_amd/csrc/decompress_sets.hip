@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void decompress_sets_kernel(
 }
 
 // Register kernel (P <= 8). A wave owns a window of 256 features (4 per
-// lane) over rows_per_wave token rows. Before the rows it reduces every
+// lane) over rows_per_wave token rows; a block, 4 adjacent windows. Before the rows it reduces every
 // shard's map, zero points and scales of its 4 features to 8 registers per
 // shard:
 //   * nib: the bit shift of each int4 feature's code within the 64 bits
@@ -140,12 +140,15 @@ __global__ __launch_bounds__(256) void decompress_sets_reg_kernel(
     const uint8_t* __restrict__ packed, int pitch, const uint16_t* __restrict__ outl, int64_t T,
     int H, int k, const float* __restrict__ scale, const uint8_t* __restrict__ zp,
     const int32_t* __restrict__ fmap, float* __restrict__ y, int nwin, int nwg,
-    int rows_per_wave) {
-  const int64_t b = blockIdx.x;
-  const int64_t rb = b / nwg;
+    int rows_per_wave, int64_t nrb) {
+  // unit = block of token rows; its nwg blocks (4 windows each) run on one
+  // XCD, so the cache lines that neighbouring windows share are fetched into
+  // one L2 once
+  int64_t rb, sub;
+  if (!xcd_unit_block(blockIdx.x, nwg, nrb, &rb, &sub)) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = (int)(b % nwg) * 4 + wave;
+  const int c = (int)sub * 4 + wave;
   if (c >= nwin) return;   // no block barrier below
   const int hw0 = c * 256;
   const int h0 = hw0 + 4 * lane;
@@ -342,13 +345,13 @@ hipError_t launch_decompress_sets(const uint8_t* packed, int64_t pitch, const ui
                    P * T * k * 2 < (int64_t(1) << 30) &&
                    (uintptr_t)packed % 4 == 0 && (uintptr_t)fmap % 16 == 0 &&
                    (uintptr_t)scale % 16 == 0 && (uintptr_t)zp % 4 == 0 &&
-                   (uintptr_t)y % 16 == 0 && nwg * nrb < (int64_t(1) << 31);
+                   (uintptr_t)y % 16 == 0 && xcd_grid(nwg, nrb) < (int64_t(1) << 31);
   if (reg) {
-    const unsigned blocks = (unsigned)(nwg * nrb);
+    const unsigned blocks = (unsigned)xcd_grid(nwg, nrb);
 #define BTQ_SETS(np, ro)                                                                        \
   decompress_sets_reg_kernel<np, ro><<<blocks, 256, 0, s>>>(packed, (int)pitch, outl, T, (int)H, \
                                                             (int)k, scale, zp, fmap, y,          \
-                                                            (int)nwin, (int)nwg, (int)rpw)
+                                                            (int)nwin, (int)nwg, (int)rpw, nrb)
 #define BTQ_SETS_P(ro)             \
   switch (P) {                     \
     case 1: BTQ_SETS(1, ro); break; \
