@@ -276,10 +276,13 @@ int btq_decompress_reduce_bf16(const uint8_t *packed, int64_t packed_pitch,
  *   +0) of fl(q - zero_point[p,h]) * scale[p,h], q being shard p's code of h
  *   at slot fmap[p,h], or of the BF16 value outliers[p,t,-1-fmap[p,h]].
  *   scale fp32 [P,H], zero_point u8 [P,H], fmap i32 [P,H] in; y fp32 [T,H]
- *   out. The maps are trusted, as in btq_decompress_reduce. A 16-byte
- *   aligned y, fmap and scale, 8-byte aligned zero_point, H a multiple of 8
- *   and a pitch that is a multiple of 4 take the vectorized kernel; any
- *   other case takes a general one.
+ *   out. The maps are trusted, as in btq_decompress_reduce. Kernel choice:
+ *   P <= 8, H a multiple of 4, a pitch that is a multiple of 4 and at least
+ *   8, a 4-byte aligned packed and zero_point, 16-byte aligned fmap, scale
+ *   and y (and packed/outliers tensors under 2^30 bytes) take the fast one;
+ *   any P with H a multiple of 8 and the same alignments (zero_point 8)
+ *   take a shard-loop one; everything else a per-element one. All three
+ *   give the same bits.
  */
 int btq_select_outliers_per_shard(const float *run_min, const float *run_max,
                                   int64_t P, int64_t H, int64_t k,
