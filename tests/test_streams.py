@@ -1,0 +1,121 @@
+"""Streams and graphs: every call enqueues on the stream it is given and
+keeps no state between calls (GPU).
+
+  * the whole path on a side stream gives the same bytes as on the default
+    stream;
+  * two codecs on two streams at once give the same bytes as one after the
+    other;
+  * compress and both receivers captured in a graph and replayed, with new
+    inputs copied in between replays and eager work between them, match
+    the eager calls on every replay (the kernels clear nothing with memset:
+    every output byte is written by a kernel, so the graph holds only
+    kernel nodes).
+"""
+import pytest
+import torch
+
+import bit_tensor_activation_amd as B
+import workloads as W
+from helpers import say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+P, T, H, K = 8, 40, 2048, 64
+COLS = list(range(3, H, 53))
+
+
+def draw(seed, T_=T):
+    return W.draw(P, T_, H, seed, sigma=0.5, cols=COLS, outlier_factor=60.0, device=DEV)
+
+
+def full_path(x_calib, x, stream=None):
+    """Calibrate, select, compress and decompress, all on `stream`."""
+    rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
+    rmax = torch.empty_like(rmin)
+    for b, xb in enumerate(x_calib):
+        B.btq_calib_update(xb, rmin, rmax, 0.9, b == 0, stream=stream)
+    sel = B.btq_select_outliers(rmin, rmax, K, stream=stream)
+    pk, ol = B.btq_compress_pack(x, K, sel["enc"], sel["outlier_idx"], sel["cmap"], stream=stream)
+    y = B.btq_decompress_reduce(pk, ol, H, sel["dec"], sel["outlier_idx"], sel["cmap"],
+                                stream=stream)
+    return [rmin, rmax, sel["scale"], sel["cmap"], sel["enc"], sel["dec"], pk, ol, y]
+
+
+def same_bytes(a, b):
+    return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+def test_side_stream_matches_default_stream():
+    say("case: side stream vs default stream")
+    calib = [draw(7000 + b) for b in range(2)]
+    x = draw(7100)
+    torch.cuda.synchronize()
+    ref = full_path(calib, x)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=DEV)   # default priority
+    with torch.cuda.stream(side):
+        got = full_path(calib, x, stream=side)
+    side.synchronize()
+    for a, b in zip(ref, got):
+        assert same_bytes(a, b)
+
+
+def test_two_streams_at_once_match_one_after_the_other():
+    say("case: two codecs on two streams at once")
+    inputs = [([draw(7200 + 10 * i + b) for b in range(2)], draw(7300 + i)) for i in range(2)]
+    torch.cuda.synchronize()
+    seq = [full_path(c, x) for c, x in inputs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=DEV) for _ in range(2)]
+    outs = []
+    for s, (c, x) in zip(streams, inputs):
+        with torch.cuda.stream(s):
+            outs.append(full_path(c, x, stream=s))
+    for s in streams:
+        s.synchronize()
+    for ref, got in zip(seq, outs):
+        for a, b in zip(ref, got):
+            assert same_bytes(a, b)
+
+
+def test_graph_replays_match_eager_calls():
+    say("case: graph capture of compress and both receivers, 3 replays")
+    calib = [draw(7400 + b) for b in range(2)]
+    rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
+    rmax = torch.empty_like(rmin)
+    for b, xb in enumerate(calib):
+        B.btq_calib_update(xb, rmin, rmax, 0.9, b == 0)
+    sel = B.btq_select_outliers(rmin, rmax, K)
+    pitch = B.btq_packed_pitch(H, K)
+    x_static = torch.empty((P, T, H), dtype=torch.int16, device=DEV)
+    pk = torch.empty((P, T, pitch), dtype=torch.uint8, device=DEV)
+    ol = torch.empty((P, T, K), dtype=torch.int16, device=DEV)
+    y = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    y16 = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    args = (sel["enc"], sel["outlier_idx"], sel["cmap"])
+
+    def step(stream=None):
+        B.btq_compress_pack(x_static, K, *args, packed=pk, outliers=ol, stream=stream)
+        B.btq_decompress_reduce(pk, ol, H, sel["dec"], sel["outlier_idx"], sel["cmap"], y=y,
+                                stream=stream)
+        B.btq_decompress_reduce_bf16(pk, ol, H, sel["dec"], sel["outlier_idx"], sel["cmap"],
+                                     y=y16, stream=stream)
+
+    x_static.copy_(draw(7500))
+    step()                      # eager warm-up, on the default stream
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()                  # calls see the capture stream as the current stream
+    for rep in range(3):
+        x_new = draw(7600 + rep)
+        x_static.copy_(x_new)   # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [pk.clone(), ol.clone(), y.clone(), y16.clone()]
+        step()                  # the same inputs, eager
+        torch.cuda.synchronize()
+        for a, b in zip(got, [pk, ol, y, y16]):
+            assert same_bytes(a, b), f"replay {rep}"
+        pk.zero_()              # the next replay must write every byte again
+        y.zero_()
