@@ -10,8 +10,9 @@
 // of tokens. Each lane streams 16-byte loads of 8 bf16 values and keeps 8
 // running min/max pairs, and the 4 waves of a block combine through LDS.
 // The result goes to a per-chunk partial array in the workspace. The second
-// kernel folds the chunks and applies the EMA. min/max are exact and do not
-// depend on order, so the split of the token axis cannot change the result.
+// kernel folds the chunks (4 waves per 64 columns) and applies the EMA.
+// min/max are exact and do not depend on order, so the split of the token
+// axis cannot change the result.
 #include <float.h>
 
 #include "common.hpp"
@@ -103,15 +104,37 @@ __global__ __launch_bounds__(256) void calib_partial_kernel(
 
 // Fold the chunk partials and apply the moving average:
 //   first batch: run = batch;  otherwise run = fl(fl(a*run) + fl(c*batch)).
+// A block takes 64 columns of (shard, feature). Its 4 waves fold every 4th
+// chunk each (a wave reads 64 consecutive floats per chunk), with several
+// chunks in flight per thread, and meet in LDS. min/max are exact and
+// order-free, so the grouping cannot change the result.
+constexpr int kFoldCols = kWave;
+constexpr int kFoldGroups = 4;
+
 __global__ __launch_bounds__(256) void calib_combine_kernel(
     const float* __restrict__ pmin, const float* __restrict__ pmax, int64_t nchunk, int64_t PH,
     float a, float c, int first, float* __restrict__ run_min, float* __restrict__ run_max) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= PH) return;
-  float m = pmin[i], M = pmax[i];
-  for (int64_t ch = 1; ch < nchunk; ++ch) {
-    m = fminf(m, pmin[ch * PH + i]);
-    M = fmaxf(M, pmax[ch * PH + i]);
+  __shared__ float smin[kFoldGroups][kFoldCols];
+  __shared__ float smax[kFoldGroups][kFoldCols];
+  const int col = threadIdx.x & (kFoldCols - 1);
+  const int g = threadIdx.x / kFoldCols;
+  const int64_t i = (int64_t)blockIdx.x * kFoldCols + col;
+  float m = INFINITY, M = -INFINITY;
+  if (i < PH) {
+#pragma unroll 4
+    for (int64_t ch = g; ch < nchunk; ch += kFoldGroups) {
+      m = fminf(m, pmin[ch * PH + i]);
+      M = fmaxf(M, pmax[ch * PH + i]);
+    }
+  }
+  smin[g][col] = m;
+  smax[g][col] = M;
+  __syncthreads();
+  if (g != 0 || i >= PH) return;
+#pragma unroll
+  for (int w = 1; w < kFoldGroups; ++w) {
+    m = fminf(m, smin[w][col]);
+    M = fmaxf(M, smax[w][col]);
   }
   if (first) {
     run_min[i] = m;
@@ -151,8 +174,8 @@ hipError_t launch_calib(const uint16_t* x, int64_t P, int64_t T, int64_t H, floa
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t PH = P * H;
-  calib_combine_kernel<<<(unsigned)((PH + 255) / 256), 256, 0, s>>>(pmin, pmax, plan.nchunk, PH, a,
-                                                                     c, first, run_min, run_max);
+  calib_combine_kernel<<<(unsigned)((PH + kFoldCols - 1) / kFoldCols), 256, 0, s>>>(
+      pmin, pmax, plan.nchunk, PH, a, c, first, run_min, run_max);
   return hipGetLastError();
 }
 
