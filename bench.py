@@ -206,6 +206,42 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, copy_mib: 
     return "\n".join(lines) + "\n"
 
 
+SQ_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY",
+               "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM", "SQ_INSTS_VALU")
+
+
+def summarize_sq(sq_dir: str, note: str, n_simd: int = 1024, mhz: float = 2400.0) -> str:
+    """Where the waves of each libbtq kernel spend their time, from one
+    rocprofv3 --pmc run with the SQ_COUNTERS (medians over dispatches).
+
+    SQ_WAVE_CYCLES and the SQ_ACTIVE_INST_* / SQ_WAIT_* counters count in
+    units of 4 cycles, summed over waves; one VALU instruction of a wave64
+    occupies its SIMD for 4 cycles. valu_us_per_simd = SQ_INSTS_VALU * 4
+    cycles / SIMDs / clock: the time each SIMD spends issuing VALU work.
+    """
+    import statistics
+    per = {}
+    for r in _csv_rows(sq_dir, "counter_collection.csv"):
+        name = r["Kernel_Name"].split("(")[0].replace("void ", "").strip()
+        if "btq::" not in name:
+            continue
+        per.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    lines = ["# " + note.replace("\n", "\n# "),
+             "# kernel | wait_inst_any | wait_any | valu_active | lds_active | vmem_active "
+             "(fractions of wave time) | VALU instructions | valu_us_per_simd"]
+    for name, cs in per.items():
+        med = {c: statistics.median(v) for c, v in cs.items()}
+        wc = med.get("SQ_WAVE_CYCLES", 0.0) or 1.0
+        valu_us = med.get("SQ_INSTS_VALU", 0.0) * 4.0 / n_simd / mhz
+        lines.append(f"{name} | {med.get('SQ_WAIT_INST_ANY', 0) / wc:.2f} | "
+                     f"{med.get('SQ_WAIT_ANY', 0) / wc:.2f} | "
+                     f"{med.get('SQ_ACTIVE_INST_VALU', 0) / wc:.2f} | "
+                     f"{med.get('SQ_ACTIVE_INST_LDS', 0) / wc:.2f} | "
+                     f"{med.get('SQ_ACTIVE_INST_VMEM', 0) / wc:.2f} | "
+                     f"{med.get('SQ_INSTS_VALU', 0):.3g} | {valu_us:.1f}")
+    return "\n".join(lines) + "\n"
+
+
 def summarize_trace(trace_dir: str, note: str) -> str:
     """The libbtq rows of a rocprofv3 --kernel-trace --stats run."""
     lines = ["# " + note.replace("\n", "\n# "),
@@ -289,6 +325,9 @@ def main() -> int:
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="print the libbtq rows of a rocprofv3 --stats run and exit")
+    ap.add_argument("--summarize-sq", metavar="SQ_DIR",
+                    help="print the wave-time breakdown of a rocprofv3 --pmc run of the SQ "
+                         "counters and exit")
     ap.add_argument("--note", default="", help="header text for the summaries")
     args = ap.parse_args()
     if args.summarize_counters:
@@ -297,6 +336,9 @@ def main() -> int:
         return 0
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.note), end="")
+        return 0
+    if args.summarize_sq:
+        print(summarize_sq(args.summarize_sq, args.note), end="")
         return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
