@@ -1,4 +1,4 @@
-"""Shared drivers for the GPU-vs-oracle parity tests.
+"""Shared helpers for the GPU-vs-oracle parity tests.
 
 Both sides always see one tensor: the inputs are drawn on the GPU by
 `workloads`, the HIP path reads them in place, and the oracle reads a host
