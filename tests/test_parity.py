@@ -107,6 +107,11 @@ CASES = [
     (2, 8, 1024, 200, "normal", list(range(100, 300)), "200 clustered BF16 features in one tile"),
     (4, 6, 2048, 600, "laplace", list(range(0, 2048, 3))[:600], "k=600: wide LDS span"),
     (1, 1, 8, 3, "normal", [1], "smallest: P=1, T=1, H=8"),
+    (3, 5, 16, 15, "normal", [2], "k=H-1: a single int4 slot"),
+    (2, 4, 1, 0, "normal", [0], "H=1, k=0"),
+    (2, 4, 1, 1, "normal", [0], "H=1, k=1"),
+    (5, 7, 2, 1, "laplace", [1], "H=2"),
+    (64, 3, 64, 2, "normal", [5, 40], "P=64: many shards"),
     (8, 1, 8192, 64, "normal", list(range(3, 8192, 200)), "decode-like T=1"),
     (8, 24, 2048, 96, "normal", list(range(600, 624)), "P=8, 24 clustered BF16: 3-4 registers"),
     (8, 20, 2048, 64, "normal", list(range(700, 745)), "P=8, 45 clustered BF16: post-loop sums"),

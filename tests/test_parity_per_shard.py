@@ -94,6 +94,9 @@ CASES = [
     (2, 5, 24, 8, 0, "pitch = 8 bytes: the code window moves back one dword"),
     (2, 5, 12, 4, 0, "pitch = 4 bytes: general kernel"),
     (8, 33, 4096, 64, 0, "7B-like rows, pitch = code bytes"),
+    (3, 5, 16, 14, None, "k=H-2: two int4 slots"),
+    (2, 4, 4, 1, None, "H=4"),
+    (16, 3, 64, 2, None, "P=16: shard-loop kernel"),
 ]
 
 
