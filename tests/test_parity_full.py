@@ -118,3 +118,70 @@ def test_full_size(name, T, k, nb):
     assert_y_bf16_close(y16[ridx].cpu().numpy(), y_o, sel_o["scale"], sel_o["idx"])
     del x, pk, ol, y, y16
     torch.cuda.empty_cache()
+
+
+def test_message_beyond_2_gib():
+    """A batch whose packed message passes 2^31 bytes (P=8, T=65552, H=8192,
+    k=64: 2.15 GB of codes). The receivers take their general kernels there
+    (the fast ones address a whole message with one 32-bit descriptor), and
+    every offset is 64-bit. Checked on sampled rows, both ends included, for
+    the shared path (fp32 and bf16 output) and for per-shard sets."""
+    from test_parity_per_shard import assert_per_shard_selection_equal
+    P, H, k, T = 8, 8192, 64, 65552
+    pitch = B.btq_packed_pitch(H, k)
+    assert P * T * pitch >= 2 ** 31
+    say(f"case: message beyond 2 GiB, P={P} T={T} H={H} k={k} pitch={pitch}")
+    cols = list(range(17, H, 199))
+    calib = [W.draw(P, 256, H, 8000 + b, sigma=0.5, cols=cols, outlier_factor=50.0, device=DEV)
+             for b in range(2)]
+    rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
+    rmax = torch.empty_like(rmin)
+    mn = mx = None
+    for b, xb in enumerate(calib):
+        B.btq_calib_update(xb, rmin, rmax, 0.9, first_batch=(b == 0))
+        mn, mx = oracle_calib(u16(xb), mn, mx, 0.9, first=(b == 0))
+    del calib
+    sel_g = B.btq_select_outliers(rmin, rmax, k)
+    sel_o = O.select_outliers(mn, mx, k)
+    ps_g = B.btq_select_outliers_per_shard(rmin, rmax, k)
+    ps_o = O.select_outliers_per_shard(mn, mx, k)
+    torch.cuda.synchronize()
+    assert_selection_equal(sel_g, sel_o)
+    assert_per_shard_selection_equal(ps_g, ps_o)
+
+    x = W.draw(P, T, H, 8100, sigma=0.5, cols=cols, outlier_factor=50.0, device=DEV)
+    rows = np.array(sorted({0, 1, 63, 64, 32767, 32768, T // 2, T - 17, T - 2, T - 1} |
+                           set(np.random.default_rng(5).integers(0, T, 16).tolist())))
+    ridx = torch.as_tensor(rows, device=DEV)
+    xs = u16(x[:, ridx, :])
+    for name, sel_gpu, sel_orc, comp, deco in (
+            ("shared", sel_g, sel_o, B.btq_compress_pack, None),
+            ("per-shard", ps_g, ps_o, B.btq_compress_pack_per_shard, None)):
+        say(f"  {name} sets")
+        pk, ol = comp(x, k, sel_gpu["enc"], sel_gpu["outlier_idx"], sel_gpu["cmap"])
+        if name == "shared":
+            y = B.btq_decompress_reduce(pk, ol, H, sel_gpu["dec"], sel_gpu["outlier_idx"],
+                                        sel_gpu["cmap"])
+            y16 = B.btq_decompress_reduce_bf16(pk, ol, H, sel_gpu["dec"],
+                                               sel_gpu["outlier_idx"], sel_gpu["cmap"])
+        else:
+            y = B.btq_decompress_reduce_per_shard(pk, ol, H, sel_gpu["scale"],
+                                                  sel_gpu["zero_point"], sel_gpu["fmap"])
+            y16 = None
+        torch.cuda.synchronize()
+        pk_o, ol_o = oracle_compress_rows(xs, sel_orc, pitch=pitch)
+        assert_bits_equal(pk[:, ridx, :], pk_o, f"packed ({name}, sampled rows)")
+        assert_bits_equal(ol[:, ridx, :].view(torch.int16), ol_o.view(np.int16),
+                          f"outliers ({name}, sampled rows)")
+        y_o = O.decompress_reduce(pk_o, ol_o, sel_orc["scale"], sel_orc["zero_point"],
+                                  sel_orc["fmap"])
+        if name == "shared":
+            assert_y_close(y[ridx].cpu().numpy(), y_o, sel_orc["scale"], sel_orc["idx"])
+            assert_y_bf16_close(y16[ridx].cpu().numpy(), y_o, sel_orc["scale"], sel_orc["idx"])
+            assert torch.equal(y16[ridx], y[ridx].to(torch.bfloat16).view(torch.int16))
+        else:
+            assert_bits_equal(y[ridx], y_o, "y (per-shard, sampled rows)")
+        del pk, ol, y, y16
+        torch.cuda.empty_cache()
+    del x
+    torch.cuda.empty_cache()
