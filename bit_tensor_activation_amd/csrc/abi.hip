@@ -282,6 +282,6 @@ const char* btq_status_str(int status) {
   }
 }
 
-const char* btq_version(void) { return "0.1.0"; }
+const char* btq_version(void) { return "0.2.0"; }
 
 }  // extern "C"
