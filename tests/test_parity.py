@@ -278,3 +278,32 @@ def test_repeatable_bitwise():
     for a, b in zip(*outs):
         assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
                            b.view(torch.uint8) if b.dtype != torch.uint8 else b)
+
+
+def test_calibration_resume_is_bitwise():
+    # The calibration state is the caller's running extremes: saving them to
+    # host memory after some batches and continuing from a restored copy
+    # gives the uninterrupted run's bytes (and the oracle's values).
+    say("case: calibration checkpoint and resume")
+    P, T, H = 4, 96, 2056
+    xs = [W.draw(P, T, H, 9000 + b, sigma=0.5, cols=[3, 700, 2055], outlier_factor=30.0,
+                 device=DEV) for b in range(4)]
+    straight = [torch.empty((P, H), dtype=torch.float32, device=DEV) for _ in range(2)]
+    for b, xb in enumerate(xs):
+        B.btq_calib_update(xb, *straight, 0.9, first_batch=(b == 0))
+    part = [torch.empty((P, H), dtype=torch.float32, device=DEV) for _ in range(2)]
+    for b, xb in enumerate(xs[:2]):
+        B.btq_calib_update(xb, *part, 0.9, first_batch=(b == 0))
+    saved = [t.cpu().clone() for t in part]          # the checkpoint
+    del part
+    resumed = [t.to(DEV) for t in saved]
+    for xb in xs[2:]:
+        B.btq_calib_update(xb, *resumed, 0.9, first_batch=False)
+    torch.cuda.synchronize()
+    for a, b in zip(straight, resumed):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    mn = mx = None
+    for b, xb in enumerate(xs):
+        mn, mx = oracle_calib(u16(xb), mn, mx, 0.9, first=(b == 0))
+    assert_stats_equal(resumed[0], mn, "run_min")
+    assert_stats_equal(resumed[1], mx, "run_max")
