@@ -120,9 +120,9 @@ __global__ __launch_bounds__(256) void decompress_sets_kernel(
 }
 
 // Register kernel (P <= 8). A wave owns a window of 256 features (4 per
-// lane) over rows_per_wave token rows; a block, 4 adjacent windows. Before the rows it reduces every
-// shard's map, zero points and scales of its 4 features to 8 registers per
-// shard:
+// lane) over rows_per_wave token rows; a block, 4 adjacent windows. Before
+// the rows, it reduces every shard's map, zero points and scales of its 4
+// features to 8 registers per shard:
 //   * nib: the bit shift of each int4 feature's code within the 64 bits
 //     loaded at byte `pb` of the row (the lane's int4 features take
 //     consecutive slots of the shard, so two aligned dwords hold them);
@@ -131,10 +131,13 @@ __global__ __launch_bounds__(256) void decompress_sets_kernel(
 //     shard's outlier block (a shard's BF16 features are listed in ascending
 //     h, so the window's ones are a contiguous run [ilo, ihi));
 //   * the 4 scales.
-// Per row it then issues, for all shards at once, the two code dwords and
-// one coalesced load of the run (lane l holds element ilo + l, RO registers
-// for runs longer than 64), and each lane fetches its BF16 values from the
-// holding lanes with ds_bpermute. Terms are summed in shard order from +0.
+// Per row, it issues the two code dwords and one coalesced load of the run
+// for all shards at once (lane l holds run element ilo + l; RO registers for
+// runs longer than 64). Two register sets take turns, so the next row's
+// loads are in flight during a row's arithmetic. Each lane fetches its BF16
+// values from the holding lanes with ds_bpermute, or, for runs longer than
+// 64, from a per-row LDS copy of the run. Terms are summed in shard order
+// from +0.
 template <int NP, int RO>
 __global__ __launch_bounds__(256) void decompress_sets_reg_kernel(
     const uint8_t* __restrict__ packed, int pitch, const uint16_t* __restrict__ outl, int64_t T,
