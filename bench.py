@@ -50,10 +50,17 @@ def log(msg: str) -> None:
 
 
 def source_hash(paths) -> str:
+    """Hash of the kernel code: comments and blank lines are left out, so
+    that only a change to the code itself invalidates a counter summary."""
+    import re
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = [line.rstrip() for line in text.splitlines() if line.strip()]
+        h.update("\n".join(code).encode())
     return h.hexdigest()[:16]
 
 

@@ -43,6 +43,10 @@
 //
 // General kernel. One thread per packed byte and per BF16 value. It serves
 // any H, k, pitch, alignment and LDS size.
+//
+// Per-shard BF16 sets (template flag kPs): cmap [P,H-k] and idx [P,k] hold
+// one set per shard, and each (shard, row block) unit offsets them by its
+// shard before it derives its tile geometry; nothing else changes.
 #include "common.hpp"
 
 namespace btq {

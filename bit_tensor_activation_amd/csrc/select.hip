@@ -17,6 +17,13 @@
 // Last, codec_tables_kernel (one thread per int4 slot) copies each slot's
 // parameters into the encoder and decoder tables in slot order, the order
 // in which the hot kernels consume them.
+//
+// Variants of the ranking (other readings of how per-device ranges rank
+// features): the score may be the widest shard's range instead of the sum;
+// one set per shard runs the top-k block once per shard on that shard's
+// widths (grid P) and shard_enc_kernel builds its sender table; and a set
+// given by the caller skips the ranking, with set_maps_kernel finding
+// membership by binary search and sharing the ordered compaction.
 #include <float.h>
 
 #include "common.hpp"

@@ -127,3 +127,14 @@ def test_more_than_one_gpu_is_refused(monkeypatch, capsys):
     monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
     assert bench.main() == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_source_hash_follows_code_not_comments(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    src.write_text("// header\nint f(int a) {  // note\n  return a + 1;\n}\n")
+    h0 = bench.source_hash(["k.hip"])
+    src.write_text("/* a longer\n   header */\n\nint f(int a) {\n  return a + 1;   // other note\n}\n")
+    assert bench.source_hash(["k.hip"]) == h0
+    src.write_text("int f(int a) {\n  return a + 2;\n}\n")
+    assert bench.source_hash(["k.hip"]) != h0
