@@ -326,8 +326,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cpu-sample-T", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="also run a plain device copy of this size (counter scaling)")
+    ap.add_argument("--copy-probe-mib", type=int, default=256,
+                    help="size of the plain device copy timed for the copy roofline (and the "
+                         "counter scale); 0 skips it")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
@@ -518,6 +519,7 @@ def main() -> int:
         n = args.copy_probe_mib * 2 ** 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
+        dst.copy_(src)   # warm-up
         torch.cuda.synchronize()
         c0, c1 = hev.new(), hev.new()
         hev.record(c0, sh)
@@ -589,6 +591,10 @@ def main() -> int:
     }
     if copy_probe:
         out["copy_probe"] = copy_probe
+        # the same kernel against what a plain device copy (read + write)
+        # reaches on this GPU
+        out["roofline"]["copy_GBps"] = copy_probe["GBps"]
+        out["roofline"]["frac_of_copy"] = round(achieved / copy_probe["GBps"], 4)
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle for >= {args.cpu_seconds:.0f} s")
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample_T, T), args.cpu_seconds)
