@@ -227,6 +227,11 @@ int btq_compress_pack(const uint16_t *x, int64_t P, int64_t T, int64_t H, int64_
  *                     only the code bytes of a row are read
  *   dec_table fp32 [2P+1,H-k], outlier_idx [k], cmap [H-k]        in
  *   y    fp32 [T,H]  out
+ * Kernel choice: P <= 8, H a multiple of 4 and H-k of 8, a pitch that is a
+ * multiple of 4, and a message (P*T*pitch bytes, and P*T*k*2 for the BF16
+ * block) under 2^31 bytes take the fast kernel. Anything else, such as more
+ * than 8 shards or a larger batch (which a caller can also split by tokens),
+ * takes a general kernel, which is correct but much slower.
  */
 int btq_decompress_reduce(const uint8_t *packed, int64_t packed_pitch,
                           const uint16_t *outliers, int64_t P, int64_t T, int64_t H,
