@@ -3,7 +3,7 @@
 Every codec step runs in the library's HIP kernels (calibration, selection,
 compress, decompress). This script only draws inputs and measures the reduced
 output y against the exact sum of the unquantized bf16 partial sums,
-sum_p x[p] in float64. It reports four things:
+sum_p x[p] in float64. It reports:
 
   * error vs k: how the error falls as range-ranked BF16 features are added;
   * selection rules at a workload's k: range-ranked (shard ranges summed,
@@ -20,7 +20,9 @@ sum_p x[p] in float64. It reports four things:
     excess kurtosis -1.2 sum_p s_p^4 / (sum_p s_p^2)^2 (-1.2/P for equal
     scales);
   * drift: outlier columns that move after calibration (the stress workload)
-    are quantized with ranges that do not hold them.
+    are quantized with ranges that do not hold them;
+  * output precision: the fp32 and the bf16-output receivers against the
+    same exact sum.
 
 Error measures over y [T,H]: nmse = sum (y - exact)^2 / sum exact^2, its
 SNR in dB, and the largest absolute error.
@@ -177,6 +179,22 @@ def selection_rules(name: str, k: int, n_random: int = 4, calib_batches=None) ->
     return out
 
 
+def output_precision(name: str, calib_batches=None) -> list:
+    """Error of the fp32 and the bf16-output receivers at the workload's k:
+    the bf16 output adds one rounding (at most half a bf16 ulp of y) to the
+    int4 error."""
+    w, rmin, rmax, x = workload_state(name, calib_batches)
+    ex = exact_sum(x)
+    sel = B.btq_select_outliers(rmin, rmax, w.k)
+    pk, ol = B.btq_compress_pack(x, w.k, sel["enc"], sel["outlier_idx"], sel["cmap"])
+    args = (pk, ol, w.H, sel["dec"], sel["outlier_idx"], sel["cmap"])
+    y32 = B.btq_decompress_reduce(*args)
+    y16 = B.btq_decompress_reduce_bf16(*args).view(torch.bfloat16).float()
+    base = dict(report="output", workload=name, P=w.P, T=x.shape[1], H=w.H, k=w.k)
+    return [dict(base, output="fp32", **error_stats(y32, ex)),
+            dict(base, output="bf16", **error_stats(y16, ex))]
+
+
 def irwin_hall(Ps, T=2048, H=4096, sigma=0.5, calib_batches=4, seed=91) -> list:
     """Statistics of the summed int4 error (k = 0) vs the shard count P.
 
@@ -269,6 +287,12 @@ def table(records: list) -> str:
             lines.append(f"{r['workload']} | {r['rule']} | {r['k']} | {r['nmse']:.3e}{extra} | "
                          f"{r['snr_db']:.1f} | {r['max_abs_err']:.3g}")
         lines.append("")
+    if "output" in by:
+        lines += ["output precision at the workload's k (fp32 vs bf16 receiver)",
+                  "workload | k | output | nmse | SNR dB | max |err|"]
+        lines += [f"{r['workload']} | {r['k']} | {r['output']} | {r['nmse']:.3e} | "
+                  f"{r['snr_db']:.1f} | {r['max_abs_err']:.3g}" for r in by["output"]]
+        lines.append("")
     if "irwin_hall" in by:
         lines += ["summed int4 error vs P (k=0, normal data, in-range elements, z = e/sd)",
                   "P | elements | in range | mean z (tol) | var z | excess kurtosis | predicted "
@@ -289,7 +313,7 @@ def table(records: list) -> str:
     return "\n".join(lines)
 
 
-REPORTS = ("error_vs_k", "selection", "irwin_hall", "drift")
+REPORTS = ("error_vs_k", "selection", "output", "irwin_hall", "drift")
 
 
 def run(only=None) -> list:
@@ -306,6 +330,9 @@ def run(only=None) -> list:
             recs += selection_rules("decode", 64)
             recs += selection_rules("shard_local", 32)
             recs += selection_rules("shard_local", 64)
+        elif rep == "output":
+            recs += output_precision("7b_prefill")
+            recs += output_precision("large_prefill")
         elif rep == "irwin_hall":
             recs += irwin_hall([1, 2, 4, 8, 16])
         elif rep == "drift":
