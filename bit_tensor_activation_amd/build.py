@@ -60,13 +60,22 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
-def device_asm(out_dir: str) -> None:
-    """Write each source's gfx950 assembly to out_dir (for reading codegen)."""
+def device_asm(out_dir: str) -> list:
+    """Write each source's gfx950 assembly to out_dir (for reading codegen).
+
+    Returns the paths written. The sources compile in parallel."""
+    from concurrent.futures import ThreadPoolExecutor
     os.makedirs(out_dir, exist_ok=True)
-    for src in sources():
+
+    def one(src):
         out = os.path.join(out_dir, os.path.basename(src).replace(".hip", ".s"))
         cmd = [hipcc(), *COMMON_FLAGS, "--cuda-device-only", "-S", src, "-o", out]
         subprocess.run(cmd, check=True, capture_output=True, text=True)
+        return out
+
+    srcs = sources()
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1, 8)) as ex:
+        return list(ex.map(one, srcs))
 
 
 if __name__ == "__main__":

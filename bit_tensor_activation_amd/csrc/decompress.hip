@@ -54,6 +54,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kDqRing = 4;
 constexpr int kDqRingSmall = 2;   // the same for short batches (decode): more, shorter waves
 constexpr int kDqSub = 2;    // token rows per sub-step (LDS y rows)
+// Chunk stores per lane per row whose LDS reads are issued together: a
+// 512-slot tile spans at most 768 features unless over 256 BF16 features
+// fall inside it.
+constexpr int kStU = 3;
 
 // fp32 -> bf16, round to nearest even: the one rounding of the bf16-output
 // receiver. Two values per instruction (v_cvt_pk_bf16_f32): a in the low
@@ -227,6 +231,35 @@ __global__ __launch_bounds__(256) void decompress_kernel(
   const uint32_t b_lds = cpad((uint32_t)(max(bpos, g.hs) - a4));
   const uint32_t b_off = bpos >= 0 ? (uint32_t)bpos * kYB : kOOB;
 
+  // y stores of one 16-byte chunk (4 features) and of one feature. The
+  // chunk store reaches its row through a per-row descriptor and takes an
+  // immediate zero as its scalar offset. A store wider than 64 bits reads
+  // its data registers after issue, so a VALU write to them on the next
+  // instruction needs one wait state. The compiler inserts it only for an
+  // immediate scalar offset: with a register there it lets the next
+  // instruction overwrite the data, and on gfx950 the stored values then
+  // come out wrong.
+  char* const ybase = static_cast<char*>(y) + t0 * H * kYB;
+  auto store_chunk = [&](const v4f& v, uint32_t off, uint32_t rowoff) {
+    const rsrc_t rr = make_rsrc(ybase + rowoff, (uint32_t)H * kYB);
+    if constexpr (kBf) {
+      typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+      __builtin_amdgcn_raw_buffer_store_b64(v2u{bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3])}, rr,
+                                            off, 0, kStream);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b128(
+          v4u{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+              __float_as_uint(v[3])},
+          rr, off, 0, kStream);
+    }
+  };
+  auto store_one = [&](float f, uint32_t off, uint32_t rowoff) {
+    if constexpr (kBf)
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bf16_bits_rne(f), ry, off, rowoff, kStream);
+    else
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), ry, off, rowoff, kStream);
+  };
+
   // nrows >= 1: a do-while has no entry guard that the ring loads could be
   // sunk below.
   int base = 0;
@@ -237,6 +270,29 @@ __global__ __launch_bounds__(256) void decompress_kernel(
       for (int r = 0; r < kDqSub; ++r) {
         const int q = sb * kDqSub + r;
         float* b = buf + r * buf_dwords;
+        // BF16 values first: the cross-lane reads are issued before the
+        // dequantization, so their LDS round trip overlaps it. Only the
+        // registers the tile fills are read (nreg is uniform); the others
+        // are never selected below.
+        const bool bf_row = compact && g.nout > 0;   // uniform
+        int t[NP][kOR];
+        if (bf_row) {
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            t[p][0] = __builtin_amdgcn_ds_bpermute(src_addr[p], (int)ov[q][0]);
+#pragma unroll
+            for (int rr = 1; rr < kOR; ++rr) t[p][rr] = 0;
+          }
+          if (nreg > 1) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+#pragma unroll
+              for (int rr = 1; rr < kOR; ++rr)
+                t[p][rr] = __builtin_amdgcn_ds_bpermute(src_addr[p], (int)ov[q][rr]);
+            }
+          }
+        }
+        issue_fence();
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = bias[e];
@@ -258,39 +314,17 @@ __global__ __launch_bounds__(256) void decompress_kernel(
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) b[ya[e]] = acc[e];
-        if (compact && g.nout > 0) {   // uniform
-          // The sum reads only the registers the tile fills; one body per
-          // register count. All cross-lane reads of the row are issued
-          // before the first is used (the fence keeps the scheduler from
-          // interleaving them with the sum, one round trip each).
-          auto bf16_sum = [&](auto regs) {
-            constexpr int nr = decltype(regs)::value;
-            int t[NP][nr];
+        if (bf_row) {
+          // the owner lane's shard values, added in shard order from 0
+          float o = 0.0f;
 #pragma unroll
-            for (int p = 0; p < NP; ++p) {
+          for (int p = 0; p < NP; ++p) {
+            int v = t[p][0];
 #pragma unroll
-              for (int rr = 0; rr < nr; ++rr)
-                t[p][rr] = __builtin_amdgcn_ds_bpermute(src_addr[p], (int)ov[q][rr]);
-            }
-            issue_fence();
-            float o = 0.0f;
-#pragma unroll
-            for (int p = 0; p < NP; ++p) {
-              int v = t[p][0];
-#pragma unroll
-              for (int rr = 1; rr < nr; ++rr) v = (src_reg[p] == rr) ? t[p][rr] : v;
-              // (the loads zero-extend the 16 bf16 bits)
-              o = __fadd_rn(o, bf16_to_f32((uint32_t)v));
-            }
-            return o;
-          };
-          float o;
-          if (nreg <= 1)   // uniform
-            o = bf16_sum(std::integral_constant<int, 1>{});
-          else if (nreg <= 2)
-            o = bf16_sum(std::integral_constant<int, 2>{});
-          else
-            o = bf16_sum(std::integral_constant<int, kOR>{});
+            for (int rr = 1; rr < kOR; ++rr) v = (src_reg[p] == rr) ? t[p][rr] : v;
+            // (the loads zero-extend the 16 bf16 bits)
+            o = __fadd_rn(o, bf16_to_f32((uint32_t)v));
+          }
           b[oa] = o;
         }
       }
@@ -298,33 +332,49 @@ __global__ __launch_bounds__(256) void decompress_kernel(
 #pragma unroll
       for (int r = 0; r < kDqSub; ++r) load(sb * kDqSub + r, base + kR + sb * kDqSub + r);
       wave_lds_sync();
+      if (st_it <= kStU) {   // uniform: the usual case
+        // Every LDS read of the sub-step is issued before its first store,
+        // so one LDS round trip is exposed per sub-step, not one per chunk.
+        // (a chunk index past the span is clamped into it; its lane's store
+        // is out of range)
+        v4f cv[kDqSub][kStU];
+        float rv[kDqSub];
 #pragma unroll
-      for (int r = 0; r < kDqSub; ++r) {
-        const int row = base + sb * kDqSub + r;
-        const bool ok = row < nrows;   // uniform
-        const float* b = buf + r * buf_dwords;
-        const uint32_t rowoff = (uint32_t)min(row, nrows - 1) * (uint32_t)H * kYB;
-        for (int it = 0; it < st_it; ++it) {
-          const int qc = q_lo + lane + kWave * it;
-          const v4f v = *reinterpret_cast<const v4f*>(b + cpad((uint32_t)(4 * min(qc, q_hi - 1))));
-          const uint32_t off = (ok && qc < q_hi) ? (uint32_t)(a4 + 4 * qc) * kYB : kOOB;
-          if constexpr (kBf) {
-            typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-            __builtin_amdgcn_raw_buffer_store_b64(v2u{bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3])},
-                                                  ry, off, rowoff, kStream);
-          } else {
-            __builtin_amdgcn_raw_buffer_store_b128(
-                v4u{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                    __float_as_uint(v[3])},
-                ry, off, rowoff, kStream);
+        for (int r = 0; r < kDqSub; ++r) {
+          const float* b = buf + r * buf_dwords;
+#pragma unroll
+          for (int it = 0; it < kStU; ++it) {
+            const int qc = min(q_lo + lane + kWave * it, q_hi - 1);
+            cv[r][it] = *reinterpret_cast<const v4f*>(b + cpad((uint32_t)(4 * max(qc, 0))));
           }
+          rv[r] = b[b_lds];
         }
-        if constexpr (kBf)
-          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bf16_bits_rne(b[b_lds]), ry,
-                                                ok ? b_off : kOOB, rowoff, kStream);
-        else
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(b[b_lds]), ry, ok ? b_off : kOOB,
-                                                rowoff, kStream);
+#pragma unroll
+        for (int r = 0; r < kDqSub; ++r) {
+          const int row = base + sb * kDqSub + r;
+          const bool ok = row < nrows;   // uniform
+          const uint32_t rowoff = (uint32_t)min(row, nrows - 1) * (uint32_t)H * kYB;
+#pragma unroll
+          for (int it = 0; it < kStU; ++it) {
+            const int qc = q_lo + lane + kWave * it;
+            store_chunk(cv[r][it], (ok && qc < q_hi) ? (uint32_t)(a4 + 4 * qc) * kYB : kOOB, rowoff);
+          }
+          store_one(rv[r], ok ? b_off : kOOB, rowoff);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < kDqSub; ++r) {
+          const int row = base + sb * kDqSub + r;
+          const bool ok = row < nrows;   // uniform
+          const float* b = buf + r * buf_dwords;
+          const uint32_t rowoff = (uint32_t)min(row, nrows - 1) * (uint32_t)H * kYB;
+          for (int it = 0; it < st_it; ++it) {
+            const int qc = q_lo + lane + kWave * it;
+            const v4f v = *reinterpret_cast<const v4f*>(b + cpad((uint32_t)(4 * min(qc, q_hi - 1))));
+            store_chunk(v, (ok && qc < q_hi) ? (uint32_t)(a4 + 4 * qc) * kYB : kOOB, rowoff);
+          }
+          store_one(b[b_lds], ok ? b_off : kOOB, rowoff);
+        }
       }
       wave_lds_sync();
     }

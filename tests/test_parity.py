@@ -152,6 +152,28 @@ def test_given_feature_set(P, T, H, k, note):
     assert sel["outlier_idx"].cpu().numpy().tolist() == feats.tolist()
 
 
+# A contiguous block of BF16 features puts one wave-tile's span far beyond
+# its 512 slots, so the receiver writes that tile's y through its
+# chunk-store loop (and, beyond 2048 features, the loop's unrolled body).
+WIDE_SPAN_CASES = [
+    (4, 37, 4096, (600, 3200), "tile spanning ~3100 features"),
+    (8, 20, 2048, (512, 1400), "tile spanning ~1400 features"),
+    (2, 9, 6000, (100, 5000), "tile spanning ~5400 features"),
+]
+
+
+@pytest.mark.parametrize("P,T,H,block,note", WIDE_SPAN_CASES, ids=[c[-1] for c in WIDE_SPAN_CASES])
+def test_wide_tile_span(P, T, H, block, note):
+    say(f"case: wide span P={P} T={T} H={H} block={block} ({note})")
+    cols = [block[0] + 5, H - 1]
+    calib = [W.draw(P, 8, H, 3300 + b, cols=cols, outlier_factor=40.0, device=DEV)
+             for b in range(2)]
+    x = W.draw(P, T, H, 3400, cols=cols, outlier_factor=40.0, device=DEV)
+    feats = np.arange(block[0], block[1])
+    sel, *_ = run_both(calib, x, len(feats), 0.9, features=feats)
+    assert sel["outlier_idx"].cpu().numpy().tolist() == feats.tolist()
+
+
 def test_given_set_reproduces_the_ranked_selection():
     say("case: select_features(top-k set) == select_outliers")
     P, H, k = 8, 4104, 64
