@@ -53,7 +53,14 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // shards a 4-row ring is the deepest whose waits stay exact.
 constexpr int kDqRing = 4;
 constexpr int kDqRingSmall = 2;   // the same for short batches (decode): more, shorter waves
-constexpr int kDqSub = 2;    // token rows per sub-step (LDS y rows)
+// Token rows per sub-step (kSub, a template parameter): the rows consumed,
+// staged in LDS and written before the ring refills. 1 when the grid is one
+// resident generation (one wave per SIMD): each row's ring slot refills as
+// soon as it is consumed, which matters most with nothing else on the SIMD
+// to hide the latency. 2 when several waves share a SIMD: half the LDS
+// round trips and waits per row.
+constexpr int kDqSubMax = 2;
+constexpr int64_t kDqGeneration = 1024;   // waves at one per SIMD (256 CUs x 4)
 // Chunk stores per lane per row whose LDS reads are issued together: a
 // 512-slot tile spans at most 768 features unless over 256 BF16 features
 // fall inside it.
@@ -82,12 +89,12 @@ __host__ __device__ constexpr int dq_row_dwords(int span) {
   return ((span + 3 + 31) / 32 * 32) * 9 / 8 + kWave;
 }
 
-// LDS: 4 waves x kDqSub y rows of buf_dwords.
+// LDS: 4 waves x kSub y rows of buf_dwords.
 // NP: shards. kOR: BF16 registers per row; a tile whose NP*nout BF16 values
 // fit in kOR*64 lanes sums them in the ring, a wider tile in a pass after it.
-// kR: ring depth. kBf: y is bf16 (one rounding of the fp32 sum) instead of
+// kR: ring depth. kSub: rows per sub-step. kBf: y is bf16 (one rounding of the fp32 sum) instead of
 // fp32.
-template <int NP, int kOR, int kR, bool kBf>
+template <int NP, int kOR, int kR, int kSub, bool kBf>
 __global__ __launch_bounds__(256) void decompress_kernel(
     const uint8_t* __restrict__ packed, int pitch, const uint16_t* __restrict__ outl, int64_t T,
     int H, int Hq, int k, int ntiles, int rows_per_wave, int64_t nrowblk, int buf_dwords,
@@ -108,7 +115,7 @@ __global__ __launch_bounds__(256) void decompress_kernel(
   const TileGeom g = tile_geom(cmap, c, ntiles, Hq, H);
   const int64_t t0 = rb * rows_per_wave;
   const int nrows = (int)min(T - t0, (int64_t)rows_per_wave);   // >= 1
-  float* const buf = reinterpret_cast<float*>(smem) + (size_t)wave * kDqSub * buf_dwords;
+  float* const buf = reinterpret_cast<float*>(smem) + (size_t)wave * kSub * buf_dwords;
   const uint32_t dummy = (uint32_t)(buf_dwords - kWave + lane);
 
   // Whole message tensors (the launcher checks they span < 2^31 bytes), and
@@ -265,10 +272,10 @@ __global__ __launch_bounds__(256) void decompress_kernel(
   int base = 0;
   do {
 #pragma unroll
-    for (int sb = 0; sb < kR / kDqSub; ++sb) {
+    for (int sb = 0; sb < kR / kSub; ++sb) {
 #pragma unroll
-      for (int r = 0; r < kDqSub; ++r) {
-        const int q = sb * kDqSub + r;
+      for (int r = 0; r < kSub; ++r) {
+        const int q = sb * kSub + r;
         float* b = buf + r * buf_dwords;
         // BF16 values first: the cross-lane reads are issued before the
         // dequantization, so their LDS round trip overlaps it. Only the
@@ -330,17 +337,17 @@ __global__ __launch_bounds__(256) void decompress_kernel(
       }
       // refill the consumed slots with the rows kR ahead
 #pragma unroll
-      for (int r = 0; r < kDqSub; ++r) load(sb * kDqSub + r, base + kR + sb * kDqSub + r);
+      for (int r = 0; r < kSub; ++r) load(sb * kSub + r, base + kR + sb * kSub + r);
       wave_lds_sync();
       if (st_it <= kStU) {   // uniform: the usual case
         // Every LDS read of the sub-step is issued before its first store,
         // so one LDS round trip is exposed per sub-step, not one per chunk.
         // (a chunk index past the span is clamped into it; its lane's store
         // is out of range)
-        v4f cv[kDqSub][kStU];
-        float rv[kDqSub];
+        v4f cv[kSub][kStU];
+        float rv[kSub];
 #pragma unroll
-        for (int r = 0; r < kDqSub; ++r) {
+        for (int r = 0; r < kSub; ++r) {
           const float* b = buf + r * buf_dwords;
 #pragma unroll
           for (int it = 0; it < kStU; ++it) {
@@ -350,8 +357,8 @@ __global__ __launch_bounds__(256) void decompress_kernel(
           rv[r] = b[b_lds];
         }
 #pragma unroll
-        for (int r = 0; r < kDqSub; ++r) {
-          const int row = base + sb * kDqSub + r;
+        for (int r = 0; r < kSub; ++r) {
+          const int row = base + sb * kSub + r;
           const bool ok = row < nrows;   // uniform
           const uint32_t rowoff = (uint32_t)min(row, nrows - 1) * (uint32_t)H * kYB;
 #pragma unroll
@@ -363,8 +370,8 @@ __global__ __launch_bounds__(256) void decompress_kernel(
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < kDqSub; ++r) {
-          const int row = base + sb * kDqSub + r;
+        for (int r = 0; r < kSub; ++r) {
+          const int row = base + sb * kSub + r;
           const bool ok = row < nrows;   // uniform
           const float* b = buf + r * buf_dwords;
           const uint32_t rowoff = (uint32_t)min(row, nrows - 1) * (uint32_t)H * kYB;
@@ -454,39 +461,43 @@ __global__ __launch_bounds__(256) void decompress_general_kernel(
   }
 }
 
-template <int NP, int kOR, int kR, bool kBf>
+template <int NP, int kOR, int kR, int kSub, bool kBf>
 static void launch_fast(const uint8_t* packed, int64_t pitch, const uint16_t* outl, int64_t T,
                         int64_t H,
                         int64_t k, int64_t Hq, int ntiles, int rpw, int64_t nrowblk,
                         int buf_dwords, const float* dec, const int32_t* idx,
                         const int32_t* cmap, void* y, hipStream_t s) {
   const int64_t ntgrp = (ntiles + kDqWaves - 1) / kDqWaves;
-  const size_t lds = (size_t)kDqWaves * kDqSub * buf_dwords * 4;
-  decompress_kernel<NP, kOR, kR, kBf><<<(unsigned)xcd_grid(ntgrp, nrowblk), 256, lds, s>>>(
+  const size_t lds = (size_t)kDqWaves * kSub * buf_dwords * 4;
+  decompress_kernel<NP, kOR, kR, kSub, kBf><<<(unsigned)xcd_grid(ntgrp, nrowblk), 256, lds, s>>>(
       packed, (int)pitch, outl, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, buf_dwords, dec,
       idx, cmap, y);
 }
 
 template <bool kBf>
-static void dispatch_fast(int64_t P, bool wide, bool small, const uint8_t* packed, int64_t pitch,
-                          const uint16_t* outl, int64_t T, int64_t H, int64_t k, int64_t Hq,
-                          int ntiles, int rpw, int64_t nrowblk, int buf_dwords, const float* dec,
-                          const int32_t* idx, const int32_t* cmap, void* y, hipStream_t s) {
+static void dispatch_fast(int64_t P, bool wide, bool small, bool one_gen, const uint8_t* packed,
+                          int64_t pitch, const uint16_t* outl, int64_t T, int64_t H, int64_t k,
+                          int64_t Hq, int ntiles, int rpw, int64_t nrowblk, int buf_dwords,
+                          const float* dec, const int32_t* idx, const int32_t* cmap, void* y,
+                          hipStream_t s) {
+  // (the 2-row ring serves short batches, whose grids are one generation)
   switch (P) {
-#define BTQ_DQ_CASE(n)                                                                          \
-  case n:                                                                                       \
-    if (wide && !small)                                                                         \
-      launch_fast<n, 4, kDqRing, kBf>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk,   \
-                                      buf_dwords, dec, idx, cmap, y, s);                        \
-    else if (wide)                                                                              \
-      launch_fast<n, 4, kDqRingSmall, kBf>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw,       \
-                                           nrowblk, buf_dwords, dec, idx, cmap, y, s);          \
-    else if (!small)                                                                            \
-      launch_fast<n, 2, kDqRing, kBf>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk,   \
-                                      buf_dwords, dec, idx, cmap, y, s);                        \
-    else                                                                                        \
-      launch_fast<n, 2, kDqRingSmall, kBf>(packed, pitch, outl, T, H, k, Hq, ntiles, rpw,       \
-                                           nrowblk, buf_dwords, dec, idx, cmap, y, s);          \
+#define BTQ_DQ_ARGS \
+  packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk, buf_dwords, dec, idx, cmap, y, s
+#define BTQ_DQ_CASE(n)                                                        \
+  case n:                                                                     \
+    if (wide && small)                                                        \
+      launch_fast<n, 4, kDqRingSmall, 1, kBf>(BTQ_DQ_ARGS);                   \
+    else if (wide && one_gen)                                                 \
+      launch_fast<n, 4, kDqRing, 1, kBf>(BTQ_DQ_ARGS);                        \
+    else if (wide)                                                            \
+      launch_fast<n, 4, kDqRing, 2, kBf>(BTQ_DQ_ARGS);                        \
+    else if (small)                                                           \
+      launch_fast<n, 2, kDqRingSmall, 1, kBf>(BTQ_DQ_ARGS);                   \
+    else if (one_gen)                                                         \
+      launch_fast<n, 2, kDqRing, 1, kBf>(BTQ_DQ_ARGS);                        \
+    else                                                                      \
+      launch_fast<n, 2, kDqRing, 2, kBf>(BTQ_DQ_ARGS);                        \
     break;
     BTQ_DQ_CASE(1)
     BTQ_DQ_CASE(2)
@@ -497,6 +508,7 @@ static void dispatch_fast(int64_t P, bool wide, bool small, const uint8_t* packe
     BTQ_DQ_CASE(7)
     BTQ_DQ_CASE(8)
 #undef BTQ_DQ_CASE
+#undef BTQ_DQ_ARGS
   }
 }
 
@@ -507,7 +519,8 @@ hipError_t launch_decompress(const uint8_t* packed, int64_t pitch, const uint16_
   const int64_t Hq = H - k;
   const int64_t span = (H < kTileSlots + k ? H : kTileSlots + k);
   const int buf_dwords = span < 65536 ? dq_row_dwords((int)span) : (1 << 30);
-  const size_t lds = (size_t)kDqWaves * kDqSub * buf_dwords * 4;
+  // (LDS for the larger sub-step, whichever the launch takes)
+  const size_t lds = (size_t)kDqWaves * kDqSubMax * buf_dwords * 4;
   // Buffer resources: the whole message, the decoder table and one wave's
   // rows of y must each span fewer than 2^31 bytes. y rows take stores of 4
   // values (16 bytes fp32, 8 bytes bf16): H a multiple of 4 and y aligned to
@@ -536,12 +549,15 @@ hipError_t launch_decompress(const uint8_t* packed, int64_t pitch, const uint16_
     // tile holds at most 64 of them on average, else 4. A tile beyond its
     // registers sums its BF16 features after the row loop.
     const bool wide = P * k > int64_t(kWave) * ntiles;
+    // one sub-step row while the grid is one generation (row counts below the
+    // 64-row cap), two once several waves share each SIMD
+    const bool one_gen = ntiles * nrowblk <= kDqGeneration;
     if (bf16)
-      dispatch_fast<true>(P, wide, small, packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk,
-                          buf_dwords, dec, idx, cmap, y, s);
+      dispatch_fast<true>(P, wide, small, one_gen, packed, pitch, outl, T, H, k, Hq, ntiles, rpw,
+                          nrowblk, buf_dwords, dec, idx, cmap, y, s);
     else
-      dispatch_fast<false>(P, wide, small, packed, pitch, outl, T, H, k, Hq, ntiles, rpw, nrowblk,
-                           buf_dwords, dec, idx, cmap, y, s);
+      dispatch_fast<false>(P, wide, small, one_gen, packed, pitch, outl, T, H, k, Hq, ntiles, rpw,
+                           nrowblk, buf_dwords, dec, idx, cmap, y, s);
     return hipGetLastError();
   }
   const int64_t n = T * H;
