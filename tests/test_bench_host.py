@@ -21,8 +21,8 @@ W7 = dict(P=8, T=2048, H=4096, k=64)
     ("btq::compress_general_kernel<false>(x)", "compress_pack"),
     ("btq::compress_ring_kernel<1, 8, true>(x)", "compress_pack_per_shard"),
     ("btq::compress_general_kernel<true>(x)", "compress_pack_per_shard"),
-    ("btq::decompress_kernel<8, 2, 4, false>(x)", "decompress_reduce"),
-    ("btq::decompress_kernel<8, 2, 4, true>(x)", "decompress_reduce_bf16"),
+    ("btq::decompress_kernel<8, 2, 4, 1, false>(x)", "decompress_reduce"),
+    ("btq::decompress_kernel<8, 2, 4, 2, true>(x)", "decompress_reduce_bf16"),
     ("btq::decompress_general_kernel<false>(x)", "decompress_reduce"),
     ("btq::decompress_general_kernel<true>(x)", "decompress_reduce_bf16"),
     ("btq::decompress_sets_reg_kernel<8, 1>(x)", "decompress_reduce_per_shard"),
@@ -67,8 +67,8 @@ def test_counter_summary(tmp_path):
             rows_f.append([d, "btq::compress_ring_kernel<1, 8, false>(x)", "FETCH_SIZE", v_f])
             rows_w.append([d, "btq::compress_ring_kernel<1, 8, false>(x)", "WRITE_SIZE", v_w])
     d += 1
-    rows_f.append([d, "btq::decompress_kernel<8, 2, 4, false>(x)", "FETCH_SIZE", 40.0])
-    rows_w.append([d, "btq::decompress_kernel<8, 2, 4, false>(x)", "WRITE_SIZE", 80.0])
+    rows_f.append([d, "btq::decompress_kernel<8, 2, 4, 1, false>(x)", "FETCH_SIZE", 40.0])
+    rows_w.append([d, "btq::decompress_kernel<8, 2, 4, 1, false>(x)", "WRITE_SIZE", 80.0])
     for _ in range(5):   # the copy probe: FETCH reads half the bytes, WRITE all of them
         d += 1
         rows_f.append([d, "void at::native::copyBuffer<x>(x)", "FETCH_SIZE", copy_kib / 2])
@@ -91,11 +91,11 @@ def test_counter_summary(tmp_path):
 def test_trace_and_sq_summaries(tmp_path):
     write_csv(str(tmp_path / "t" / "run_kernel_stats.csv"),
               ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"],
-              [["void btq::decompress_kernel<8, 2, 4, false>(x)", 10, 19000.4, 18000, 22000, 12.5],
+              [["void btq::decompress_kernel<8, 2, 4, 1, false>(x)", 10, 19000.4, 18000, 22000, 12.5],
                ["void at::native::elementwise(x)", 3, 5.0, 4, 6, 1.0]])
     out = bench.summarize_trace(str(tmp_path / "t"), "note")
     rows = [l for l in out.splitlines() if not l.startswith("#")]
-    assert rows == ["btq::decompress_kernel<8, 2, 4, false> | 10 | 19000 | 18000 | 22000 | 12.50"]
+    assert rows == ["btq::decompress_kernel<8, 2, 4, 1, false> | 10 | 19000 | 18000 | 22000 | 12.50"]
     hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
     vals = {"SQ_WAVE_CYCLES": 1000.0, "SQ_WAIT_INST_ANY": 590.0, "SQ_WAIT_ANY": 130.0,
             "SQ_ACTIVE_INST_VALU": 150.0, "SQ_ACTIVE_INST_LDS": 50.0,
