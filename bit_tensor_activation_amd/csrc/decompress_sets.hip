@@ -326,10 +326,408 @@ __global__ __launch_bounds__(256) void decompress_sets_general_kernel(
   }
 }
 
+// Lane-window kernel (P <= 8, H a multiple of 8). A wave-tile is 512
+// consecutive features, 8 per lane; a 256-thread block takes 4 adjacent
+// tiles of one block of token rows, and all blocks of a row block run on one
+// XCD. Unlike the two kernels above it sums with one fma per int4 term (see
+// below), so its output matches the sequential formula within fp32 rounding,
+// not bit for bit.
+//  0. Setup, once per wave, per shard p, from fmap, scale and zero_point:
+//     * the lane's int4 features of shard p take consecutive slots from the
+//       first one's slot jf, so their codes are the 32 bits at bit 4*jf of
+//       the row: one 8-byte load (moved back one dword where it would pass
+//       the row's end) and a 64-bit shift give one nibble per slot;
+//     * two byte selectors spread those nibbles over the lane's 8 feature
+//       positions (v_perm of the low and high nibbles of every byte: even
+//       positions into one register, odd into the other, BF16 positions 0);
+//     * the scales (0 at BF16 positions) and the per-feature constant
+//       -sum_p z*s that seeds the accumulator.
+//     The tile's BF16 values: shard p's BF16 features in the tile are a run
+//     [ilo_p, ihi_p) of its outlier block, read off fmap at the tile's ends.
+//     The runs of all shards, concatenated, are the tile's entries, entry
+//     e = r*64 + lane held in register r. Each entry's position in the tile
+//     comes from an LDS table that the lanes owning BF16 positions fill.
+//  1. Per token row: one code load per shard and kOR entry loads, a ring of
+//     kR rows in flight; per shard a shift, the nibble split and two perms,
+//     then 8 byte-to-float conversions and 8 fmas.
+//  2. The lane writes its 8 sums to a wave-private LDS row, the entry lanes
+//     add their BF16 values there (ds_add_f32), and each lane stores its 8
+//     values to y with two 16-byte stores. A tile with more entries than its
+//     kOR*64 registers adds the rest after the row loop, rereading its rows
+//     of y.
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+constexpr int kPsWaves = 4;
+constexpr int kPsTile = kWave * 8;   // features per wave-tile
+constexpr int kPsRing = 4;           // token rows in flight (2 for short batches)
+constexpr int kPsRingSmall = 2;
+constexpr int kPsSubMax = 2;
+// LDS y row: feature i of the tile at dword ps_pad(i) (4 dwords of padding
+// per 32, so the lanes' 32-byte runs spread over the banks), then one dummy
+// dword per lane for the adds of idle entry lanes.
+__device__ __forceinline__ uint32_t ps_pad(uint32_t i) { return i + ((i >> 5) << 2); }
+constexpr int kPsYDw = kPsTile + kPsTile / 8;   // ps_pad(512)
+constexpr int kPsRowDw = kPsYDw + kWave;
+
+template <int NP, int kOR, int kR, int kSub>
+__global__ __launch_bounds__(256) void decompress_sets_perm_kernel(
+    const uint8_t* __restrict__ packed, int pitch, const uint16_t* __restrict__ outl, int64_t T,
+    int H, int k, const float* __restrict__ scale, const uint8_t* __restrict__ zp,
+    const int32_t* __restrict__ fmap, float* __restrict__ y, int ntiles, int rows_per_wave,
+    int64_t nrowblk, int tbl_dwords) {
+  extern __shared__ __align__(16) char smem[];
+  int64_t rb, sub;
+  const int ntgrp = (ntiles + kPsWaves - 1) / kPsWaves;
+  if (!xcd_unit_block(blockIdx.x, ntgrp, nrowblk, &rb, &sub)) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = (int)sub * kPsWaves + wave;
+  if (c >= ntiles) return;   // no block barrier below
+  const int hs = c * kPsTile;
+  const int he = min(hs + kPsTile, H);
+  const int h0 = hs + 8 * lane;
+  const bool active = h0 < he;   // H % 8 == 0: a lane's window is whole or empty
+  const int hh = active ? h0 : hs;
+  const int64_t t0 = rb * rows_per_wave;
+  const int nrows = (int)min(T - t0, (int64_t)rows_per_wave);   // >= 1
+  float* const ybuf =
+      reinterpret_cast<float*>(smem) + (size_t)wave * (kSub * kPsRowDw + tbl_dwords);
+  uint16_t* const tbl = reinterpret_cast<uint16_t*>(ybuf + kSub * kPsRowDw);
+  const uint32_t ya = ps_pad((uint32_t)(8 * lane));   // the lane's 8 sums, 16-byte aligned
+
+  // One descriptor per tensor (the launcher keeps each below 2^30 bytes).
+  const rsrc_t rp = make_rsrc(packed, (uint32_t)(NP * T * (int64_t)pitch));
+  const rsrc_t ro = make_rsrc(outl, (uint32_t)(NP * T * (int64_t)k * 2));
+  const rsrc_t rf = make_rsrc(fmap, (uint32_t)(NP * (int64_t)H * 4));
+  const rsrc_t rs = make_rsrc(scale, (uint32_t)(NP * (int64_t)H * 4));
+  const rsrc_t rz = make_rsrc(zp, (uint32_t)(NP * (int64_t)H));
+
+  // (a) setup loads: the window's maps, scales and zero points of every
+  // shard, and every shard's map at the tile's end
+  v4u fa[NP], fb[NP], sa[NP], sb[NP];
+  v2u zz[NP];
+  uint32_t fend[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const uint32_t o = (uint32_t)(p * H + hh);
+    fa[p] = __builtin_amdgcn_raw_buffer_load_b128(rf, o * 4u, 0, 0);
+    fb[p] = __builtin_amdgcn_raw_buffer_load_b128(rf, o * 4u + 16u, 0, 0);
+    sa[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, o * 4u, 0, 0);
+    sb[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, o * 4u + 16u, 0, 0);
+    zz[p] = __builtin_amdgcn_raw_buffer_load_b64(rz, o, 0, 0);
+    fend[p] = __builtin_amdgcn_raw_buffer_load_b32(
+        rf, he < H ? (uint32_t)(p * H + he) * 4u : kOOB, 0, 0);
+  }
+
+  // (b) per-shard lane constants
+  uint32_t cofs[NP], csh[NP], selE[NP], selO[NP];
+  float sc[NP][8], bias[8];
+  int ilo[NP], E[NP + 1];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bias[e] = 0.0f;
+  E[0] = 0;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int f[8] = {(int)fa[p][0], (int)fa[p][1], (int)fa[p][2], (int)fa[p][3],
+                      (int)fb[p][0], (int)fb[p][1], (int)fb[p][2], (int)fb[p][3]};
+    int jf = 0x7FFFFFFF;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (f[e] >= 0) jf = min(jf, f[e]);
+    const bool any = active && jf != 0x7FFFFFFF;
+    uint32_t b = any ? ((uint32_t)jf >> 3) * 4u : 0u;
+    uint32_t sh = any ? 4u * ((uint32_t)jf & 7u) : 0u;
+    if (b + 8u > (uint32_t)pitch) {   // keep the 8 bytes inside the row (pitch >= 8)
+      b -= 4u;
+      sh += 32u;
+    }
+    cofs[p] = any ? b : kOOB;
+    csh[p] = sh;
+    uint32_t se = 0u, so = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // nibble n of the shifted code word: byte n/2 of the low nibbles
+      // (selector n/2) or of the high nibbles (selector 4 + n/2); 12 selects
+      // a zero byte
+      const int n = f[e] - jf;
+      const uint32_t sel = (any && f[e] >= 0) ? ((n & 1) ? 4u + (uint32_t)(n >> 1)
+                                                         : (uint32_t)(n >> 1))
+                                              : 12u;
+      if (e & 1)
+        so |= sel << (8 * (e >> 1));
+      else
+        se |= sel << (8 * (e >> 1));
+    }
+    selE[p] = se;
+    selO[p] = so;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float s = __uint_as_float(e < 4 ? sa[p][e] : sb[p][e - 4]);
+      sc[p][e] = (active && f[e] >= 0) ? s : 0.0f;
+      const float z = (float)((zz[p][e >> 2] >> (8 * (e & 3))) & 0xFFu);
+      bias[e] = fmaf(-z, sc[p][e], bias[e]);
+    }
+    // shard p's BF16 features below h: h - fmap[h] where h is int4, -1 - fmap[h]
+    // where it is BF16, k at h = H. Lane 0 holds h = hs.
+    const int f0 = __builtin_amdgcn_readfirstlane(f[0]);
+    const int fe = __builtin_amdgcn_readfirstlane((int)fend[p]);
+    ilo[p] = f0 >= 0 ? hs - f0 : -1 - f0;
+    const int ihi = he < H ? (fe >= 0 ? he - fe : -1 - fe) : k;
+    E[p + 1] = E[p] + (ihi - ilo[p]);
+    // entry of each BF16 position of the window: its tile position goes into
+    // the table
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (active && f[e] < 0) tbl[E[p] + (-1 - f[e]) - ilo[p]] = (uint16_t)ps_pad(8 * lane + e);
+  }
+  const int nE = E[NP];
+  wave_lds_sync();
+  // the entries in registers: outlier-block offset and LDS position (idle
+  // lanes load out of range and add to their dummy dword)
+  uint32_t eoff[kOR], epos[kOR];
+#pragma unroll
+  for (int r = 0; r < kOR; ++r) {
+    const int e = r * kWave + lane;
+    int p = 0;
+#pragma unroll
+    for (int q = 1; q < NP; ++q)
+      if (E[q] <= e) p = q;
+    const bool ok = e < nE;
+    eoff[r] = ok ? (uint32_t)(((int64_t)p * T * k + ilo[p] + (e - E[p])) * 2) : kOOB;
+    const uint32_t t = tbl[ok ? e : 0];
+    epos[r] = ok ? t : (uint32_t)(kPsYDw + lane);
+  }
+#pragma unroll
+  for (int p = 0; p < NP; ++p) settle(cofs[p]);
+
+  // (c) the ring
+  v2u cw[kR][NP];
+  uint32_t ev[kR][kOR];
+  auto load = [&](int q, int row) {
+    const bool ok = row < nrows;   // uniform
+    const int64_t rowg = t0 + min(row, nrows - 1);
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      cw[q][p] = __builtin_amdgcn_raw_buffer_load_b64(
+          rp, ok ? cofs[p] : kOOB, (uint32_t)(((int64_t)p * T + rowg) * pitch), kStream);
+#pragma unroll
+    for (int r = 0; r < kOR; ++r)
+      ev[q][r] = __builtin_amdgcn_raw_buffer_load_b16(ro, ok ? eoff[r] : kOOB,
+                                                      (uint32_t)(rowg * k * 2), 0);
+  };
+  issue_fence();
+#pragma unroll
+  for (int q = 0; q < kR; ++q) {
+    load(q, q);
+    issue_fence();
+  }
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    settle(csh[p]);
+    settle(selE[p]);
+    settle(selO[p]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) settle(sc[p][e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) settle(bias[e]);
+
+  // y stores: 16 bytes through a per-row descriptor with an immediate-zero
+  // scalar offset (the compiler then keeps the data registers of the wide
+  // store from being overwritten on the next instruction)
+  float* const yrows = y + t0 * H;
+  const uint32_t yoff = active ? (uint32_t)h0 * 4u : kOOB;
+  // (a row past the wave's last stores out of range, so the stores are not
+  // under a branch)
+  auto store_row = [&](int row, const v4f& lo, const v4f& hi) {
+    const bool ok = row < nrows;   // uniform
+    const rsrc_t rr = make_rsrc(yrows + (int64_t)min(row, nrows - 1) * H, (uint32_t)H * 4u);
+    const uint32_t o = ok ? yoff : kOOB;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, lo), rr, o, 0, kStream);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, hi), rr, o + 16u, 0, kStream);
+  };
+
+  int base = 0;
+  do {
+#pragma unroll
+    for (int sbk = 0; sbk < kR / kSub; ++sbk) {
+#pragma unroll
+      for (int r = 0; r < kSub; ++r) {
+        const int q = sbk * kSub + r;
+        float* bq = ybuf + r * kPsRowDw;
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = bias[e];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const uint64_t w = (uint64_t)cw[q][p][0] | ((uint64_t)cw[q][p][1] << 32);
+          const uint32_t code = (uint32_t)(w >> csh[p]);
+          const uint32_t lo = code & 0x0F0F0F0Fu;
+          const uint32_t hi = (code >> 4) & 0x0F0F0F0Fu;
+          uint32_t pe = __builtin_amdgcn_perm(hi, lo, selE[p]);
+          uint32_t po = __builtin_amdgcn_perm(hi, lo, selO[p]);
+          opaque(pe);
+          opaque(po);
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            acc[2 * bb] = fmaf((float)((pe >> (8 * bb)) & 0xFFu), sc[p][2 * bb], acc[2 * bb]);
+            acc[2 * bb + 1] =
+                fmaf((float)((po >> (8 * bb)) & 0xFFu), sc[p][2 * bb + 1], acc[2 * bb + 1]);
+          }
+        }
+        *reinterpret_cast<v4f*>(bq + ya) = v4f{acc[0], acc[1], acc[2], acc[3]};
+        *reinterpret_cast<v4f*>(bq + ya + 4) = v4f{acc[4], acc[5], acc[6], acc[7]};
+#pragma unroll
+        for (int rr = 0; rr < kOR; ++rr)
+          __hip_atomic_fetch_add(bq + epos[rr], bf16_to_f32(ev[q][rr]), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WAVEFRONT);
+      }
+      // refill the consumed slots with the rows kR ahead
+#pragma unroll
+      for (int r = 0; r < kSub; ++r) load(sbk * kSub + r, base + kR + sbk * kSub + r);
+      wave_lds_sync();
+      v4f vlo[kSub], vhi[kSub];
+#pragma unroll
+      for (int r = 0; r < kSub; ++r) {
+        const float* bq = ybuf + r * kPsRowDw;
+        vlo[r] = *reinterpret_cast<const v4f*>(bq + ya);
+        vhi[r] = *reinterpret_cast<const v4f*>(bq + ya + 4);
+      }
+#pragma unroll
+      for (int r = 0; r < kSub; ++r) {
+        store_row(base + sbk * kSub + r, vlo[r], vhi[r]);
+      }
+      wave_lds_sync();
+    }
+    base += kR;
+  } while (base < nrows);
+
+  if (nE > kOR * kWave) {   // uniform
+    // Entries past the registers: wait for the row loop's stores, then add
+    // them row by row to y through the LDS row.
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int row = 0; row < nrows; ++row) {
+      const rsrc_t rr = make_rsrc(yrows + (int64_t)row * H, (uint32_t)H * 4u);
+      const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(rr, yoff, 0, 0);
+      const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(rr, yoff + 16u, 0, 0);
+      *reinterpret_cast<v4u*>(ybuf + ya) = lo;
+      *reinterpret_cast<v4u*>(ybuf + ya + 4) = hi;
+      for (int e0 = kOR * kWave; e0 < nE; e0 += kWave) {
+        const int e = e0 + lane;
+        int p = 0;
+#pragma unroll
+        for (int q = 1; q < NP; ++q)
+          if (E[q] <= e) p = q;
+        const bool ok = e < nE;
+        const uint32_t off =
+            ok ? (uint32_t)((((int64_t)p * T + t0 + row) * k + ilo[p] + (e - E[p])) * 2) : kOOB;
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b16(ro, off, 0, 0);
+        const uint32_t t = tbl[ok ? e : 0];
+        const uint32_t pos = ok ? t : (uint32_t)(kPsYDw + lane);
+        __hip_atomic_fetch_add(ybuf + pos, bf16_to_f32(v), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WAVEFRONT);
+      }
+      wave_lds_sync();
+      const v4f vl = *reinterpret_cast<const v4f*>(ybuf + ya);
+      const v4f vh = *reinterpret_cast<const v4f*>(ybuf + ya + 4);
+      store_row(row, vl, vh);
+      wave_lds_sync();
+    }
+  }
+}
+
+template <int NP, int kOR, int kR, int kSub>
+static void launch_sets_perm(const uint8_t* packed, int64_t pitch, const uint16_t* outl,
+                             int64_t T, int64_t H, int64_t k, const float* scale,
+                             const uint8_t* zp, const int32_t* fmap, float* y, int64_t ntiles,
+                             int64_t rpw, int64_t nrowblk, int64_t tbl_dwords, hipStream_t s) {
+  const int64_t ntgrp = (ntiles + kPsWaves - 1) / kPsWaves;
+  const size_t lds = (size_t)kPsWaves * (kSub * kPsRowDw + tbl_dwords) * 4;
+  decompress_sets_perm_kernel<NP, kOR, kR, kSub>
+      <<<(unsigned)xcd_grid(ntgrp, nrowblk), 256, lds, s>>>(
+          packed, (int)pitch, outl, T, (int)H, (int)k, scale, zp, fmap, y, (int)ntiles, (int)rpw,
+          nrowblk, (int)tbl_dwords);
+}
+
+template <int NP>
+static void dispatch_sets_perm(bool wide, bool small, bool one_gen, const uint8_t* packed,
+                               int64_t pitch, const uint16_t* outl, int64_t T, int64_t H,
+                               int64_t k, const float* scale, const uint8_t* zp,
+                               const int32_t* fmap, float* y, int64_t ntiles, int64_t rpw,
+                               int64_t nrowblk, int64_t tbl_dwords, hipStream_t s) {
+#define BTQ_PS_ARGS \
+  packed, pitch, outl, T, H, k, scale, zp, fmap, y, ntiles, rpw, nrowblk, tbl_dwords, s
+  if (wide && small)
+    launch_sets_perm<NP, 4, kPsRingSmall, 1>(BTQ_PS_ARGS);
+  else if (wide && one_gen)
+    launch_sets_perm<NP, 4, kPsRing, 1>(BTQ_PS_ARGS);
+  else if (wide)
+    launch_sets_perm<NP, 4, kPsRing, 2>(BTQ_PS_ARGS);
+  else if (small)
+    launch_sets_perm<NP, 2, kPsRingSmall, 1>(BTQ_PS_ARGS);
+  else if (one_gen)
+    launch_sets_perm<NP, 2, kPsRing, 1>(BTQ_PS_ARGS);
+  else
+    launch_sets_perm<NP, 2, kPsRing, 2>(BTQ_PS_ARGS);
+#undef BTQ_PS_ARGS
+}
+
 hipError_t launch_decompress_sets(const uint8_t* packed, int64_t pitch, const uint16_t* outl,
                                   int64_t P, int64_t T, int64_t H, int64_t k, const float* scale,
                                   const uint8_t* zp, const int32_t* fmap, float* y,
                                   hipStream_t s) {
+  // Lane-window kernel: P <= 8, whole 8-feature windows. Every descriptor
+  // (message, outlier blocks, maps, scales) spans fewer than 2^30 bytes, and
+  // pitch and k below 2^25 keep kOOB plus a row offset from wrapping past
+  // 2^32. LDS: the y rows and a table of up to P*min(k, 512) 2-byte entry
+  // positions per wave.
+  {
+    const int64_t ntiles = (H + kPsTile - 1) / kPsTile;
+    const int64_t tbl_entries = P * (k < kPsTile ? k : kPsTile);
+    const int64_t tbl_dwords = ((tbl_entries + 1) / 2 + 3) / 4 * 4;
+    const int64_t lds_max = int64_t(kPsWaves) * (kPsSubMax * kPsRowDw + tbl_dwords) * 4;
+    int64_t rpw = (ntiles * T + 1023) / 1024;
+    const bool small = rpw < kPsRing;
+    const int64_t ring = small ? kPsRingSmall : kPsRing;
+    rpw = (rpw + ring - 1) / ring * ring;
+    if (rpw < ring) rpw = ring;
+    if (rpw > 64) rpw = 64;
+    const int64_t nrowblk = (T + rpw - 1) / rpw;
+    const int64_t ntgrp = (ntiles + kPsWaves - 1) / kPsWaves;
+    const int64_t lim = int64_t(1) << 30;
+    const bool perm = P >= 1 && P <= 8 && H % 8 == 0 && pitch % 4 == 0 && pitch >= 8 &&
+                      pitch < (int64_t(1) << 25) && k < (int64_t(1) << 25) &&
+                      P * T * (pitch + 8) < lim && P * T * k * 2 < lim && P * H * 4 < lim &&
+                      lds_max <= 65536 && (uintptr_t)packed % 4 == 0 &&
+                      (uintptr_t)fmap % 16 == 0 && (uintptr_t)scale % 16 == 0 &&
+                      (uintptr_t)zp % 8 == 0 && (uintptr_t)y % 16 == 0 &&
+                      xcd_grid(ntgrp, nrowblk) < (int64_t(1) << 31);
+    if (perm) {
+      // entry registers: 2 (128 entries per tile) while the tiles hold at
+      // most 64 on average, else 4; one sub-step row while the grid is one
+      // generation (1024 waves, one per SIMD), two beyond
+      const bool wide = P * k > int64_t(kWave) * ntiles;
+      const bool one_gen = ntiles * nrowblk <= 1024;
+#define BTQ_PS_CASE(n)                                                                          \
+  case n:                                                                                       \
+    dispatch_sets_perm<n>(wide, small, one_gen, packed, pitch, outl, T, H, k, scale, zp, fmap,  \
+                          y, ntiles, rpw, nrowblk, tbl_dwords, s);                              \
+    break;
+      switch (P) {
+        BTQ_PS_CASE(1)
+        BTQ_PS_CASE(2)
+        BTQ_PS_CASE(3)
+        BTQ_PS_CASE(4)
+        BTQ_PS_CASE(5)
+        BTQ_PS_CASE(6)
+        BTQ_PS_CASE(7)
+        BTQ_PS_CASE(8)
+      }
+#undef BTQ_PS_CASE
+      return hipGetLastError();
+    }
+  }
   // Register kernel: P <= 8, 4-feature lanes. Rows per wave: about 4096
   // waves, 4..32 rows. Every buffer offset (rows * pitch, rows * k * 2)
   // stays below 2^30.

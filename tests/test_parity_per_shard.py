@@ -2,9 +2,14 @@
 features): selection, sender and receiver against the oracle.
 
 Bar: parameters, per-shard sets, maps and sender table bitwise; packed rows
-(with padding) and BF16 blocks bitwise; y bitwise. The receiver evaluates
-every term as fl(q - z) * s and adds the terms in shard order from +0, the
-oracle's arithmetic step for step, so its output has one correct value.
+(with padding) and BF16 blocks bitwise; y within the receiver tolerance, with
+the features that are BF16 on every shard bit-exact. The lane-window receiver
+(P <= 8, H a multiple of 8) seeds each feature with -sum z*s and adds one fma
+per int4 term, then the BF16 values: within fp32 rounding of the oracle. The
+other two receivers evaluate every term as fl(q - z) * s and add the terms in
+shard order from +0, the oracle's arithmetic step for step, so their output
+is checked bit for bit. Every receiver output is also checked to repeat
+bitwise on a second call.
 """
 import numpy as np
 import pytest
@@ -57,11 +62,21 @@ def run_both(calib_xs, x, k, momentum, *, pitch=None):
     assert_bits_equal(ol.view(torch.int16), ol_o.view(np.int16), "outliers")
     y = B.btq_decompress_reduce_per_shard(pk, ol, H, sel_g["scale"], sel_g["zero_point"],
                                           sel_g["fmap"])
+    y2 = B.btq_decompress_reduce_per_shard(pk, ol, H, sel_g["scale"], sel_g["zero_point"],
+                                           sel_g["fmap"])
     y_o = O.decompress_reduce(pk_o, ol_o, sel_o["scale"], sel_o["zero_point"], sel_o["fmap"])
     torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32)), "y does not repeat"
     assert_y_close(y.cpu().numpy(), y_o, sel_o["scale"], bf16_everywhere(sel_o))
-    assert_bits_equal(y, y_o, "y")
+    if not lane_window_receiver(P, H, pk.shape[2]):
+        assert_bits_equal(y, y_o, "y")
     return sel_g, sel_o
+
+
+def lane_window_receiver(P, H, pitch):
+    """Whether btq_decompress_reduce_per_shard takes its lane-window kernel
+    (torch's allocations meet its alignment and size conditions here)."""
+    return P <= 8 and H % 8 == 0 and pitch % 4 == 0 and pitch >= 8
 
 
 def shard_local(P, T, H, seed, factor=30.0):
@@ -165,4 +180,20 @@ def test_full_size_7b_sampled_rows():
     assert_bits_equal(ol[:, ridx, :].view(torch.int16), ol_o.view(np.int16), "outliers")
     y_o = O.decompress_reduce(pk_o, ol_o, sel_o["scale"], sel_o["zero_point"], sel_o["fmap"])
     assert_y_close(y[ridx].cpu().numpy(), y_o, sel_o["scale"], bf16_everywhere(sel_o))
-    assert_bits_equal(y[ridx], y_o, "y (sampled rows)")
+    assert lane_window_receiver(P, H, pk.shape[2])
+
+
+def test_sets_concentrated_in_one_tile():
+    """Every shard keeps the same wide block of features, all inside the first
+    512-feature tile: that tile holds P*k BF16 values per row, more than the
+    receiver's registers, so it adds the rest after its row loop."""
+    for P, T, H, k in ((8, 21, 1024, 200), (4, 9, 2048, 300)):
+        say(f"case: per-shard sets concentrated P={P} T={T} H={H} k={k}")
+        def draw(T_, seed):
+            x = W.draw(P, T_, H, seed, cols=[], outlier_factor=1.0, device=DEV)
+            xb = x.view(torch.bfloat16).clone()
+            xb[:, :, 40:40 + k] *= 30.0
+            return xb.view(torch.int16)
+        calib = [draw(8, 4200 + b) for b in range(2)]
+        sel_g, sel_o = run_both(calib, draw(T, 4300), k, 0.9)
+        assert sel_o["idx"].tolist() == [list(range(40, 40 + k))] * P
