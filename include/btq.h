@@ -277,17 +277,24 @@ int btq_decompress_reduce_bf16(const uint8_t *packed, int64_t packed_pitch,
  *   cmap [P,H-k] from btq_select_outliers_per_shard; row (p,t) is coded with
  *   shard p's maps. Same packed and outliers layouts.
  *
- * btq_decompress_reduce_per_shard: y[t,h] = sum over p = 0,1,... (fp32, from
- *   +0) of fl(q - zero_point[p,h]) * scale[p,h], q being shard p's code of h
- *   at slot fmap[p,h], or of the BF16 value outliers[p,t,-1-fmap[p,h]].
- *   scale fp32 [P,H], zero_point u8 [P,H], fmap i32 [P,H] in; y fp32 [T,H]
- *   out. The maps are trusted, as in btq_decompress_reduce. Kernel choice:
- *   P <= 8, H a multiple of 4, a pitch that is a multiple of 4 and at least
- *   8, a 4-byte aligned packed and zero_point, 16-byte aligned fmap, scale
- *   and y (and packed/outliers tensors under 2^30 bytes) take the fast one;
- *   any P with H a multiple of 8 and the same alignments (zero_point 8)
- *   take a shard-loop one; everything else a per-element one. All three
- *   give the same bits.
+ * btq_decompress_reduce_per_shard: y[t,h] = sum over p of the dequantized
+ *   value of feature h on shard p: (q - zero_point[p,h]) * scale[p,h], q
+ *   being shard p's code of h at slot fmap[p,h], or the BF16 value
+ *   outliers[p,t,-1-fmap[p,h]]. scale fp32 [P,H], zero_point u8 [P,H], fmap
+ *   i32 [P,H] in; y fp32 [T,H] out. The maps are trusted, as in
+ *   btq_decompress_reduce. Kernel choice:
+ *   - P <= 8, H a multiple of 8, a pitch that is a multiple of 4 and at
+ *     least 8, a 4-byte aligned packed, 8-byte aligned zero_point, 16-byte
+ *     aligned fmap, scale and y, and message, outlier blocks and maps each
+ *     under 2^30 bytes: the lane-window kernel. It seeds each feature with
+ *     -sum_p z*s and adds one fma per int4 term, then the BF16 values, so
+ *     its output is within fp32 rounding of the sequential sum (features
+ *     BF16 on every shard are summed in shard order from +0, exactly);
+ *   - otherwise P <= 8 with H a multiple of 4 (same alignments, zero_point
+ *     4-byte aligned): a register kernel; any P with H a multiple of 8: a
+ *     shard-loop kernel; everything else a per-element kernel. These three
+ *     evaluate fl(q - z) * s and add the terms in shard order from +0, so
+ *     their outputs agree bit for bit.
  */
 int btq_select_outliers_per_shard(const float *run_min, const float *run_max,
                                   int64_t P, int64_t H, int64_t k,
