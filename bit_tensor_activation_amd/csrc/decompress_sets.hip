@@ -351,8 +351,9 @@ __global__ __launch_bounds__(256) void decompress_sets_general_kernel(
 //     kR rows in flight; per shard a shift, the nibble split and two perms,
 //     then 8 byte-to-float conversions and 8 fmas.
 //  2. The lane writes its 8 sums to a wave-private LDS row, the entry lanes
-//     add their BF16 values there (ds_add_f32), and each lane stores its 8
-//     values to y with two 16-byte stores. A tile with more entries than its
+//     add their BF16 values there (ds_add_f32), and the wave stores the row
+//     with two 16-byte stores per lane, each instruction 1 KB of consecutive
+//     features. A tile with more entries than its
 //     kOR*64 registers adds the rest after the row loop, rereading its rows
 //     of y.
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -537,15 +538,23 @@ __global__ __launch_bounds__(256) void decompress_sets_perm_kernel(
   // scalar offset (the compiler then keeps the data registers of the wide
   // store from being overwritten on the next instruction)
   float* const yrows = y + t0 * H;
-  const uint32_t yoff = active ? (uint32_t)h0 * 4u : kOOB;
+  // y is read back from the LDS row in 16-byte chunks: lane l stores chunk l
+  // of each half of the tile, so each store instruction writes 1 KB of
+  // whole cache lines
+  const int hA = hs + 4 * lane, hB = hs + kPsTile / 2 + 4 * lane;
+  const uint32_t yoA = hA < he ? (uint32_t)hA * 4u : kOOB;
+  const uint32_t yoB = hB < he ? (uint32_t)hB * 4u : kOOB;
+  const uint32_t yaA = ps_pad((uint32_t)(4 * lane));
+  const uint32_t yaB = ps_pad((uint32_t)(kPsTile / 2 + 4 * lane));
   // (a row past the wave's last stores out of range, so the stores are not
   // under a branch)
   auto store_row = [&](int row, const v4f& lo, const v4f& hi) {
     const bool ok = row < nrows;   // uniform
     const rsrc_t rr = make_rsrc(yrows + (int64_t)min(row, nrows - 1) * H, (uint32_t)H * 4u);
-    const uint32_t o = ok ? yoff : kOOB;
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, lo), rr, o, 0, kStream);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, hi), rr, o + 16u, 0, kStream);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, lo), rr, ok ? yoA : kOOB, 0,
+                                           kStream);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, hi), rr, ok ? yoB : kOOB, 0,
+                                           kStream);
   };
 
   int base = 0;
@@ -591,8 +600,8 @@ __global__ __launch_bounds__(256) void decompress_sets_perm_kernel(
 #pragma unroll
       for (int r = 0; r < kSub; ++r) {
         const float* bq = ybuf + r * kPsRowDw;
-        vlo[r] = *reinterpret_cast<const v4f*>(bq + ya);
-        vhi[r] = *reinterpret_cast<const v4f*>(bq + ya + 4);
+        vlo[r] = *reinterpret_cast<const v4f*>(bq + yaA);
+        vhi[r] = *reinterpret_cast<const v4f*>(bq + yaB);
       }
 #pragma unroll
       for (int r = 0; r < kSub; ++r) {
@@ -609,10 +618,10 @@ __global__ __launch_bounds__(256) void decompress_sets_perm_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     for (int row = 0; row < nrows; ++row) {
       const rsrc_t rr = make_rsrc(yrows + (int64_t)row * H, (uint32_t)H * 4u);
-      const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(rr, yoff, 0, 0);
-      const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(rr, yoff + 16u, 0, 0);
-      *reinterpret_cast<v4u*>(ybuf + ya) = lo;
-      *reinterpret_cast<v4u*>(ybuf + ya + 4) = hi;
+      const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(rr, yoA, 0, 0);
+      const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(rr, yoB, 0, 0);
+      *reinterpret_cast<v4u*>(ybuf + yaA) = lo;
+      *reinterpret_cast<v4u*>(ybuf + yaB) = hi;
       for (int e0 = kOR * kWave; e0 < nE; e0 += kWave) {
         const int e = e0 + lane;
         int p = 0;
@@ -629,8 +638,8 @@ __global__ __launch_bounds__(256) void decompress_sets_perm_kernel(
                                __HIP_MEMORY_SCOPE_WAVEFRONT);
       }
       wave_lds_sync();
-      const v4f vl = *reinterpret_cast<const v4f*>(ybuf + ya);
-      const v4f vh = *reinterpret_cast<const v4f*>(ybuf + ya + 4);
+      const v4f vl = *reinterpret_cast<const v4f*>(ybuf + yaA);
+      const v4f vh = *reinterpret_cast<const v4f*>(ybuf + yaB);
       store_row(row, vl, vh);
       wave_lds_sync();
     }
