@@ -350,12 +350,13 @@ __global__ __launch_bounds__(256) void decompress_sets_general_kernel(
 //  1. Per token row: one code load per shard and kOR entry loads, a ring of
 //     kR rows in flight; per shard a shift, the nibble split and two perms,
 //     then 8 byte-to-float conversions and 8 fmas.
-//  2. The lane writes its 8 sums to a wave-private LDS row, the entry lanes
-//     add their BF16 values there (ds_add_f32), and the wave stores the row
-//     with two 16-byte stores per lane, each instruction 1 KB of consecutive
-//     features. A tile with more entries than its
-//     kOR*64 registers adds the rest after the row loop, rereading its rows
-//     of y.
+//  2. The lane writes its 8 sums to one of two wave-private LDS rows, and the
+//     entry lanes add their BF16 values there (ds_add_f32). The previous row
+//     is read back from the other LDS row after this row's arithmetic, when
+//     its adds are done, and stored with two 16-byte stores per lane, each
+//     instruction 1 KB of consecutive features. A tile with more entries than
+//     its kOR*64 registers adds the rest after the row loop, rereading its
+//     rows of y.
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -363,7 +364,6 @@ constexpr int kPsWaves = 4;
 constexpr int kPsTile = kWave * 8;   // features per wave-tile
 constexpr int kPsRing = 4;           // token rows in flight (2 for short batches)
 constexpr int kPsRingSmall = 2;
-constexpr int kPsSubMax = 2;
 // LDS y row: feature i of the tile at dword ps_pad(i) (4 dwords of padding
 // per 32, so the lanes' 32-byte runs spread over the banks), then one dummy
 // dword per lane for the adds of idle entry lanes.
@@ -371,7 +371,7 @@ __device__ __forceinline__ uint32_t ps_pad(uint32_t i) { return i + ((i >> 5) <<
 constexpr int kPsYDw = kPsTile + kPsTile / 8;   // ps_pad(512)
 constexpr int kPsRowDw = kPsYDw + kWave;
 
-template <int NP, int kOR, int kR, int kSub>
+template <int NP, int kOR, int kR>
 __global__ __launch_bounds__(256) void decompress_sets_perm_kernel(
     const uint8_t* __restrict__ packed, int pitch, const uint16_t* __restrict__ outl, int64_t T,
     int H, int k, const float* __restrict__ scale, const uint8_t* __restrict__ zp,
@@ -393,8 +393,8 @@ __global__ __launch_bounds__(256) void decompress_sets_perm_kernel(
   const int64_t t0 = rb * rows_per_wave;
   const int nrows = (int)min(T - t0, (int64_t)rows_per_wave);   // >= 1
   float* const ybuf =
-      reinterpret_cast<float*>(smem) + (size_t)wave * (kSub * kPsRowDw + tbl_dwords);
-  uint16_t* const tbl = reinterpret_cast<uint16_t*>(ybuf + kSub * kPsRowDw);
+      reinterpret_cast<float*>(smem) + (size_t)wave * (2 * kPsRowDw + tbl_dwords);
+  uint16_t* const tbl = reinterpret_cast<uint16_t*>(ybuf + 2 * kPsRowDw);
   const uint32_t ya = ps_pad((uint32_t)(8 * lane));   // the lane's 8 sums, 16-byte aligned
 
   // One descriptor per tensor (the launcher keeps each below 2^30 bytes).
@@ -546,71 +546,73 @@ __global__ __launch_bounds__(256) void decompress_sets_perm_kernel(
   const uint32_t yoB = hB < he ? (uint32_t)hB * 4u : kOOB;
   const uint32_t yaA = ps_pad((uint32_t)(4 * lane));
   const uint32_t yaB = ps_pad((uint32_t)(kPsTile / 2 + 4 * lane));
-  // (a row past the wave's last stores out of range, so the stores are not
+  // (a row outside the wave's stores out of range, so the stores are not
   // under a branch)
   auto store_row = [&](int row, const v4f& lo, const v4f& hi) {
-    const bool ok = row < nrows;   // uniform
-    const rsrc_t rr = make_rsrc(yrows + (int64_t)min(row, nrows - 1) * H, (uint32_t)H * 4u);
+    const bool ok = row >= 0 && row < nrows;   // uniform
+    const rsrc_t rr =
+        make_rsrc(yrows + (int64_t)min(max(row, 0), nrows - 1) * H, (uint32_t)H * 4u);
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, lo), rr, ok ? yoA : kOOB, 0,
                                            kStream);
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, hi), rr, ok ? yoB : kOOB, 0,
                                            kStream);
   };
 
+  // Rows alternate between two LDS rows. A row's sums and BF16 adds are
+  // issued to one; the previous row is read back from the other only after
+  // this row's arithmetic, by when its adds are done, and stored.
   int base = 0;
   do {
 #pragma unroll
-    for (int sbk = 0; sbk < kR / kSub; ++sbk) {
+    for (int q = 0; q < kR; ++q) {
+      const int row = base + q;   // base is a multiple of kR, so row & 1 == q & 1
+      float* const bcur = ybuf + (q & 1) * kPsRowDw;
+      const float* const bprev = ybuf + ((q + 1) & 1) * kPsRowDw;
+      float acc[8];
 #pragma unroll
-      for (int r = 0; r < kSub; ++r) {
-        const int q = sbk * kSub + r;
-        float* bq = ybuf + r * kPsRowDw;
-        float acc[8];
+      for (int e = 0; e < 8; ++e) acc[e] = bias[e];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = bias[e];
+      for (int p = 0; p < NP; ++p) {
+        const uint64_t w = (uint64_t)cw[q][p][0] | ((uint64_t)cw[q][p][1] << 32);
+        const uint32_t code = (uint32_t)(w >> csh[p]);
+        const uint32_t lo = code & 0x0F0F0F0Fu;
+        const uint32_t hi = (code >> 4) & 0x0F0F0F0Fu;
+        uint32_t pe = __builtin_amdgcn_perm(hi, lo, selE[p]);
+        uint32_t po = __builtin_amdgcn_perm(hi, lo, selO[p]);
+        opaque(pe);
+        opaque(po);
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          const uint64_t w = (uint64_t)cw[q][p][0] | ((uint64_t)cw[q][p][1] << 32);
-          const uint32_t code = (uint32_t)(w >> csh[p]);
-          const uint32_t lo = code & 0x0F0F0F0Fu;
-          const uint32_t hi = (code >> 4) & 0x0F0F0F0Fu;
-          uint32_t pe = __builtin_amdgcn_perm(hi, lo, selE[p]);
-          uint32_t po = __builtin_amdgcn_perm(hi, lo, selO[p]);
-          opaque(pe);
-          opaque(po);
-#pragma unroll
-          for (int bb = 0; bb < 4; ++bb) {
-            acc[2 * bb] = fmaf((float)((pe >> (8 * bb)) & 0xFFu), sc[p][2 * bb], acc[2 * bb]);
-            acc[2 * bb + 1] =
-                fmaf((float)((po >> (8 * bb)) & 0xFFu), sc[p][2 * bb + 1], acc[2 * bb + 1]);
-          }
+        for (int bb = 0; bb < 4; ++bb) {
+          acc[2 * bb] = fmaf((float)((pe >> (8 * bb)) & 0xFFu), sc[p][2 * bb], acc[2 * bb]);
+          acc[2 * bb + 1] =
+              fmaf((float)((po >> (8 * bb)) & 0xFFu), sc[p][2 * bb + 1], acc[2 * bb + 1]);
         }
-        *reinterpret_cast<v4f*>(bq + ya) = v4f{acc[0], acc[1], acc[2], acc[3]};
-        *reinterpret_cast<v4f*>(bq + ya + 4) = v4f{acc[4], acc[5], acc[6], acc[7]};
-#pragma unroll
-        for (int rr = 0; rr < kOR; ++rr)
-          __hip_atomic_fetch_add(bq + epos[rr], bf16_to_f32(ev[q][rr]), __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_WAVEFRONT);
-      }
-      // refill the consumed slots with the rows kR ahead
-#pragma unroll
-      for (int r = 0; r < kSub; ++r) load(sbk * kSub + r, base + kR + sbk * kSub + r);
-      wave_lds_sync();
-      v4f vlo[kSub], vhi[kSub];
-#pragma unroll
-      for (int r = 0; r < kSub; ++r) {
-        const float* bq = ybuf + r * kPsRowDw;
-        vlo[r] = *reinterpret_cast<const v4f*>(bq + yaA);
-        vhi[r] = *reinterpret_cast<const v4f*>(bq + yaB);
-      }
-#pragma unroll
-      for (int r = 0; r < kSub; ++r) {
-        store_row(base + sbk * kSub + r, vlo[r], vhi[r]);
       }
       wave_lds_sync();
+      const v4f plo = *reinterpret_cast<const v4f*>(bprev + yaA);
+      const v4f phi = *reinterpret_cast<const v4f*>(bprev + yaB);
+      *reinterpret_cast<v4f*>(bcur + ya) = v4f{acc[0], acc[1], acc[2], acc[3]};
+      *reinterpret_cast<v4f*>(bcur + ya + 4) = v4f{acc[4], acc[5], acc[6], acc[7]};
+      // other lanes add to these sums: the writes go first (LDS executes a
+      // wave's operations in order; the fence keeps the compiler's order)
+      wave_lds_sync();
+#pragma unroll
+      for (int rr = 0; rr < kOR; ++rr)
+        __hip_atomic_fetch_add(bcur + epos[rr], bf16_to_f32(ev[q][rr]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WAVEFRONT);
+      // refill the consumed slot (codes and BF16 values) with the row kR ahead
+      load(q, row + kR);
+      store_row(row - 1, plo, phi);   // row -1 stores out of range
     }
     base += kR;
   } while (base < nrows);
+  {   // the loop's last row (base - 1; out of range if past nrows - 1)
+    wave_lds_sync();
+    const float* const bl = ybuf + ((kR - 1) & 1) * kPsRowDw;
+    const v4f llo = *reinterpret_cast<const v4f*>(bl + yaA);
+    const v4f lhi = *reinterpret_cast<const v4f*>(bl + yaB);
+    store_row(base - 1, llo, lhi);
+  }
 
   if (nE > kOR * kWave) {   // uniform
     // Entries past the registers: wait for the row loop's stores, then add
@@ -622,6 +624,7 @@ __global__ __launch_bounds__(256) void decompress_sets_perm_kernel(
       const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(rr, yoB, 0, 0);
       *reinterpret_cast<v4u*>(ybuf + yaA) = lo;
       *reinterpret_cast<v4u*>(ybuf + yaB) = hi;
+      wave_lds_sync();
       for (int e0 = kOR * kWave; e0 < nE; e0 += kWave) {
         const int e = e0 + lane;
         int p = 0;
@@ -646,39 +649,35 @@ __global__ __launch_bounds__(256) void decompress_sets_perm_kernel(
   }
 }
 
-template <int NP, int kOR, int kR, int kSub>
+template <int NP, int kOR, int kR>
 static void launch_sets_perm(const uint8_t* packed, int64_t pitch, const uint16_t* outl,
                              int64_t T, int64_t H, int64_t k, const float* scale,
                              const uint8_t* zp, const int32_t* fmap, float* y, int64_t ntiles,
                              int64_t rpw, int64_t nrowblk, int64_t tbl_dwords, hipStream_t s) {
   const int64_t ntgrp = (ntiles + kPsWaves - 1) / kPsWaves;
-  const size_t lds = (size_t)kPsWaves * (kSub * kPsRowDw + tbl_dwords) * 4;
-  decompress_sets_perm_kernel<NP, kOR, kR, kSub>
+  const size_t lds = (size_t)kPsWaves * (2 * kPsRowDw + tbl_dwords) * 4;
+  decompress_sets_perm_kernel<NP, kOR, kR>
       <<<(unsigned)xcd_grid(ntgrp, nrowblk), 256, lds, s>>>(
           packed, (int)pitch, outl, T, (int)H, (int)k, scale, zp, fmap, y, (int)ntiles, (int)rpw,
           nrowblk, (int)tbl_dwords);
 }
 
 template <int NP>
-static void dispatch_sets_perm(bool wide, bool small, bool one_gen, const uint8_t* packed,
-                               int64_t pitch, const uint16_t* outl, int64_t T, int64_t H,
-                               int64_t k, const float* scale, const uint8_t* zp,
-                               const int32_t* fmap, float* y, int64_t ntiles, int64_t rpw,
-                               int64_t nrowblk, int64_t tbl_dwords, hipStream_t s) {
+static void dispatch_sets_perm(bool wide, bool small, const uint8_t* packed, int64_t pitch,
+                               const uint16_t* outl, int64_t T, int64_t H, int64_t k,
+                               const float* scale, const uint8_t* zp, const int32_t* fmap,
+                               float* y, int64_t ntiles, int64_t rpw, int64_t nrowblk,
+                               int64_t tbl_dwords, hipStream_t s) {
 #define BTQ_PS_ARGS \
   packed, pitch, outl, T, H, k, scale, zp, fmap, y, ntiles, rpw, nrowblk, tbl_dwords, s
   if (wide && small)
-    launch_sets_perm<NP, 4, kPsRingSmall, 1>(BTQ_PS_ARGS);
-  else if (wide && one_gen)
-    launch_sets_perm<NP, 4, kPsRing, 1>(BTQ_PS_ARGS);
+    launch_sets_perm<NP, 4, kPsRingSmall>(BTQ_PS_ARGS);
   else if (wide)
-    launch_sets_perm<NP, 4, kPsRing, 2>(BTQ_PS_ARGS);
+    launch_sets_perm<NP, 4, kPsRing>(BTQ_PS_ARGS);
   else if (small)
-    launch_sets_perm<NP, 2, kPsRingSmall, 1>(BTQ_PS_ARGS);
-  else if (one_gen)
-    launch_sets_perm<NP, 2, kPsRing, 1>(BTQ_PS_ARGS);
+    launch_sets_perm<NP, 2, kPsRingSmall>(BTQ_PS_ARGS);
   else
-    launch_sets_perm<NP, 2, kPsRing, 2>(BTQ_PS_ARGS);
+    launch_sets_perm<NP, 2, kPsRing>(BTQ_PS_ARGS);
 #undef BTQ_PS_ARGS
 }
 
@@ -695,7 +694,7 @@ hipError_t launch_decompress_sets(const uint8_t* packed, int64_t pitch, const ui
     const int64_t ntiles = (H + kPsTile - 1) / kPsTile;
     const int64_t tbl_entries = P * (k < kPsTile ? k : kPsTile);
     const int64_t tbl_dwords = ((tbl_entries + 1) / 2 + 3) / 4 * 4;
-    const int64_t lds_max = int64_t(kPsWaves) * (kPsSubMax * kPsRowDw + tbl_dwords) * 4;
+    const int64_t lds_max = int64_t(kPsWaves) * (2 * kPsRowDw + tbl_dwords) * 4;
     int64_t rpw = (ntiles * T + 1023) / 1024;
     const bool small = rpw < kPsRing;
     const int64_t ring = small ? kPsRingSmall : kPsRing;
@@ -714,14 +713,12 @@ hipError_t launch_decompress_sets(const uint8_t* packed, int64_t pitch, const ui
                       xcd_grid(ntgrp, nrowblk) < (int64_t(1) << 31);
     if (perm) {
       // entry registers: 2 (128 entries per tile) while the tiles hold at
-      // most 64 on average, else 4; one sub-step row while the grid is one
-      // generation (1024 waves, one per SIMD), two beyond
+      // most 64 on average, else 4
       const bool wide = P * k > int64_t(kWave) * ntiles;
-      const bool one_gen = ntiles * nrowblk <= 1024;
 #define BTQ_PS_CASE(n)                                                                          \
   case n:                                                                                       \
-    dispatch_sets_perm<n>(wide, small, one_gen, packed, pitch, outl, T, H, k, scale, zp, fmap,  \
-                          y, ntiles, rpw, nrowblk, tbl_dwords, s);                              \
+    dispatch_sets_perm<n>(wide, small, packed, pitch, outl, T, H, k, scale, zp, fmap, y,        \
+                          ntiles, rpw, nrowblk, tbl_dwords, s);                                 \
     break;
       switch (P) {
         BTQ_PS_CASE(1)
