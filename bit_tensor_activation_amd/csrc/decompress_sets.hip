@@ -685,7 +685,9 @@ hipError_t launch_decompress_sets(const uint8_t* packed, int64_t pitch, const ui
                                   int64_t P, int64_t T, int64_t H, int64_t k, const float* scale,
                                   const uint8_t* zp, const int32_t* fmap, float* y,
                                   hipStream_t s) {
-  // Lane-window kernel: P <= 8, whole 8-feature windows. Every descriptor
+  // Lane-window kernel: P <= 8, whole 8-feature windows, more than 2 token
+  // rows (for 1 or 2 rows its two dependent setup round trips make it slower
+  // than the register kernel: decode at T=1 10.8 against 7.4 us). Every descriptor
   // (message, outlier blocks, maps, scales) spans fewer than 2^30 bytes, and
   // pitch and k below 2^25 keep kOOB plus a row offset from wrapping past
   // 2^32. LDS: the y rows and a table of up to P*min(k, 512) 2-byte entry
@@ -704,7 +706,7 @@ hipError_t launch_decompress_sets(const uint8_t* packed, int64_t pitch, const ui
     const int64_t nrowblk = (T + rpw - 1) / rpw;
     const int64_t ntgrp = (ntiles + kPsWaves - 1) / kPsWaves;
     const int64_t lim = int64_t(1) << 30;
-    const bool perm = P >= 1 && P <= 8 && H % 8 == 0 && pitch % 4 == 0 && pitch >= 8 &&
+    const bool perm = T > 2 && P >= 1 && P <= 8 && H % 8 == 0 && pitch % 4 == 0 && pitch >= 8 &&
                       pitch < (int64_t(1) << 25) && k < (int64_t(1) << 25) &&
                       P * T * (pitch + 8) < lim && P * T * k * 2 < lim && P * H * 4 < lim &&
                       lds_max <= 65536 && (uintptr_t)packed % 4 == 0 &&

@@ -283,8 +283,8 @@ int btq_decompress_reduce_bf16(const uint8_t *packed, int64_t packed_pitch,
  *   outliers[p,t,-1-fmap[p,h]]. scale fp32 [P,H], zero_point u8 [P,H], fmap
  *   i32 [P,H] in; y fp32 [T,H] out. The maps are trusted, as in
  *   btq_decompress_reduce. Kernel choice:
- *   - P <= 8, H a multiple of 8, a pitch that is a multiple of 4 and at
- *     least 8, a 4-byte aligned packed, 8-byte aligned zero_point, 16-byte
+ *   - T > 2, P <= 8, H a multiple of 8, a pitch that is a multiple of 4 and
+ *     at least 8, a 4-byte aligned packed, 8-byte aligned zero_point, 16-byte
  *     aligned fmap, scale and y, and message, outlier blocks and maps each
  *     under 2^30 bytes: the lane-window kernel. It seeds each feature with
  *     -sum_p z*s and adds one fma per int4 term, then the BF16 values, so

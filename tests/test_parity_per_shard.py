@@ -68,15 +68,15 @@ def run_both(calib_xs, x, k, momentum, *, pitch=None):
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int32), y2.view(torch.int32)), "y does not repeat"
     assert_y_close(y.cpu().numpy(), y_o, sel_o["scale"], bf16_everywhere(sel_o))
-    if not lane_window_receiver(P, H, pk.shape[2]):
+    if not lane_window_receiver(P, T, H, pk.shape[2]):
         assert_bits_equal(y, y_o, "y")
     return sel_g, sel_o
 
 
-def lane_window_receiver(P, H, pitch):
+def lane_window_receiver(P, T, H, pitch):
     """Whether btq_decompress_reduce_per_shard takes its lane-window kernel
     (torch's allocations meet its alignment and size conditions here)."""
-    return P <= 8 and H % 8 == 0 and pitch % 4 == 0 and pitch >= 8
+    return T > 2 and P <= 8 and H % 8 == 0 and pitch % 4 == 0 and pitch >= 8
 
 
 def shard_local(P, T, H, seed, factor=30.0):
@@ -112,6 +112,8 @@ CASES = [
     (3, 5, 16, 14, None, "k=H-2: two int4 slots"),
     (2, 4, 4, 1, None, "H=4"),
     (16, 3, 64, 2, None, "P=16: shard-loop kernel"),
+    (8, 1, 8192, 64, None, "T=1 (decode): register kernel"),
+    (4, 2, 1024, 16, None, "T=2: register kernel"),
 ]
 
 
@@ -180,7 +182,7 @@ def test_full_size_7b_sampled_rows():
     assert_bits_equal(ol[:, ridx, :].view(torch.int16), ol_o.view(np.int16), "outliers")
     y_o = O.decompress_reduce(pk_o, ol_o, sel_o["scale"], sel_o["zero_point"], sel_o["fmap"])
     assert_y_close(y[ridx].cpu().numpy(), y_o, sel_o["scale"], bf16_everywhere(sel_o))
-    assert lane_window_receiver(P, H, pk.shape[2])
+    assert lane_window_receiver(P, T, H, pk.shape[2])
 
 
 def test_sets_concentrated_in_one_tile():
