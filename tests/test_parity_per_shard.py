@@ -149,16 +149,21 @@ def test_signed_zero_ranges_rank_by_feature():
     assert o["idx"].tolist() == [list(range(k))] * P
 
 
-def test_full_size_7b_sampled_rows():
-    """7b_prefill shape with its calibration batches (4 of them), through the
-    per-shard calls; sampled rows against the oracle."""
-    w = W.WORKLOADS["7b_prefill"]
-    P, H, k, T = w.P, w.H, w.k, w.T[0]
-    say(f"case: per-shard sets at full size P={P} T={T} H={H} k={k}")
+@pytest.mark.parametrize("name,k,T,nb", [("7b_prefill", 64, 2048, 4), ("stress", 256, 16384, 2),
+                                         ("large_prefill", 128, 8192, 2)])
+def test_full_size_sampled_rows(name, k, T, nb):
+    """A workload's full shape with nb of its calibration batches, through the
+    per-shard calls; sampled rows against the oracle. At stress size the
+    tiles hold up to P*k/16 BF16 values per row on average, so the receiver
+    runs with four entry registers and 64-row waves, and tiles beyond four
+    registers take the post-loop pass."""
+    w = W.WORKLOADS[name]
+    P, H = w.P, w.H
+    say(f"case: per-shard sets at full size {name} P={P} T={T} H={H} k={k}")
     rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
     rmax = torch.empty_like(rmin)
     mn = mx = None
-    for b in range(4):
+    for b in range(nb):
         xb = W.batch(w, W.PHASE_CALIB, b, device=DEV)
         B.btq_calib_update(xb, rmin, rmax, w.momentum, first_batch=(b == 0))
         mn, mx = oracle_calib(u16(xb), mn, mx, w.momentum, first=(b == 0))
@@ -166,7 +171,7 @@ def test_full_size_7b_sampled_rows():
     sel_o = O.select_outliers_per_shard(mn, mx, k)
     torch.cuda.synchronize()
     assert_per_shard_selection_equal(sel_g, sel_o)
-    x = W.batch(w, W.PHASE_INFER, 0, device=DEV)
+    x = W.batch(w, W.PHASE_INFER, 0, T=T, device=DEV)
     pk, ol = B.btq_compress_pack_per_shard(x, k, sel_g["enc"], sel_g["outlier_idx"],
                                            sel_g["cmap"])
     y = B.btq_decompress_reduce_per_shard(pk, ol, H, sel_g["scale"], sel_g["zero_point"],
