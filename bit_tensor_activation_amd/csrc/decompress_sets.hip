@@ -596,10 +596,13 @@ __global__ __launch_bounds__(256) void decompress_sets_perm_kernel(
       // other lanes add to these sums: the writes go first (LDS executes a
       // wave's operations in order; the fence keeps the compiler's order)
       wave_lds_sync();
+      // LDS float adds are costly per instruction and per lane: registers
+      // past the tile's entries are skipped, idle lanes masked off
 #pragma unroll
       for (int rr = 0; rr < kOR; ++rr)
-        __hip_atomic_fetch_add(bcur + epos[rr], bf16_to_f32(ev[q][rr]), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WAVEFRONT);
+        if (rr * kWave < nE && rr * kWave + lane < nE)
+          __hip_atomic_fetch_add(bcur + epos[rr], bf16_to_f32(ev[q][rr]), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WAVEFRONT);
       // refill the consumed slot (codes and BF16 values) with the row kR ahead
       load(q, row + kR);
       store_row(row - 1, plo, phi);   // row -1 stores out of range
@@ -636,9 +639,9 @@ __global__ __launch_bounds__(256) void decompress_sets_perm_kernel(
             ok ? (uint32_t)((((int64_t)p * T + t0 + row) * k + ilo[p] + (e - E[p])) * 2) : kOOB;
         const uint32_t v = __builtin_amdgcn_raw_buffer_load_b16(ro, off, 0, 0);
         const uint32_t t = tbl[ok ? e : 0];
-        const uint32_t pos = ok ? t : (uint32_t)(kPsYDw + lane);
-        __hip_atomic_fetch_add(ybuf + pos, bf16_to_f32(v), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WAVEFRONT);
+        if (ok)
+          __hip_atomic_fetch_add(ybuf + t, bf16_to_f32(v), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WAVEFRONT);
       }
       wave_lds_sync();
       const v4f vl = *reinterpret_cast<const v4f*>(ybuf + yaA);
