@@ -9,7 +9,7 @@ keeps no state between calls (GPU).
     inputs copied in between replays and eager work between them, match
     the eager calls on every replay (the kernels clear nothing with memset:
     every output byte is written by a kernel, so the graph holds only
-    kernel nodes).
+    kernel nodes); the same for the per-shard sender and receiver.
 """
 import pytest
 import torch
@@ -118,4 +118,43 @@ def test_graph_replays_match_eager_calls():
         for a, b in zip(got, [pk, ol, y, y16]):
             assert same_bytes(a, b), f"replay {rep}"
         pk.zero_()              # the next replay must write every byte again
+        y.zero_()
+
+
+def test_graph_replays_per_shard_sets():
+    say("case: graph capture of the per-shard sender and receiver, 3 replays")
+    calib = [draw(7700 + b) for b in range(2)]
+    rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
+    rmax = torch.empty_like(rmin)
+    for b, xb in enumerate(calib):
+        B.btq_calib_update(xb, rmin, rmax, 0.9, b == 0)
+    sel = B.btq_select_outliers_per_shard(rmin, rmax, K)
+    pitch = B.btq_packed_pitch(H, K)
+    x_static = torch.empty((P, T, H), dtype=torch.int16, device=DEV)
+    pk = torch.empty((P, T, pitch), dtype=torch.uint8, device=DEV)
+    ol = torch.empty((P, T, K), dtype=torch.int16, device=DEV)
+    y = torch.empty((T, H), dtype=torch.float32, device=DEV)
+
+    def step():
+        B.btq_compress_pack_per_shard(x_static, K, sel["enc"], sel["outlier_idx"], sel["cmap"],
+                                      packed=pk, outliers=ol)
+        B.btq_decompress_reduce_per_shard(pk, ol, H, sel["scale"], sel["zero_point"],
+                                          sel["fmap"], y=y)
+
+    x_static.copy_(draw(7800))
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        x_static.copy_(draw(7900 + rep))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [pk.clone(), ol.clone(), y.clone()]
+        step()
+        torch.cuda.synchronize()
+        for a, b in zip(got, [pk, ol, y]):
+            assert same_bytes(a, b), f"replay {rep}"
+        pk.zero_()
         y.zero_()
