@@ -351,7 +351,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the P shards of one tensor-parallel group share one GPU's HBM). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
