@@ -351,7 +351,9 @@ __global__ __launch_bounds__(256) void decompress_sets_general_kernel(
 //     kR rows in flight; per shard a shift, the nibble split and two perms,
 //     then 8 byte-to-float conversions and 8 fmas.
 //  2. The lane writes its 8 sums to one of two wave-private LDS rows, and the
-//     entry lanes add their BF16 values there (ds_add_f32). The previous row
+//     entry lanes add their BF16 values there (ds_add_f32, which costs per
+//     instruction and per active lane: registers past the tile's entries
+//     are skipped and idle lanes masked off). The previous row
 //     is read back from the other LDS row after this row's arithmetic, when
 //     its adds are done, and stored with two 16-byte stores per lane, each
 //     instruction 1 KB of consecutive features. A tile with more entries than
@@ -365,11 +367,9 @@ constexpr int kPsTile = kWave * 8;   // features per wave-tile
 constexpr int kPsRing = 4;           // token rows in flight (2 for short batches)
 constexpr int kPsRingSmall = 2;
 // LDS y row: feature i of the tile at dword ps_pad(i) (4 dwords of padding
-// per 32, so the lanes' 32-byte runs spread over the banks), then one dummy
-// dword per lane for the adds of idle entry lanes.
+// per 32, so the lanes' 32-byte runs spread over the banks).
 __device__ __forceinline__ uint32_t ps_pad(uint32_t i) { return i + ((i >> 5) << 2); }
-constexpr int kPsYDw = kPsTile + kPsTile / 8;   // ps_pad(512)
-constexpr int kPsRowDw = kPsYDw + kWave;
+constexpr int kPsRowDw = kPsTile + kPsTile / 8;   // ps_pad(512)
 
 template <int NP, int kOR, int kR>
 __global__ __launch_bounds__(256) void decompress_sets_perm_kernel(
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(256) void decompress_sets_perm_kernel(
   const int nE = E[NP];
   wave_lds_sync();
   // the entries in registers: outlier-block offset and LDS position (idle
-  // lanes load out of range and add to their dummy dword)
+  // lanes load out of range and add nothing)
   uint32_t eoff[kOR], epos[kOR];
 #pragma unroll
   for (int r = 0; r < kOR; ++r) {
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(256) void decompress_sets_perm_kernel(
     const bool ok = e < nE;
     eoff[r] = ok ? (uint32_t)(((int64_t)p * T * k + ilo[p] + (e - E[p])) * 2) : kOOB;
     const uint32_t t = tbl[ok ? e : 0];
-    epos[r] = ok ? t : (uint32_t)(kPsYDw + lane);
+    epos[r] = ok ? t : 0u;
   }
 #pragma unroll
   for (int p = 0; p < NP; ++p) settle(cofs[p]);
