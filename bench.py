@@ -13,6 +13,8 @@ timed steps, launched back to back with nothing between them. Inputs are
 resident in HBM before timing starts. R copies of the batch and of every
 output rotate, so that each step streams from HBM and not from the 256 MB
 last-level cache. The receiver reads the message written two steps earlier.
+The same steps captured in a HIP graph (one rotation, replayed) are timed too
+and reported under "timing" (graph_ms_per_step); value stays the eager rate.
 
 Roofline: the dominant kernel (compress) is HBM-bound. achieved = its
 algorithmic bytes per launch / its mean duration. The durations come from
@@ -465,6 +467,32 @@ def main() -> int:
     deco_mean = sum(deco_ms) / len(deco_ms)
     med = lambda v: sorted(v)[len(v) // 2]
 
+    # Timed region 3 (reported beside value, not value): G steps of the
+    # rotation (all R, at most 512, which still spans well past the last-level
+    # cache) captured in a HIP graph on a side stream (default priority) and
+    # replayed, as a caller that captures its steps would run them. The
+    # kernels clear nothing with memset, so the graph holds kernel nodes only.
+    G = min(R, 512)
+    gs = torch.cuda.Stream(device=dev)
+    g_comp = [a[:-1] + (gs.cuda_stream,) for a in comp_args[:G]]
+    g_deco = [a[:-1] + (gs.cuda_stream,) for a in deco_args[:G]]
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=gs):
+        for r in range(G):
+            st |= compress(*g_comp[r])
+            st |= decompress(*g_deco[r])
+    _lib.check(st, "graph capture")
+    graph.replay()
+    torch.cuda.synchronize()
+    n_rep = max(1, args.steps // G)
+    t2 = time.perf_counter()
+    for _ in range(n_rep):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t2) / (n_rep * G) * 1e3
+    del graph
+
     # The bf16-output receiver, timed on its own after the steps (it is not
     # part of a step: the step's receiver writes fp32).
     y16 = [torch.empty((T, H), dtype=torch.int16, device=dev) for _ in range(2)]
@@ -584,7 +612,11 @@ def main() -> int:
         "timing": {"value": f"{args.steps} steps with no instrumentation between launches",
                    "kernels": f"the same {args.steps} steps again with HIP events around every "
                               "launch on the launch stream (fence-free events)",
-                   "ms_per_step_instrumented": round(wall_ev / args.steps * 1e3, 5)},
+                   "ms_per_step_instrumented": round(wall_ev / args.steps * 1e3, 5),
+                   "graph": f"{min(R, 512)} steps of the rotation captured in a HIP graph, "
+                            f"replayed {max(1, args.steps // min(R, 512))} times",
+                   "graph_ms_per_step": round(graph_ms, 5),
+                   "graph_GBps": round(bf16_bytes / (graph_ms * 1e-3) / 1e9, 2)},
         "offline": {"calib_batches": w.calib_batches, "calib_ms_total": round(calib_ms, 3),
                     "calib_GBps": round(w.calib_batches * P * w.calib_T * H * 2 / (calib_ms * 1e-3) / 1e9, 1),
                     "select_us": round(select_ms * 1e3, 2)},
