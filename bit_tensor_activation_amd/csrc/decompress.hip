@@ -536,8 +536,13 @@ hipError_t launch_decompress(const uint8_t* packed, int64_t pitch, const uint16_
     // about 1024 waves (4 per CU: each wave's table loads then serve at
     // least 16 rows where the batch allows), a multiple of the ring depth,
     // up to 64 rows; batches too short to give every wave a full 8-row ring
-    // take the 2-row ring
-    int64_t rpw64 = (ntiles * T + 1023) / 1024;
+    // take the 2-row ring. The bf16-output receiver writes half the bytes
+    // and gains from two waves per SIMD once the batch has 32768 row-tiles
+    // or more (about 2048 waves): 7B at T=8192 51.6 -> 47.2 us, large prefill
+    // at T=4096 36.3 -> 32.3 us; the fp32 receiver loses there (7B at
+    // T=8192 56.2 -> 59.5 us).
+    const int64_t waves = (bf16 && ntiles * T >= 32768) ? 2 * kDqGeneration : kDqGeneration;
+    int64_t rpw64 = (ntiles * T + waves - 1) / waves;
     const bool small = rpw64 < kDqRing;
     const int ring = small ? kDqRingSmall : kDqRing;
     rpw64 = (rpw64 + ring - 1) / ring * ring;
@@ -549,8 +554,8 @@ hipError_t launch_decompress(const uint8_t* packed, int64_t pitch, const uint16_
     // tile holds at most 64 of them on average, else 4. A tile beyond its
     // registers sums its BF16 features after the row loop.
     const bool wide = P * k > int64_t(kWave) * ntiles;
-    // one sub-step row while the grid is one generation (row counts below the
-    // 64-row cap), two once several waves share each SIMD
+    // one sub-step row while the grid is one generation (at most one wave per
+    // SIMD), two once several waves share each SIMD
     const bool one_gen = ntiles * nrowblk <= kDqGeneration;
     if (bf16)
       dispatch_fast<true>(P, wide, small, one_gen, packed, pitch, outl, T, H, k, Hq, ntiles, rpw,
