@@ -47,15 +47,32 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into bit_tensor_activation_amd/libbtq.so."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *COMMON_FLAGS, "-shared", *sources(), "-o", tmp]
+OBJ_DIR = os.path.join(PKG, "_build")
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into bit_tensor_activation_amd/libbtq.so.
+
+    Each source compiles to an object of its own, in parallel (every kernel
+    is launched from its own translation unit, so no device linking is
+    needed), and the objects link into the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs = sources()
+    objs = [os.path.join(OBJ_DIR, os.path.basename(src).replace(".hip", ".o")) for src in srcs]
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1, 8)) as ex:
+        list(ex.map(lambda so: _run([hipcc(), *COMMON_FLAGS, "-c", so[0], "-o", so[1]], verbose),
+                    zip(srcs, objs)))
+    tmp = LIB + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 
