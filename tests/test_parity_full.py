@@ -36,6 +36,9 @@ DEV = torch.device("cuda:0")
 # (workload, inference T, k, calibration batches used here)
 CASES = [
     ("7b_prefill", 2048, 64, 4),
+    # 32768 row-tiles: the bf16-output receiver takes about 2048 waves here
+    ("7b_prefill", 4096, 64, 4),
+    ("large_prefill", 2048, 128, 3),
     ("decode", 1, 64, 3),
     ("decode", 8, 64, 3),
     ("decode", 32, 64, 3),
