@@ -145,17 +145,35 @@ __global__ __launch_bounds__(256) void decompress_kernel(
   uint32_t w[kR][NP], ov[kR][kOR];
   // The lane's offsets stay in fixed VGPRs; the (shard, row) offset is
   // uniform and rides in the instruction's SGPR offset.
+  // A row past the wave's last loads out of range. With one wave per SIMD
+  // (kSub == 1) through empty descriptors, a scalar choice that spares the
+  // per-row selection of every lane offset (7B: 17.6 -> 17.0 us); with
+  // several waves per SIMD through the lane offsets, which measured faster
+  // there (large prefill 88.8 against 91.8 us).
   auto load = [&](int q, int row) {
     const bool ok = row < nrows;   // uniform
     const int64_t rowg = t0 + min(row, nrows - 1);
+    if constexpr (kSub == 1) {
+      const rsrc_t rpq = make_rsrc(packed, ok ? (uint32_t)(NP * T * (int64_t)pitch) : 0u);
+      const rsrc_t roq = make_rsrc(outl, ok ? (uint32_t)(NP * T * (int64_t)k * 2) : 0u);
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
-      w[q][p] = __builtin_amdgcn_raw_buffer_load_b32(
-          rp, ok ? pk_off : kOOB, (uint32_t)(((int64_t)p * T + rowg) * pitch), kStream);
+      for (int p = 0; p < NP; ++p)
+        w[q][p] = __builtin_amdgcn_raw_buffer_load_b32(
+            rpq, pk_off, (uint32_t)(((int64_t)p * T + rowg) * pitch), kStream);
 #pragma unroll
-    for (int r = 0; r < kOR; ++r)
-      ov[q][r] = __builtin_amdgcn_raw_buffer_load_b16(ro, ok ? o_off[r] : kOOB,
-                                                      (uint32_t)(rowg * k * 2), 0);
+      for (int r = 0; r < kOR; ++r)
+        ov[q][r] = __builtin_amdgcn_raw_buffer_load_b16(roq, o_off[r], (uint32_t)(rowg * k * 2),
+                                                        0);
+    } else {
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+        w[q][p] = __builtin_amdgcn_raw_buffer_load_b32(
+            rp, ok ? pk_off : kOOB, (uint32_t)(((int64_t)p * T + rowg) * pitch), kStream);
+#pragma unroll
+      for (int r = 0; r < kOR; ++r)
+        ov[q][r] = __builtin_amdgcn_raw_buffer_load_b16(ro, ok ? o_off[r] : kOOB,
+                                                        (uint32_t)(rowg * k * 2), 0);
+    }
   };
 
   // Setup loads first, ring loads second: the vector-memory counter retires
@@ -247,8 +265,13 @@ __global__ __launch_bounds__(256) void decompress_kernel(
   // instruction overwrite the data, and on gfx950 the stored values then
   // come out wrong.
   char* const ybase = static_cast<char*>(y) + t0 * H * kYB;
-  auto store_chunk = [&](const v4f& v, uint32_t off, uint32_t rowoff) {
-    const rsrc_t rr = make_rsrc(ybase + rowoff, (uint32_t)H * kYB);
+  // (a row past the wave's last stores through an empty descriptor, so the
+  // lanes' offsets are the same for every row)
+  auto row_rsrc = [&](int row) {
+    return make_rsrc(ybase + (int64_t)min(row, nrows - 1) * H * kYB,
+                     row < nrows ? (uint32_t)H * kYB : 0u);
+  };
+  auto store_chunk = [&](const v4f& v, uint32_t off, const rsrc_t& rr) {
     if constexpr (kBf) {
       typedef unsigned int v2u __attribute__((ext_vector_type(2)));
       __builtin_amdgcn_raw_buffer_store_b64(v2u{bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3])}, rr,
@@ -260,12 +283,19 @@ __global__ __launch_bounds__(256) void decompress_kernel(
           rr, off, 0, kStream);
     }
   };
-  auto store_one = [&](float f, uint32_t off, uint32_t rowoff) {
+  auto store_one = [&](float f, uint32_t off, const rsrc_t& rr) {
     if constexpr (kBf)
-      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bf16_bits_rne(f), ry, off, rowoff, kStream);
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bf16_bits_rne(f), rr, off, 0, kStream);
     else
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), ry, off, rowoff, kStream);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), rr, off, 0, kStream);
   };
+  // the lane's chunk offsets for the usual spans (out of range past the span)
+  uint32_t c_off[kStU];
+#pragma unroll
+  for (int it = 0; it < kStU; ++it) {
+    const int qc = q_lo + lane + kWave * it;
+    c_off[it] = qc < q_hi ? (uint32_t)(a4 + 4 * qc) * kYB : kOOB;
+  }
 
   // nrows >= 1: a do-while has no entry guard that the ring loads could be
   // sunk below.
@@ -286,7 +316,7 @@ __global__ __launch_bounds__(256) void decompress_kernel(
         if (bf_row) {
 #pragma unroll
           for (int p = 0; p < NP; ++p) {
-            t[p][0] = __builtin_amdgcn_ds_bpermute(src_addr[p], (int)ov[q][0]);
+            t[p][0] = __builtin_amdgcn_ds_bpermute(src_addr[p], (int)(ov[q][0] << 16));
 #pragma unroll
             for (int rr = 1; rr < kOR; ++rr) t[p][rr] = 0;
           }
@@ -295,7 +325,7 @@ __global__ __launch_bounds__(256) void decompress_kernel(
             for (int p = 0; p < NP; ++p) {
 #pragma unroll
               for (int rr = 1; rr < kOR; ++rr)
-                t[p][rr] = __builtin_amdgcn_ds_bpermute(src_addr[p], (int)ov[q][rr]);
+                t[p][rr] = __builtin_amdgcn_ds_bpermute(src_addr[p], (int)(ov[q][rr] << 16));
             }
           }
         }
@@ -329,8 +359,9 @@ __global__ __launch_bounds__(256) void decompress_kernel(
             int v = t[p][0];
 #pragma unroll
             for (int rr = 1; rr < kOR; ++rr) v = (src_reg[p] == rr) ? t[p][rr] : v;
-            // (the loads zero-extend the 16 bf16 bits)
-            o = __fadd_rn(o, bf16_to_f32((uint32_t)v));
+            // (each value was moved to the high half before the cross-lane
+            // read: its fp32 bits)
+            o = __fadd_rn(o, __uint_as_float((uint32_t)v));
           }
           b[oa] = o;
         }
@@ -358,29 +389,22 @@ __global__ __launch_bounds__(256) void decompress_kernel(
         }
 #pragma unroll
         for (int r = 0; r < kSub; ++r) {
-          const int row = base + sb * kSub + r;
-          const bool ok = row < nrows;   // uniform
-          const uint32_t rowoff = (uint32_t)min(row, nrows - 1) * (uint32_t)H * kYB;
+          const rsrc_t rr = row_rsrc(base + sb * kSub + r);
 #pragma unroll
-          for (int it = 0; it < kStU; ++it) {
-            const int qc = q_lo + lane + kWave * it;
-            store_chunk(cv[r][it], (ok && qc < q_hi) ? (uint32_t)(a4 + 4 * qc) * kYB : kOOB, rowoff);
-          }
-          store_one(rv[r], ok ? b_off : kOOB, rowoff);
+          for (int it = 0; it < kStU; ++it) store_chunk(cv[r][it], c_off[it], rr);
+          store_one(rv[r], b_off, rr);
         }
       } else {
 #pragma unroll
         for (int r = 0; r < kSub; ++r) {
-          const int row = base + sb * kSub + r;
-          const bool ok = row < nrows;   // uniform
           const float* b = buf + r * buf_dwords;
-          const uint32_t rowoff = (uint32_t)min(row, nrows - 1) * (uint32_t)H * kYB;
+          const rsrc_t rr = row_rsrc(base + sb * kSub + r);
           for (int it = 0; it < st_it; ++it) {
             const int qc = q_lo + lane + kWave * it;
             const v4f v = *reinterpret_cast<const v4f*>(b + cpad((uint32_t)(4 * min(qc, q_hi - 1))));
-            store_chunk(v, (ok && qc < q_hi) ? (uint32_t)(a4 + 4 * qc) * kYB : kOOB, rowoff);
+            store_chunk(v, qc < q_hi ? (uint32_t)(a4 + 4 * qc) * kYB : kOOB, rr);
           }
-          store_one(b[b_lds], ok ? b_off : kOOB, rowoff);
+          store_one(b[b_lds], b_off, rr);
         }
       }
       wave_lds_sync();
