@@ -52,6 +52,16 @@ MUTANTS = [
     ("score takes the first shard's range only",
      [("score = score + width[p] if rule == \"sum\"",
        "score = width[0] if rule == \"sum\"")]),
+    ("max rule takes the minimum", [("else np.maximum(score, width[p])",
+                                     "else np.minimum(score, width[p])")]),
+    ("given set replaced by the ranked one",
+     [("idx, fmap, cmap = maps_for_set(idx, scale.shape[1])",
+       "idx, fmap, cmap = top_k_features(score, len(idx))")]),
+    ("fmap inverted without the -1 offset", [("idx[-1 - fmap[~ints]] = h[~ints]",
+                                              "idx[np.abs(fmap[~ints]) % len(idx)] = h[~ints]")]),
+    ("bias summed from the last shard",
+     [("for p in range(s.shape[0]):\n        bias = bias - (z[p] * s[p])",
+       "for p in reversed(range(s.shape[0])):\n        bias = bias - (z[p] * s[p])")]),
     ("ties go to the higher feature", [("np.lexsort((h, -score))", "np.lexsort((-h, -score))")]),
     ("the narrowest features kept", [("np.lexsort((h, -score))", "np.lexsort((h, score))")]),
     ("BF16 set listed in rank order", [("return maps_for_set(np.sort(order[:k]), H)",

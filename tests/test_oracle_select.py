@@ -114,6 +114,18 @@ def test_codec_tables_are_the_parameters_in_message_order():
         assert abs(dec[2 * P, j] - exact) <= 2 * P * 2.0 ** -24 * (abs(exact) + 15 * P * sel["scale"][:, h].max())
 
 
+def test_codec_bias_sums_in_shard_order():
+    # Hand-worked: three shards with z = 1 and scales 1, 2^-24, 2^-24, so the
+    # products z*s are exact. From shard 0: -1 - 2^-24 lies halfway between
+    # -1 and -(1 + 2^-23) and rounds to the even -1, twice, so the bias is
+    # -1 (0xbf800000). Summed from the last shard, -2^-24 - 2^-24 = -2^-23
+    # exactly, and -2^-23 - 1 = -(1 + 2^-23) (0xbf800001) is exact too.
+    scale = np.array([[1.0], [2.0 ** -24], [2.0 ** -24]], np.float32)
+    zp = np.ones((3, 1), np.uint8)
+    _, dec = O.codec_tables(scale, np.float32(1) / scale, zp, np.array([0], np.int32))
+    assert dec[6].view(np.uint32).tolist() == [0xBF800000]
+
+
 @pytest.mark.parametrize("H,k,seed", [(1, 0, 0), (1, 1, 1), (40, 7, 2), (300, 0, 3), (300, 300, 4),
                                       (517, 64, 5)])
 def test_maps_for_a_given_set_brute_force(H, k, seed):
