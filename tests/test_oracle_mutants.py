@@ -111,6 +111,10 @@ MUTANTS = [
                                 "(u >> np.uint64(16))")]),
     ("bf16 output ties round up", [("((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16))",
                                     "((u + np.uint64(0x8000)) >> np.uint64(16))")]),
+    ("per-shard sender table in feature order", [("enc[p, :, 0] = rscale[p, cmap[p]]",
+                                                  "enc[p, :, 0] = rscale[p, :H - k]")]),
+    ("per-shard sender table with shard 0's zero points",
+     [("enc[p, :, 1] = zp[p, cmap[p]].astype(F32)", "enc[p, :, 1] = zp[0, cmap[p]].astype(F32)")]),
     ("per-shard sets ranked by the shared score",
      [("idx[p], fmap[p], cmap[p] = top_k_features(width[p], k)",
        "idx[p], fmap[p], cmap[p] = top_k_features(range_score(width), k)")]),
