@@ -1,12 +1,18 @@
 #!/usr/bin/env python3
 """Throughput of the hybrid int4/BF16 partial-sum codec on one MI355X.
 
-One step = one pass of the per-batch hot path over one inference batch:
-btq_compress_pack (every shard's sender message) and then
-btq_decompress_reduce (the receiver's fused dequantize and fp32 sum over
-P shards). Calibration and selection run once before the timed region, as
-the method prescribes: they are computed offline on calibration batches.
-They are timed separately and reported under "offline".
+One step = one pass of the per-batch hot path over one inference batch: the
+sender (every shard's message) and then the receiver (the fused dequantize
+and fp32 sum over P shards). Calibration and selection run once before the
+timed region, as the method prescribes: they are computed offline on
+calibration batches. They are timed separately and reported under "offline".
+
+Two message layouts are timed, each as a caller runs it:
+  * padded: btq_compress_pack_ex / btq_decompress_reduce_ex with rows at
+    btq_packed_pitch (the code bytes rounded up to 128, so every row starts
+    on a cache line) -- this gives `value`;
+  * dense: the path's own calls btq_compress_pack / btq_decompress_reduce,
+    rows of exactly the code bytes.
 
 Metric: bf16-equivalent GB/s = steps * P*T*H*2 bytes / wall time of the
 timed steps, launched back to back with nothing between them. Inputs are
@@ -16,17 +22,24 @@ last-level cache. The receiver reads the message written two steps earlier.
 The same steps captured in a HIP graph (one rotation, replayed) are timed too
 and reported under "timing" (graph_ms_per_step); value stays the eager rate.
 
-Roofline: the dominant kernel (compress) is HBM-bound. achieved = its
-algorithmic bytes per launch / its mean duration. The durations come from
-the same steps run a second time, with HIP events recorded on the launch
-stream around every launch (events without the system-scope fence, so
-recording them flushes no cache; they still add a few microseconds per
-step, which is why the throughput is taken from the first run). traffic =
-HBM bytes per launch from rocprofv3 counters (profiles/), reported only
-while the kernel source still matches the hash those counters were taken
-at.
+Roofline: the dominant kernel (the sender) is HBM-bound. achieved = its
+algorithmic bytes per launch / its mean duration. The algorithmic bytes are
+what the method must move: the bf16 input, the message, and the per-feature
+parameters and maps (5 bytes per (shard, feature) and 4 per feature). The
+durations come from the same steps run a second time, with HIP events
+recorded on the launch stream around every launch (events without the
+system-scope fence, so recording them flushes no cache; they still add a few
+microseconds per step, which is why the throughput is taken from the first
+run). traffic = HBM bytes per launch from rocprofv3 counters (profiles/),
+reported only while the kernel source still matches the hash those counters
+were taken at.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 7b_prefill]
+CPU baseline: the oracle as it stands, on a bounded sample of the same
+workload, on one core and on a pool of worker processes (one row chunk of
+every shard per task), each with its core count. It runs before the GPU is
+touched, so the pool's workers fork from a process with no GPU state.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stress] [--k 32]
 """
 from __future__ import annotations
 
@@ -66,9 +79,14 @@ def source_hash(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per compress launch from the committed counter summary."""
-    path = os.path.join(PROFILES, f"compress_{workload}_traffic.txt")
+def traffic_path(workload: str, k: int) -> str:
+    return os.path.join(PROFILES, f"compress_{workload}_k{k}_traffic.txt")
+
+
+def read_traffic(workload: str, k: int):
+    """HBM bytes per sender launch (padded layout) from the committed counter
+    summary, while the kernel code still matches the hash it was taken at."""
+    path = traffic_path(workload, k)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -137,25 +155,30 @@ def _csv_rows(d: str, suffix: str):
             yield from csv.DictReader(fh)
 
 
+def _template_args(name: str):
+    head = name.split("(")[0]
+    return [t.strip() for t in head[head.index("<") + 1:head.rindex(">")].split(",")] \
+        if "<" in head else []
+
+
 def _kernel_class(name: str):
-    head = name.split("(")[0].rstrip()
-    if "btq::" in name and "decompress_sets" in name:
-        return "decompress_reduce_per_shard"
-    if "btq::" in name and "compress" in name and "decompress" not in name and \
-            head.endswith("true>"):
-        return "compress_pack_per_shard"   # the sender's per-shard template flag
-    if "btq::" in name and "decompress" in name:
-        # the receiver's template flag selects bf16 output
-        bf16 = name.split("(")[0].rstrip().endswith("true>")
-        return "decompress_reduce_bf16" if bf16 else "decompress_reduce"
-    if "btq::" in name and "compress" in name:
-        return "compress_pack"
+    """The benchmark's name for a kernel of a rocprofv3 record, or None."""
+    if "btq::" in name and "dq_window_kernel" in name:
+        # template <NP, kOR, kR, kPs, kBf>
+        t = _template_args(name)
+        per, bf = t[3] == "true", t[4] == "true"
+        return ("decompress_reduce_per_shard" if per else
+                "decompress_reduce_bf16" if bf else "decompress_reduce")
+    if "btq::" in name and "compress" in name and "decompress" not in name:
+        # the sender's last template flag: one set per shard
+        per = _template_args(name)[-1:] == ["true"]
+        return "compress_pack_per_shard" if per else "compress_pack"
     if "copyBuffer" in name:
         return "copy"
     return None
 
 
-def summarize_counters(fetch_dir: str, write_dir: str, workload: str, copy_mib: int,
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str, k, copy_mib: int,
                        note: str) -> str:
     """Traffic summary from two rocprofv3 --pmc runs of this script.
 
@@ -186,13 +209,15 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, copy_mib: 
     fscale = statistics.median(copies["FETCH_SIZE"]) / kib
     wscale = statistics.median(copies["WRITE_SIZE"]) / kib
     w = W.WORKLOADS[workload]
-    comp_alg, deco_alg = algorithmic_bytes(w.P, w.T[0], w.H, w.k)
-    deco16_alg = algorithmic_bytes(w.P, w.T[0], w.H, w.k, y_bytes=2)[1]
-    comp_ps_alg, deco_ps_alg = algorithmic_bytes_per_shard(w.P, w.T[0], w.H, w.k)
-    lines = [f"# HBM traffic per launch, workload {workload} (P={w.P}, T={w.T[0]}, H={w.H}, k={w.k})",
+    k = w.k if k is None else k
+    comp_alg, deco_alg = algorithmic_bytes(w.P, w.T[0], w.H, k)
+    deco16_alg = algorithmic_bytes(w.P, w.T[0], w.H, k, y_bytes=2)[1]
+    comp_ps_alg, deco_ps_alg = algorithmic_bytes_per_shard(w.P, w.T[0], w.H, k)
+    lines = [f"# HBM traffic per launch, workload {workload} (P={w.P}, T={w.T[0]}, H={w.H}, k={k})",
              "# " + note.replace("\n", "\n# "),
              f"source_hash={source_hash(KERNEL_SOURCES)}",
              f"workload={workload}",
+             f"k={k}",
              f"copy_probe_bytes={copy_mib * 2 ** 20}",
              f"copy_fetch_kib={statistics.median(copies['FETCH_SIZE']):.1f}",
              f"copy_write_kib={statistics.median(copies['WRITE_SIZE']):.1f}",
@@ -264,70 +289,125 @@ def summarize_trace(trace_dir: str, note: str) -> str:
 
 
 def algorithmic_bytes(P, T, H, k, y_bytes=4):
-    """Bytes the method must move per launch (inputs once, outputs once);
-    y_bytes is 4 for the fp32 receiver, 2 for the bf16 one."""
+    """Bytes the method must move per launch, inputs once and outputs once:
+    sender  P*T*H*2 (bf16 input) + P*T*(Bq + 2k) (message) + 5*P*H (rscale
+            and zero point per (shard, feature)) + 4*H (cmap and outlier_idx);
+    receiver P*T*(Bq + 2k) + T*H*y_bytes (4: fp32 y, 2: bf16 y) + 5*P*H
+            (scale and zero point) + 4*H (fmap).
+    The padded layout's zero bytes past each row's codes are not counted."""
     Bq = (H - k + 1) // 2
-    Hq = H - k
-    maps = 4 * H                             # cmap and outlier_idx
     message = P * T * (Bq + 2 * k)
-    compress = P * T * H * 2 + message + P * Hq * 8 + maps           # + (rscale, zero point) table
-    decompress = message + T * H * y_bytes + (P + 1) * Hq * 4 + maps  # + scale rows, constant row
-    return compress, decompress
+    params = 5 * P * H + 4 * H
+    return P * T * H * 2 + message + params, message + T * H * y_bytes + params
 
 
 def algorithmic_bytes_per_shard(P, T, H, k):
-    """The same for per-shard BF16 sets: per-shard maps; the receiver reads
-    scale, zero point and fmap by feature (9 bytes per (p,h))."""
+    """The same for one BF16 set per shard: the maps are per shard
+    (4*P*H bytes in place of 4*H)."""
     Bq = (H - k + 1) // 2
     message = P * T * (Bq + 2 * k)
-    compress = P * T * H * 2 + message + P * (H - k) * 8 + 4 * P * H
-    decompress = message + T * H * 4 + 9 * P * H
-    return compress, decompress
+    params = 5 * P * H + 4 * P * H
+    return P * T * H * 2 + message + params, message + T * H * 4 + params
 
 
-def cpu_baseline(w, T_sample: int, min_seconds: float):
-    """The oracle, as it is, on a bounded sample of the same workload."""
-    import numpy as np
-    import workloads as W
+def cpu_cores() -> int:
+    """Host cores for the oracle pool: this process's CPUs, at most 16 (the
+    host share of one GPU)."""
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
+# The pool's task state: set in the parent before the workers fork.
+_POOL_STATE = {}
+
+
+def _oracle_rows(span):
+    """Sender then receiver of the oracle on token rows [a, b) of every shard
+    (rows are independent)."""
     from oracle import oracle as O
+    x, sel = _POOL_STATE["x"], _POOL_STATE["sel"]
+    a, b = span
+    pk, ol = O.compress_pack(x[:, a:b], sel["rscale"], sel["zero_point"], sel["idx"], sel["cmap"])
+    y = O.decompress_reduce(pk, ol, sel["scale"], sel["zero_point"], sel["fmap"])
+    return int(pk.nbytes + y.nbytes)
+
+
+def _limit_threads():
     try:
         from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(1)
+        threadpool_limits(1)
     except Exception:   # numpy's elementwise ops are single-threaded anyway
-        limiter = None
-    x = W.to_u16(W.batch(w, W.PHASE_INFER, 0, T=T_sample, device="cpu"))
+        pass
+
+
+def cpu_baseline(w, k: int, T: int, T_sample: int, min_seconds: float):
+    """The oracle, as it is, on a bounded sample of the same workload: one
+    core, then a pool of worker processes over row chunks of every shard."""
+    import multiprocessing as mp
+    import workloads as W
+    from oracle import oracle as O
+    _limit_threads()
+    cores = cpu_cores()
+    rows_pool = min(T, T_sample * cores)
+    x = W.to_u16(W.batch(w, W.PHASE_INFER, 0, T=rows_pool, device="cpu"))
     mn, mx = O.batch_min_max(x)
-    sel = O.select_outliers(mn, mx, w.k)
+    sel = O.select_outliers(mn, mx, k)
+    _POOL_STATE.update(x=x, sel=sel)
+    bytes_per_row = w.P * w.H * 2
+    # one core: T_sample rows per call, repeated for >= min_seconds
     reps, t0 = 0, time.perf_counter()
     while True:
-        pk, ol = O.compress_pack(x, sel["rscale"], sel["zero_point"], sel["idx"], sel["cmap"])
-        O.decompress_reduce(pk, ol, sel["scale"], sel["zero_point"], sel["fmap"])
+        _oracle_rows((0, min(T_sample, rows_pool)))
         reps += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
+        el1 = time.perf_counter() - t0
+        if el1 >= min_seconds:
             break
-    if limiter is not None:
-        limiter.unregister()
-    gbps = reps * x.nbytes / el / 1e9
-    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": (f"{w.name}: P={w.P} x T={T_sample} of {w.T[0]} tokens x H={w.H}, k={w.k}; "
-                       f"numpy oracle compress_pack + decompress_reduce, {reps} reps in "
-                       f"{el:.1f} s, one thread; parameters from the sample's own min/max")}
+    one = reps * min(T_sample, rows_pool) * bytes_per_row / el1 / 1e9
+    # a pool: every task is a chunk of 32 rows of all shards
+    chunk = 32
+    spans = [(a, min(rows_pool, a + chunk)) for a in range(0, rows_pool, chunk)]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores, initializer=_limit_threads) as pool:
+        pool.map(_oracle_rows, spans[:cores])   # workers up
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            pool.map(_oracle_rows, spans, chunksize=1)
+            passes += 1
+            elp = time.perf_counter() - t0
+            if elp >= min_seconds:
+                break
+    pooled = passes * rows_pool * bytes_per_row / elp / 1e9
+    _POOL_STATE.clear()
+    return {"value": round(pooled, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "value_1core": round(one, 4), "cores_1core": 1,
+            "sample": (f"{w.name}: P={w.P} x H={w.H}, k={k}, bf16-equiv rate of the numpy oracle's "
+                       f"compress_pack + decompress_reduce; one core: {reps} calls on "
+                       f"{min(T_sample, rows_pool)} of {T} tokens in {el1:.1f} s; "
+                       f"{cores} worker processes: {passes} passes over {rows_pool} tokens in "
+                       f"{len(spans)} tasks of {chunk} rows of every shard, {elp:.1f} s; "
+                       "parameters from the sample's own min/max")}
 
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="7b_prefill")
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="stress")
     ap.add_argument("--T", type=int, default=None, help="token count (decode sweep)")
-    ap.add_argument("--k", type=int, default=None, help="BF16 feature count (stress sweep)")
+    ap.add_argument("--k", type=int, default=None,
+                    help="BF16 feature count (default: the workload's first, 32 for stress)")
+    ap.add_argument("--layouts", default="padded,dense",
+                    help="message layouts to time, the first gives value: padded (rows at "
+                         "btq_packed_pitch, the *_ex calls) and/or dense (rows of the code "
+                         "bytes, the path's own calls)")
     ap.add_argument("--rotate-mib", type=int, default=1024,
                     help="minimum MiB streamed between reuses of one buffer set")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--cpu-sample-T", type=int, default=256)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-sample-T", type=int, default=128,
+                    help="token rows of the one-core sample (the pool takes this many per core)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the steps (no bf16 receiver, per-shard sets or graph)")
     ap.add_argument("--copy-probe-mib", type=int, default=256,
                     help="size of the plain device copy timed for the copy roofline (and the "
                          "counter scale); 0 skips it")
@@ -341,8 +421,8 @@ def main() -> int:
     ap.add_argument("--note", default="", help="header text for the summaries")
     args = ap.parse_args()
     if args.summarize_counters:
-        print(summarize_counters(*args.summarize_counters, args.workload, args.copy_probe_mib,
-                                 args.note), end="")
+        print(summarize_counters(*args.summarize_counters, args.workload, args.k,
+                                 args.copy_probe_mib, args.note), end="")
         return 0
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.note), end="")
@@ -357,20 +437,31 @@ def main() -> int:
               "(the P shards of one tensor-parallel group share one GPU's HBM). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
+    layouts = [l.strip() for l in args.layouts.split(",") if l.strip()]
+    if not layouts or any(l not in ("padded", "dense") for l in layouts):
+        print("--layouts takes padded and/or dense", file=sys.stderr)
+        return 2
+
+    import workloads as W
+    w = W.WORKLOADS[args.workload]
+    T = args.T if args.T is not None else w.T[0]
+    k = args.k if args.k is not None else w.k
+    P, H = w.P, w.H
+
+    # ---- the CPU baseline first: its worker processes fork before any GPU use
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for >= {args.cpu_seconds:.0f} s on one core and on a pool")
+        cpu = cpu_baseline(w, k, T, min(args.cpu_sample_T, T), args.cpu_seconds)
 
     import torch
     import bit_tensor_activation_amd as B
     from bit_tensor_activation_amd import _lib
-    import workloads as W
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     dev = torch.device("cuda:0")
-    w = W.WORKLOADS[args.workload]
-    T = args.T if args.T is not None else w.T[0]
-    k = args.k if args.k is not None else w.k
-    P, H = w.P, w.H
     lib = _lib.load()
     stream = torch.cuda.current_stream(dev)
     sh = int(stream.cuda_stream)
@@ -402,120 +493,116 @@ def main() -> int:
 
     # ---- resident inputs and rotated buffer sets ----
     x0 = W.batch(w, W.PHASE_INFER, 0, T=T, device=dev)
-    pitch = B.btq_packed_pitch(H, k)
-    set_bytes = P * T * H * 2 + P * T * (pitch + 2 * k) + T * H * 4
+    Bq = B.btq_packed_row_bytes(H, k)
+    pitches = {"padded": B.btq_packed_pitch(H, k), "dense": Bq}
+    wmax = max(pitches[l] for l in layouts)
+    set_bytes = P * T * H * 2 + P * T * (wmax + 2 * k) + T * H * 4
     R = max(3, -(-args.rotate_mib * 2 ** 20 // set_bytes) + 1)
     xs = [x0.clone() for _ in range(R)]
-    pks = [torch.empty((P, T, pitch), dtype=torch.uint8, device=dev) for _ in range(R)]
+    msg = [torch.empty(P * T * wmax, dtype=torch.uint8, device=dev) for _ in range(R)]
     ols = [torch.empty((P, T, k), dtype=torch.int16, device=dev) for _ in range(R)]
     ys = [torch.empty((T, H), dtype=torch.float32, device=dev) for _ in range(R)]
     del x0
     p = lambda t: t.data_ptr() if t.numel() else None
-    enc, dec, oi, cm = p(sel["enc"]), p(sel["dec"]), p(sel["outlier_idx"]), p(sel["cmap"])
-    comp_args = [(p(xs[r]), P, T, H, k, enc, oi, cm, p(pks[r]), pitch, p(ols[r]), sh)
-                 for r in range(R)]
-    deco_args = [(p(pks[(r - 2) % R]), pitch, p(ols[(r - 2) % R]), P, T, H, k, dec, oi, cm,
-                  p(ys[r]), sh) for r in range(R)]
-    compress, decompress = lib.btq_compress_pack, lib.btq_decompress_reduce
-    # first fill every message buffer once, so the receiver always reads a real message
-    for r in range(R):
-        _lib.check(compress(*comp_args[r]), "btq_compress_pack")
-    torch.cuda.synchronize()
-    log(f"{R} rotating buffer sets of {set_bytes / 2**20:.1f} MiB; warmup {args.warmup}, "
-        f"steps {args.steps}")
+    rs, sc, zp = p(sel["rscale"]), p(sel["scale"]), p(sel["zero_point"])
+    oi, cm, fm = p(sel["outlier_idx"]), p(sel["cmap"]), p(sel["fmap"])
+    SHARED, F32 = _lib.BTQ_SETS_SHARED, _lib.BTQ_Y_F32
 
-    def step(i, ev=None):
-        r = i % R
-        if ev is not None:
-            hev.record(ev[0], sh)
-        st = compress(*comp_args[r])
-        if ev is not None:
-            hev.record(ev[1], sh)
-        st |= decompress(*deco_args[r])
-        if ev is not None:
-            hev.record(ev[2], sh)
-        return st
+    def calls(layout):
+        """(sender, receiver, their argument tuples per buffer set)."""
+        pitch = pitches[layout]
+        if layout == "padded":
+            comp = [(p(xs[r]), P, T, H, k, rs, zp, oi, cm, SHARED, p(msg[r]), pitch, p(ols[r]), sh)
+                    for r in range(R)]
+            deco = [(p(msg[(r - 2) % R]), pitch, p(ols[(r - 2) % R]), P, T, H, k, sc, zp, fm,
+                     SHARED, p(ys[r]), F32, sh) for r in range(R)]
+            return lib.btq_compress_pack_ex, lib.btq_decompress_reduce_ex, comp, deco
+        comp = [(p(xs[r]), P, T, H, k, rs, zp, oi, cm, p(msg[r]), p(ols[r]), sh) for r in range(R)]
+        deco = [(p(msg[(r - 2) % R]), p(ols[(r - 2) % R]), P, T, H, k, sc, zp, fm, p(ys[r]), sh)
+                for r in range(R)]
+        return lib.btq_compress_pack, lib.btq_decompress_reduce, comp, deco
 
-    st = 0
-    for i in range(args.warmup):
-        st |= step(i)
-    torch.cuda.synchronize()
-    _lib.check(st, "warmup")
-    # Timed region 1: the steps as a caller runs them, with no instrumentation
-    # between the launches (value, ms_per_step).
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        st |= step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    _lib.check(st, "timed steps")
-    # Timed region 2: the same steps again with a HIP event around every
-    # launch, on the launch stream (each kernel's duration). The events cost
-    # a few microseconds per step, so region 1 alone gives the throughput.
-    evs = [[hev.new() for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for i in range(args.steps):
-        st |= step(i, evs[i])
-    torch.cuda.synchronize()
-    wall_ev = time.perf_counter() - t1
-    _lib.check(st, "instrumented steps")
-    comp_ms = [hev.ms(e[0], e[1]) for e in evs]
-    deco_ms = [hev.ms(e[1], e[2]) for e in evs]
-    comp_mean = sum(comp_ms) / len(comp_ms)
-    deco_mean = sum(deco_ms) / len(deco_ms)
+    log(f"{R} rotating buffer sets of {set_bytes / 2**20:.1f} MiB; layouts {layouts}; "
+        f"warmup {args.warmup}, steps {args.steps}")
+    bf16_bytes = P * T * H * 2
+    comp_bytes, deco_bytes = algorithmic_bytes(P, T, H, k)
     med = lambda v: sorted(v)[len(v) // 2]
+    results = {}
+    for layout in layouts:
+        compress, decompress, comp_args, deco_args = calls(layout)
+        # first fill every message buffer once, so the receiver always reads a real message
+        for r in range(R):
+            _lib.check(compress(*comp_args[r]), "sender")
+        torch.cuda.synchronize()
 
-    # Timed region 3 (reported beside value, not value): G steps of the
-    # rotation (all R, at most 512, which still spans well past the last-level
-    # cache) captured in a HIP graph on a side stream (default priority) and
-    # replayed, as a caller that captures its steps would run them. The
-    # kernels clear nothing with memset, so the graph holds kernel nodes only.
-    G = min(R, 512)
-    gs = torch.cuda.Stream(device=dev)
-    g_comp = [a[:-1] + (gs.cuda_stream,) for a in comp_args[:G]]
-    g_deco = [a[:-1] + (gs.cuda_stream,) for a in deco_args[:G]]
-    graph = torch.cuda.CUDAGraph()
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph, stream=gs):
-        for r in range(G):
-            st |= compress(*g_comp[r])
-            st |= decompress(*g_deco[r])
-    _lib.check(st, "graph capture")
-    graph.replay()
-    torch.cuda.synchronize()
-    n_rep = max(1, args.steps // G)
-    t2 = time.perf_counter()
-    for _ in range(n_rep):
-        graph.replay()
-    torch.cuda.synchronize()
-    graph_ms = (time.perf_counter() - t2) / (n_rep * G) * 1e3
-    del graph
+        def step(i, ev=None):
+            r = i % R
+            if ev is not None:
+                hev.record(ev[0], sh)
+            st = compress(*comp_args[r])
+            if ev is not None:
+                hev.record(ev[1], sh)
+            st |= decompress(*deco_args[r])
+            if ev is not None:
+                hev.record(ev[2], sh)
+            return st
 
-    # The bf16-output receiver, timed on its own after the steps (it is not
-    # part of a step: the step's receiver writes fp32).
-    y16 = [torch.empty((T, H), dtype=torch.int16, device=dev) for _ in range(2)]
-    d16_args = [(a[0], a[1], a[2], P, T, H, k, dec, oi, cm, p(y16[r % 2]), sh)
-                for r, a in enumerate(deco_args)]
-    n16 = max(20, min(args.steps, 200))
-    for i in range(5):
-        st |= lib.btq_decompress_reduce_bf16(*d16_args[i % R])
-    e16 = [(hev.new(), hev.new()) for _ in range(n16)]
-    torch.cuda.synchronize()
-    for i in range(n16):
-        hev.record(e16[i][0], sh)
-        st |= lib.btq_decompress_reduce_bf16(*d16_args[i % R])
-        hev.record(e16[i][1], sh)
-    torch.cuda.synchronize()
-    _lib.check(st, "bf16-output receiver")
-    d16_mean = sum(hev.ms(a, b) for a, b in e16) / n16
-    d16_bytes = algorithmic_bytes(P, T, H, k, y_bytes=2)[1]
-    del y16
+        st = 0
+        for i in range(args.warmup):
+            st |= step(i)
+        torch.cuda.synchronize()
+        _lib.check(st, "warmup")
+        # Timed region 1: the steps as a caller runs them, with no instrumentation
+        # between the launches (value, ms_per_step).
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            st |= step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        _lib.check(st, "timed steps")
+        # Timed region 2: the same steps again with a HIP event around every
+        # launch, on the launch stream (each kernel's duration). The events cost
+        # a few microseconds per step, so region 1 alone gives the throughput.
+        evs = [[hev.new() for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(args.steps):
+            st |= step(i, evs[i])
+        torch.cuda.synchronize()
+        wall_ev = time.perf_counter() - t1
+        _lib.check(st, "instrumented steps")
+        comp_ms = [hev.ms(e[0], e[1]) for e in evs]
+        deco_ms = [hev.ms(e[1], e[2]) for e in evs]
+        results[layout] = dict(wall=wall, wall_ev=wall_ev, comp_ms=comp_ms, deco_ms=deco_ms,
+                               calls=(compress, decompress, comp_args, deco_args))
+        log(f"{layout}: {wall / args.steps * 1e6:.1f} us per step, sender "
+            f"{sum(comp_ms) / len(comp_ms) * 1e3:.1f} us, receiver "
+            f"{sum(deco_ms) / len(deco_ms) * 1e3:.1f} us")
 
-    # Per-shard BF16 sets (every shard keeps its own k features), timed on
-    # their own in the same rotation: another selection reading, not part of
-    # a step.
+    def kernel_entry(ms_list, nbytes):
+        mean = sum(ms_list) / len(ms_list)
+        return {"mean_us": round(mean * 1e3, 2), "median_us": round(med(ms_list) * 1e3, 2),
+                "algorithmic_bytes": nbytes, "hbm_GBps": round(nbytes / (mean * 1e-3) / 1e9, 1),
+                "frac": round(nbytes / (mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                "bf16_equiv_GBps": round(bf16_bytes / (mean * 1e-3) / 1e9, 1)}
+
+    head = results[layouts[0]]
+    comp_mean = sum(head["comp_ms"]) / len(head["comp_ms"])
+    value = args.steps * bf16_bytes / head["wall"] / 1e9
+    achieved = comp_bytes / (comp_mean * 1e-3) / 1e9
+    kernels = {}
+    for layout in layouts:
+        r = results[layout]
+        tag = "" if layout == layouts[0] else f"_{layout}"
+        kernels["compress_pack" + tag] = kernel_entry(r["comp_ms"], comp_bytes)
+        kernels["decompress_reduce" + tag] = kernel_entry(r["deco_ms"], deco_bytes)
+        kernels["compress_pack" + tag]["layout"] = layout
+        kernels["decompress_reduce" + tag]["layout"] = layout
+    layout_rates = {l: {"ms_per_step": round(results[l]["wall"] / args.steps * 1e3, 5),
+                        "GBps": round(args.steps * bf16_bytes / results[l]["wall"] / 1e9, 2),
+                        "pitch": pitches[l]} for l in layouts}
+
     def time_calls(fn, args_list, n, what):
         for i in range(5):
             _lib.check(fn(*args_list[i % len(args_list)]), what)
@@ -528,19 +615,71 @@ def main() -> int:
             hev.record(ev[i][1], sh)
         torch.cuda.synchronize()
         _lib.check(s_, what)
-        return sum(hev.ms(a, b) for a, b in ev) / n
+        return [hev.ms(a, b) for a, b in ev]
 
-    sps = B.btq_select_outliers_per_shard(rmin, rmax, k)
-    cps_args = [(p(xs[r]), P, T, H, k, p(sps["enc"]), p(sps["outlier_idx"]), p(sps["cmap"]),
-                 p(pks[r]), pitch, p(ols[r]), sh) for r in range(R)]
-    dps_args = [(p(pks[(r - 2) % R]), pitch, p(ols[(r - 2) % R]), P, T, H, k, p(sps["scale"]),
-                 p(sps["zero_point"]), p(sps["fmap"]), p(ys[r]), sh) for r in range(R)]
-    for r in range(R):
-        _lib.check(lib.btq_compress_pack_per_shard(*cps_args[r]), "per-shard sender")
-    cps_mean = time_calls(lib.btq_compress_pack_per_shard, cps_args, n16, "per-shard sender")
-    dps_mean = time_calls(lib.btq_decompress_reduce_per_shard, dps_args, n16,
-                          "per-shard receiver")
-    cps_bytes, dps_bytes = algorithmic_bytes_per_shard(P, T, H, k)
+    graph_ms = None
+    if not args.no_extras:
+        compress, decompress, comp_args, deco_args = head["calls"]
+        # Timed region 3 (reported beside value, not value): G steps of the
+        # rotation captured in a HIP graph on a side stream (default priority)
+        # and replayed. The kernels clear nothing with memset, so the graph holds
+        # kernel nodes only.
+        G = min(R, 512)
+        gs = torch.cuda.Stream(device=dev)
+        g_comp = [a[:-1] + (gs.cuda_stream,) for a in comp_args[:G]]
+        g_deco = [a[:-1] + (gs.cuda_stream,) for a in deco_args[:G]]
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        st = 0
+        with torch.cuda.graph(graph, stream=gs):
+            for r in range(G):
+                st |= compress(*g_comp[r])
+                st |= decompress(*g_deco[r])
+        _lib.check(st, "graph capture")
+        graph.replay()
+        torch.cuda.synchronize()
+        n_rep = max(1, args.steps // G)
+        t2 = time.perf_counter()
+        for _ in range(n_rep):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t2) / (n_rep * G) * 1e3
+        del graph
+
+        n16 = max(20, min(args.steps, 200))
+        pitch = pitches[layouts[0]]
+        msg_of = lambda r: p(msg[(r - 2) % R])
+        # The bf16-output receiver (not part of a step: the step's receiver
+        # writes fp32), on the headline layout.
+        y16 = [torch.empty((T, H), dtype=torch.int16, device=dev) for _ in range(2)]
+        d16_args = [(msg_of(r), pitch, p(ols[(r - 2) % R]), P, T, H, k, sc, zp, fm, SHARED,
+                     p(y16[r % 2]), _lib.BTQ_Y_BF16, sh) for r in range(R)]
+        d16 = time_calls(lib.btq_decompress_reduce_ex, d16_args, n16, "bf16-output receiver")
+        kernels["decompress_reduce_bf16"] = kernel_entry(
+            d16, algorithmic_bytes(P, T, H, k, y_bytes=2)[1])
+        kernels["decompress_reduce_bf16"]["note"] = ("bf16 output (one rounding of the fp32 sum); "
+                                                     "timed separately, not part of value")
+        del y16
+        # Per-shard BF16 sets (every shard keeps its own k features), in the
+        # same rotation: another selection reading, not part of a step.
+        sps = B.btq_select_outliers_per_shard(rmin, rmax, k)
+        PER = _lib.BTQ_SETS_PER_SHARD
+        cps_args = [(p(xs[r]), P, T, H, k, p(sps["rscale"]), p(sps["zero_point"]),
+                     p(sps["outlier_idx"]), p(sps["cmap"]), PER, p(msg[r]), pitch, p(ols[r]), sh)
+                    for r in range(R)]
+        dps_args = [(msg_of(r), pitch, p(ols[(r - 2) % R]), P, T, H, k, p(sps["scale"]),
+                     p(sps["zero_point"]), p(sps["fmap"]), PER, p(ys[r]), F32, sh)
+                    for r in range(R)]
+        for r in range(R):
+            _lib.check(lib.btq_compress_pack_ex(*cps_args[r]), "per-shard sender")
+        cps_bytes, dps_bytes = algorithmic_bytes_per_shard(P, T, H, k)
+        kernels["compress_pack_per_shard"] = kernel_entry(
+            time_calls(lib.btq_compress_pack_ex, cps_args, n16, "per-shard sender"), cps_bytes)
+        kernels["decompress_reduce_per_shard"] = kernel_entry(
+            time_calls(lib.btq_decompress_reduce_ex, dps_args, n16, "per-shard receiver"),
+            dps_bytes)
+        for key in ("compress_pack_per_shard", "decompress_reduce_per_shard"):
+            kernels[key]["note"] = "one BF16 set per shard; timed separately, not part of value"
 
     copy_probe = None
     if args.copy_probe_mib:
@@ -555,14 +694,11 @@ def main() -> int:
             dst.copy_(src)
         hev.record(c1, sh)
         torch.cuda.synchronize()
-        copy_probe = {"bytes_per_copy": 2 * n, "GBps": round(5 * 2 * n / (hev.ms(c0, c1) * 1e-3) / 1e9, 1)}
+        copy_probe = {"bytes_per_copy": 2 * n,
+                      "GBps": round(5 * 2 * n / (hev.ms(c0, c1) * 1e-3) / 1e9, 1)}
         del src, dst
 
-    bf16_bytes = P * T * H * 2
-    comp_bytes, deco_bytes = algorithmic_bytes(P, T, H, k)
-    value = args.steps * bf16_bytes / wall / 1e9
-    achieved = comp_bytes / (comp_mean * 1e-3) / 1e9
-    traffic = read_traffic(w.name) if (T == w.T[0] and k == w.k) else None
+    traffic = read_traffic(w.name, k) if (T == w.T[0] and layouts[0] == "padded") else None
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -570,7 +706,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "ms_per_step": round(head["wall"] / args.steps * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -578,58 +714,34 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "P": P, "T": T, "H": H, "k": k,
                    "input": "bf16 partial sums", "message": "int4 packed + bf16 outlier block",
+                   "layout": layouts[0], "packed_pitch": pitches[layouts[0]],
                    "output": "fp32", "rotating_sets": R},
         "roofline": {"bound": "hbm", "kernel": "compress_pack", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes": comp_bytes},
-        "kernels": {
-            "compress_pack": {"mean_us": round(comp_mean * 1e3, 2), "median_us": round(med(comp_ms) * 1e3, 2),
-                              "algorithmic_bytes": comp_bytes,
-                              "hbm_GBps": round(comp_bytes / (comp_mean * 1e-3) / 1e9, 1),
-                              "bf16_equiv_GBps": round(bf16_bytes / (comp_mean * 1e-3) / 1e9, 1)},
-            "decompress_reduce": {"mean_us": round(deco_mean * 1e3, 2), "median_us": round(med(deco_ms) * 1e3, 2),
-                                  "algorithmic_bytes": deco_bytes,
-                                  "hbm_GBps": round(deco_bytes / (deco_mean * 1e-3) / 1e9, 1),
-                                  "frac": round(deco_bytes / (deco_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                                  "bf16_equiv_GBps": round(bf16_bytes / (deco_mean * 1e-3) / 1e9, 1)},
-            "kernel_sum_bf16_equiv_GBps": round(bf16_bytes / ((comp_mean + deco_mean) * 1e-3) / 1e9, 1),
-            "decompress_reduce_bf16": {"mean_us": round(d16_mean * 1e3, 2), "algorithmic_bytes": d16_bytes,
-                                       "hbm_GBps": round(d16_bytes / (d16_mean * 1e-3) / 1e9, 1),
-                                       "frac": round(d16_bytes / (d16_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                                       "note": "bf16 output (one rounding of the fp32 sum); "
-                                               "timed separately, not part of value"},
-            "compress_pack_per_shard": {
-                "mean_us": round(cps_mean * 1e3, 2), "algorithmic_bytes": cps_bytes,
-                "hbm_GBps": round(cps_bytes / (cps_mean * 1e-3) / 1e9, 1),
-                "frac": round(cps_bytes / (cps_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                "note": "one BF16 set per shard; timed separately, not part of value"},
-            "decompress_reduce_per_shard": {
-                "mean_us": round(dps_mean * 1e3, 2), "algorithmic_bytes": dps_bytes,
-                "hbm_GBps": round(dps_bytes / (dps_mean * 1e-3) / 1e9, 1),
-                "frac": round(dps_bytes / (dps_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                "note": "one BF16 set per shard; timed separately, not part of value"},
-        },
+        "layouts": layout_rates,
+        "kernels": kernels,
         "timing": {"value": f"{args.steps} steps with no instrumentation between launches",
                    "kernels": f"the same {args.steps} steps again with HIP events around every "
                               "launch on the launch stream (fence-free events)",
-                   "ms_per_step_instrumented": round(wall_ev / args.steps * 1e3, 5),
-                   "graph": f"{min(R, 512)} steps of the rotation captured in a HIP graph, "
-                            f"replayed {max(1, args.steps // min(R, 512))} times",
-                   "graph_ms_per_step": round(graph_ms, 5),
-                   "graph_GBps": round(bf16_bytes / (graph_ms * 1e-3) / 1e9, 2)},
+                   "ms_per_step_instrumented": round(head["wall_ev"] / args.steps * 1e3, 5)},
         "offline": {"calib_batches": w.calib_batches, "calib_ms_total": round(calib_ms, 3),
                     "calib_GBps": round(w.calib_batches * P * w.calib_T * H * 2 / (calib_ms * 1e-3) / 1e9, 1),
                     "select_us": round(select_ms * 1e3, 2)},
     }
+    if graph_ms is not None:
+        out["timing"]["graph"] = (f"{min(R, 512)} steps of the rotation captured in a HIP graph, "
+                                  f"replayed {max(1, args.steps // min(R, 512))} times")
+        out["timing"]["graph_ms_per_step"] = round(graph_ms, 5)
+        out["timing"]["graph_GBps"] = round(bf16_bytes / (graph_ms * 1e-3) / 1e9, 2)
     if copy_probe:
         out["copy_probe"] = copy_probe
         # the same kernel against what a plain device copy (read + write)
         # reaches on this GPU
         out["roofline"]["copy_GBps"] = copy_probe["GBps"]
         out["roofline"]["frac_of_copy"] = round(achieved / copy_probe["GBps"], 4)
-    if not args.no_cpu_baseline:
-        log(f"timing the CPU oracle for >= {args.cpu_seconds:.0f} s")
-        out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_sample_T, T), args.cpu_seconds)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     hev.close()
     print(json.dumps(out), flush=True)
     return 0

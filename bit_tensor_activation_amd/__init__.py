@@ -8,12 +8,12 @@ from .api import (  # noqa: F401
     btq_calib_update,
     btq_calib_workspace_bytes,
     btq_compress_pack,
+    btq_compress_pack_ex,
     btq_compress_pack_per_shard,
-    btq_dec_table_floats,
     btq_decompress_reduce,
     btq_decompress_reduce_bf16,
+    btq_decompress_reduce_ex,
     btq_decompress_reduce_per_shard,
-    btq_enc_table_floats,
     btq_packed_pitch,
     btq_packed_row_bytes,
     btq_select_features,

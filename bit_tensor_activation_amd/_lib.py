@@ -18,25 +18,24 @@ _P, _I64, _I, _F, _SZ = _c.c_void_p, _c.c_int64, _c.c_int, _c.c_float, _c.c_size
 SIGNATURES = {
     "btq_calib_update": (_I, [_P, _I64, _I64, _I64, _F, _I, _P, _P, _P, _SZ, _P]),
     "btq_calib_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
-    "btq_select_outliers": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                 _SZ, _P]),
-    "btq_select_outliers_rule": (_I, [_P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P,
-                                      _P, _P, _SZ, _P]),
-    "btq_select_workspace_bytes": (_SZ, [_I64, _I64]),
-    "btq_select_outliers_per_shard": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P,
-                                           _P, _SZ, _P]),
-    "btq_compress_pack_per_shard": (_I, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _P,
-                                         _P]),
-    "btq_decompress_reduce_per_shard": (_I, [_P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, _P,
-                                             _P, _P]),
-    "btq_select_features": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                 _P]),
-    "btq_enc_table_floats": (_I64, [_I64, _I64, _I64]),
-    "btq_dec_table_floats": (_I64, [_I64, _I64, _I64]),
-    "btq_compress_pack": (_I, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _P, _P]),
-    "btq_decompress_reduce": (_I, [_P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
-    "btq_decompress_reduce_bf16": (_I, [_P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "btq_select_outliers": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "btq_select_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "btq_compress_pack": (_I, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "btq_decompress_reduce": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "btq_packed_row_bytes": (_I64, [_I64, _I64]),
+    "btq_decompress_reduce_bf16": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "btq_select_outliers_rule": (_I, [_P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P,
+                                      _SZ, _P]),
+    "btq_select_features": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "btq_select_outliers_per_shard": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P,
+                                           _SZ, _P]),
+    "btq_compress_pack_per_shard": (_I, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "btq_decompress_reduce_per_shard": (_I, [_P, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P,
+                                             _P]),
+    "btq_compress_pack_ex": (_I, [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _I, _P, _I64, _P,
+                                  _P]),
+    "btq_decompress_reduce_ex": (_I, [_P, _I64, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _I, _P,
+                                      _I, _P]),
     "btq_packed_pitch": (_I64, [_I64, _I64]),
     "btq_status_str": (_c.c_char_p, [_I]),
     "btq_version": (_c.c_char_p, []),
@@ -51,6 +50,12 @@ BTQ_ERR_HIP = -5
 
 BTQ_SCORE_SUM = 0
 BTQ_SCORE_MAX = 1
+
+BTQ_SETS_SHARED = 0
+BTQ_SETS_PER_SHARD = 1
+
+BTQ_Y_F32 = 0
+BTQ_Y_BF16 = 1
 
 _lock = threading.Lock()
 _lib = None

@@ -134,34 +134,32 @@ hipError_t launch_calib(const uint16_t* x, int64_t P, int64_t T, int64_t H, floa
 
 hipError_t launch_select(const float* run_min, const float* run_max, int64_t P, int64_t H,
                          int64_t k, float* scale, float* rscale, uint8_t* zp, int32_t* idx,
-                         int32_t* fmap, int32_t* cmap, float* enc, float* dec, float* ws_score,
-                         bool score_max, hipStream_t s);
-// One BF16 set per shard: idx [P,k], fmap [P,H], cmap [P,H-k], enc [P,H-k,2];
-// ws_width holds P*H floats.
+                         int32_t* fmap, int32_t* cmap, float* ws_score, bool score_max,
+                         hipStream_t s);
+// One BF16 set per shard: idx [P,k], fmap [P,H], cmap [P,H-k]; ws_width
+// holds P*H floats.
 hipError_t launch_select_per_shard(const float* run_min, const float* run_max, int64_t P,
                                    int64_t H, int64_t k, float* scale, float* rscale, uint8_t* zp,
-                                   int32_t* idx, int32_t* fmap, int32_t* cmap, float* enc,
-                                   float* ws_width, hipStream_t s);
+                                   int32_t* idx, int32_t* fmap, int32_t* cmap, float* ws_width,
+                                   hipStream_t s);
 // The same outputs for a given BF16 set: idx is a device copy of k distinct
 // features in ascending order.
 hipError_t launch_select_set(const float* run_min, const float* run_max, int64_t P, int64_t H,
                              int64_t k, float* scale, float* rscale, uint8_t* zp,
-                             const int32_t* idx, int32_t* fmap, int32_t* cmap, float* enc,
-                             float* dec, hipStream_t s);
+                             const int32_t* idx, int32_t* fmap, int32_t* cmap, hipStream_t s);
 
-// per_shard: idx [P,k] and cmap [P,H-k] hold one set per shard.
+// rscale [P,H], zp [P,H]; per_shard: idx [P,k] and cmap [P,H-k] hold one
+// set per shard, else idx [k] and cmap [H-k].
 hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
-                           const float* enc, const int32_t* idx, const int32_t* cmap,
-                           uint8_t* packed, int64_t pitch, uint16_t* outl, bool per_shard,
-                           hipStream_t s);
+                           const float* rscale, const uint8_t* zp, const int32_t* idx,
+                           const int32_t* cmap, uint8_t* packed, int64_t pitch, uint16_t* outl,
+                           bool per_shard, hipStream_t s);
 
+// scale [P,H], zp [P,H]; fmap [P,H] when per_shard, else [H]. y is fp32,
+// or bf16 bits when bf16.
 hipError_t launch_decompress(const uint8_t* packed, int64_t pitch, const uint16_t* outl, int64_t P,
-                             int64_t T, int64_t H, int64_t k, const float* dec, const int32_t* idx,
-                             const int32_t* cmap, void* y, bool bf16, hipStream_t s);
-// Receiver of per-shard sets: scale [P,H], zp [P,H] and fmap [P,H] by feature.
-hipError_t launch_decompress_sets(const uint8_t* packed, int64_t pitch, const uint16_t* outl,
-                                  int64_t P, int64_t T, int64_t H, int64_t k, const float* scale,
-                                  const uint8_t* zp, const int32_t* fmap, float* y,
-                                  hipStream_t s);
+                             int64_t T, int64_t H, int64_t k, const float* scale,
+                             const uint8_t* zp, const int32_t* fmap, bool per_shard, void* y,
+                             bool bf16, hipStream_t s);
 
 }  // namespace btq

@@ -18,11 +18,13 @@
 // one shard's block of token rows, one wave per tile, so the block reads
 // about 4 KB of each row in one go. All blocks of a row block run on one XCD
 // (xcd_unit_block).
-//  0. Setup, once per wave: the lane's 8 feature indices, its 8 (rscale,
-//     zero point) pairs from the encoder table (64 contiguous bytes, in slot
-//     order) and its BF16 feature index. Then the first kRing token rows are
-//     issued, and only then does the wave wait for the setup values. No LDS
-//     staging of parameters and no block barrier.
+//  0. Setup, once per wave: the lane's 8 feature indices, its BF16 feature
+//     index, and the shard's rscale and zero points over the tile's feature
+//     span (contiguous 16- and 8-byte loads). Then the first kRing token rows
+//     are issued, and only then does the wave wait for the setup values: the
+//     span's parameters go through the wave's LDS buffer, where each lane
+//     picks its 8 features' (rscale, zero point), before the buffer serves
+//     the rows. No block barrier.
 //  1. Each ring row arrives as one 16-byte load per lane (the span's first
 //     64 chunks) plus a narrow tail load for the chunks past 64 (BF16
 //     features and alignment slack). kSub rows at a time are staged in a
@@ -66,20 +68,56 @@ __device__ __forceinline__ uint32_t quant4(uint32_t bits16, float r, float z) {
   return (uint32_t)q;
 }
 
-// The lane's 8 slot parameters from the encoder table [P, Hq, 2]: `re` spans
-// the tile's slots of one shard. Lanes past the tile read zeros.
-__device__ __forceinline__ void load_enc(rsrc_t re, bool active, int lane, float rs[8],
-                                         float zf[8]) {
-  const uint32_t o = active ? (uint32_t)lane * 64u : kOOB;
+// Per-feature parameters of one shard over a tile's feature span
+// [a0, a0 + 8*nch): rscale as 16-byte chunks of 4 floats, zero points as
+// 8-byte chunks of 8 bytes. kR, kZ: chunks per lane that cover the widest
+// span the kernel takes. A chunk past the span loads out of range (zeros).
+template <int kR, int kZ>
+struct SpanParams {
+  v4u r[kR];
+  uint64_t z[kZ];
+
+  __device__ __forceinline__ void load(const float* rscale, const uint8_t* zp, int nch,
+                                       int lane) {
+    const rsrc_t rr = make_rsrc(rscale, (uint32_t)nch * 32u);
+    const rsrc_t rz = make_rsrc(zp, (uint32_t)nch * 8u);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const v4u t = __builtin_amdgcn_raw_buffer_load_b128(re, o + 16u * m, 0, 0);
-    rs[2 * m] = __uint_as_float(t[0]);
-    zf[2 * m] = __uint_as_float(t[1]);
-    rs[2 * m + 1] = __uint_as_float(t[2]);
-    zf[2 * m + 1] = __uint_as_float(t[3]);
+    for (int m = 0; m < kR; ++m)
+      r[m] = __builtin_amdgcn_raw_buffer_load_b128(rr, (uint32_t)(lane + kWave * m) * 16u, 0, 0);
+#pragma unroll
+    for (int m = 0; m < kZ; ++m) {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b64(rz, (uint32_t)(lane + kWave * m) * 8u,
+                                                          0, 0);
+      z[m] = (uint64_t)t[0] | ((uint64_t)t[1] << 32);
+    }
   }
-}
+
+  // Writes the span to LDS (rscale floats at byte 0, zero-point bytes at
+  // byte 32*nch; 40*nch bytes in all), then reads the lane's 8 features
+  // hh[e] (each in the span) back as (rscale, zero point as a float).
+  __device__ __forceinline__ void pick(char* buf, int nch, int lane, int a0, const int hh[8],
+                                       float rs[8], float zf[8]) const {
+#pragma unroll
+    for (int m = 0; m < kR; ++m) {
+      const int c = lane + kWave * m;
+      if (c < 2 * nch) *reinterpret_cast<v4u*>(buf + 16 * c) = r[m];
+    }
+#pragma unroll
+    for (int m = 0; m < kZ; ++m) {
+      const int c = lane + kWave * m;
+      if (c < nch) *reinterpret_cast<uint64_t*>(buf + 32 * nch + 8 * c) = z[m];
+    }
+    wave_lds_sync();
+    const float* pf = reinterpret_cast<const float*>(buf);
+    const uint8_t* pb = reinterpret_cast<const uint8_t*>(buf + 32 * nch);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      rs[e] = pf[hh[e] - a0];
+      zf[e] = (float)pb[hh[e] - a0];
+    }
+    wave_lds_sync();   // the buffer serves the token rows next
+  }
+};
 
 // Staged kernel. LDS: 4 waves x kCpRows staging buffers of buf_bytes.
 // kPs: idx [P,k] and cmap [P,Hq] hold one BF16 set per shard.
@@ -87,7 +125,7 @@ template <int kMaxChunks, bool kPs>
 __global__ __launch_bounds__(256) void compress_kernel(
     const uint16_t* __restrict__ x, int64_t T, int H, int Hq, int k, int ntiles,
     int rows_per_wave, int64_t nrowblk, int64_t ngroups, int buf_bytes,
-    int64_t P, const float* __restrict__ enc,
+    int64_t P, const float* __restrict__ rscale, const uint8_t* __restrict__ zp,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cmap,
     uint8_t* __restrict__ packed, int pitch, uint16_t* __restrict__ outl) {
   extern __shared__ __align__(16) char smem[];
@@ -153,12 +191,14 @@ __global__ __launch_bounds__(256) void compress_kernel(
   const int jj = active ? j0 : g.jstart;
   const v4u hA = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)jj * 4u, 0, 0);
   const v4u hB = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)jj * 4u + 16u, 0, 0);
-  float rs[8], zf[8];
-  load_enc(make_rsrc(enc + (p * Hq + g.jstart) * 2, (uint32_t)(g.jend - g.jstart) * 8u), active,
-           lane, rs, zf);
+  // the shard's parameters over the span (at most 4*kWave chunks of 8 features)
+  SpanParams<8, 4> sp;
+  sp.load(rscale + p * H + a0, zp + p * H + a0, nch, lane);
   load_rows(0);
   const int hh[8] = {(int)hA[0], (int)hA[1], (int)hA[2], (int)hA[3],
                      (int)hB[0], (int)hB[1], (int)hB[2], (int)hB[3]};
+  float rs[8], zf[8];
+  sp.pick(buf, nch, lane, a0, hh, rs, zf);   // (kCpRows*buf_bytes >= 40*nch)
   uint32_t ad[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) ad[e] = pad_byte_off((uint32_t)(hh[e] - a0));
@@ -242,9 +282,9 @@ template <int kRemDw, int kR, bool kPs>
 __global__ __launch_bounds__(256) void compress_ring_kernel(
     const uint16_t* __restrict__ x, int64_t T, int H, int Hq, int k, int ntiles,
     int rows_per_wave, int64_t nrowblk, int ntgrp, int64_t P,
-    const float* __restrict__ enc, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ cmap, uint8_t* __restrict__ packed, int pitch,
-    uint16_t* __restrict__ outl) {
+    const float* __restrict__ rscale, const uint8_t* __restrict__ zp,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ cmap,
+    uint8_t* __restrict__ packed, int pitch, uint16_t* __restrict__ outl) {
   constexpr int buf_bytes = ring_row_bytes<kRemDw>();
   extern __shared__ __align__(16) char smem[];
   // unit = (shard, row block); its ntgrp blocks of 4 adjacent tiles run on
@@ -319,10 +359,11 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
   const rsrc_t ri_ = make_rsrc(idx, (uint32_t)k * 4u);
   const uint32_t oh = __builtin_amdgcn_raw_buffer_load_b32(
       ri_, (g.nout > 0) ? (uint32_t)(g.ilo + min(lane, g.nout - 1)) * 4u : kOOB, 0, 0);
-  // (b) the lane's 8 slot parameters (4 x 16 contiguous bytes)
-  float rs[8], zf[8];
-  load_enc(make_rsrc(enc + (p * Hq + g.jstart) * 2, (uint32_t)(g.jend - g.jstart) * 8u), active,
-           lane, rs, zf);
+  // (b) the shard's parameters over the span: its nch <= 64 + 16*kRemDw
+  // chunks of 8 features take 2*nch rscale and nch zero-point chunks
+  constexpr int kNchMax = kWave + 16 * kRemDw;
+  SpanParams<(2 * kNchMax + kWave - 1) / kWave, (kNchMax + kWave - 1) / kWave> sp;
+  sp.load(rscale + p * H + a0, zp + p * H + a0, nch, lane);
   // (c) the ring: the first kR rows. Unconditional: a branch around it
   // would make the compiler assume at the join that these loads might not
   // exist, and wait for the ring when it waits for the setup loads.
@@ -337,6 +378,10 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
 
   const int hh[8] = {(int)hA[0], (int)hA[1], (int)hA[2], (int)hA[3],
                      (int)hB[0], (int)hB[1], (int)hB[2], (int)hB[3]};
+  // the lane's 8 (rscale, zero point) pairs, through the staging buffer
+  // (kSub*buf_bytes = 40*kNchMax bytes: it holds any span's parameters)
+  float rs[8], zf[8];
+  sp.pick(buf, nch, lane, a0, hh, rs, zf);
   uint32_t ad[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -420,7 +465,8 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
 template <bool kPs>
 __global__ __launch_bounds__(256) void compress_general_kernel(
     const uint16_t* __restrict__ x, int64_t P, int64_t T, int64_t H, int64_t k, int64_t Hq,
-    int64_t Bq, const float* __restrict__ enc, const int32_t* __restrict__ idx,
+    int64_t Bq, const float* __restrict__ rscale, const uint8_t* __restrict__ zp,
+    const int32_t* __restrict__ idx,
     const int32_t* __restrict__ cmap, uint8_t* __restrict__ packed, int64_t pitch,
     uint16_t* __restrict__ outl) {
   const int64_t n1 = P * T * pitch;
@@ -433,10 +479,13 @@ __global__ __launch_bounds__(256) void compress_general_kernel(
       const int64_t j = 2 * byte;
       uint32_t q = 0;   // padding bytes past the codes stay zero
       if (byte < Bq) {
-        const float* e = enc + (p * Hq + j) * 2;   // (rscale, zero point) of slot j
         const int32_t* cm = cmap + (kPs ? p * Hq : 0);
-        q = quant4(x[row * H + cm[j]], e[0], e[1]);
-        if (j + 1 < Hq) q |= quant4(x[row * H + cm[j + 1]], e[2], e[3]) << 4;
+        const int64_t h0 = cm[j];
+        q = quant4(x[row * H + h0], rscale[p * H + h0], (float)zp[p * H + h0]);
+        if (j + 1 < Hq) {
+          const int64_t h1 = cm[j + 1];
+          q |= quant4(x[row * H + h1], rscale[p * H + h1], (float)zp[p * H + h1]) << 4;
+        }
       }
       packed[i] = (uint8_t)q;
     } else {
@@ -459,7 +508,8 @@ static int pick_rows_per_wave(int64_t tile_waves, int64_t T) {
 
 template <bool kPs>
 static hipError_t launch_compress_t(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
-                                    const float* enc, const int32_t* idx, const int32_t* cmap,
+                                    const float* rscale, const uint8_t* zp, const int32_t* idx,
+                                    const int32_t* cmap,
                                     uint8_t* packed, int64_t pitch, uint16_t* outl,
                                     hipStream_t s) {
   const int64_t Hq = H - k;
@@ -475,7 +525,8 @@ static hipError_t launch_compress_t(const uint16_t* x, int64_t P, int64_t T, int
   // H < 2^24 keeps them below 2^31 bytes.
   const bool fast = Hq > 0 && H % 8 == 0 && Hq % 8 == 0 && H < (int64_t(1) << 24) &&
                     (uintptr_t)x % 16 == 0 && (uintptr_t)packed % 4 == 0 &&
-                    (uintptr_t)enc % 16 == 0 && nch_max <= 4 * kWave && lds <= 65536 &&
+                    (uintptr_t)rscale % 4 == 0 && (uintptr_t)zp % 4 == 0 &&
+                    nch_max <= 4 * kWave && lds <= 65536 &&
                     // the pitch: dword stores, and the lanes of the last
                     // tile reach every padding byte
                     pitch % 4 == 0 && pitch <= ntiles64 * (kTileSlots / 2);
@@ -503,8 +554,8 @@ static hipError_t launch_compress_t(const uint16_t* x, int64_t P, int64_t T, int
     const unsigned blocks = (unsigned)xcd_grid(ntgrp, P * nrowblk);
 #define BTQ_RING(n, r)                                                                    \
   compress_ring_kernel<n, r, kPs><<<blocks, 256, ring_lds, s>>>(                           \
-      x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, ntgrp, P, enc, idx, cmap, packed,  \
-      (int)pitch, outl)
+      x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, ntgrp, P, rscale, zp, idx, cmap,   \
+      packed, (int)pitch, outl)
 #define BTQ_RING_R(n) \
   if (ring == kRing) BTQ_RING(n, kRing); else BTQ_RING(n, kRingSmall);
     switch (rem_dw) {
@@ -525,30 +576,31 @@ static hipError_t launch_compress_t(const uint16_t* x, int64_t P, int64_t T, int
     const int64_t blocks = xcd_grid(ntiles, P * ngroups);
     if (nch_max <= 2 * kWave)
       compress_kernel<2, kPs><<<(unsigned)blocks, 256, lds, s>>>(
-          x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, ngroups, buf_bytes, P, enc, idx,
-          cmap, packed, (int)pitch, outl);
+          x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, ngroups, buf_bytes, P, rscale,
+          zp, idx, cmap, packed, (int)pitch, outl);
     else
       compress_kernel<4, kPs><<<(unsigned)blocks, 256, lds, s>>>(
-          x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, ngroups, buf_bytes, P, enc, idx,
-          cmap, packed, (int)pitch, outl);
+          x, T, (int)H, (int)Hq, (int)k, ntiles, rpw, nrowblk, ngroups, buf_bytes, P, rscale,
+          zp, idx, cmap, packed, (int)pitch, outl);
     return hipGetLastError();
   }
   const int64_t n = P * T * (pitch + k);
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  compress_general_kernel<kPs><<<(unsigned)blocks, 256, 0, s>>>(x, P, T, H, k, Hq, Bq, enc, idx,
-                                                                cmap, packed, pitch, outl);
+  compress_general_kernel<kPs><<<(unsigned)blocks, 256, 0, s>>>(x, P, T, H, k, Hq, Bq, rscale, zp,
+                                                                idx, cmap, packed, pitch, outl);
   return hipGetLastError();
 }
 
 hipError_t launch_compress(const uint16_t* x, int64_t P, int64_t T, int64_t H, int64_t k,
-                           const float* enc, const int32_t* idx, const int32_t* cmap,
-                           uint8_t* packed, int64_t pitch, uint16_t* outl, bool per_shard,
-                           hipStream_t s) {
-  return per_shard
-             ? launch_compress_t<true>(x, P, T, H, k, enc, idx, cmap, packed, pitch, outl, s)
-             : launch_compress_t<false>(x, P, T, H, k, enc, idx, cmap, packed, pitch, outl, s);
+                           const float* rscale, const uint8_t* zp, const int32_t* idx,
+                           const int32_t* cmap, uint8_t* packed, int64_t pitch, uint16_t* outl,
+                           bool per_shard, hipStream_t s) {
+  return per_shard ? launch_compress_t<true>(x, P, T, H, k, rscale, zp, idx, cmap, packed, pitch,
+                                             outl, s)
+                   : launch_compress_t<false>(x, P, T, H, k, rscale, zp, idx, cmap, packed, pitch,
+                                              outl, s);
 }
 
 }  // namespace btq

@@ -14,14 +14,11 @@
 // histograms. The keys are unique, so the selected set is exactly
 // {key >= k-th key}, with ties in score going to the lower h. A ballot +
 // popcount scan over h in ascending order then writes idx, fmap and cmap.
-// Last, codec_tables_kernel (one thread per int4 slot) copies each slot's
-// parameters into the encoder and decoder tables in slot order, the order
-// in which the hot kernels consume them.
 //
 // Variants of the ranking (other readings of how per-device ranges rank
 // features): the score may be the widest shard's range instead of the sum;
 // one set per shard runs the top-k block once per shard on that shard's
-// widths (grid P) and shard_enc_kernel builds its sender table; and a set
+// widths (grid P); and a set
 // given by the caller skips the ranking, with set_maps_kernel finding
 // membership by binary search and sharing the ordered compaction.
 #include <float.h>
@@ -184,98 +181,41 @@ __global__ __launch_bounds__(kSelThreads) void set_maps_kernel(const int32_t* __
       H, k, nullptr, fmap, cmap, wave_cnt);
 }
 
-// enc[p, j] = (rscale, zero point) and dec[p, j] = scale, dec[P+p, j] = zero
-// point of feature cmap[j] on shard p; dec[2P, j] = -sum_p z*s, one fp32
-// product and one fp32 subtraction per shard, in shard order from +0.
-__global__ __launch_bounds__(256) void codec_tables_kernel(
-    const float* __restrict__ scale, const float* __restrict__ rscale,
-    const uint8_t* __restrict__ zp, const int32_t* __restrict__ cmap, int64_t P, int64_t H,
-    int64_t Hq, float* __restrict__ enc, float* __restrict__ dec) {
-  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= Hq) return;
-  const int64_t h = cmap[j];
-  float b = 0.0f;
-  for (int64_t p = 0; p < P; ++p) {
-    const float sv = scale[p * H + h];
-    const float z = (float)zp[p * H + h];
-    enc[(p * Hq + j) * 2] = rscale[p * H + h];
-    enc[(p * Hq + j) * 2 + 1] = z;
-    dec[p * Hq + j] = sv;
-    dec[(P + p) * Hq + j] = z;
-    b = __fsub_rn(b, __fmul_rn(z, sv));
-  }
-  dec[2 * P * Hq + j] = b;
-}
-
 hipError_t launch_select(const float* run_min, const float* run_max, int64_t P, int64_t H,
                          int64_t k, float* scale, float* rscale, uint8_t* zp, int32_t* idx,
-                         int32_t* fmap, int32_t* cmap, float* enc, float* dec, float* ws_score,
-                         bool score_max, hipStream_t s) {
+                         int32_t* fmap, int32_t* cmap, float* ws_score, bool score_max,
+                         hipStream_t s) {
   qparams_kernel<<<(unsigned)((H + 255) / 256), 256, 0, s>>>(run_min, run_max, P, H, scale,
                                                               rscale, zp, ws_score, score_max,
                                                               nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   topk_maps_kernel<<<1, kSelThreads, 0, s>>>(ws_score, H, k, idx, fmap, cmap);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t Hq = H - k;
-  if (Hq == 0) return hipSuccess;
-  codec_tables_kernel<<<(unsigned)((Hq + 255) / 256), 256, 0, s>>>(scale, rscale, zp, cmap, P, H,
-                                                                    Hq, enc, dec);
   return hipGetLastError();
-}
-
-// Sender table of per-shard sets: enc[p, j] = (rscale, zero point) of
-// feature cmap[p, j] on shard p.
-__global__ __launch_bounds__(256) void shard_enc_kernel(const float* __restrict__ rscale,
-                                                        const uint8_t* __restrict__ zp,
-                                                        const int32_t* __restrict__ cmap,
-                                                        int64_t P, int64_t H, int64_t Hq,
-                                                        float* __restrict__ enc) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // p * Hq + j
-  if (i >= P * Hq) return;
-  const int64_t p = i / Hq;
-  const int64_t h = cmap[i];
-  enc[2 * i] = rscale[p * H + h];
-  enc[2 * i + 1] = (float)zp[p * H + h];
 }
 
 hipError_t launch_select_per_shard(const float* run_min, const float* run_max, int64_t P,
                                    int64_t H, int64_t k, float* scale, float* rscale, uint8_t* zp,
-                                   int32_t* idx, int32_t* fmap, int32_t* cmap, float* enc,
-                                   float* ws_width, hipStream_t s) {
+                                   int32_t* idx, int32_t* fmap, int32_t* cmap, float* ws_width,
+                                   hipStream_t s) {
   qparams_kernel<<<(unsigned)((H + 255) / 256), 256, 0, s>>>(run_min, run_max, P, H, scale,
                                                               rscale, zp, nullptr, false,
                                                               ws_width);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   topk_maps_kernel<<<(unsigned)P, kSelThreads, 0, s>>>(ws_width, H, k, idx, fmap, cmap);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t n = P * (H - k);
-  if (n == 0) return hipSuccess;
-  shard_enc_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(rscale, zp, cmap, P, H, H - k,
-                                                                enc);
   return hipGetLastError();
 }
 
 hipError_t launch_select_set(const float* run_min, const float* run_max, int64_t P, int64_t H,
                              int64_t k, float* scale, float* rscale, uint8_t* zp,
-                             const int32_t* idx, int32_t* fmap, int32_t* cmap, float* enc,
-                             float* dec, hipStream_t s) {
+                             const int32_t* idx, int32_t* fmap, int32_t* cmap, hipStream_t s) {
   qparams_kernel<<<(unsigned)((H + 255) / 256), 256, 0, s>>>(run_min, run_max, P, H, scale,
                                                               rscale, zp, nullptr, false,
                                                               nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   set_maps_kernel<<<1, kSelThreads, 0, s>>>(idx, H, k, fmap, cmap);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t Hq = H - k;
-  if (Hq == 0) return hipSuccess;
-  codec_tables_kernel<<<(unsigned)((Hq + 255) / 256), 256, 0, s>>>(scale, rscale, zp, cmap, P, H,
-                                                                    Hq, enc, dec);
   return hipGetLastError();
 }
 

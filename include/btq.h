@@ -16,18 +16,24 @@
  * Section "Combating Quantization Errors with Tensor Parallelism" places the
  * quantization on each device's partial sum, before the sum.
  *
- * One call per step. Here all P shards' partial sums sit in one GPU's HBM,
- * so the exchange between devices is the identity: the buffers written by
- * btq_compress_pack are the ones read by btq_decompress_reduce.
+ * Four calls follow those steps: btq_calib_update, btq_select_outliers,
+ * btq_compress_pack (the sender) and btq_decompress_reduce (the receiver).
+ * Here all P shards' partial sums sit in one GPU's HBM, so the exchange
+ * between devices is the identity: the buffers written by btq_compress_pack
+ * are the ones read by btq_decompress_reduce. The other calls widen the path:
+ * a bf16-output receiver, other readings of the selection step and a packed
+ * row pitch.
  *
  * Conventions shared by every call
  *  - Tensor pointers are DEVICE pointers (hipMalloc'd or from PyTorch) to
  *    caller-owned, contiguous, row-major memory with the last index fastest.
  *    The library never allocates, frees or keeps them.
  *  - bf16 values are raw 16-bit patterns (uint16_t).
- *  - A pointer must be aligned to its element type. Faster paths are taken
- *    when x/packed/outliers/y are 16-byte aligned and H, H-k are multiples
- *    of 8; every other layout runs on a slower general path.
+ *  - A pointer must be aligned to its element type (BTQ_ERR_ALIGN
+ *    otherwise). Fast kernels run when x, packed, outliers and y are 16-byte
+ *    aligned, the per-feature arrays 16-byte aligned, P <= 8 for the
+ *    receiver, and H and H-k are multiples of 8; every other layout runs on
+ *    a general kernel that is correct but much slower.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call checks its arguments on the host, enqueues its kernels on
  *    `stream` and returns. It does not synchronize, print, throw or abort.
@@ -43,6 +49,23 @@
  *    operation. Divisions are correctly rounded. Nothing is flushed to zero.
  *    Inputs must be finite; NaN and Inf give unspecified (but in-bounds)
  *    results.
+ *
+ * Layouts
+ *  x            bf16 [P,T,H]     partial sums, one [T,H] block per shard
+ *  run_min/max  fp32 [P,H]
+ *  scale        fp32 [P,H]       4-bit step of feature h on shard p
+ *  rscale       fp32 [P,H]       1/scale
+ *  zero_point   u8   [P,H]       0..15
+ *  outlier_idx  i32  [k]         BF16 features, ascending h
+ *  fmap         i32  [H]         fmap[h] = j (int4 slot j of h), or -1-i when
+ *                                h = outlier_idx[i]
+ *  cmap         i32  [H-k]       cmap[j] = h of int4 slot j, ascending
+ *  packed       u8   [P,T,Bq]    Bq = btq_packed_row_bytes(H,k) = ceil((H-k)/2);
+ *                                slot 2b in the low nibble of byte b, slot
+ *                                2b+1 in the high nibble; an odd H-k leaves
+ *                                the last high nibble 0
+ *  outliers     bf16 [P,T,k]     outliers[p,t,i] = x[p,t,outlier_idx[i]]
+ *  y            fp32 [T,H]       (bf16 [T,H] for the bf16-output receiver)
  */
 #ifndef BTQ_H
 #define BTQ_H
@@ -56,11 +79,11 @@ extern "C" {
 
 typedef enum {
   BTQ_OK = 0,
-  BTQ_ERR_ARG = -1,        /* null pointer, or momentum outside [0,1] / NaN    */
-  BTQ_ERR_SHAPE = -2,      /* P, T, H or k out of range                         */
+  BTQ_ERR_ARG = -1,        /* null pointer, or momentum outside [0,1) / NaN    */
+  BTQ_ERR_SHAPE = -2,      /* P, T, H, k or the pitch out of range              */
   BTQ_ERR_ALIGN = -3,      /* pointer not aligned to its element type           */
   BTQ_ERR_WORKSPACE = -4,  /* workspace smaller than the *_workspace_bytes size */
-  BTQ_ERR_HIP = -5         /* a kernel launch failed (hipGetLastError, cleared)  */
+  BTQ_ERR_HIP = -5         /* a HIP call failed (hipGetLastError, cleared)      */
 } btq_status;
 
 /*
@@ -72,7 +95,9 @@ typedef enum {
  *   otherwise        : run = fl(fl(a*run) + fl(c*batch)),  a = momentum,
  *                      c = fl(1 - a), all fp32 (moving average; the page
  *                      gives no formula -- the momentum weights the old value)
- *   x        bf16 [P,T,H]   in
+ *   x        bf16 [P,T,H]   in, T >= 1
+ *   momentum in [0,1): the weight of the running value (BTQ_ERR_ARG
+ *            otherwise, NaN included)
  *   run_min  fp32 [P,H]     in/out (ignored on input when first_batch != 0)
  *   run_max  fp32 [P,H]     in/out
  *   workspace  device scratch of at least btq_calib_workspace_bytes(P,T,H)
@@ -86,6 +111,7 @@ int btq_calib_update(const uint16_t *x, int64_t P, int64_t T, int64_t H,
                      float *run_min, float *run_max,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* Workspace bytes for btq_calib_update (0 for invalid sizes). */
 size_t btq_calib_workspace_bytes(int64_t P, int64_t T, int64_t H);
 
 /*
@@ -103,33 +129,88 @@ size_t btq_calib_workspace_bytes(int64_t P, int64_t T, int64_t H);
  *   scale, rscale     fp32 [P,H]  out
  *   zero_point        u8   [P,H]  out, values 0..15
  *   outlier_idx       i32  [k]    out, the BF16 features in ascending h
- *   fmap              i32  [H]    out, fmap[h] = j (the int4 slot of h), or
- *                                 -1-i when h = outlier_idx[i]
- *   cmap              i32  [H-k]  out, cmap[j] = h of int4 slot j (ascending)
- *   enc_table   fp32 [P, H-k, 2]  out: (rscale, zero_point) of slot j's
- *                                 feature cmap[j], per shard: the sender's
- *                                 parameters in message order
- *   dec_table   fp32 [2P+1, H-k]  out: rows 0..P-1 scale, rows P..2P-1
- *                                 zero_point, row 2P the per-slot constant
- *                                 -sum_p zero_point*scale (fp32 steps in
- *                                 shard order): the receiver's parameters in
- *                                 message order
- *   workspace  at least btq_select_workspace_bytes(P,H) bytes of scratch.
- * The two tables only reorder the per-feature parameters (and add one
- * derived sum), so the hot kernels read them with contiguous vector loads.
- * Pointers for zero-length outputs (k == 0, or k == H for cmap and the
- * tables) may be NULL. The tables should be 16-byte aligned (other
- * alignments run on the general path).
+ *   fmap              i32  [H]    out
+ *   cmap              i32  [H-k]  out
+ *   workspace  at least btq_select_workspace_bytes(P,H,k) bytes of scratch.
+ * Pointers for zero-length outputs (k == 0, or k == H for cmap) may be NULL.
  */
 int btq_select_outliers(const float *run_min, const float *run_max,
                         int64_t P, int64_t H, int64_t k,
                         float *scale, float *rscale, uint8_t *zero_point,
                         int32_t *outlier_idx, int32_t *fmap, int32_t *cmap,
-                        float *enc_table, float *dec_table,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /* Scratch bytes for the ranked selections: P*H floats (0 for invalid sizes). */
-size_t btq_select_workspace_bytes(int64_t P, int64_t H);
+size_t btq_select_workspace_bytes(int64_t P, int64_t H, int64_t k);
+
+/*
+ * Sender side of inference -- "The Hybrid Quantization Algorithm", Inference
+ * bullet; quantization before the sum per "Combating Quantization Errors
+ * with Tensor Parallelism".
+ *
+ * For each token row (p,t), the int4 slots j = 0..H-k-1 take feature
+ * h = cmap[j]:  q = clamp(rint_half_even(fl(x*rscale[p,h])) + zero_point[p,h],
+ * 0, 15), packed two per byte into a row of Bq = btq_packed_row_bytes(H,k)
+ * bytes (rows follow each other with no gap). The BF16 features are copied
+ * bit for bit: outliers[p,t,i] = x[p,t,outlier_idx[i]].
+ *   x            bf16 [P,T,H]    in
+ *   rscale       fp32 [P,H], zero_point u8 [P,H]   in (from a selection call)
+ *   outlier_idx  i32 [k], cmap i32 [H-k]           in (from a selection call)
+ *   packed       u8   [P,T,Bq]   out
+ *   outliers     bf16 [P,T,k]    out
+ * The maps are trusted: outlier_idx and cmap must partition 0..H-1, each in
+ * ascending order, as the selection calls write them.
+ */
+int btq_compress_pack(const uint16_t *x, int64_t P, int64_t T, int64_t H, int64_t k,
+                      const float *rscale, const uint8_t *zero_point,
+                      const int32_t *outlier_idx, const int32_t *cmap,
+                      uint8_t *packed, uint16_t *outliers, void *stream);
+
+/*
+ * Receiver side of inference -- "The Hybrid Quantization Algorithm",
+ * Inference bullet (convert back, sum across devices).
+ *
+ * y[t,h] = sum over p = 0..P-1 of term_p, in fp32, where
+ *   fmap[h] = j >= 0:  term_p = (q_p - zero_point[p,h]) * scale[p,h], q_p
+ *                      the code of slot j in packed row (p,t)
+ *   fmap[h] = -1-i:    term_p = the bf16 value outliers[p,t,i]
+ * Features kept in BF16 are summed in p order from +0, so they equal a
+ * sequential fp32 sum bit for bit. int4 features are evaluated as
+ * fma(q_p, scale, acc) from the constant -sum_p zero_point*scale, which
+ * stays within 1e-3*|y| + 1e-2*max_p scale[p,h] of the sequential sum.
+ *   packed [P,T,Bq], outliers [P,T,k]   in, as written by btq_compress_pack
+ *   scale fp32 [P,H], zero_point u8 [P,H], fmap i32 [H]   in
+ *   y      fp32 [T,H]   out
+ * Fast kernel: P <= 8, H a multiple of 8, Bq a multiple of 4 and at least
+ * 8, 16-byte aligned scale, fmap and y, and the outlier block under 2^31
+ * bytes. Anything else, such as more than 8 shards, takes a general kernel
+ * (correct, much slower, and exactly the sequential sum).
+ */
+int btq_decompress_reduce(const uint8_t *packed, const uint16_t *outliers,
+                          int64_t P, int64_t T, int64_t H, int64_t k,
+                          const float *scale, const uint8_t *zero_point, const int32_t *fmap,
+                          float *y, void *stream);
+
+/* Code bytes per packed row: ceil((H-k)/2); -1 if H < 1 or k is outside [0,H]. */
+int64_t btq_packed_row_bytes(int64_t H, int64_t k);
+
+/* ------------------------------------------------------------------------
+ * Widened path.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Receiver with bf16 output -- "The Hybrid Quantization Algorithm",
+ * Inference bullet (after communication the tensors convert back to BF16).
+ *
+ * The same sum as btq_decompress_reduce, rounded once from fp32 to bf16
+ * (round to nearest even): y[t,h] = bf16(fp32 sum), bit for bit the rounding
+ * of what btq_decompress_reduce writes. y is bf16 [T,H] (uint16 bits), 2-byte
+ * aligned (16-byte aligned for the fast kernel).
+ */
+int btq_decompress_reduce_bf16(const uint8_t *packed, const uint16_t *outliers,
+                               int64_t P, int64_t T, int64_t H, int64_t k,
+                               const float *scale, const uint8_t *zero_point,
+                               const int32_t *fmap, uint16_t *y, void *stream);
 
 /* How a feature's P per-shard ranges become its rank score. */
 typedef enum {
@@ -143,15 +224,14 @@ typedef enum {
  * quantization ranges, which are per device, and the page does not say how
  * one feature's ranges on the P devices combine. BTQ_SCORE_SUM is the
  * reading btq_select_outliers uses; BTQ_SCORE_MAX ranks a feature by its
- * widest shard. Only the score (and so the set, maps and tables) changes;
- * every other output and argument is as in btq_select_outliers. Any other
+ * widest shard. Only the score (and so the set and maps) changes; every
+ * other output and argument is as in btq_select_outliers. Any other
  * score_rule returns BTQ_ERR_ARG.
  */
 int btq_select_outliers_rule(const float *run_min, const float *run_max,
                              int64_t P, int64_t H, int64_t k, int score_rule,
                              float *scale, float *rscale, uint8_t *zero_point,
                              int32_t *outlier_idx, int32_t *fmap, int32_t *cmap,
-                             float *enc_table, float *dec_table,
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -159,8 +239,8 @@ int btq_select_outliers_rule(const float *run_min, const float *run_max,
  * "Key Observations and Future Directions" (features picked at random
  * instead of by range), and any other selection rule computed elsewhere.
  *
- * Same parameters, maps and tables as btq_select_outliers, with the
- * ranking replaced by the given set:
+ * Same parameters and maps as btq_select_outliers, with the ranking
+ * replaced by the given set:
  *   features      i32 [k]  in, HOST memory: k distinct features in
  *                          ascending order, each in [0, H). Anything else
  *                          returns BTQ_ERR_ARG and enqueues nothing.
@@ -172,89 +252,7 @@ int btq_select_outliers_rule(const float *run_min, const float *run_max,
 int btq_select_features(const float *run_min, const float *run_max,
                         int64_t P, int64_t H, int64_t k, const int32_t *features,
                         float *scale, float *rscale, uint8_t *zero_point,
-                        int32_t *outlier_idx, int32_t *fmap, int32_t *cmap,
-                        float *enc_table, float *dec_table, void *stream);
-
-/* Floats in enc_table (2*P*(H-k)) and dec_table ((2P+1)*(H-k)); -1 for
- * invalid sizes. */
-int64_t btq_enc_table_floats(int64_t P, int64_t H, int64_t k);
-int64_t btq_dec_table_floats(int64_t P, int64_t H, int64_t k);
-
-/*
- * Sender side of inference -- "The Hybrid Quantization Algorithm", Inference
- * bullet; quantization before the sum per "Combating Quantization Errors
- * with Tensor Parallelism".
- *
- * For each token row (p,t), the int4 slots j = 0..H-k-1 take feature
- * h = cmap[j]:  q = clamp(rint_half_even(fl(x*rscale)) + zero_point, 0, 15),
- * with (rscale, zero_point) = enc_table[p,j]. Codes are packed two per byte:
- * slot 2b in the low nibble of byte b, slot 2b+1 in the high nibble. An odd
- * H-k leaves the last high nibble 0. The BF16 features are copied bit for
- * bit: outliers[p,t,i] = x[p,t,outlier_idx[i]].
- *   x          bf16 [P,T,H]                       in
- *   enc_table  fp32 [P,H-k,2]                     in (from a selection call)
- *   outlier_idx i32 [k], cmap i32 [H-k]           in (from a selection call)
- *   packed     u8   [P,T,packed_pitch]            out: row (p,t) holds its
- *              Bq = btq_packed_row_bytes(H,k) code bytes, then packed_pitch-Bq
- *              zero bytes
- *   packed_pitch  bytes per packed row, >= Bq. btq_packed_pitch(H,k) (Bq
- *              rounded up to 128) lets every row start on a cache line, so
- *              the kernels write whole lines; Bq gives the densest message.
- *   outliers   bf16 [P,T,k]                       out
- * The maps are trusted: outlier_idx and cmap must partition 0..H-1, each in
- * ascending order, as the selection calls write them.
- */
-int btq_compress_pack(const uint16_t *x, int64_t P, int64_t T, int64_t H, int64_t k,
-                      const float *enc_table, const int32_t *outlier_idx,
-                      const int32_t *cmap, uint8_t *packed, int64_t packed_pitch,
-                      uint16_t *outliers, void *stream);
-
-/*
- * Receiver side of inference -- "The Hybrid Quantization Algorithm",
- * Inference bullet (convert back, sum across devices).
- *
- * y[t,h] = sum over p = 0..P-1 of term_p, in fp32, where
- *   int4 feature h = cmap[j]:       term_p = (q_p - zero_point) * scale
- *                                   (q_p = nibble j of packed row (p,t);
- *                                   scale, zero_point from dec_table[.,j])
- *   BF16 feature h = outlier_idx[i]: term_p = the bf16 value outliers[p,t,i]
- * BF16 features are summed in p order starting from 0, so they match a
- * sequential fp32 sum bit for bit. int4 features may be evaluated as
- * fma(q_p, scale, acc) seeded with the table's per-slot constant, which
- * stays within 1e-3*|y| + 1e-2*max_p scale of the sequential sum.
- *   packed, outliers  as written by btq_compress_pack (P shards)  in
- *   packed_pitch      bytes per packed row, >= btq_packed_row_bytes(H,k);
- *                     only the code bytes of a row are read
- *   dec_table fp32 [2P+1,H-k], outlier_idx [k], cmap [H-k]        in
- *   y    fp32 [T,H]  out
- * Kernel choice: P <= 8, H a multiple of 4 and H-k of 8, a pitch that is a
- * multiple of 4, and a message (P*T*pitch bytes, and P*T*k*2 for the BF16
- * block) under 2^31 bytes take the fast kernel. Anything else, such as more
- * than 8 shards or a larger batch (which a caller can also split by tokens),
- * takes a general kernel, which is correct but much slower.
- */
-int btq_decompress_reduce(const uint8_t *packed, int64_t packed_pitch,
-                          const uint16_t *outliers, int64_t P, int64_t T, int64_t H,
-                          int64_t k, const float *dec_table, const int32_t *outlier_idx,
-                          const int32_t *cmap, float *y, void *stream);
-
-/*
- * Receiver with bf16 output -- "The Hybrid Quantization Algorithm",
- * Inference bullet (after communication the tensors convert back to BF16).
- *
- * The same sum as btq_decompress_reduce, rounded once from fp32 to bf16
- * (round to nearest even): y[t,h] = bf16(fp32 sum). Arguments, layouts and
- * errors as for btq_decompress_reduce, except:
- *   y    bf16 [T,H] (uint16 bits)  out, 2-byte aligned (8-byte aligned for
- *        the fast path)
- * For BF16 features the result is the bf16 rounding of the exact sequential
- * fp32 sum. For int4 features it is the bf16 rounding of the value that
- * btq_decompress_reduce writes.
- */
-int btq_decompress_reduce_bf16(const uint8_t *packed, int64_t packed_pitch,
-                               const uint16_t *outliers, int64_t P, int64_t T, int64_t H,
-                               int64_t k, const float *dec_table, const int32_t *outlier_idx,
-                               const int32_t *cmap, uint16_t *y, void *stream);
+                        int32_t *outlier_idx, int32_t *fmap, int32_t *cmap, void *stream);
 
 /*
  * Per-shard BF16 sets -- a second reading of "The Hybrid Quantization
@@ -268,54 +266,59 @@ int btq_decompress_reduce_bf16(const uint8_t *packed, int64_t packed_pitch,
  *   outlier_idx  i32 [P,k]      out, shard p's BF16 features, ascending h
  *   fmap         i32 [P,H]      out, shard p's map (slot j, or -1-i)
  *   cmap         i32 [P,H-k]    out, shard p's int4 features, ascending h
- *   enc_table    fp32 [P,H-k,2] out, (rscale, zero_point) of cmap[p,j] on p
- *   workspace    at least btq_select_workspace_bytes(P,H) bytes.
- * The receiver reads scale and zero_point by feature, so there is no
- * decoder table.
- *
+ *   workspace    at least btq_select_workspace_bytes(P,H,k) bytes.
  * btq_compress_pack_per_shard: btq_compress_pack with outlier_idx [P,k] and
- *   cmap [P,H-k] from btq_select_outliers_per_shard; row (p,t) is coded with
- *   shard p's maps. Same packed and outliers layouts.
- *
- * btq_decompress_reduce_per_shard: y[t,h] = sum over p of the dequantized
- *   value of feature h on shard p: (q - zero_point[p,h]) * scale[p,h], q
- *   being shard p's code of h at slot fmap[p,h], or the BF16 value
- *   outliers[p,t,-1-fmap[p,h]]. scale fp32 [P,H], zero_point u8 [P,H], fmap
- *   i32 [P,H] in; y fp32 [T,H] out. The maps are trusted, as in
- *   btq_decompress_reduce. Kernel choice:
- *   - T > 2, P <= 8, H a multiple of 8, a pitch that is a multiple of 4 and
- *     at least 8, a 4-byte aligned packed, 8-byte aligned zero_point, 16-byte
- *     aligned fmap, scale and y, and message, outlier blocks and maps each
- *     under 2^30 bytes: the lane-window kernel. It seeds each feature with
- *     -sum_p z*s and adds one fma per int4 term, then the BF16 values, so
- *     its output is within fp32 rounding of the sequential sum (features
- *     BF16 on every shard are summed in shard order from +0, exactly);
- *   - otherwise P <= 8 with H a multiple of 4 (same alignments, zero_point
- *     4-byte aligned): a register kernel; any P with H a multiple of 8: a
- *     shard-loop kernel; everything else a per-element kernel. These three
- *     evaluate fl(q - z) * s and add the terms in shard order from +0, so
- *     their outputs agree bit for bit.
+ *   cmap [P,H-k]; row (p,t) is coded with shard p's maps. Same layouts.
+ * btq_decompress_reduce_per_shard: btq_decompress_reduce with fmap [P,H]:
+ *   term_p follows shard p's map. Features BF16 on every shard are summed in
+ *   shard order from +0, exactly; the others are within the receiver's
+ *   tolerance of the sequential sum.
  */
 int btq_select_outliers_per_shard(const float *run_min, const float *run_max,
                                   int64_t P, int64_t H, int64_t k,
                                   float *scale, float *rscale, uint8_t *zero_point,
                                   int32_t *outlier_idx, int32_t *fmap, int32_t *cmap,
-                                  float *enc_table, void *workspace, size_t workspace_bytes,
-                                  void *stream);
+                                  void *workspace, size_t workspace_bytes, void *stream);
 int btq_compress_pack_per_shard(const uint16_t *x, int64_t P, int64_t T, int64_t H, int64_t k,
-                                const float *enc_table, const int32_t *outlier_idx,
-                                const int32_t *cmap, uint8_t *packed, int64_t packed_pitch,
-                                uint16_t *outliers, void *stream);
-int btq_decompress_reduce_per_shard(const uint8_t *packed, int64_t packed_pitch,
-                                    const uint16_t *outliers, int64_t P, int64_t T, int64_t H,
-                                    int64_t k, const float *scale, const uint8_t *zero_point,
+                                const float *rscale, const uint8_t *zero_point,
+                                const int32_t *outlier_idx, const int32_t *cmap,
+                                uint8_t *packed, uint16_t *outliers, void *stream);
+int btq_decompress_reduce_per_shard(const uint8_t *packed, const uint16_t *outliers,
+                                    int64_t P, int64_t T, int64_t H, int64_t k,
+                                    const float *scale, const uint8_t *zero_point,
                                     const int32_t *fmap, float *y, void *stream);
 
-/* Code bytes per packed row: ceil((H-k)/2); -1 if H < 1 or k is outside [0,H]. */
-int64_t btq_packed_row_bytes(int64_t H, int64_t k);
+/* Set layout of the *_ex calls: one set for all shards, or one per shard. */
+typedef enum { BTQ_SETS_SHARED = 0, BTQ_SETS_PER_SHARD = 1 } btq_sets;
+/* Output type of btq_decompress_reduce_ex. */
+typedef enum { BTQ_Y_F32 = 0, BTQ_Y_BF16 = 1 } btq_ytype;
 
-/* Recommended packed row pitch: the code bytes rounded up to a multiple of
- * 128; -1 for invalid sizes. */
+/*
+ * The sender and receiver with every option: the set layout, the output
+ * type, and a packed row pitch. Row (p,t) of the message starts at byte
+ * (p*T+t)*packed_pitch; its first Bq bytes hold the codes and the sender
+ * writes the rest of the row as zeros, which the receiver never reads.
+ * packed_pitch = Bq is the layout of btq_compress_pack; btq_packed_pitch(H,k)
+ * (Bq rounded up to 128) starts every row on a cache line, so the kernels
+ * write and read whole lines (the message grows by less than 128 bytes a
+ * row). packed_pitch < Bq returns BTQ_ERR_SHAPE. The fast kernels need a
+ * pitch that is a multiple of 4.
+ * For sets == BTQ_SETS_PER_SHARD outlier_idx, cmap and fmap carry one set
+ * per shard as in the *_per_shard calls. y_type BTQ_Y_BF16 makes y bf16
+ * [T,H] (uint16 bits). Any other sets or y_type returns BTQ_ERR_ARG.
+ */
+int btq_compress_pack_ex(const uint16_t *x, int64_t P, int64_t T, int64_t H, int64_t k,
+                         const float *rscale, const uint8_t *zero_point,
+                         const int32_t *outlier_idx, const int32_t *cmap, int sets,
+                         uint8_t *packed, int64_t packed_pitch, uint16_t *outliers,
+                         void *stream);
+int btq_decompress_reduce_ex(const uint8_t *packed, int64_t packed_pitch,
+                             const uint16_t *outliers, int64_t P, int64_t T, int64_t H, int64_t k,
+                             const float *scale, const uint8_t *zero_point, const int32_t *fmap,
+                             int sets, void *y, int y_type, void *stream);
+
+/* Recommended packed row pitch for the *_ex calls: the code bytes rounded up
+ * to a multiple of 128; -1 for invalid sizes. */
 int64_t btq_packed_pitch(int64_t H, int64_t k);
 
 /* Static text for a btq_status value (never NULL). */

@@ -166,40 +166,15 @@ def maps_for_set(idx, H: int):
     return idx.astype(np.int32), fmap, cmap
 
 
-def codec_tables(scale, rscale, zero_point, cmap):
-    """The parameters in message order, as the selection step hands them on.
-
-    Slot j of the int4 message carries feature h = cmap[j]. The sender's
-    table holds (rscale, zero_point) of that feature for each shard. The
-    receiver's table holds scale and zero_point per shard and slot, plus
-    one constant per slot, bias[j] = -(z_0*s_0 + z_1*s_1 + ...). The bias
-    is evaluated as fp32 steps b = fl(b - fl(z_p*s_p)) in shard order from
-    0. These are the same numbers as the per-feature arrays, reordered;
-    the bias is a derived sum. Returns
-      enc  float32 [P, H-k, 2]   (rscale, zero_point)
-      dec  float32 [2P+1, H-k]   rows 0..P-1 scale, P..2P-1 zero_point, 2P bias
-    """
-    cmap = np.asarray(cmap, np.int64)
-    s = np.asarray(scale, F32)[:, cmap]
-    r = np.asarray(rscale, F32)[:, cmap]
-    z = np.asarray(zero_point).astype(F32)[:, cmap]
-    enc = np.stack([r, z], axis=-1).astype(F32)
-    bias = np.zeros(cmap.shape[0], F32)
-    for p in range(s.shape[0]):
-        bias = bias - (z[p] * s[p])
-    dec = np.concatenate([s, z, bias[None, :]], axis=0).astype(F32)
-    return enc, dec
-
-
 def select_outliers(run_min, run_max, k: int, rule: str = "sum") -> dict:
-    """[Selection] after [Calibration]: parameters, scores, BF16 set, maps,
-    and the same parameters in message order. rule: see range_score."""
+    """[Selection] after [Calibration]: the per-(shard, feature) parameters,
+    the rank scores, the BF16 set and the maps between features and message
+    slots. rule: see range_score."""
     scale, rscale, zp, width = quant_params(run_min, run_max)
     score = range_score(width, rule)
     idx, fmap, cmap = top_k_features(score, k)
-    enc, dec = codec_tables(scale, rscale, zp, cmap)
     return dict(scale=scale, rscale=rscale, zero_point=zp, width=width,
-                score=score, idx=idx, fmap=fmap, cmap=cmap, enc=enc, dec=dec)
+                score=score, idx=idx, fmap=fmap, cmap=cmap)
 
 
 def select_features(run_min, run_max, idx) -> dict:
@@ -210,9 +185,8 @@ def select_features(run_min, run_max, idx) -> dict:
     scale, rscale, zp, width = quant_params(run_min, run_max)
     score = range_score(width)
     idx, fmap, cmap = maps_for_set(idx, scale.shape[1])
-    enc, dec = codec_tables(scale, rscale, zp, cmap)
     return dict(scale=scale, rscale=rscale, zero_point=zp, width=width,
-                score=score, idx=idx, fmap=fmap, cmap=cmap, enc=enc, dec=dec)
+                score=score, idx=idx, fmap=fmap, cmap=cmap)
 
 
 def select_outliers_per_shard(run_min, run_max, k: int) -> dict:
@@ -223,8 +197,7 @@ def select_outliers_per_shard(run_min, run_max, k: int) -> dict:
     The message stays k BF16 values and H-k codes per row, but its layout
     now differs between shards, so the receiver needs every shard's map.
     Returns scale, rscale, zero_point, width, and per shard idx [P,k],
-    fmap [P,H], cmap [P,H-k] and the sender's table enc [P,H-k,2] with
-    enc[p,j] = (rscale, zero_point) of feature cmap[p,j] on shard p.
+    fmap [P,H] and cmap [P,H-k].
     """
     scale, rscale, zp, width = quant_params(run_min, run_max)
     P, H = width.shape
@@ -233,13 +206,10 @@ def select_outliers_per_shard(run_min, run_max, k: int) -> dict:
     idx = np.empty((P, k), np.int32)
     fmap = np.empty((P, H), np.int32)
     cmap = np.empty((P, H - k), np.int32)
-    enc = np.empty((P, H - k, 2), F32)
     for p in range(P):
         idx[p], fmap[p], cmap[p] = top_k_features(width[p], k)
-        enc[p, :, 0] = rscale[p, cmap[p]]
-        enc[p, :, 1] = zp[p, cmap[p]].astype(F32)
     return dict(scale=scale, rscale=rscale, zero_point=zp, width=width, idx=idx, fmap=fmap,
-                cmap=cmap, enc=enc)
+                cmap=cmap)
 
 
 # ------------------------------------------------- inference, sender ----

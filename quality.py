@@ -84,18 +84,19 @@ def calibrate(P, H, batches, momentum):
 
 
 def run_codec(x: torch.Tensor, sel: dict) -> torch.Tensor:
-    """y = decompress_reduce(compress_pack(x)) with the selection's tables
-    (the per-shard calls when the selection holds one set per shard)."""
+    """y = decompress_reduce(compress_pack(x)) with the selection's parameters
+    and maps (the per-shard calls when the selection holds one set per
+    shard)."""
     H = x.shape[2]
+    enc = (sel["rscale"], sel["zero_point"], sel["outlier_idx"], sel["cmap"])
+    dec = (sel["scale"], sel["zero_point"], sel["fmap"])
     if sel["outlier_idx"].dim() == 2:
         k = sel["outlier_idx"].shape[1]
-        pk, ol = B.btq_compress_pack_per_shard(x, k, sel["enc"], sel["outlier_idx"],
-                                               sel["cmap"])
-        return B.btq_decompress_reduce_per_shard(pk, ol, H, sel["scale"], sel["zero_point"],
-                                                 sel["fmap"])
+        pk, ol = B.btq_compress_pack_per_shard(x, k, *enc)
+        return B.btq_decompress_reduce_per_shard(pk, ol, H, *dec)
     k = sel["outlier_idx"].numel()
-    pk, ol = B.btq_compress_pack(x, k, sel["enc"], sel["outlier_idx"], sel["cmap"])
-    return B.btq_decompress_reduce(pk, ol, H, sel["dec"], sel["outlier_idx"], sel["cmap"])
+    pk, ol = B.btq_compress_pack(x, k, *enc)
+    return B.btq_decompress_reduce(pk, ol, H, *dec)
 
 
 def workload_state(name: str, calib_batches=None, T=None):
@@ -186,8 +187,9 @@ def output_precision(name: str, calib_batches=None) -> list:
     w, rmin, rmax, x = workload_state(name, calib_batches)
     ex = exact_sum(x)
     sel = B.btq_select_outliers(rmin, rmax, w.k)
-    pk, ol = B.btq_compress_pack(x, w.k, sel["enc"], sel["outlier_idx"], sel["cmap"])
-    args = (pk, ol, w.H, sel["dec"], sel["outlier_idx"], sel["cmap"])
+    pk, ol = B.btq_compress_pack(x, w.k, sel["rscale"], sel["zero_point"], sel["outlier_idx"],
+                                 sel["cmap"])
+    args = (pk, ol, w.H, sel["scale"], sel["zero_point"], sel["fmap"])
     y32 = B.btq_decompress_reduce(*args)
     y16 = B.btq_decompress_reduce_bf16(*args).view(torch.bfloat16).float()
     base = dict(report="output", workload=name, P=w.P, T=x.shape[1], H=w.H, k=w.k)

@@ -26,29 +26,32 @@ int main(void) {
   CHECK(btq_packed_row_bytes(9, 2) == 4);
   CHECK(btq_packed_row_bytes(8, 9) == -1);
   CHECK(btq_packed_pitch(4096, 64) == 2048);
-  CHECK(btq_enc_table_floats(8, 4096, 64) == 2 * 8 * 4032);
-  CHECK(btq_dec_table_floats(8, 4096, 64) == 17 * 4032);
-  CHECK(btq_select_workspace_bytes(8, 4096) == (size_t)8 * 4096 * 4);
+  CHECK(btq_select_workspace_bytes(8, 4096, 64) == (size_t)8 * 4096 * 4);
   CHECK(btq_calib_workspace_bytes(0, 1, 1) == 0);
   CHECK(strcmp(btq_status_str(BTQ_OK), "ok") == 0);
   CHECK(btq_status_str(12345) != NULL);
   CHECK(btq_version() != NULL && strlen(btq_version()) >= 5);
-  CHECK(btq_compress_pack(A, 2, 4, 16, 17, A, A, A, A, 128, A, NULL) == BTQ_ERR_SHAPE);
-  CHECK(btq_decompress_reduce(A, 5, A, 2, 4, 16, 4, A, A, A, A, NULL) == BTQ_ERR_SHAPE);
-  CHECK(btq_decompress_reduce_bf16(A, 128, A, 2, 4, 16, 4, A, A, A, NULL, NULL) == BTQ_ERR_ARG);
-  CHECK(btq_calib_update(A, 2, 4, 16, 1.5f, 1, A, A, A, 1u << 20, NULL) == BTQ_ERR_ARG);
-  CHECK(btq_select_outliers_rule(A, A, 2, 16, 4, 7, A, A, A, A, A, A, A, A, A, 1u << 20, NULL) ==
+  CHECK(btq_compress_pack(A, 2, 4, 16, 17, A, A, A, A, A, A, NULL) == BTQ_ERR_SHAPE);
+  CHECK(btq_compress_pack(A, 2, 4, 16, 4, NULL, A, A, A, A, A, NULL) == BTQ_ERR_ARG);
+  CHECK(btq_decompress_reduce(A, A, 2, 4, 16, 4, A, A, NULL, A, NULL) == BTQ_ERR_ARG);
+  CHECK(btq_decompress_reduce(A, A, 0, 4, 16, 4, A, A, A, A, NULL) == BTQ_ERR_SHAPE);
+  CHECK(btq_decompress_reduce_bf16(A, A, 2, 4, 16, 4, A, A, A, NULL, NULL) == BTQ_ERR_ARG);
+  CHECK(btq_calib_update(A, 2, 4, 16, 1.0f, 1, A, A, A, 1u << 20, NULL) == BTQ_ERR_ARG);
+  CHECK(btq_select_outliers(A, A, 2, 16, 4, A, A, A, A, A, A, A, 4, NULL) == BTQ_ERR_WORKSPACE);
+  CHECK(btq_select_outliers_rule(A, A, 2, 16, 4, 7, A, A, A, A, A, A, A, 1u << 20, NULL) ==
         BTQ_ERR_ARG);
   {
     const int32_t unsorted[2] = {5, 3};
-    CHECK(btq_select_features(A, A, 2, 16, 2, unsorted, A, A, A, A, A, A, A, A, NULL) ==
-          BTQ_ERR_ARG);
+    CHECK(btq_select_features(A, A, 2, 16, 2, unsorted, A, A, A, A, A, A, NULL) == BTQ_ERR_ARG);
   }
-  CHECK(btq_compress_pack_per_shard(A, 2, 4, 16, 4, A, NULL, A, A, 128, A, NULL) == BTQ_ERR_ARG);
-  CHECK(btq_decompress_reduce_per_shard(A, 128, A, 2, 4, 16, 4, A, A, NULL, A, NULL) ==
-        BTQ_ERR_ARG);
-  CHECK(btq_select_outliers_per_shard(A, A, 2, 16, 4, A, A, A, A, A, A, A, A, 4, NULL) ==
+  CHECK(btq_compress_pack_per_shard(A, 2, 4, 16, 4, A, A, NULL, A, A, A, NULL) == BTQ_ERR_ARG);
+  CHECK(btq_decompress_reduce_per_shard(A, A, 2, 4, 16, 4, A, A, NULL, A, NULL) == BTQ_ERR_ARG);
+  CHECK(btq_select_outliers_per_shard(A, A, 2, 16, 4, A, A, A, A, A, A, A, 4, NULL) ==
         BTQ_ERR_WORKSPACE);
+  CHECK(btq_compress_pack_ex(A, 2, 4, 16, 4, A, A, A, A, BTQ_SETS_SHARED, A, 5, A, NULL) ==
+        BTQ_ERR_SHAPE);
+  CHECK(btq_decompress_reduce_ex(A, 128, A, 2, 4, 16, 4, A, A, A, BTQ_SETS_PER_SHARD, A, 9,
+                                 NULL) == BTQ_ERR_ARG);
   printf("all ok\n");
   return 0;
 }

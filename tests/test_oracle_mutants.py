@@ -59,19 +59,12 @@ MUTANTS = [
        "idx, fmap, cmap = top_k_features(score, len(idx))")]),
     ("fmap inverted without the -1 offset", [("idx[-1 - fmap[~ints]] = h[~ints]",
                                               "idx[np.abs(fmap[~ints]) % len(idx)] = h[~ints]")]),
-    ("bias summed from the last shard",
-     [("for p in range(s.shape[0]):\n        bias = bias - (z[p] * s[p])",
-       "for p in reversed(range(s.shape[0])):\n        bias = bias - (z[p] * s[p])")]),
     ("ties go to the higher feature", [("np.lexsort((h, -score))", "np.lexsort((-h, -score))")]),
     ("the narrowest features kept", [("np.lexsort((h, -score))", "np.lexsort((h, score))")]),
     ("BF16 set listed in rank order", [("return maps_for_set(np.sort(order[:k]), H)",
                                         "return maps_for_set(order[:k], H)")]),
     ("BF16 slot code off by one", [("fmap[idx] = -1 - np.arange(k, dtype=np.int32)",
                                     "fmap[idx] = -np.arange(k, dtype=np.int32)")]),
-    ("bias sign", [("bias = bias - (z[p] * s[p])", "bias = bias + (z[p] * s[p])")]),
-    ("encoder table fields swapped", [("np.stack([r, z], axis=-1)", "np.stack([z, r], axis=-1)")]),
-    ("decoder table rows swapped", [("np.concatenate([s, z, bias[None, :]], axis=0)",
-                                     "np.concatenate([z, s, bias[None, :]], axis=0)")]),
     ("zero point added before rounding",
      [("q = np.rint(v) + np.asarray(zero_point).astype(F32)",
        "q = np.rint(v + np.asarray(zero_point).astype(F32))")]),
@@ -111,10 +104,6 @@ MUTANTS = [
                                 "(u >> np.uint64(16))")]),
     ("bf16 output ties round up", [("((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16))",
                                     "((u + np.uint64(0x8000)) >> np.uint64(16))")]),
-    ("per-shard sender table in feature order", [("enc[p, :, 0] = rscale[p, cmap[p]]",
-                                                  "enc[p, :, 0] = rscale[p, :H - k]")]),
-    ("per-shard sender table with shard 0's zero points",
-     [("enc[p, :, 1] = zp[p, cmap[p]].astype(F32)", "enc[p, :, 1] = zp[0, cmap[p]].astype(F32)")]),
     ("per-shard sets ranked by the shared score",
      [("idx[p], fmap[p], cmap[p] = top_k_features(width[p], k)",
        "idx[p], fmap[p], cmap[p] = top_k_features(range_score(width), k)")]),

@@ -93,39 +93,6 @@ def test_zero_inclusion_holds_on_tiny_workload():
     assert np.all(mn < 0) and np.all(mx > 0)
 
 
-def test_codec_tables_are_the_parameters_in_message_order():
-    # Brute force: walk the slots and read the per-feature arrays directly.
-    rng = np.random.default_rng(9)
-    P, H, k = 3, 40, 6
-    mn = -np.abs(rng.standard_normal((P, H))).astype(np.float32) * 3
-    mx = np.abs(rng.standard_normal((P, H))).astype(np.float32) * 3
-    sel = O.select_outliers(mn, mx, k)
-    enc, dec = sel["enc"], sel["dec"]
-    assert enc.shape == (P, H - k, 2) and dec.shape == (2 * P + 1, H - k)
-    for j, h in enumerate(sel["cmap"]):
-        exact = 0.0
-        for p in range(P):
-            assert enc[p, j, 0] == sel["rscale"][p, h]
-            assert enc[p, j, 1] == float(sel["zero_point"][p, h])
-            assert dec[p, j] == sel["scale"][p, h]
-            assert dec[P + p, j] == float(sel["zero_point"][p, h])
-            exact -= float(sel["zero_point"][p, h]) * float(sel["scale"][p, h])
-        # the fp32 bias is the exact sum up to P roundings
-        assert abs(dec[2 * P, j] - exact) <= 2 * P * 2.0 ** -24 * (abs(exact) + 15 * P * sel["scale"][:, h].max())
-
-
-def test_codec_bias_sums_in_shard_order():
-    # Hand-worked: three shards with z = 1 and scales 1, 2^-24, 2^-24, so the
-    # products z*s are exact. From shard 0: -1 - 2^-24 lies halfway between
-    # -1 and -(1 + 2^-23) and rounds to the even -1, twice, so the bias is
-    # -1 (0xbf800000). Summed from the last shard, -2^-24 - 2^-24 = -2^-23
-    # exactly, and -2^-23 - 1 = -(1 + 2^-23) (0xbf800001) is exact too.
-    scale = np.array([[1.0], [2.0 ** -24], [2.0 ** -24]], np.float32)
-    zp = np.ones((3, 1), np.uint8)
-    _, dec = O.codec_tables(scale, np.float32(1) / scale, zp, np.array([0], np.int32))
-    assert dec[6].view(np.uint32).tolist() == [0xBF800000]
-
-
 @pytest.mark.parametrize("H,k,seed", [(1, 0, 0), (1, 1, 1), (40, 7, 2), (300, 0, 3), (300, 300, 4),
                                       (517, 64, 5)])
 def test_maps_for_a_given_set_brute_force(H, k, seed):
@@ -148,10 +115,10 @@ def test_given_set_selection_matches_ranked_selection_on_its_set():
     mx = np.abs(rng.standard_normal((4, 70))).astype(np.float32) * 2
     ranked = O.select_outliers(mn, mx, 9)
     given = O.select_features(mn, mx, ranked["idx"])
-    for key in ("scale", "rscale", "zero_point", "score", "idx", "fmap", "cmap", "enc", "dec"):
+    for key in ("scale", "rscale", "zero_point", "score", "idx", "fmap", "cmap"):
         assert np.array_equal(np.ascontiguousarray(given[key]).view(np.uint8),
                               np.ascontiguousarray(ranked[key]).view(np.uint8)), key
-    # a random set: maps and tables follow the set, parameters do not change
+    # a random set: the maps follow the set, the parameters do not change
     other = np.sort(rng.choice(70, 9, replace=False))
     g2 = O.select_features(mn, mx, other)
     assert g2["idx"].tolist() == other.tolist()
@@ -195,7 +162,7 @@ def test_select_outliers_rule_changes_only_score_and_set():
     for key in ("scale", "rscale", "zero_point"):
         assert np.array_equal(a[key], b[key])
     c = O.select_features(mn, mx, b["idx"])
-    for key in ("fmap", "cmap", "enc", "dec"):
+    for key in ("fmap", "cmap"):
         assert np.array_equal(b[key], c[key])
 
 
@@ -208,9 +175,9 @@ def test_per_shard_selection_worked_example():
     assert sel["idx"].tolist() == [[1], [0]]
     assert sel["fmap"].tolist() == [[0, -1, 1, 2], [-1, 0, 1, 2]]
     assert sel["cmap"].tolist() == [[0, 2, 3], [1, 2, 3]]
-    # enc[p, j] = (1/scale, zero point) of feature cmap[p, j]; scale = w/15
-    assert sel["enc"][0, :, 1].tolist() == [0.0, 0.0, 0.0]
-    assert np.array_equal(sel["enc"][1, :, 0], sel["rscale"][1, [1, 2, 3]])
+    # the parameters stay per (shard, feature): scale = w/15, zero point 0
+    assert np.array_equal(sel["scale"], mx / np.float32(15))
+    assert not sel["zero_point"].any()
 
 
 def test_per_shard_selection_of_equal_shards_is_the_shared_one():
@@ -225,7 +192,7 @@ def test_per_shard_selection_of_equal_shards_is_the_shared_one():
     for p in range(2):
         assert per["idx"][p].tolist() == shared["idx"].tolist()
         assert per["cmap"][p].tolist() == shared["cmap"].tolist()
-        assert np.array_equal(per["enc"][p], shared["enc"][p])
+        assert per["fmap"][p].tolist() == shared["fmap"].tolist()
 
 
 @pytest.mark.parametrize("P,H,k", [(3, 50, 0), (3, 50, 7), (4, 64, 64), (5, 33, 32)])
@@ -240,6 +207,3 @@ def test_per_shard_selection_invariants(P, H, k):
         rest = sel["width"][p, sel["cmap"][p]]
         if k and k < H:
             assert chosen.min() >= rest.max()
-        for j, h in enumerate(sel["cmap"][p]):
-            assert sel["enc"][p, j, 0] == sel["rscale"][p, h]
-            assert sel["enc"][p, j, 1] == float(sel["zero_point"][p, h])

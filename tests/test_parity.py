@@ -1,10 +1,16 @@
 """GPU parity: every HIP step against the CPU oracle, element by element.
 
 Bar: calibration statistics equal by value; parameters, outlier set, maps,
-codec tables, packed codes and BF16 blocks bitwise; reduced output within
+packed codes and BF16 blocks bitwise; reduced output within
 1e-3*|y| + 1e-2*max_p scale (BF16 feature columns bit-exact). The bf16-output
 receiver: within that bound plus half a bf16 ulp, BF16 columns equal to the
 oracle's rounding, and bit-identical to rounding the fp32 receiver's output.
+
+Every case runs the four calls of the path with rows of Bq code bytes and no
+gap (btq_compress_pack, btq_decompress_reduce), and again through the *_ex
+calls with a packed row pitch (by default Bq rounded up to 128): the padded
+message must be the oracle's rows padded with zeros, and its receivers must
+meet the same bar.
 """
 import numpy as np
 import pytest
@@ -27,12 +33,14 @@ def _shifted(t: torch.Tensor, off: int) -> torch.Tensor:
     return big[off:].view(t.shape)
 
 
-def run_both(calib_xs, x, k, momentum, *, x_offset=0, table_offset=0, pitch=None,
+def run_both(calib_xs, x, k, momentum, *, x_offset=0, param_offset=0, pitch=None,
              features=None, rule=None):
     """Calibrate, select, compress and decompress on both sides; compare all.
 
     features: a BF16 set given to both sides in place of the range ranking.
-    rule: the rank score ("sum" or "max") through btq_select_outliers_rule."""
+    rule: the rank score ("sum" or "max") through btq_select_outliers_rule.
+    param_offset: the per-feature arrays and fmap moved off 16-byte alignment.
+    pitch: the packed row pitch of the *_ex pass (default btq_packed_pitch)."""
     P, T, H = x.shape
     rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
     rmax = torch.empty_like(rmin)
@@ -58,25 +66,41 @@ def run_both(calib_xs, x, k, momentum, *, x_offset=0, table_offset=0, pitch=None
 
     if x_offset:   # misaligned base pointer: same values, shifted storage
         x = _shifted(x, x_offset)
-    enc, dec = sel_g["enc"], sel_g["dec"]
-    if table_offset:   # tables aligned to 4 bytes but not to 16
-        enc, dec = _shifted(enc, table_offset), _shifted(dec, table_offset)
-    if pitch is None:
-        pitch = B.btq_packed_pitch(H, k)
-    pk, ol = B.btq_compress_pack(x, k, enc, sel_g["outlier_idx"], sel_g["cmap"], pitch=pitch)
-    pk_o, ol_o = oracle_compress_rows(u16(x), sel_o, pitch=pitch)
+    par = {key: sel_g[key] for key in ("scale", "rscale", "zero_point", "fmap")}
+    if param_offset:   # aligned to the element type but not to 16 bytes
+        par = {key: _shifted(v, param_offset) for key, v in par.items()}
+    idx, cmap = sel_g["outlier_idx"], sel_g["cmap"]
+
+    # the path's four calls: rows of Bq bytes, no gap
+    pk, ol = B.btq_compress_pack(x, k, par["rscale"], par["zero_point"], idx, cmap)
+    pk_o, ol_o = oracle_compress_rows(u16(x), sel_o)
     torch.cuda.synchronize()
+    assert pk.shape == (P, T, B.btq_packed_row_bytes(H, k))
     assert_bits_equal(pk, pk_o, "packed")
     assert_bits_equal(ol.view(torch.int16), ol_o.view(np.int16), "outliers")
-
-    y = B.btq_decompress_reduce(pk, ol, H, dec, sel_g["outlier_idx"], sel_g["cmap"])
-    y16 = B.btq_decompress_reduce_bf16(pk, ol, H, dec, sel_g["outlier_idx"], sel_g["cmap"])
+    y = B.btq_decompress_reduce(pk, ol, H, par["scale"], par["zero_point"], par["fmap"])
+    y16 = B.btq_decompress_reduce_bf16(pk, ol, H, par["scale"], par["zero_point"], par["fmap"])
     y_o = O.decompress_reduce(pk_o, ol_o, sel_o["scale"], sel_o["zero_point"], sel_o["fmap"])
     torch.cuda.synchronize()
     assert_y_close(y.cpu().numpy(), y_o, sel_o["scale"], sel_o["idx"])
     assert_y_bf16_close(y16.cpu().numpy(), y_o, sel_o["scale"], sel_o["idx"])
     # the bf16 output is one round-to-nearest-even of the fp32 output
     assert torch.equal(y16, y.to(torch.bfloat16).view(torch.int16))
+
+    # the same through the *_ex calls with a row pitch
+    if pitch is None:
+        pitch = B.btq_packed_pitch(H, k)
+    pkp, olp = B.btq_compress_pack_ex(x, k, par["rscale"], par["zero_point"], idx, cmap,
+                                      pitch=pitch)
+    torch.cuda.synchronize()
+    assert_bits_equal(pkp, O.pad_rows(pk_o, pitch), "packed (pitched)")
+    assert torch.equal(olp, ol)
+    yp = B.btq_decompress_reduce_ex(pkp, olp, H, par["scale"], par["zero_point"], par["fmap"])
+    yp16 = B.btq_decompress_reduce_ex(pkp, olp, H, par["scale"], par["zero_point"], par["fmap"],
+                                      bf16=True)
+    torch.cuda.synchronize()
+    assert_y_close(yp.cpu().numpy(), y_o, sel_o["scale"], sel_o["idx"])
+    assert torch.equal(yp16, yp.to(torch.bfloat16).view(torch.int16))
     return sel_g, pk, ol, y
 
 
@@ -152,9 +176,9 @@ def test_given_feature_set(P, T, H, k, note):
     assert sel["outlier_idx"].cpu().numpy().tolist() == feats.tolist()
 
 
-# A contiguous block of BF16 features puts one wave-tile's span far beyond
-# its 512 slots, so the receiver writes that tile's y through its
-# chunk-store loop (and, beyond 2048 features, the loop's unrolled body).
+# A contiguous block of BF16 features puts one sender tile's span far beyond
+# its 512 slots (the staged sender kernel), and gives the receiver's tiles
+# more BF16 entries than its registers hold (its post-loop recompute).
 WIDE_SPAN_CASES = [
     (4, 37, 4096, (600, 3200), "tile spanning ~3100 features"),
     (8, 20, 2048, (512, 1400), "tile spanning ~1400 features"),
@@ -236,9 +260,10 @@ def test_misaligned_input_pointer():
     run_both(calib, x, k, 0.95, x_offset=1)
 
 
-@pytest.mark.parametrize("pitch_extra", [0, 4, 130])
+@pytest.mark.parametrize("pitch_extra", [0, 4, 130, 1])
 def test_packed_pitch(pitch_extra):
-    # pitch = code bytes (densest), a few bytes more, and more than one line
+    # pitch = code bytes (densest), a few bytes more, more than one line, and
+    # an odd pitch (general kernels)
     P, T, H, k = 3, 20, 2048, 64
     say(f"case: packed pitch = code bytes + {pitch_extra}")
     calib = [W.draw(P, T, H, 3400 + b, device=DEV) for b in range(2)]
@@ -246,20 +271,23 @@ def test_packed_pitch(pitch_extra):
     run_both(calib, x, k, 0.9, pitch=B.btq_packed_row_bytes(H, k) + pitch_extra)
 
 
-def test_misaligned_tables():
-    say("case: codec tables offset by one float")
+def test_misaligned_parameter_arrays():
+    say("case: scale, rscale, zero points and fmap offset by one element")
     P, T, H, k = 3, 12, 1024, 8
     calib = [W.draw(P, T, H, 3200 + b, device=DEV) for b in range(2)]
     x = W.draw(P, T, H, 3300, device=DEV)
-    run_both(calib, x, k, 0.9, table_offset=1)
+    run_both(calib, x, k, 0.9, param_offset=1)
 
 
-def test_momentum_extremes():
-    say("case: momentum 0 and 1")
+def test_momentum_range():
+    say("case: momentum 0 and the largest fp32 below 1; 1 is rejected")
     P, T, H = 2, 8, 64
     xs = [W.draw(P, T, H, 4000 + b, device=DEV) for b in range(3)]
-    for m in (0.0, 1.0):
+    for m in (0.0, float(np.nextafter(np.float32(1), np.float32(0)))):
         run_both(xs, xs[-1], 4, m)
+    rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
+    with pytest.raises(RuntimeError):
+        B.btq_calib_update(xs[0], rmin, rmin.clone(), 1.0, first_batch=False)
 
 
 def test_empty_batch_leaves_outputs_untouched():
@@ -271,9 +299,10 @@ def test_empty_batch_leaves_outputs_untouched():
     B.btq_calib_update(xs[0], rmin, rmax, 0.9, True)
     sel = B.btq_select_outliers(rmin, rmax, k)
     x0 = torch.empty((P, 0, H), dtype=torch.int16, device=DEV)
-    pk, ol = B.btq_compress_pack(x0, k, sel["enc"], sel["outlier_idx"], sel["cmap"])
-    assert pk.shape == (P, 0, B.btq_packed_pitch(H, k)) and ol.shape == (P, 0, k)
-    y = B.btq_decompress_reduce(pk, ol, H, sel["dec"], sel["outlier_idx"], sel["cmap"])
+    pk, ol = B.btq_compress_pack(x0, k, sel["rscale"], sel["zero_point"], sel["outlier_idx"],
+                                 sel["cmap"])
+    assert pk.shape == (P, 0, B.btq_packed_row_bytes(H, k)) and ol.shape == (P, 0, k)
+    y = B.btq_decompress_reduce(pk, ol, H, sel["scale"], sel["zero_point"], sel["fmap"])
     torch.cuda.synchronize()
     assert y.shape == (0, H)
 
@@ -293,8 +322,9 @@ def test_repeatable_bitwise():
         for b, xb in enumerate(calib):
             B.btq_calib_update(xb, rmin, rmax, 0.9, b == 0)
         sel = B.btq_select_outliers(rmin, rmax, k)
-        pk, ol = B.btq_compress_pack(x, k, sel["enc"], sel["outlier_idx"], sel["cmap"])
-        y = B.btq_decompress_reduce(pk, ol, H, sel["dec"], sel["outlier_idx"], sel["cmap"])
+        pk, ol = B.btq_compress_pack(x, k, sel["rscale"], sel["zero_point"], sel["outlier_idx"],
+                                     sel["cmap"])
+        y = B.btq_decompress_reduce(pk, ol, H, sel["scale"], sel["zero_point"], sel["fmap"])
         torch.cuda.synchronize()
         outs.append([t.cpu().clone() for t in (rmin, rmax, sel["scale"], sel["cmap"], pk, ol, y)])
     for a, b in zip(*outs):

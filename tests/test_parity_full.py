@@ -1,24 +1,25 @@
-"""GPU parity at the workloads' full sizes, through the same calls and
-launch configuration that the benchmark times (default stream, default
-packed pitch).
+"""GPU parity at the workloads' full sizes, every element compared.
 
-Every workload runs at its real [P,T,H] and k. Its calibration uses the
-workload's batch shape, but fewer batches than the full recipe, so that the
-oracle's exact statistics over all of H stay cheap. The kernels' launch
-shape depends on (P,T,H) only, not on the number of batches.
+Every workload runs at its real [P,T,H] and k, through the path's four calls
+(rows of Bq code bytes, no gap) and through the padded launch that the
+benchmark also times (btq_compress_pack_ex / btq_decompress_reduce_ex with
+btq_packed_pitch, default stream). Its calibration uses the workload's batch
+shape; 7B prefill and decode run their full recipes (32 batches), large
+prefill and stress fewer batches, so the oracle's exact statistics stay
+cheap. The kernels' launch shape depends on (P,T,H) only, not on the number
+of batches; deep moving-average chains are compared at small sizes too.
 
-Checked on every case:
+Checked on every case, over whole tensors:
   * running min/max over all (p,h): equal by value;
-  * parameters, outlier set, maps and codec tables: bitwise;
-  * packed rows and BF16 blocks of sampled token rows: bitwise against the
-    oracle's message for those rows (the rows include both ends, the
-    benchmark's row-block boundaries and random rows);
-  * y on the same rows: within 1e-3*|y| + 1e-2*max_p scale, BF16 columns
+  * parameters, outlier set and maps: bitwise;
+  * packed rows and BF16 blocks of every token row: bitwise against the
+    oracle's message; the padded message: the same codes, zero padding;
+  * y of every row: within 1e-3*|y| + 1e-2*max_p scale, BF16 columns
     bit-exact; the bf16-output receiver within that plus half a bf16 ulp,
-    its BF16 columns equal to the oracle's rounding, and over the whole
-    tensor bit-identical to rounding the fp32 receiver's output;
-  * properties over the whole tensors: every padding byte of the packed
-    rows is zero and y is finite.
+    its BF16 columns equal to the oracle's rounding, and bit-identical to
+    rounding the fp32 receiver's output; the padded message's y to the
+    same bar.
+The oracle runs over (shard, row-chunk) tiles in a thread pool.
 """
 import numpy as np
 import pytest
@@ -28,25 +29,26 @@ import bit_tensor_activation_amd as B
 from oracle import oracle as O
 import workloads as W
 from helpers import (assert_bits_equal, assert_selection_equal, assert_stats_equal, assert_y_close,
-                     assert_y_bf16_close, oracle_calib, oracle_compress_rows, say, u16)
+                     assert_y_bf16_close, assert_y_close_rows, oracle_calib,
+                     oracle_compress_rows, oracle_path, say, u16)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 # (workload, inference T, k, calibration batches used here)
 CASES = [
-    ("7b_prefill", 2048, 64, 4),
-    # 32768 row-tiles: the bf16-output receiver takes about 2048 waves here
-    ("7b_prefill", 4096, 64, 4),
-    ("large_prefill", 2048, 128, 3),
-    ("decode", 1, 64, 3),
-    ("decode", 8, 64, 3),
-    ("decode", 32, 64, 3),
-    ("decode", 64, 64, 3),
-    ("large_prefill", 8192, 128, 3),
-    ("stress", 16384, 0, 2),
-    ("stress", 16384, 32, 2),
-    ("stress", 16384, 256, 2),
+    ("7b_prefill", 2048, 64, 32),
+    # 32768 row-tiles: two waves per SIMD
+    ("7b_prefill", 4096, 64, 32),
+    ("decode", 1, 64, 32),
+    ("decode", 8, 64, 32),
+    ("decode", 32, 64, 32),
+    ("decode", 64, 64, 32),
+    ("large_prefill", 2048, 128, 8),
+    ("large_prefill", 8192, 128, 8),
+    ("stress", 16384, 0, 4),
+    ("stress", 16384, 32, 4),
+    ("stress", 16384, 256, 4),
 ]
 
 _calib_cache = {}
@@ -71,12 +73,21 @@ def calibrated(name: str, nb: int):
     return _calib_cache[key]
 
 
-def sample_rows(T: int, seed: int) -> np.ndarray:
-    rng = np.random.default_rng(seed)
-    fixed = [0, 1, 7, 8, 15, 16, 31, 32, 63, 64, T // 2, T - 2, T - 1]
-    rows = set(r for r in fixed if 0 <= r < T)
-    rows |= set(rng.integers(0, T, size=min(T, 24)).tolist())
-    return np.array(sorted(rows), np.int64)
+def compare_all(x, pk, ol, y, y16, pkp, olp, yp, sel_o):
+    """Every element of both messages and all outputs against the oracle."""
+    H = x.shape[2]
+    pk_o, ol_o, y_o = oracle_path(u16(x), sel_o)
+    Bq = pk_o.shape[2]
+    assert_bits_equal(pk, pk_o, "packed")
+    assert_bits_equal(ol.view(torch.int16), ol_o.view(np.int16), "outliers")
+    assert_bits_equal(pkp[:, :, :Bq], pk_o, "packed (padded rows)")
+    assert not bool(pkp[:, :, Bq:].any()), "padding bytes must be zero"
+    assert torch.equal(olp, ol)
+    assert torch.equal(y16, y.to(torch.bfloat16).view(torch.int16)), "bf16 y is not RNE(fp32 y)"
+    assert_y_close_rows(y, y_o, sel_o["scale"], sel_o["idx"])
+    assert_y_close_rows(y16, y_o, sel_o["scale"], sel_o["idx"], bf16=True)
+    assert_y_close_rows(yp, y_o, sel_o["scale"], sel_o["idx"])
+    assert y.shape == (x.shape[1], H)
 
 
 @pytest.mark.parametrize("name,T,k,nb", CASES, ids=[f"{c[0]}-T{c[1]}-k{c[2]}" for c in CASES])
@@ -95,41 +106,27 @@ def test_full_size(name, T, k, nb):
 
     b = w.T.index(T) if T in w.T else 0
     x = W.batch(w, W.PHASE_INFER, b, T=T, device=DEV)
-    pk, ol = B.btq_compress_pack(x, k, sel_g["enc"], sel_g["outlier_idx"], sel_g["cmap"])
-    y = B.btq_decompress_reduce(pk, ol, H, sel_g["dec"], sel_g["outlier_idx"], sel_g["cmap"])
-    y16 = B.btq_decompress_reduce_bf16(pk, ol, H, sel_g["dec"], sel_g["outlier_idx"],
-                                       sel_g["cmap"])
+    enc = (sel_g["rscale"], sel_g["zero_point"], sel_g["outlier_idx"], sel_g["cmap"])
+    dec = (sel_g["scale"], sel_g["zero_point"], sel_g["fmap"])
+    pk, ol = B.btq_compress_pack(x, k, *enc)
+    y = B.btq_decompress_reduce(pk, ol, H, *dec)
+    y16 = B.btq_decompress_reduce_bf16(pk, ol, H, *dec)
+    pkp, olp = B.btq_compress_pack_ex(x, k, *enc, pitch=B.btq_packed_pitch(H, k))
+    yp = B.btq_decompress_reduce_ex(pkp, olp, H, *dec)
     torch.cuda.synchronize()
-    assert torch.equal(y16, y.to(torch.bfloat16).view(torch.int16)), "bf16 y is not RNE(fp32 y)"
-    pitch = pk.shape[2]
-    assert pitch == B.btq_packed_pitch(H, k)
-    Bq = B.btq_packed_row_bytes(H, k)
-
-    # whole-tensor properties
-    assert not bool(pk[:, :, Bq:].any()), "packed padding bytes must be zero"
-    assert bool(torch.isfinite(y).all()), "y must be finite"
-
-    rows = sample_rows(T, seed=T * 131 + k)
-    xs = u16(x[:, torch.as_tensor(rows, device=DEV), :])
-    pk_o, ol_o = oracle_compress_rows(xs, sel_o, pitch=pitch)
-    ridx = torch.as_tensor(rows, device=DEV)
-    assert_bits_equal(pk[:, ridx, :], pk_o, "packed (sampled rows)")
-    assert_bits_equal(ol[:, ridx, :].view(torch.int16), ol_o.view(np.int16),
-                      "outliers (sampled rows)")
-    y_o = O.decompress_reduce(pk_o, ol_o, sel_o["scale"], sel_o["zero_point"], sel_o["fmap"])
-    assert_y_close(y[ridx].cpu().numpy(), y_o, sel_o["scale"], sel_o["idx"])
-    assert_y_bf16_close(y16[ridx].cpu().numpy(), y_o, sel_o["scale"], sel_o["idx"])
-    del x, pk, ol, y, y16
+    compare_all(x, pk, ol, y, y16, pkp, olp, yp, sel_o)
+    del x, pk, ol, y, y16, pkp, olp, yp
     torch.cuda.empty_cache()
 
 
 def test_message_beyond_2_gib():
     """A batch whose packed message passes 2^31 bytes (P=8, T=65552, H=8192,
-    k=64: 2.15 GB of codes). The receivers take their general kernels there
-    (the fast ones address a whole message with one 32-bit descriptor), and
-    every offset is 64-bit. Checked on sampled rows, both ends included, for
-    the shared path (fp32 and bf16 output) and for per-shard sets."""
-    from test_parity_per_shard import assert_per_shard_selection_equal
+    k=64: 2.15 GB of codes, padded rows). The senders address it through
+    per-wave descriptors; the receivers take their general kernel there (the
+    window kernel spans a whole message with one 32-bit descriptor), and every
+    offset is 64-bit. Checked on sampled rows, both ends included, for the
+    shared path (fp32 and bf16 output) and for per-shard sets."""
+    from test_parity_per_shard import assert_per_shard_selection_equal, bf16_everywhere
     P, H, k, T = 8, 8192, 64, 65552
     pitch = B.btq_packed_pitch(H, k)
     assert P * T * pitch >= 2 ** 31
@@ -157,20 +154,15 @@ def test_message_beyond_2_gib():
                            set(np.random.default_rng(5).integers(0, T, 16).tolist())))
     ridx = torch.as_tensor(rows, device=DEV)
     xs = u16(x[:, ridx, :])
-    for name, sel_gpu, sel_orc, comp, deco in (
-            ("shared", sel_g, sel_o, B.btq_compress_pack, None),
-            ("per-shard", ps_g, ps_o, B.btq_compress_pack_per_shard, None)):
+    for name, sel_gpu, sel_orc, per in (("shared", sel_g, sel_o, False),
+                                        ("per-shard", ps_g, ps_o, True)):
         say(f"  {name} sets")
-        pk, ol = comp(x, k, sel_gpu["enc"], sel_gpu["outlier_idx"], sel_gpu["cmap"])
-        if name == "shared":
-            y = B.btq_decompress_reduce(pk, ol, H, sel_gpu["dec"], sel_gpu["outlier_idx"],
-                                        sel_gpu["cmap"])
-            y16 = B.btq_decompress_reduce_bf16(pk, ol, H, sel_gpu["dec"],
-                                               sel_gpu["outlier_idx"], sel_gpu["cmap"])
-        else:
-            y = B.btq_decompress_reduce_per_shard(pk, ol, H, sel_gpu["scale"],
-                                                  sel_gpu["zero_point"], sel_gpu["fmap"])
-            y16 = None
+        pk, ol = B.btq_compress_pack_ex(x, k, sel_gpu["rscale"], sel_gpu["zero_point"],
+                                        sel_gpu["outlier_idx"], sel_gpu["cmap"], per_shard=per,
+                                        pitch=pitch)
+        dec = (sel_gpu["scale"], sel_gpu["zero_point"], sel_gpu["fmap"])
+        y = B.btq_decompress_reduce_ex(pk, ol, H, *dec, per_shard=per)
+        y16 = None if per else B.btq_decompress_reduce_ex(pk, ol, H, *dec, bf16=True)
         torch.cuda.synchronize()
         pk_o, ol_o = oracle_compress_rows(xs, sel_orc, pitch=pitch)
         assert_bits_equal(pk[:, ridx, :], pk_o, f"packed ({name}, sampled rows)")
@@ -183,7 +175,8 @@ def test_message_beyond_2_gib():
             assert_y_bf16_close(y16[ridx].cpu().numpy(), y_o, sel_orc["scale"], sel_orc["idx"])
             assert torch.equal(y16[ridx], y[ridx].to(torch.bfloat16).view(torch.int16))
         else:
-            assert_bits_equal(y[ridx], y_o, "y (per-shard, sampled rows)")
+            assert_y_close(y[ridx].cpu().numpy(), y_o, sel_orc["scale"],
+                           bf16_everywhere(sel_orc))
         del pk, ol, y, y16
         torch.cuda.empty_cache()
     del x

@@ -1,15 +1,16 @@
 """GPU parity of per-shard BF16 sets (every shard keeps its own k widest
 features): selection, sender and receiver against the oracle.
 
-Bar: parameters, per-shard sets, maps and sender table bitwise; packed rows
-(with padding) and BF16 blocks bitwise; y within the receiver tolerance, with
-the features that are BF16 on every shard bit-exact. The lane-window receiver
-(P <= 8, H a multiple of 8) seeds each feature with -sum z*s and adds one fma
-per int4 term, then the BF16 values: within fp32 rounding of the oracle. The
-other two receivers evaluate every term as fl(q - z) * s and add the terms in
-shard order from +0, the oracle's arithmetic step for step, so their output
-is checked bit for bit. Every receiver output is also checked to repeat
-bitwise on a second call.
+Bar: parameters, per-shard sets and maps bitwise; packed rows (with
+padding) and BF16 blocks bitwise; y within the receiver tolerance, with the
+features that are BF16 on every shard bit-exact. The window receiver (P <= 8,
+H a multiple of 8, a pitch of at least 8 bytes and a multiple of 4) seeds
+each feature with -sum z*s over its int4 shards and adds one fma per int4
+term, then the shard-ordered sum of its BF16 values: within fp32 rounding of
+the oracle. The general receiver evaluates every term as fl(q - z) * s and
+adds the terms in shard order from +0, the oracle's arithmetic step for
+step, so its output is checked bit for bit. Every receiver output is also
+checked to repeat bitwise on a second call.
 """
 import numpy as np
 import pytest
@@ -18,8 +19,8 @@ import torch
 import bit_tensor_activation_amd as B
 from oracle import oracle as O
 import workloads as W
-from helpers import (assert_bits_equal, assert_stats_equal, assert_y_close, oracle_calib,
-                     oracle_compress_rows, say, u16)
+from helpers import (assert_bits_equal, assert_stats_equal, assert_y_close, assert_y_close_rows,
+                     oracle_calib, oracle_compress_rows, oracle_path, say, u16)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -27,8 +28,7 @@ DEV = torch.device("cuda:0")
 
 def assert_per_shard_selection_equal(g: dict, o: dict) -> None:
     for key, okey in (("scale", "scale"), ("rscale", "rscale"), ("zero_point", "zero_point"),
-                      ("outlier_idx", "idx"), ("fmap", "fmap"), ("cmap", "cmap"),
-                      ("enc", "enc")):
+                      ("outlier_idx", "idx"), ("fmap", "fmap"), ("cmap", "cmap")):
         assert_bits_equal(g[key], np.asarray(o[okey]), key)
 
 
@@ -54,29 +54,36 @@ def run_both(calib_xs, x, k, momentum, *, pitch=None):
     assert_per_shard_selection_equal(sel_g, sel_o)
     if pitch is None:
         pitch = B.btq_packed_pitch(H, k)
-    pk, ol = B.btq_compress_pack_per_shard(x, k, sel_g["enc"], sel_g["outlier_idx"],
-                                           sel_g["cmap"], pitch=pitch)
+    args = (sel_g["rscale"], sel_g["zero_point"], sel_g["outlier_idx"], sel_g["cmap"])
+    if pitch == B.btq_packed_row_bytes(H, k):   # the per-shard call: rows with no gap
+        pk, ol = B.btq_compress_pack_per_shard(x, k, *args)
+    else:
+        pk, ol = B.btq_compress_pack_ex(x, k, *args, per_shard=True, pitch=pitch)
     pk_o, ol_o = oracle_compress_rows(u16(x), sel_o, pitch=pitch)
     torch.cuda.synchronize()
     assert_bits_equal(pk, pk_o, "packed")
     assert_bits_equal(ol.view(torch.int16), ol_o.view(np.int16), "outliers")
-    y = B.btq_decompress_reduce_per_shard(pk, ol, H, sel_g["scale"], sel_g["zero_point"],
-                                          sel_g["fmap"])
-    y2 = B.btq_decompress_reduce_per_shard(pk, ol, H, sel_g["scale"], sel_g["zero_point"],
-                                           sel_g["fmap"])
+    par = (sel_g["scale"], sel_g["zero_point"], sel_g["fmap"])
+    if pitch == B.btq_packed_row_bytes(H, k):
+        y = B.btq_decompress_reduce_per_shard(pk, ol, H, *par)
+    else:
+        y = B.btq_decompress_reduce_ex(pk, ol, H, *par, per_shard=True)
+    y2 = B.btq_decompress_reduce_ex(pk, ol, H, *par, per_shard=True)
+    y16 = B.btq_decompress_reduce_ex(pk, ol, H, *par, per_shard=True, bf16=True)
     y_o = O.decompress_reduce(pk_o, ol_o, sel_o["scale"], sel_o["zero_point"], sel_o["fmap"])
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int32), y2.view(torch.int32)), "y does not repeat"
+    assert torch.equal(y16, y.to(torch.bfloat16).view(torch.int16)), "bf16 y is not RNE(fp32 y)"
     assert_y_close(y.cpu().numpy(), y_o, sel_o["scale"], bf16_everywhere(sel_o))
-    if not lane_window_receiver(P, T, H, pk.shape[2]):
+    if not window_receiver(P, H, pk.shape[2]):
         assert_bits_equal(y, y_o, "y")
     return sel_g, sel_o
 
 
-def lane_window_receiver(P, T, H, pitch):
-    """Whether btq_decompress_reduce_per_shard takes its lane-window kernel
-    (torch's allocations meet its alignment and size conditions here)."""
-    return T > 2 and P <= 8 and H % 8 == 0 and pitch % 4 == 0 and pitch >= 8
+def window_receiver(P, H, pitch):
+    """Whether the receiver takes its window kernel (torch's allocations meet
+    its alignment and size conditions here)."""
+    return P <= 8 and H % 8 == 0 and pitch % 4 == 0 and pitch >= 8
 
 
 def shard_local(P, T, H, seed, factor=30.0):
@@ -96,24 +103,24 @@ CASES = [
     (2, 9, 256, 0, None, "k=0"),
     (2, 9, 256, 256, None, "k=H"),
     (5, 33, 1032, 13, None, "H-k odd"),
-    (8, 3, 4104, 64, None, "T below the rows per thread, partial feature block"),
+    (8, 3, 4104, 64, None, "T=3, partial last tile"),
     (4, 6, 2048, 24, 0, "pitch = code bytes (multiple of 4)"),
     (4, 6, 2048, 23, 0, "pitch = code bytes (odd): general receiver"),
     (4, 6, 2048, 24, 4, "pitch = code bytes + 4"),
     (1, 16, 512, 16, None, "one shard"),
-    (4, 6, 2048, 100, None, "k in (64, 128]: two outlier registers"),
-    (8, 5, 4096, 300, None, "k > 128: four outlier registers"),
-    (9, 7, 1024, 16, None, "P=9: shard-loop kernel"),
+    (4, 6, 2048, 100, None, "k in (64, 128]: two entry registers"),
+    (8, 5, 4096, 300, None, "k > 128: four entry registers, post-loop recompute"),
+    (9, 7, 1024, 16, None, "P=9: general kernel"),
     (9, 7, 1020, 16, None, "P=9, H not a multiple of 8: general kernel"),
-    (3, 40, 1028, 9, None, "H a multiple of 4 but not 8, partial last window"),
+    (3, 40, 1028, 9, None, "H a multiple of 4 but not 8: general kernel"),
     (2, 5, 24, 8, 0, "pitch = 8 bytes: the code window moves back one dword"),
     (2, 5, 12, 4, 0, "pitch = 4 bytes: general kernel"),
     (8, 33, 4096, 64, 0, "7B-like rows, pitch = code bytes"),
     (3, 5, 16, 14, None, "k=H-2: two int4 slots"),
     (2, 4, 4, 1, None, "H=4"),
-    (16, 3, 64, 2, None, "P=16: shard-loop kernel"),
-    (8, 1, 8192, 64, None, "T=1 (decode): register kernel"),
-    (4, 2, 1024, 16, None, "T=2: register kernel"),
+    (16, 3, 64, 2, None, "P=16: general kernel"),
+    (8, 1, 8192, 64, None, "T=1 (decode): 2-row ring"),
+    (4, 2, 1024, 16, None, "T=2"),
 ]
 
 
@@ -151,12 +158,12 @@ def test_signed_zero_ranges_rank_by_feature():
 
 @pytest.mark.parametrize("name,k,T,nb", [("7b_prefill", 64, 2048, 4), ("stress", 256, 16384, 2),
                                          ("large_prefill", 128, 8192, 2)])
-def test_full_size_sampled_rows(name, k, T, nb):
+def test_full_size(name, k, T, nb):
     """A workload's full shape with nb of its calibration batches, through the
-    per-shard calls; sampled rows against the oracle. At stress size the
+    per-shard calls; every element against the oracle. At stress size the
     tiles hold up to P*k/16 BF16 values per row on average, so the receiver
-    runs with four entry registers and 64-row waves, and tiles beyond four
-    registers take the post-loop pass."""
+    runs with four entry registers, and tiles beyond four registers take the
+    post-loop recompute."""
     w = W.WORKLOADS[name]
     P, H = w.P, w.H
     say(f"case: per-shard sets at full size {name} P={P} T={T} H={H} k={k}")
@@ -172,22 +179,16 @@ def test_full_size_sampled_rows(name, k, T, nb):
     torch.cuda.synchronize()
     assert_per_shard_selection_equal(sel_g, sel_o)
     x = W.batch(w, W.PHASE_INFER, 0, T=T, device=DEV)
-    pk, ol = B.btq_compress_pack_per_shard(x, k, sel_g["enc"], sel_g["outlier_idx"],
-                                           sel_g["cmap"])
+    pk, ol = B.btq_compress_pack_per_shard(x, k, sel_g["rscale"], sel_g["zero_point"],
+                                           sel_g["outlier_idx"], sel_g["cmap"])
     y = B.btq_decompress_reduce_per_shard(pk, ol, H, sel_g["scale"], sel_g["zero_point"],
                                           sel_g["fmap"])
     torch.cuda.synchronize()
-    Bq = B.btq_packed_row_bytes(H, k)
-    assert not bool(pk[:, :, Bq:].any()), "packed padding bytes must be zero"
-    rows = np.array(sorted({0, 1, 3, 4, 511, 1024, T - 2, T - 1} |
-                           set(np.random.default_rng(7).integers(0, T, 20).tolist())))
-    ridx = torch.as_tensor(rows, device=DEV)
-    pk_o, ol_o = oracle_compress_rows(u16(x[:, ridx, :]), sel_o, pitch=pk.shape[2])
-    assert_bits_equal(pk[:, ridx, :], pk_o, "packed (sampled rows)")
-    assert_bits_equal(ol[:, ridx, :].view(torch.int16), ol_o.view(np.int16), "outliers")
-    y_o = O.decompress_reduce(pk_o, ol_o, sel_o["scale"], sel_o["zero_point"], sel_o["fmap"])
-    assert_y_close(y[ridx].cpu().numpy(), y_o, sel_o["scale"], bf16_everywhere(sel_o))
-    assert lane_window_receiver(P, T, H, pk.shape[2])
+    pk_o, ol_o, y_o = oracle_path(u16(x), sel_o)
+    assert_bits_equal(pk, pk_o, "packed")
+    assert_bits_equal(ol.view(torch.int16), ol_o.view(np.int16), "outliers")
+    assert_y_close_rows(y, y_o, sel_o["scale"], bf16_everywhere(sel_o))
+    assert window_receiver(P, H, pk.shape[2])
 
 
 def test_sets_concentrated_in_one_tile():

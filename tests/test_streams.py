@@ -2,7 +2,9 @@
 keeps no state between calls (GPU).
 
   * the whole path on a side stream gives the same bytes as on the default
-    stream;
+    stream, also when the stream is only passed as an argument (outputs and
+    workspaces the binding allocates belong to that stream, so torch does not
+    hand them to other work while the kernels still use them);
   * two codecs on two streams at once give the same bytes as one after the
     other;
   * compress and both receivers captured in a graph and replayed, with new
@@ -35,10 +37,11 @@ def full_path(x_calib, x, stream=None):
     for b, xb in enumerate(x_calib):
         B.btq_calib_update(xb, rmin, rmax, 0.9, b == 0, stream=stream)
     sel = B.btq_select_outliers(rmin, rmax, K, stream=stream)
-    pk, ol = B.btq_compress_pack(x, K, sel["enc"], sel["outlier_idx"], sel["cmap"], stream=stream)
-    y = B.btq_decompress_reduce(pk, ol, H, sel["dec"], sel["outlier_idx"], sel["cmap"],
+    pk, ol = B.btq_compress_pack(x, K, sel["rscale"], sel["zero_point"], sel["outlier_idx"],
+                                 sel["cmap"], stream=stream)
+    y = B.btq_decompress_reduce(pk, ol, H, sel["scale"], sel["zero_point"], sel["fmap"],
                                 stream=stream)
-    return [rmin, rmax, sel["scale"], sel["cmap"], sel["enc"], sel["dec"], pk, ol, y]
+    return [rmin, rmax, sel["scale"], sel["zero_point"], sel["cmap"], sel["fmap"], pk, ol, y]
 
 
 def same_bytes(a, b):
@@ -56,6 +59,31 @@ def test_side_stream_matches_default_stream():
     with torch.cuda.stream(side):
         got = full_path(calib, x, stream=side)
     side.synchronize()
+    for a, b in zip(ref, got):
+        assert same_bytes(a, b)
+
+
+def test_stream_argument_alone_orders_the_binding_allocations():
+    # The side stream is kept busy, so its calls run late. Their workspaces
+    # and outputs are allocated by the binding and (the workspaces) freed
+    # when each call returns; the default stream then allocates and fills
+    # memory of the same sizes at once. Were the binding's memory tied to the
+    # default stream, those fills could land in a workspace or output before
+    # the side stream's kernels are done with it.
+    say("case: stream passed as an argument only, side stream busy")
+    calib = [draw(7000 + b) for b in range(2)]
+    x = draw(7100)
+    torch.cuda.synchronize()
+    ref = full_path(calib, x)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=DEV)   # default priority
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)      # a bounded spin: the side stream runs late
+    got = full_path(calib, x, stream=side)
+    junk = [torch.full((1 << 20,), -7, dtype=torch.int32, device=DEV) for _ in range(64)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
     for a, b in zip(ref, got):
         assert same_bytes(a, b)
 
@@ -92,14 +120,13 @@ def test_graph_replays_match_eager_calls():
     ol = torch.empty((P, T, K), dtype=torch.int16, device=DEV)
     y = torch.empty((T, H), dtype=torch.float32, device=DEV)
     y16 = torch.empty((T, H), dtype=torch.int16, device=DEV)
-    args = (sel["enc"], sel["outlier_idx"], sel["cmap"])
+    enc = (sel["rscale"], sel["zero_point"], sel["outlier_idx"], sel["cmap"])
+    dec = (sel["scale"], sel["zero_point"], sel["fmap"])
 
     def step(stream=None):
-        B.btq_compress_pack(x_static, K, *args, packed=pk, outliers=ol, stream=stream)
-        B.btq_decompress_reduce(pk, ol, H, sel["dec"], sel["outlier_idx"], sel["cmap"], y=y,
-                                stream=stream)
-        B.btq_decompress_reduce_bf16(pk, ol, H, sel["dec"], sel["outlier_idx"], sel["cmap"],
-                                     y=y16, stream=stream)
+        B.btq_compress_pack_ex(x_static, K, *enc, packed=pk, outliers=ol, stream=stream)
+        B.btq_decompress_reduce_ex(pk, ol, H, *dec, y=y, stream=stream)
+        B.btq_decompress_reduce_ex(pk, ol, H, *dec, y=y16, bf16=True, stream=stream)
 
     x_static.copy_(draw(7500))
     step()                      # eager warm-up, on the default stream
@@ -129,15 +156,15 @@ def test_graph_replays_per_shard_sets():
     for b, xb in enumerate(calib):
         B.btq_calib_update(xb, rmin, rmax, 0.9, b == 0)
     sel = B.btq_select_outliers_per_shard(rmin, rmax, K)
-    pitch = B.btq_packed_pitch(H, K)
+    pitch = B.btq_packed_row_bytes(H, K)
     x_static = torch.empty((P, T, H), dtype=torch.int16, device=DEV)
     pk = torch.empty((P, T, pitch), dtype=torch.uint8, device=DEV)
     ol = torch.empty((P, T, K), dtype=torch.int16, device=DEV)
     y = torch.empty((T, H), dtype=torch.float32, device=DEV)
 
     def step():
-        B.btq_compress_pack_per_shard(x_static, K, sel["enc"], sel["outlier_idx"], sel["cmap"],
-                                      packed=pk, outliers=ol)
+        B.btq_compress_pack_per_shard(x_static, K, sel["rscale"], sel["zero_point"],
+                                      sel["outlier_idx"], sel["cmap"], packed=pk, outliers=ol)
         B.btq_decompress_reduce_per_shard(pk, ol, H, sel["scale"], sel["zero_point"],
                                           sel["fmap"], y=y)
 

@@ -41,7 +41,7 @@ class Workload:
     P: int                   # shards (tensor-parallel devices)
     T: tuple                 # token counts of the inference batches
     H: int                   # hidden features
-    ks: tuple                # BF16 feature counts to run
+    ks: tuple                # BF16 feature counts to run (the first is the default)
     base: str                # "normal" or "laplace"
     sigma: float             # std of the normal base (ignored for laplace)
     n_outliers: int          # planted outlier columns
@@ -71,7 +71,7 @@ WORKLOADS = {
         Workload("large_prefill", 3, P=4, T=(8192,), H=8192, ks=(128,), base="normal",
                  sigma=1.0, n_outliers=164, outlier_mode="scale", outlier_factor=200.0,
                  calib_batches=64, calib_T=8192, momentum=0.95),
-        Workload("stress", 4, P=8, T=(16384,), H=8192, ks=(0, 32, 256), base="laplace",
+        Workload("stress", 4, P=8, T=(16384,), H=8192, ks=(32, 0, 256), base="laplace",
                  sigma=1.0, n_outliers=164, outlier_mode="scale", outlier_factor=100.0,
                  calib_batches=32, calib_T=16384, momentum=0.9, drift=16),
     )
