@@ -152,6 +152,34 @@ def test_shapes(P, T, H, k, base, cols, note):
     run_both(calib, x, k, 0.9)
 
 
+# Batches long enough for the LDS-ring receiver (at least 8 rows per wave of
+# about 1024 waves): ragged row blocks, a partial last tile, 1-8 shards, an
+# odd code count (dense rows then take the general receiver, padded rows the
+# LDS ring), clustered BF16 features (four entry registers; tiles beyond
+# them take the post-loop pass) and k = 256 of 8192.
+# (P, T, H, k, base, outlier columns, note)
+LDS_RING_CASES = [
+    (8, 2050, 4096, 64, "normal", list(range(5, 4096, 97)), "7B-like, ragged last row block"),
+    (4, 2600, 4104, 8, "laplace", [0, 1, 2, 4103], "partial last tile"),
+    (3, 3000, 2056, 24, "normal", [10, 500, 2055], "P=3"),
+    (1, 9000, 1024, 0, "normal", [], "P=1, k=0"),
+    (8, 2048, 2048, 200, "normal", list(range(300, 500)), "200 clustered BF16 features"),
+    (8, 1024, 8192, 256, "laplace", list(range(3, 8192, 61)), "k=256 of 8192"),
+    (5, 4000, 2048, 13, "normal", [1, 2, 3], "odd code count"),
+    (8, 2048, 4096, 0, "laplace", [], "P=8, k=0"),
+]
+
+
+@pytest.mark.parametrize("P,T,H,k,base,cols,note", LDS_RING_CASES,
+                         ids=[c[-1] for c in LDS_RING_CASES])
+def test_lds_ring_shapes(P, T, H, k, base, cols, note):
+    say(f"case: LDS ring P={P} T={T} H={H} k={k} ({note})")
+    calib = [W.draw(P, 64, H, 1500 + b, base=base, cols=cols, outlier_factor=40.0, device=DEV)
+             for b in range(2)]
+    x = W.draw(P, T, H, 2500, base=base, cols=cols, outlier_factor=40.0, device=DEV)
+    run_both(calib, x, k, 0.9)
+
+
 # (P, T, H, k, note): a seeded random BF16 set of size k
 SET_CASES = [
     (2, 16, 256, 8, "tiny shape"),
