@@ -21,9 +21,12 @@
 //     starts from the constant -sum_p z*s over its int4 shards, and a high
 //     nibble, kept in place as 16q, meets its scale divided by 16 (exact).
 //     The first kR token rows are issued once the map has arrived.
-//  1. Per token row, one 8-byte code load per shard and lane: each packed
-//     byte is read from HBM once (neighbouring lanes' windows overlap in the
-//     L1, not in HBM). Each term is one byte-to-float conversion and one fma.
+//  1. Per token row and shard, the tile's code span (at most 66 dwords) is
+//     one coalesced 8-byte load on the first 33 lanes, so every packed byte
+//     is requested once; the span goes through the wave's LDS stage, where
+//     each lane reads its 8-byte window. (Loading the overlapping windows
+//     straight from memory requests most bytes twice, and measured about
+//     15% slower.) Each term is one byte-to-float conversion and one fma.
 //  2. BF16 values: the tile's entries of every shard (a contiguous run of
 //     each shard's outlier block) ride in kOR registers across the wave,
 //     loaded coalesced. They are written to a per-wave LDS table with one
@@ -31,8 +34,10 @@
 //     it is int4), and the lane that owns the feature adds its row in shard
 //     order from +0: no atomics, so the order is fixed by construction. A
 //     feature BF16 on every shard has no int4 term, so its output is that
-//     sum exactly. A tile with more entries than the registers hold
-//     recomputes its BF16 features after the row loop, term by term.
+//     sum exactly. The sum reaches its feature through a select, so no other
+//     feature sees it (not even a non-finite one). A tile with more entries
+//     than the registers hold recomputes its BF16 features after the row
+//     loop, term by term.
 //
 // General kernel: one thread per (token, feature). It evaluates each term as
 // fl(q - z) * s, or the BF16 value, and adds the terms in shard order from
@@ -92,30 +97,23 @@ __device__ __forceinline__ int first_lane_value(bool has, int v) {
   return m ? __builtin_amdgcn_readlane(v, __ffsll((unsigned long long)m) - 1) : 0;
 }
 
-// The owner's BF16 sums into its 8 outputs: the first one's feature takes
-// it through an fma with a 0/1 mask fixed for the wave (adding o*0 leaves a
-// value unchanged, o*1 is exact), further ones, rare, through selects.
-__device__ __forceinline__ void place_bf16_first(float (&acc)[kWinFeat], const float (&m0)[kWinFeat],
-                                                 float o) {
-#pragma unroll
-  for (int e = 0; e < kWinFeat; ++e) acc[e] = fmaf(o, m0[e], acc[e]);
-}
-__device__ __forceinline__ void place_bf16_at(float (&acc)[kWinFeat], int eu, float o) {
-#pragma unroll
-  for (int e = 0; e < kWinFeat; ++e) acc[e] = (e == eu) ? __fadd_rn(acc[e], o) : acc[e];
-}
+// Staged code dwords per shard and row: every lane writes 8 bytes, the
+// first 33 lanes the tile's code span of at most 66 dwords.
+constexpr int kStageDwords = 2 * kWave;
+constexpr int kStageLanes = 33;
 
 // LDS per wave of the window kernel, in dwords: the BF16 table (one row of
 // NP floats per BF16 feature of the tile, at most kOR*64 entries), the entry
 // -> table-row map of per-shard sets (kOR*64 ints), one private dummy dword
-// per lane for entries past the tile's count, and for fp32 output the 2 KB
-// row that turns the lanes' 32-byte runs into whole-line stores.
+// per lane for entries past the tile's count, for fp32 output the 2 KB row
+// that turns the lanes' 32-byte runs into whole-line stores, and the stage
+// of one row's code spans.
 template <int NP, int kOR, bool kPs>
 __host__ __device__ constexpr int win_tab_dwords() { return kPs ? NP * kOR * kWave : kOR * kWave; }
 template <int NP, int kOR, bool kPs, bool kBf>
 __host__ __device__ constexpr int win_lds_dwords() {
   return win_tab_dwords<NP, kOR, kPs>() + (kPs ? kOR * kWave : 0) + kWave +
-         (kBf ? 0 : kWinTile);
+         (kBf ? 0 : kWinTile) + NP * kStageDwords;
 }
 
 // NP: shards (1..8). kOR: BF16 entry registers per row. kR: ring depth.
@@ -145,6 +143,7 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
   int* const inv = reinterpret_cast<int*>(tab + win_tab_dwords<NP, kOR, kPs>());
   float* const dummy = tab + win_tab_dwords<NP, kOR, kPs>() + (kPs ? kOR * kWave : 0);
   float* const yrow = dummy + kWave;   // fp32 output only
+  uint32_t* const stage = reinterpret_cast<uint32_t*>(yrow + (kBf ? 0 : kWinTile));
 
   // ---- setup (a): the lane's map entries first, then scales and zero points
   const rsrc_t rf = make_rsrc(fmap, (uint32_t)(NM * (int64_t)H * 4));
@@ -217,6 +216,23 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
     nib_hi[m] = hi;
   }
 
+  // ---- the tile's code span per map. The lanes' windows are nondecreasing
+  // in lane order and the last starts at most 63 dwords after the first, so
+  // the span from the first window's dword (rounded down to even) holds at
+  // most 66 dwords: the first 33 lanes load it with one coalesced 8-byte
+  // load each, every code byte once. Each row's span goes through the
+  // wave's LDS stage, where each lane reads its own window.
+  uint32_t cl[NM], dwin[NM];   // lane's load offset in the row; its window's stage dword
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const uint64_t has = __ballot(cb[m] != kOOB);
+    const uint32_t a = has ? ((uint32_t)__builtin_amdgcn_readlane(
+                                  (int)cb[m], __ffsll((unsigned long long)has) - 1) >> 2) & ~1u
+                           : 0u;
+    cl[m] = (has && lane < kStageLanes) ? 4u * a + 8u * (uint32_t)lane : kOOB;
+    dwin[m] = cb[m] != kOOB ? (cb[m] >> 2) - a : 0u;
+  }
+
   // ---- the ring's code loads: the first kR rows, issued before anything
   // else waits. One descriptor spans this wave's rows of every shard (the
   // launcher keeps the message under 2^31 bytes); the shard and row ride in
@@ -233,7 +249,7 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
     const uint32_t so = (uint32_t)min(row, nrows - 1) * (uint32_t)pitch;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const auto t = __builtin_amdgcn_raw_buffer_load_b64(ok ? rpk : rnone, cb[kPs ? p : 0],
+      const auto t = __builtin_amdgcn_raw_buffer_load_b64(ok ? rpk : rnone, cl[kPs ? p : 0],
                                                           so + (uint32_t)p * shard_bytes, kStream);
       w[q][p] = v2u{t[0], t[1]};
     }
@@ -327,7 +343,9 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
     issue_fence();
   }
 
-  // ---- per-lane constants (their loads are older than the ring)
+  // ---- per-lane constants (their loads are older than the ring). A term
+  // of a shard where the feature is BF16 has code 0 and scale 0, so it adds
+  // exactly 0 whatever that shard's scale is.
   float sc[NP][kWinFeat], bias[kWinFeat];
 #pragma unroll
   for (int e = 0; e < kWinFeat; ++e) bias[e] = 0.0f;
@@ -341,7 +359,7 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
       const bool q4 = fm[m][e] >= 0 && fm[m][e] != INT_MAX;
       // -sum_p z*s over the int4 shards, fp32 steps in shard order from +0
       if (q4) bias[e] = __fsub_rn(bias[e], __fmul_rn(z, s));
-      sc[p][e] = ((nib_hi[m] >> e) & 1) ? s * 0.0625f : s;
+      sc[p][e] = q4 ? (((nib_hi[m] >> e) & 1) ? s * 0.0625f : s) : 0.0f;
       settle(sc[p][e]);
     }
   }
@@ -352,10 +370,16 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
   // wave's LDS row (values 0-3 of every lane in the first half, 4-7 in the
   // second), and lane m stores features 4m..4m+3 and 256+4m..256+4m+3 of
   // the tile: each store instruction writes 1 KB of whole lines.
-  float m0[kWinFeat];   // 1 at the lane's first BF16 feature
+  const int e_first = __builtin_ctz(any | (1 << kWinFeat));   // kWinFeat: none
+  const int any_rest = any & (any - 1);                      // BF16 features past the first
+  // The owner's BF16 sum into its feature eu: one set per shard adds it to
+  // the int4 part; with one set it is the whole value (the int4 part is +0).
+  // A select, so no other feature ever sees the sum.
+  auto place = [&](float (&acc)[kWinFeat], int eu, float o) {
 #pragma unroll
-  for (int e = 0; e < kWinFeat; ++e) m0[e] = (any != 0 && e == __builtin_ctz(any | 256)) ? 1.0f : 0.0f;
-  const int any_rest = any & (any - 1);   // BF16 features past the first
+    for (int e = 0; e < kWinFeat; ++e)
+      acc[e] = (e == eu) ? (kPs ? __fadd_rn(acc[e], o) : o) : acc[e];
+  };
   const uint32_t st_off = active ? (uint32_t)h0 * kYB : kOOB;
   const uint32_t st_a = (f0 + 4 * lane < H) ? (uint32_t)(f0 + 4 * lane) * 4u : kOOB;
   const uint32_t st_b = (f0 + 256 + 4 * lane < H) ? (uint32_t)(f0 + 256 + 4 * lane) * 4u : kOOB;
@@ -376,13 +400,22 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
 #pragma unroll
     for (int q = 0; q < kR; ++q) {
       const int row = base + q;
-      // BF16 entries of the row into the table, then the owners' first row
-      // read, so its LDS round trip overlaps the int4 arithmetic
+      // the row's code spans and BF16 entries into LDS; then each lane's
+      // code windows and the owners' first table row
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+        *reinterpret_cast<v2u*>(stage + p * kStageDwords + 2 * lane) = w[q][p];
       if (compact && nb_any > 0) {
 #pragma unroll
         for (int r = 0; r < kOR; ++r) tab[e_dst[r]] = __uint_as_float(ov[q][r] << 16);
       }
       wave_lds_sync();
+      v2u x[NP];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const uint32_t* src = stage + p * kStageDwords + dwin[kPs ? p : 0];
+        x[p] = v2u{src[0], src[1]};
+      }
       float v0[NP];
       if (compact && umax > 0) {
         const float* t = tab + (cnt_any > 0 ? pos0 : 0) * NP;
@@ -404,8 +437,8 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const int m = kPs ? p : 0;
-        uint32_t a = __builtin_amdgcn_perm(w[q][p][1], w[q][p][0], selA[m]) & mskA[m];
-        uint32_t b = __builtin_amdgcn_perm(w[q][p][1], w[q][p][0], selB[m]) & mskB[m];
+        uint32_t a = __builtin_amdgcn_perm(x[p][1], x[p][0], selA[m]) & mskA[m];
+        uint32_t b = __builtin_amdgcn_perm(x[p][1], x[p][0], selB[m]) & mskB[m];
         // kept whole: each byte converts with one v_cvt_f32_ubyteN
         opaque(a);
         opaque(b);
@@ -424,14 +457,14 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
         float o = 0.0f;
 #pragma unroll
         for (int p = 0; p < NP; ++p) o = __fadd_rn(o, v0[p]);
-        place_bf16_first(acc, m0, o);
+        place(acc, e_first, o);
         int rest = any_rest;
         for (int u = 1; u < umax; ++u) {   // lanes with several BF16 features
           const float* t = tab + (u < cnt_any ? pos0 + u : 0) * NP;
           float ou = 0.0f;
 #pragma unroll
           for (int p = 0; p < NP; ++p) ou = __fadd_rn(ou, t[p]);
-          place_bf16_at(acc, rest ? __builtin_ctz(rest) : kWinFeat, ou);
+          place(acc, rest ? __builtin_ctz(rest) : kWinFeat, ou);
           rest &= rest - 1;
         }
       }
@@ -455,8 +488,8 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
             v4u{__float_as_uint(yb[0]), __float_as_uint(yb[1]), __float_as_uint(yb[2]),
                 __float_as_uint(yb[3])},
             ry, st_b, 0, kStream);
-        wave_lds_sync();   // the next row's values overwrite the LDS row
       }
+      wave_lds_sync();   // the next row overwrites the stage, the table and the LDS row
     }
     base += kR;
   } while (base < nrows);
@@ -487,378 +520,6 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
             term = bf16_to_f32(outl[rowg * k + (-1 - f)]);
           }
           o = __fadd_rn(o, term);
-        }
-        char* d = ybase + ((int64_t)r * H + h) * kYB;
-        if constexpr (kBf)
-          *reinterpret_cast<uint16_t*>(d) = bf16_rne(o);
-        else
-          *reinterpret_cast<float*>(d) = o;
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// LDS-ring kernel (shared set; the fast path where it fits). The same tiles,
-// lane windows, arithmetic and BF16 table as the window kernel, but the
-// token rows' codes travel from HBM straight into LDS (buffer loads with an
-// LDS destination, 16 bytes per lane): a ring slot holds one row's code span
-// of every shard, so the ring's depth costs LDS instead of registers and a
-// wave keeps kD rows in flight. Per row and shard the tile's codes lie in a
-// span of at most kSpanChunks 16-byte chunks starting at the 16-byte aligned
-// offset at or below the first lane's window; chunk g = p*nck + c of a row
-// lands at LDS byte 16*g of its slot, and each lane reads its 8 bytes of
-// shard p there with two dword reads.
-//
-// The vector-memory counter retires in issue order, and the compiler does
-// not wait for loads into LDS before reading LDS, so each row waits
-// explicitly: when row r is consumed, exactly the loads and stores issued
-// after its own may still be in flight (counted at compile time).
-constexpr int kSpanChunks = 18;   // 256 code bytes of a tile + alignment slack
-constexpr int kLdsRingMax = 8;    // rows per wave are a multiple of the ring depth
-
-__host__ __device__ constexpr int lds_code_insts(int np) { return (np * kSpanChunks + kWave - 1) / kWave; }
-// ring depth: the deepest whose waits fit the 6-bit counter (<= 63 in flight)
-// and whose LDS fits 4 waves in 152 KB
-__host__ __device__ constexpr int lds_ring_depth(int np, int kor, bool bf) {
-  const int per_row = lds_code_insts(np) + kor + (bf ? 1 : 2);
-  const int by_cnt = (63 - (bf ? 1 : 2)) / per_row + 1;
-  const int fixed = kor * kWave + kWave + (bf ? 0 : kWinTile);   // dwords
-  const int by_lds = (38 * 1024 / 4 - fixed) / (lds_code_insts(np) * 256);
-  const int d = by_cnt < by_lds ? by_cnt : by_lds;
-  return d < kLdsRingMax ? d : kLdsRingMax;
-}
-template <int NP, int kOR, bool kBf>
-__host__ __device__ constexpr int lds_wave_dwords() {
-  return lds_ring_depth(NP, kOR, kBf) * lds_code_insts(NP) * 256 + kOR * kWave + kWave +
-         (kBf ? 0 : kWinTile);
-}
-
-// s_waitcnt with only the vector-memory count (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N <= 63, "vmcnt range");
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
-// lds + 16*l. (A device function of its own: the host pass of a kernel
-// template does not take this builtin in the kernel's body.)
-__device__ __forceinline__ void lds_load16(rsrc_t r, float* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voff, soff, 0, kStream);
-}
-
-template <int NP, int kOR, bool kBf>
-__global__ __launch_bounds__(256) void dq_lds_kernel(
-    const uint8_t* __restrict__ packed, int pitch, const uint16_t* __restrict__ outl, int64_t T,
-    int H, int k, int ntiles, int rows_per_wave, int64_t nrowblk, const float* __restrict__ scale,
-    const uint8_t* __restrict__ zp, const int32_t* __restrict__ fmap, void* __restrict__ y) {
-  constexpr int kCI = lds_code_insts(NP);         // code loads per row (16 B per lane)
-  constexpr int kD = lds_ring_depth(NP, kOR, kBf); // rows in flight
-  constexpr int kS = kBf ? 1 : 2;                 // y stores per row
-  constexpr int kSlot = kCI * 256;                 // dwords of codes per ring slot
-  constexpr uint32_t kYB = kBf ? 2u : 4u;
-  // (static LDS: more than 64 KB per block, which gfx950's 160 KB allows)
-  __shared__ __align__(16) float lds_smem[kDqWaves * lds_wave_dwords<NP, kOR, kBf>()];
-  int64_t rb, sub;
-  const int ntgrp = (ntiles + kDqWaves - 1) / kDqWaves;
-  if (!xcd_unit_block(blockIdx.x, ntgrp, nrowblk, &rb, &sub)) return;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = (int)sub * kDqWaves + wave;
-  if (c >= ntiles) return;   // past the last tile (no block barrier below)
-  const int f0 = c * kWinTile;
-  const int h0 = f0 + kWinFeat * lane;
-  const bool active = h0 < H;
-  const int64_t t0 = rb * rows_per_wave;
-  const int nrows = (int)min(T - t0, (int64_t)rows_per_wave);   // >= 1
-  float* const ring = lds_smem + (size_t)wave * lds_wave_dwords<NP, kOR, kBf>();
-  float* const tab = ring + kD * kSlot;
-  float* const dummy = tab + kOR * kWave;
-  float* const yrow = dummy + kWave;   // fp32 output only
-
-  // ---- setup (a): the lane's map entries first, then scales and zero points
-  const rsrc_t rf = make_rsrc(fmap, (uint32_t)((int64_t)H * 4));
-  const rsrc_t rs = make_rsrc(scale, (uint32_t)(NP * (int64_t)H * 4));
-  const rsrc_t rz = make_rsrc(zp, (uint32_t)(NP * (int64_t)H));
-  const uint32_t lo4 = active ? (uint32_t)h0 * 4u : kOOB;
-  const uint32_t lo1 = active ? (uint32_t)h0 : kOOB;
-  const v4u fva = __builtin_amdgcn_raw_buffer_load_b128(rf, lo4, 0, 0);
-  const v4u fvb = __builtin_amdgcn_raw_buffer_load_b128(rf, lo4 + 16u, 0, 0);
-  v4u sv[NP][2];
-  v2u zv[NP];
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    sv[p][0] = __builtin_amdgcn_raw_buffer_load_b128(rs, lo4, (uint32_t)(p * H * 4), 0);
-    sv[p][1] = __builtin_amdgcn_raw_buffer_load_b128(rs, lo4 + 16u, (uint32_t)(p * H * 4), 0);
-    const auto t = __builtin_amdgcn_raw_buffer_load_b64(rz, lo1, (uint32_t)(p * H), 0);
-    zv[p] = v2u{t[0], t[1]};
-  }
-  issue_fence();
-
-  // ---- setup (b): the code window and byte selectors (one map)
-  int fm[kWinFeat];
-#pragma unroll
-  for (int e = 0; e < kWinFeat; ++e)
-    fm[e] = active ? (int)(e < 4 ? fva[e] : fvb[e - 4]) : INT_MAX;
-  int jf = INT_MAX;
-  uint32_t bfm = 0;
-#pragma unroll
-  for (int e = 0; e < kWinFeat; ++e) {
-    if (fm[e] >= 0 && fm[e] != INT_MAX) jf = min(jf, fm[e]);
-    if (fm[e] < 0) bfm |= 1u << e;
-  }
-  int cbase = jf == INT_MAX ? 0 : ((jf >> 1) & ~3);
-  if (cbase + 8 > pitch) cbase -= 4;   // (pitch >= 8)
-  const bool has4 = jf != INT_MAX;
-  uint32_t selA = 0, selB = 0, mskA = 0, mskB = 0;
-  int nib_hi = 0;
-#pragma unroll
-  for (int e = 0; e < kWinFeat; ++e) {
-    uint32_t sel = 0x0Cu, msk = 0u;   // selector 0x0C gives a zero byte
-    if (fm[e] >= 0 && fm[e] != INT_MAX) {
-      const int n = fm[e] - 2 * cbase;   // nibble 0..15 of the 8 bytes
-      sel = (uint32_t)(n >> 1);
-      msk = (n & 1) ? 0xF0u : 0x0Fu;
-      nib_hi |= (n & 1) << e;
-    }
-    if (e < 4) {
-      selA |= sel << (8 * e);
-      mskA |= msk << (8 * e);
-    } else {
-      selB |= sel << (8 * (e - 4));
-      mskB |= msk << (8 * (e - 4));
-    }
-  }
-  // ---- the tile's code span: windows are nondecreasing in lane order, so
-  // it runs from the first window (aligned down to 16) to the last one's end
-  const uint64_t m4 = __ballot(has4);
-  int A = 0, nck = 0;
-  if (m4) {
-    const int first = __ffsll((unsigned long long)m4) - 1;
-    const int last = 63 - __clzll((long long)m4);
-    A = __builtin_amdgcn_readlane(cbase, first) & ~15;
-    nck = (__builtin_amdgcn_readlane(cbase, last) + 8 - A + 15) >> 4;   // <= kSpanChunks
-  }
-  const uint32_t shard_bytes = (uint32_t)(T * pitch);
-  uint32_t coff[kCI];   // chunk g = i*64 + lane -> (shard p, chunk cc)
-#pragma unroll
-  for (int i = 0; i < kCI; ++i) {
-    const int g = i * kWave + lane;
-    coff[i] = kOOB;
-    if (nck > 0 && g < NP * nck) {
-      const int p = g / nck, cc = g - p * nck;
-      coff[i] = (uint32_t)p * shard_bytes + (uint32_t)(A + 16 * cc);
-    }
-  }
-  const uint32_t rdo = has4 ? (uint32_t)(cbase - A) : 0u;   // the lane's bytes in a shard's span
-  const rsrc_t rpk = make_rsrc(packed + t0 * pitch,
-                               (uint32_t)(((NP - 1) * T + nrows) * (int64_t)pitch));
-  const rsrc_t rnone = make_rsrc(packed, 0u);
-
-  // ---- setup (c): the BF16 entries, in table order (row of the feature,
-  // then shard): entry L = pos*NP + sp, feature ilo + pos of shard sp
-  const int cnt = __builtin_popcount(bfm);
-  const int pos0 = wave_prefix16(cnt, lane);
-  const int nb = wave_sum16(cnt);
-  const int umax = wave_max8(cnt);
-  int mn = INT_MAX;
-#pragma unroll
-  for (int e = 0; e < kWinFeat; ++e)
-    if (fm[e] < 0) mn = min(mn, -1 - fm[e]);
-  const int ilo = first_lane_value(bfm != 0, mn);
-  const int E = NP * nb;
-  const bool compact = E <= kOR * kWave;   // uniform
-  uint32_t e_off[kOR], e_dst[kOR];
-#pragma unroll
-  for (int r = 0; r < kOR; ++r) {
-    const int L = r * kWave + lane;
-    e_off[r] = kOOB;
-    e_dst[r] = (uint32_t)(dummy - tab) + lane;
-    if (compact && L < E) {
-      const int pos = L / NP, sp = L - pos * NP;
-      e_off[r] = (uint32_t)(((int64_t)sp * T * k + ilo + pos) * 2);
-      e_dst[r] = (uint32_t)L;
-    }
-  }
-  const rsrc_t ro = make_rsrc(outl + t0 * k, (uint32_t)(((NP - 1) * T + nrows) * (int64_t)k * 2));
-  const rsrc_t rnone_o = make_rsrc(outl, 0u);
-
-  uint32_t ov[kD][kOR];
-  // one row into ring slot q: the code chunks into LDS, the entries into
-  // registers (a row past the wave's last loads through empty descriptors)
-  auto issue_row = [&](int q, int row) {
-    const bool ok = row < nrows;   // uniform
-    const uint32_t so = (uint32_t)min(row, nrows - 1) * (uint32_t)pitch;
-    float* const slot = ring + q * kSlot;
-#pragma unroll
-    for (int i = 0; i < kCI; ++i)
-      lds_load16(ok ? rpk : rnone, slot + i * 256, coff[i], so);
-    const uint32_t soo = (uint32_t)(min(row, nrows - 1) * k * 2);
-#pragma unroll
-    for (int r = 0; r < kOR; ++r)
-      ov[q][r] = __builtin_amdgcn_raw_buffer_load_b16(ok ? ro : rnone_o, e_off[r], soo, 0);
-  };
-  // The ring's first kD rows, each followed by kS stores through an empty
-  // descriptor (dropped): every row then has the same loads and stores issued
-  // after it as in the steady state, so one wait count serves every row.
-  // (The dummy stores go to offsets 4 KB apart, so that the compiler can
-  // neither drop one as overwritten nor merge them into one wider store.)
-  const rsrc_t ynone = make_rsrc(y, 0u);
-#pragma unroll
-  for (int q = 0; q < kD; ++q) {
-    issue_row(q, q);
-    issue_fence();
-#pragma unroll
-    for (int i = 0; i < kS; ++i)
-      __builtin_amdgcn_raw_buffer_store_b32(0u, ynone, (uint32_t)(4096 * i), 0, 0);
-    issue_fence();
-  }
-
-  // ---- per-lane constants (their loads are older than the ring)
-  float sc[NP][kWinFeat], bias[kWinFeat];
-#pragma unroll
-  for (int e = 0; e < kWinFeat; ++e) bias[e] = 0.0f;
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-#pragma unroll
-    for (int e = 0; e < kWinFeat; ++e) {
-      const float sv_ = __uint_as_float(sv[p][e >> 2][e & 3]);
-      const float z = (float)((zv[p][e >> 2] >> (8 * (e & 3))) & 0xFFu);
-      const bool q4 = fm[e] >= 0 && fm[e] != INT_MAX;
-      if (q4) bias[e] = __fsub_rn(bias[e], __fmul_rn(z, sv_));   // -sum_p z*s, shard order
-      sc[p][e] = ((nib_hi >> e) & 1) ? sv_ * 0.0625f : sv_;
-      settle(sc[p][e]);
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < kWinFeat; ++e) settle(bias[e]);
-  float m0[kWinFeat];   // 1 at the lane's first BF16 feature
-#pragma unroll
-  for (int e = 0; e < kWinFeat; ++e) m0[e] = (bfm != 0 && e == __builtin_ctz(bfm | 256u)) ? 1.0f : 0.0f;
-  const int bfm_rest = (int)(bfm & (bfm - 1));
-  const uint32_t st_off = active ? (uint32_t)h0 * kYB : kOOB;
-  const uint32_t st_a = (f0 + 4 * lane < H) ? (uint32_t)(f0 + 4 * lane) * 4u : kOOB;
-  const uint32_t st_b = (f0 + 256 + 4 * lane < H) ? (uint32_t)(f0 + 256 + 4 * lane) * 4u : kOOB;
-  const uint32_t ld_a = (uint32_t)((lane & 1) * 256 + (lane >> 1) * 4);
-  const uint32_t ld_b = (uint32_t)((lane & 1) * 256 + (32 + (lane >> 1)) * 4);
-  char* const ybase = static_cast<char*>(y) + t0 * H * (int64_t)kYB;
-  auto row_rsrc = [&](int row) {
-    return make_rsrc(ybase + (int64_t)min(row, nrows - 1) * H * kYB,
-                     row < nrows ? (uint32_t)H * kYB : 0u);
-  };
-
-  // One row from ring slot q: its loads and those issued after them (the
-  // prologue's dummy stores stand in for the first pass's missing ones)
-  auto consume = [&](int q, int row) {
-    wait_vmcnt<kS + (kD - 1) * (kCI + kOR + kS)>();
-    const float* const slot = ring + q * kSlot;
-    // codes of every shard (two dword reads each), then the BF16 entries
-    // into the table and the owners' first table row
-    v2u w[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const uint32_t* src =
-          reinterpret_cast<const uint32_t*>(slot) + ((uint32_t)(p * nck * 16) + rdo) / 4;
-      w[p] = v2u{src[0], src[1]};
-    }
-    if (compact && nb > 0) {
-#pragma unroll
-      for (int r = 0; r < kOR; ++r) tab[e_dst[r]] = __uint_as_float(ov[q][r] << 16);
-    }
-    wave_lds_sync();
-    float v0[NP];
-    if (compact && umax > 0) {
-      const float* t = tab + (cnt > 0 ? pos0 : 0) * NP;
-#pragma unroll
-      for (int p = 0; p < NP; ++p) v0[p] = t[p];
-    }
-    float acc[kWinFeat];
-#pragma unroll
-    for (int e = 0; e < kWinFeat; ++e) acc[e] = bias[e];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      uint32_t a = __builtin_amdgcn_perm(w[p][1], w[p][0], selA) & mskA;
-      uint32_t b = __builtin_amdgcn_perm(w[p][1], w[p][0], selB) & mskB;
-      opaque(a);
-      opaque(b);
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        acc[bb] = fmaf((float)((a >> (8 * bb)) & 0xFFu), sc[p][bb], acc[bb]);
-        acc[4 + bb] = fmaf((float)((b >> (8 * bb)) & 0xFFu), sc[p][4 + bb], acc[4 + bb]);
-      }
-    }
-    // the slot's codes are in registers now (every LDS read of the row
-    // complete): refill it kD rows ahead
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));   // lgkmcnt(0)
-    __builtin_amdgcn_sched_barrier(0);
-    issue_row(q, row + kD);
-    issue_fence();
-    if (compact && umax > 0) {
-      float o = 0.0f;
-#pragma unroll
-      for (int p = 0; p < NP; ++p) o = __fadd_rn(o, v0[p]);
-      place_bf16_first(acc, m0, o);
-      int rest = bfm_rest;
-      for (int u = 1; u < umax; ++u) {
-        const float* t = tab + (u < cnt ? pos0 + u : 0) * NP;
-        float ou = 0.0f;
-#pragma unroll
-        for (int p = 0; p < NP; ++p) ou = __fadd_rn(ou, t[p]);
-        place_bf16_at(acc, rest ? __builtin_ctz(rest) : kWinFeat, ou);
-        rest &= rest - 1;
-      }
-    }
-    const rsrc_t ry = row_rsrc(row);
-    if constexpr (kBf) {
-      __builtin_amdgcn_raw_buffer_store_b128(
-          v4u{bf16_pair(acc[0], acc[1]), bf16_pair(acc[2], acc[3]), bf16_pair(acc[4], acc[5]),
-              bf16_pair(acc[6], acc[7])},
-          ry, st_off, 0, kStream);
-    } else {
-      *reinterpret_cast<v4f*>(yrow + 4 * lane) = v4f{acc[0], acc[1], acc[2], acc[3]};
-      *reinterpret_cast<v4f*>(yrow + 256 + 4 * lane) = v4f{acc[4], acc[5], acc[6], acc[7]};
-      wave_lds_sync();
-      const v4f ya = *reinterpret_cast<const v4f*>(yrow + ld_a);
-      const v4f yb = *reinterpret_cast<const v4f*>(yrow + ld_b);
-      __builtin_amdgcn_raw_buffer_store_b128(
-          v4u{__float_as_uint(ya[0]), __float_as_uint(ya[1]), __float_as_uint(ya[2]),
-              __float_as_uint(ya[3])},
-          ry, st_a, 0, kStream);
-      __builtin_amdgcn_raw_buffer_store_b128(
-          v4u{__float_as_uint(yb[0]), __float_as_uint(yb[1]), __float_as_uint(yb[2]),
-              __float_as_uint(yb[3])},
-          ry, st_b, 0, kStream);
-    }
-    wave_lds_sync();   // the next row's values overwrite the table and the LDS row
-  };
-
-  for (int base = 0; base < nrows; base += kD) {
-#pragma unroll
-    for (int q = 0; q < kD; ++q) consume(q, base + q);
-  }
-  // every load and store of the ring done before the wave exits or reuses
-  __builtin_amdgcn_s_waitcnt(0);
-
-  if (!compact) {   // uniform
-    // More BF16 entries than the registers hold: the loop stored only the
-    // int4 part of these features; each owner recomputes its BF16 features
-    // term by term (fl(q - z) * s or the BF16 value, in shard order from +0).
-    int rest = (int)bfm;
-    while (rest) {
-      const int e = __builtin_ctz(rest);
-      rest &= rest - 1;
-      const int64_t h = h0 + e;
-      for (int r = 0; r < nrows; ++r) {
-        float o = 0.0f;
-        for (int p = 0; p < NP; ++p) {
-          const int64_t rowg = (int64_t)p * T + t0 + r;
-          o = __fadd_rn(o, bf16_to_f32(outl[rowg * k + (-1 - fmap[h])]));
         }
         char* d = ybase + ((int64_t)r * H + h) * kYB;
         if constexpr (kBf)
@@ -942,43 +603,6 @@ static void dispatch_window(int64_t P, bool wide, bool small, const uint8_t* pac
 #undef BTQ_WIN_ARGS
 }
 
-template <int NP, int kOR, bool kBf>
-static void launch_lds(const uint8_t* packed, int64_t pitch, const uint16_t* outl, int64_t T,
-                       int64_t H, int64_t k, int ntiles, int rpw, int64_t nrowblk,
-                       const float* scale, const uint8_t* zp, const int32_t* fmap, void* y,
-                       hipStream_t s) {
-  const int64_t ntgrp = (ntiles + kDqWaves - 1) / kDqWaves;
-  dq_lds_kernel<NP, kOR, kBf><<<(unsigned)xcd_grid(ntgrp, nrowblk), 256, 0, s>>>(
-      packed, (int)pitch, outl, T, (int)H, (int)k, ntiles, rpw, nrowblk, scale, zp, fmap, y);
-}
-
-template <bool kBf>
-static void dispatch_lds(int64_t P, bool wide, const uint8_t* packed, int64_t pitch,
-                         const uint16_t* outl, int64_t T, int64_t H, int64_t k, int ntiles,
-                         int rpw, int64_t nrowblk, const float* scale, const uint8_t* zp,
-                         const int32_t* fmap, void* y, hipStream_t s) {
-#define BTQ_LDS_ARGS packed, pitch, outl, T, H, k, ntiles, rpw, nrowblk, scale, zp, fmap, y, s
-#define BTQ_LDS_CASE(n)                                   \
-  case n:                                                 \
-    if (wide)                                             \
-      launch_lds<n, 4, kBf>(BTQ_LDS_ARGS);                \
-    else                                                  \
-      launch_lds<n, 2, kBf>(BTQ_LDS_ARGS);                \
-    break;
-  switch (P) {
-    BTQ_LDS_CASE(1)
-    BTQ_LDS_CASE(2)
-    BTQ_LDS_CASE(3)
-    BTQ_LDS_CASE(4)
-    BTQ_LDS_CASE(5)
-    BTQ_LDS_CASE(6)
-    BTQ_LDS_CASE(7)
-    BTQ_LDS_CASE(8)
-  }
-#undef BTQ_LDS_CASE
-#undef BTQ_LDS_ARGS
-}
-
 template <bool kPs, bool kBf>
 static hipError_t launch_decompress_t(const uint8_t* packed, int64_t pitch, const uint16_t* outl,
                                       int64_t P, int64_t T, int64_t H, int64_t k,
@@ -996,23 +620,6 @@ static hipError_t launch_decompress_t(const uint8_t* packed, int64_t pitch, cons
                     (uintptr_t)y % 16 == 0 && (uintptr_t)outl % 2 == 0 &&
                     nm * H * 4 < lim && P * H * 4 < lim && P * T * k * 2 < lim &&
                     P * T * pitch < lim && 64 * H * 4 < lim;
-  if (fast && !kPs) {
-    // LDS-ring kernel: one block per CU (its ring fills the LDS), about 1024
-    // waves, rows per wave a multiple of the ring depth and at least one
-    // ring, up to 64; shorter batches take the window kernel
-    const int ntiles = (int)((H + kWinTile - 1) / kWinTile);
-    int64_t rpw64 = (ntiles * T + kDqGeneration - 1) / kDqGeneration;
-    if (rpw64 >= kLdsRingMax) {
-      rpw64 = (rpw64 + kLdsRingMax - 1) / kLdsRingMax * kLdsRingMax;
-      if (rpw64 > 64) rpw64 = 64;
-      const int rpw = (int)rpw64;
-      const int64_t nrowblk = (T + rpw - 1) / rpw;
-      const bool wide = P * k > int64_t(kWave) * ntiles;
-      dispatch_lds<kBf>(P, wide, packed, pitch, outl, T, H, k, ntiles, rpw, nrowblk, scale, zp,
-                        fmap, y, s);
-      return hipGetLastError();
-    }
-  }
   if (fast) {
     const int ntiles = (int)((H + kWinTile - 1) / kWinTile);
     // about 1024 waves (one per SIMD) where the batch allows, each with at

@@ -126,7 +126,8 @@ CASES = [
     (1, 40, 512, 0, "normal", [], "P=1, k=0, one full tile"),
     (2, 9, 256, 256, "normal", [1, 2], "k=H: all BF16"),
     (9, 17, 512, 16, "laplace", [100, 101], "P=9: general receiver"),
-    (3, 5, 250, 7, "normal", [0, 249, 100], "H not a multiple of 8"),
+    (3, 5, 250, 7, "normal", [0, 249, 100], "H not a multiple of 4: general receiver"),
+    (3, 40, 1028, 9, "normal", [5, 600, 1027], "H=1028: a partial last tile of 4-feature lanes"),
     (5, 33, 1032, 13, "normal", [1, 2, 3], "H-k odd: pad nibble, general sender"),
     (2, 8, 1024, 200, "normal", list(range(100, 300)), "200 clustered BF16 features in one tile"),
     (4, 6, 2048, 600, "laplace", list(range(0, 2048, 3))[:600], "k=600: wide LDS span"),
@@ -152,13 +153,13 @@ def test_shapes(P, T, H, k, base, cols, note):
     run_both(calib, x, k, 0.9)
 
 
-# Batches long enough for the LDS-ring receiver (at least 8 rows per wave of
-# about 1024 waves): ragged row blocks, a partial last tile, 1-8 shards, an
-# odd code count (dense rows then take the general receiver, padded rows the
-# LDS ring), clustered BF16 features (four entry registers; tiles beyond
-# them take the post-loop pass) and k = 256 of 8192.
+# Batches long enough for many token rows per receiver wave (the window
+# kernel's 4-row ring and ragged last row blocks): a partial last tile, 1-8
+# shards, an odd code count (dense rows then take the general receiver,
+# padded rows the window kernel), clustered BF16 features (four entry
+# registers; tiles beyond them take the post-loop pass) and k = 256 of 8192.
 # (P, T, H, k, base, outlier columns, note)
-LDS_RING_CASES = [
+LONG_BATCH_CASES = [
     (8, 2050, 4096, 64, "normal", list(range(5, 4096, 97)), "7B-like, ragged last row block"),
     (4, 2600, 4104, 8, "laplace", [0, 1, 2, 4103], "partial last tile"),
     (3, 3000, 2056, 24, "normal", [10, 500, 2055], "P=3"),
@@ -170,10 +171,10 @@ LDS_RING_CASES = [
 ]
 
 
-@pytest.mark.parametrize("P,T,H,k,base,cols,note", LDS_RING_CASES,
-                         ids=[c[-1] for c in LDS_RING_CASES])
-def test_lds_ring_shapes(P, T, H, k, base, cols, note):
-    say(f"case: LDS ring P={P} T={T} H={H} k={k} ({note})")
+@pytest.mark.parametrize("P,T,H,k,base,cols,note", LONG_BATCH_CASES,
+                         ids=[c[-1] for c in LONG_BATCH_CASES])
+def test_long_batches(P, T, H, k, base, cols, note):
+    say(f"case: long batch P={P} T={T} H={H} k={k} ({note})")
     calib = [W.draw(P, 64, H, 1500 + b, base=base, cols=cols, outlier_factor=40.0, device=DEV)
              for b in range(2)]
     x = W.draw(P, T, H, 2500, base=base, cols=cols, outlier_factor=40.0, device=DEV)
