@@ -55,8 +55,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kDqWaves = 4;
 constexpr int kWinFeat = 8;                    // features per lane
 constexpr int kWinTile = kWave * kWinFeat;     // 512 features per wave-tile
-constexpr int kDqRing = 4;                     // token rows in flight per wave
-constexpr int kDqRingSmall = 2;                // the same for short batches
+// Token rows in flight per wave. Two rows (with 2-3 waves per SIMD) keep
+// HBM as busy as four, and measured up to 7% faster at large batches: fewer
+// requests in flight per CU, and fewer registers.
+constexpr int kDqRing = 2;
 constexpr int64_t kDqGeneration = 1024;        // waves at one per SIMD
 
 // fp32 -> bf16, round to nearest even, two values per instruction
@@ -118,8 +120,13 @@ __host__ __device__ constexpr int win_lds_dwords() {
 
 // NP: shards (1..8). kOR: BF16 entry registers per row. kR: ring depth.
 // kPs: fmap is [P,H] (one set per shard) instead of [H]. kBf: y is bf16.
+// Waves per SIMD the register budget aims at: 3 (at most 168 registers) for
+// one set with two entry registers, 2 with four; one set per shard needs
+// more registers than 2 waves leave.
 template <int NP, int kOR, int kR, bool kPs, bool kBf>
-__global__ __launch_bounds__(256) void dq_window_kernel(
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(kPs ? 1 : (kOR == 2 ? 3 : 2))))
+void dq_window_kernel(
     const uint8_t* __restrict__ packed, int pitch, const uint16_t* __restrict__ outl, int64_t T,
     int H, int k, int ntiles, int rows_per_wave, int64_t nrowblk, const float* __restrict__ scale,
     const uint8_t* __restrict__ zp, const int32_t* __restrict__ fmap, void* __restrict__ y) {
@@ -145,7 +152,7 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
   float* const yrow = dummy + kWave;   // fp32 output only
   uint32_t* const stage = reinterpret_cast<uint32_t*>(yrow + (kBf ? 0 : kWinTile));
 
-  // ---- setup (a): the lane's map entries first, then scales and zero points
+  // ---- setup (a): the lane's map entries, scales and zero points
   const rsrc_t rf = make_rsrc(fmap, (uint32_t)(NM * (int64_t)H * 4));
   const rsrc_t rs = make_rsrc(scale, (uint32_t)(NP * (int64_t)H * 4));
   const rsrc_t rz = make_rsrc(zp, (uint32_t)(NP * (int64_t)H));
@@ -168,10 +175,105 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
   }
   issue_fence();
 
+  // ---- the tile's geometry per map, from the map entries of its first
+  // feature and of the next tile's (scalar loads): the slot of its first
+  // int4 feature, and the run [ilo, ilo + nb) of BF16 indices inside it. A
+  // feature h with slot j has h - j BF16 features below it; a BF16 feature
+  // with index i has i. So the ring's loads need nothing from the lanes'
+  // setup and go out right behind it.
+  uint32_t abase[NM];   // dword where the code span of a row starts
+  int ilo[NP], nbp[NP], off[NP + 1];
+  const bool last_tile = f0 + kWinTile >= H;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const int32_t* fr = fmap + (kPs ? (int64_t)m * H : 0);
+    const int fa = fr[f0];
+    const int fb = last_tile ? 0 : fr[f0 + kWinTile];
+    const int ia = fa >= 0 ? f0 - fa : -1 - fa;
+    const int ib = last_tile ? k : (fb >= 0 ? f0 + kWinTile - fb : -1 - fb);
+    ilo[m] = ia;
+    nbp[m] = ib - ia;
+    // the lanes' 8-byte windows start at or after the first int4 slot's
+    // 4-byte aligned byte, or at pitch - 8 when pulled back inside the row
+    const int cb0 = min(((f0 - ia) >> 1) & ~3, pitch - 8);
+    abase[m] = ((uint32_t)cb0 >> 2) & ~1u;
+  }
+#pragma unroll
+  for (int p = 1; p < NP; ++p) {
+    if (!kPs) {
+      ilo[p] = ilo[0];
+      nbp[p] = nbp[0];
+    }
+  }
+  off[0] = 0;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) off[p + 1] = off[p] + nbp[p];
+  const int E = off[NP];                           // entries per row
+  const bool compact = E <= kOR * kWave;           // uniform
+
+  // ---- the tile's code span per map. The lanes' windows are nondecreasing
+  // in lane order and the last starts at most 63 dwords after the first, so
+  // the span from the first window's dword (rounded down to even) holds at
+  // most 66 dwords: the first 33 lanes load it with one coalesced 8-byte
+  // load each, every code byte once. Each row's span goes through the
+  // wave's LDS stage, where each lane reads its own window.
+  uint32_t cl[NM];   // lane's load offset in the row
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+    cl[m] = lane < kStageLanes ? 4u * abase[m] + 8u * (uint32_t)lane : kOOB;
+  // BF16 entry e = off[p] + j of a row is index ilo[p] + j of shard p
+  uint32_t e_off[kOR];
+#pragma unroll
+  for (int r = 0; r < kOR; ++r) {
+    const int e = r * kWave + lane;
+    e_off[r] = kOOB;
+    if (compact && e < E) {
+      int sp = 0;
+#pragma unroll
+      for (int p = 1; p < NP; ++p) sp = e >= off[p] ? p : sp;
+      e_off[r] = (uint32_t)(((int64_t)sp * T * k + ilo[sp] + (e - off[sp])) * 2);
+    }
+  }
+
+  // ---- the ring: the first kR rows' code spans and BF16 entries. One
+  // descriptor spans this wave's rows of every shard (the launcher keeps the
+  // message under 2^31 bytes); the shard and row ride in the scalar offset.
+  // A row past the wave's last loads through an empty descriptor (a scalar
+  // choice). The code loads carry no streaming hint: the lines at tile
+  // boundaries are read by two waves, and with the hint the L2 drops many
+  // of them before the second read (about 20% more HBM reads, measured).
+  const rsrc_t rpk = make_rsrc(packed + t0 * pitch,
+                               (uint32_t)(((NP - 1) * T + nrows) * (int64_t)pitch));
+  const rsrc_t rnone = make_rsrc(packed, 0u);
+  const uint32_t shard_bytes = (uint32_t)(T * pitch);
+  const rsrc_t ro = make_rsrc(outl + t0 * k, (uint32_t)(((NP - 1) * T + nrows) * (int64_t)k * 2));
+  const rsrc_t rnone_o = make_rsrc(outl, 0u);
+  v2u w[kR][NP];
+  uint32_t ov[kR][kOR];
+  auto load_row = [&](int q, int row) {
+    const bool ok = row < nrows;   // uniform
+    const uint32_t so = (uint32_t)min(row, nrows - 1) * (uint32_t)pitch;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b64(ok ? rpk : rnone, cl[kPs ? p : 0],
+                                                          so + (uint32_t)p * shard_bytes, 0);
+      w[q][p] = v2u{t[0], t[1]};
+    }
+    const uint32_t soo = (uint32_t)(min(row, nrows - 1) * k * 2);
+#pragma unroll
+    for (int r = 0; r < kOR; ++r)
+      ov[q][r] = __builtin_amdgcn_raw_buffer_load_b16(ok ? ro : rnone_o, e_off[r], soo, 0);
+  };
+#pragma unroll
+  for (int q = 0; q < kR; ++q) {
+    load_row(q, q);
+    issue_fence();
+  }
+
   // ---- setup (b): per map, the code window and byte selectors
   // fm[m][e] >= 0: int4 slot; < 0: BF16 index -1-fm. Inactive lanes: none.
   int fm[NM][kWinFeat];
-  uint32_t cb[NM], selA[NM], selB[NM], mskA[NM], mskB[NM], bfm[NM];
+  uint32_t dwin[NM], selA[NM], selB[NM], mskA[NM], mskB[NM], bfm[NM];
   int nib_hi[NM];   // bit e: feature e's code is a high nibble
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
@@ -189,7 +291,8 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
     // (the launcher guarantees pitch >= 8)
     int base = jf == INT_MAX ? 0 : ((jf >> 1) & ~3);
     if (base + 8 > pitch) base -= 4;
-    cb[m] = jf == INT_MAX ? kOOB : (uint32_t)base;
+    // the window's dword in the staged span (0 .. 64)
+    dwin[m] = jf == INT_MAX ? 0u : ((uint32_t)base >> 2) - abase[m];
     uint32_t sa = 0, sb = 0, ma = 0, mb = 0;
     int hi = 0;
 #pragma unroll
@@ -216,83 +319,16 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
     nib_hi[m] = hi;
   }
 
-  // ---- the tile's code span per map. The lanes' windows are nondecreasing
-  // in lane order and the last starts at most 63 dwords after the first, so
-  // the span from the first window's dword (rounded down to even) holds at
-  // most 66 dwords: the first 33 lanes load it with one coalesced 8-byte
-  // load each, every code byte once. Each row's span goes through the
-  // wave's LDS stage, where each lane reads its own window.
-  uint32_t cl[NM], dwin[NM];   // lane's load offset in the row; its window's stage dword
-#pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    const uint64_t has = __ballot(cb[m] != kOOB);
-    const uint32_t a = has ? ((uint32_t)__builtin_amdgcn_readlane(
-                                  (int)cb[m], __ffsll((unsigned long long)has) - 1) >> 2) & ~1u
-                           : 0u;
-    cl[m] = (has && lane < kStageLanes) ? 4u * a + 8u * (uint32_t)lane : kOOB;
-    dwin[m] = cb[m] != kOOB ? (cb[m] >> 2) - a : 0u;
-  }
-
-  // ---- the ring's code loads: the first kR rows, issued before anything
-  // else waits. One descriptor spans this wave's rows of every shard (the
-  // launcher keeps the message under 2^31 bytes); the shard and row ride in
-  // the scalar offset. A row past the wave's last loads through an empty
-  // descriptor (a scalar choice).
-  const rsrc_t rpk = make_rsrc(packed + t0 * pitch,
-                               (uint32_t)(((NP - 1) * T + nrows) * (int64_t)pitch));
-  const rsrc_t rnone = make_rsrc(packed, 0u);
-  const uint32_t shard_bytes = (uint32_t)(T * pitch);
-  v2u w[kR][NP];
-  uint32_t ov[kR][kOR];
-  auto load_codes = [&](int q, int row) {
-    const bool ok = row < nrows;   // uniform
-    const uint32_t so = (uint32_t)min(row, nrows - 1) * (uint32_t)pitch;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const auto t = __builtin_amdgcn_raw_buffer_load_b64(ok ? rpk : rnone, cl[kPs ? p : 0],
-                                                          so + (uint32_t)p * shard_bytes, kStream);
-      w[q][p] = v2u{t[0], t[1]};
-    }
-  };
-#pragma unroll
-  for (int q = 0; q < kR; ++q) {
-    load_codes(q, q);
-    issue_fence();
-  }
-
-  // ---- setup (c): the tile's BF16 entries (wave counts from ballots)
-  // Per shard: the lane's BF16 features have consecutive indices; the
-  // tile's form the run [ilo_p, ilo_p + nb_p) of the shard's outlier block,
-  // which starts at the lowest lane that has one.
+  // ---- setup (c): the lanes' BF16 features (wave counts from ballots) and
+  // the table row of each entry. Shared set: entry (p, i) -> row i - ilo.
+  // One set per shard: through the inverse map that the owners write here.
   int any = 0;   // features BF16 on some shard
 #pragma unroll
   for (int m = 0; m < NM; ++m) any |= (int)bfm[m];
   const int cnt_any = __builtin_popcount(any);
   const int pos0 = wave_prefix16(cnt_any, lane);   // table row of the lane's first
-  const int nb_any = wave_sum16(cnt_any);
+  const int nb_any = kPs ? wave_sum16(cnt_any) : nbp[0];
   const int umax = wave_max8(cnt_any);
-  int ilo[NP], nbp[NP], off[NP + 1];
-  off[0] = 0;
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    const int m = kPs ? p : 0;
-    if (!kPs && p > 0) {
-      ilo[p] = ilo[0];
-      nbp[p] = nbp[0];
-    } else {
-      int mn = INT_MAX;
-#pragma unroll
-      for (int e = 0; e < kWinFeat; ++e)
-        if (fm[m][e] < 0) mn = min(mn, -1 - fm[m][e]);
-      ilo[p] = first_lane_value(bfm[m] != 0, mn);
-      nbp[p] = wave_sum16(__builtin_popcount(bfm[m]));
-    }
-    off[p + 1] = off[p] + nbp[p];
-  }
-  const int E = off[NP];                           // entries per row
-  const bool compact = E <= kOR * kWave;           // uniform
-  // Table row of each entry. Shared set: entry (p, i) -> row i - ilo. One
-  // set per shard: through the inverse map that the owners write here.
   if constexpr (kPs) {
     if (compact) {
 #pragma unroll
@@ -309,39 +345,20 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
   // zero the table rows of this tile (int4 shards of a BF16 feature stay 0)
   for (int i = lane; i < nb_any * NP && compact; i += kWave) tab[i] = 0.0f;
   wave_lds_sync();
-  uint32_t e_off[kOR], e_dst[kOR];   // entry: outlier-block offset, LDS dword
+  uint32_t e_dst[kOR];   // entry: LDS dword
 #pragma unroll
   for (int r = 0; r < kOR; ++r) {
     const int e = r * kWave + lane;
-    e_off[r] = kOOB;
     e_dst[r] = (uint32_t)(dummy - tab) + lane;
     if (compact && e < E) {
       int sp = 0;
 #pragma unroll
       for (int p = 1; p < NP; ++p) sp = e >= off[p] ? p : sp;
-      const int i = ilo[sp] + (e - off[sp]);
-      e_off[r] = (uint32_t)(((int64_t)sp * T * k + i) * 2);
-      const int row = kPs ? inv[e] : i - ilo[0];
+      const int row = kPs ? inv[e] : e - off[sp];
       e_dst[r] = (uint32_t)(row * NP + sp);
     }
   }
   wave_lds_sync();
-  // the ring's BF16 entries (every shard's run, one descriptor over this
-  // wave's rows of the outlier blocks)
-  const rsrc_t ro = make_rsrc(outl + t0 * k, (uint32_t)(((NP - 1) * T + nrows) * (int64_t)k * 2));
-  const rsrc_t rnone_o = make_rsrc(outl, 0u);
-  auto load_entries = [&](int q, int row) {
-    const bool ok = row < nrows;   // uniform
-    const uint32_t so = (uint32_t)(min(row, nrows - 1) * k * 2);
-#pragma unroll
-    for (int r = 0; r < kOR; ++r)
-      ov[q][r] = __builtin_amdgcn_raw_buffer_load_b16(ok ? ro : rnone_o, e_off[r], so, 0);
-  };
-#pragma unroll
-  for (int q = 0; q < kR; ++q) {
-    load_entries(q, q);
-    issue_fence();
-  }
 
   // ---- per-lane constants (their loads are older than the ring). A term
   // of a shard where the feature is BF16 has code 0 and scale 0, so it adds
@@ -357,9 +374,9 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
       const float s = __uint_as_float(sv[p][e >> 2][e & 3]);
       const float z = (float)((zv[p][e >> 2] >> (8 * (e & 3))) & 0xFFu);
       const bool q4 = fm[m][e] >= 0 && fm[m][e] != INT_MAX;
-      // -sum_p z*s over the int4 shards, fp32 steps in shard order from +0
-      if (q4) bias[e] = __fsub_rn(bias[e], __fmul_rn(z, s));
-      sc[p][e] = q4 ? (((nib_hi[m] >> e) & 1) ? s * 0.0625f : s) : 0.0f;
+      // -sum_p z*s over the int4 shards, in shard order from +0
+      if (q4) bias[e] = fmaf(-z, s, bias[e]);
+      sc[p][e] = q4 ? s * (((nib_hi[m] >> e) & 1) ? 0.0625f : 1.0f) : 0.0f;
       settle(sc[p][e]);
     }
   }
@@ -416,18 +433,19 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
         const uint32_t* src = stage + p * kStageDwords + dwin[kPs ? p : 0];
         x[p] = v2u{src[0], src[1]};
       }
-      float v0[NP];
+      // the owner's first BF16 feature: its row summed in shard order from +0
+      float o = 0.0f;
       if (compact && umax > 0) {
         const float* t = tab + (cnt_any > 0 ? pos0 : 0) * NP;
         if constexpr (NP % 4 == 0) {
 #pragma unroll
           for (int p = 0; p < NP; p += 4) {
             const v4f f = *reinterpret_cast<const v4f*>(t + p);
-            v0[p] = f[0]; v0[p + 1] = f[1]; v0[p + 2] = f[2]; v0[p + 3] = f[3];
+            o = __fadd_rn(__fadd_rn(__fadd_rn(__fadd_rn(o, f[0]), f[1]), f[2]), f[3]);
           }
         } else {
 #pragma unroll
-          for (int p = 0; p < NP; ++p) v0[p] = t[p];
+          for (int p = 0; p < NP; ++p) o = __fadd_rn(o, t[p]);
         }
       }
       issue_fence();   // the read goes out before the arithmetic below
@@ -449,14 +467,9 @@ __global__ __launch_bounds__(256) void dq_window_kernel(
         }
       }
       // this row's registers are consumed: refill the slot kR rows ahead
-      load_codes(q, row + kR);
-      load_entries(q, row + kR);
+      load_row(q, row + kR);
       issue_fence();
       if (compact && umax > 0) {
-        // owners add their features' rows in shard order from +0
-        float o = 0.0f;
-#pragma unroll
-        for (int p = 0; p < NP; ++p) o = __fadd_rn(o, v0[p]);
         place(acc, e_first, o);
         int rest = any_rest;
         for (int u = 1; u < umax; ++u) {   // lanes with several BF16 features
@@ -573,19 +586,15 @@ static void launch_window(const uint8_t* packed, int64_t pitch, const uint16_t* 
 }
 
 template <bool kPs, bool kBf>
-static void dispatch_window(int64_t P, bool wide, bool small, const uint8_t* packed, int64_t pitch,
+static void dispatch_window(int64_t P, bool wide, const uint8_t* packed, int64_t pitch,
                             const uint16_t* outl, int64_t T, int64_t H, int64_t k, int ntiles,
                             int rpw, int64_t nrowblk, const float* scale, const uint8_t* zp,
                             const int32_t* fmap, void* y, hipStream_t s) {
 #define BTQ_WIN_ARGS packed, pitch, outl, T, H, k, ntiles, rpw, nrowblk, scale, zp, fmap, y, s
 #define BTQ_WIN_CASE(n)                                                         \
   case n:                                                                       \
-    if (wide && small)                                                          \
-      launch_window<n, 4, kDqRingSmall, kPs, kBf>(BTQ_WIN_ARGS);                \
-    else if (wide)                                                              \
+    if (wide)                                                                   \
       launch_window<n, 4, kDqRing, kPs, kBf>(BTQ_WIN_ARGS);                     \
-    else if (small)                                                             \
-      launch_window<n, 2, kDqRingSmall, kPs, kBf>(BTQ_WIN_ARGS);                \
     else                                                                        \
       launch_window<n, 2, kDqRing, kPs, kBf>(BTQ_WIN_ARGS);                     \
     break;
@@ -622,20 +631,18 @@ static hipError_t launch_decompress_t(const uint8_t* packed, int64_t pitch, cons
                     P * T * pitch < lim && 64 * H * 4 < lim;
   if (fast) {
     const int ntiles = (int)((H + kWinTile - 1) / kWinTile);
-    // about 1024 waves (one per SIMD) where the batch allows, each with at
-    // least a full ring of rows; up to 64 rows per wave
+    // about kDqGeneration waves where the batch allows, each with at least a
+    // full ring of rows; up to 64 rows per wave
     int64_t rpw64 = (ntiles * T + kDqGeneration - 1) / kDqGeneration;
-    const bool small = rpw64 < kDqRing;
-    const int ring = small ? kDqRingSmall : kDqRing;
-    rpw64 = (rpw64 + ring - 1) / ring * ring;
-    if (rpw64 < ring) rpw64 = ring;
+    rpw64 = (rpw64 + kDqRing - 1) / kDqRing * kDqRing;
+    if (rpw64 < kDqRing) rpw64 = kDqRing;
     if (rpw64 > 64) rpw64 = 64;
     const int rpw = (int)rpw64;
     const int64_t nrowblk = (T + rpw - 1) / rpw;
     // BF16 entry registers: 2 (128 entries per tile-row) while the tiles hold
     // at most 64 on average, else 4
     const bool wide = P * k > int64_t(kWave) * ntiles;
-    dispatch_window<kPs, kBf>(P, wide, small, packed, pitch, outl, T, H, k, ntiles, rpw, nrowblk,
+    dispatch_window<kPs, kBf>(P, wide, packed, pitch, outl, T, H, k, ntiles, rpw, nrowblk,
                               scale, zp, fmap, y, s);
     return hipGetLastError();
   }
