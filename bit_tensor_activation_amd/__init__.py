@@ -6,6 +6,7 @@ script, and a thin torch binding whose functions carry the C names.
 """
 from .api import (  # noqa: F401
     btq_calib_update,
+    btq_calib_update_noalloc,
     btq_calib_workspace_bytes,
     btq_compress_pack,
     btq_compress_pack_ex,

@@ -17,6 +17,7 @@ _c = ctypes
 _P, _I64, _I, _F, _SZ = _c.c_void_p, _c.c_int64, _c.c_int, _c.c_float, _c.c_size_t
 SIGNATURES = {
     "btq_calib_update": (_I, [_P, _I64, _I64, _I64, _F, _I, _P, _P, _P, _SZ, _P]),
+    "btq_calib_update_noalloc": (_I, [_P, _I64, _I64, _I64, _F, _I, _P, _P, _P]),
     "btq_calib_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "btq_select_outliers": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "btq_select_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
@@ -47,6 +48,8 @@ BTQ_ERR_SHAPE = -2
 BTQ_ERR_ALIGN = -3
 BTQ_ERR_WORKSPACE = -4
 BTQ_ERR_HIP = -5
+BTQ_ERR_SCRATCH = -6
+BTQ_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 BTQ_SCORE_SUM = 0
 BTQ_SCORE_MAX = 1

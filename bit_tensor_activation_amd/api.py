@@ -113,6 +113,23 @@ def btq_calib_update(x: torch.Tensor, run_min: torch.Tensor, run_max: torch.Tens
     _lib.check(st, "btq_calib_update")
 
 
+def btq_calib_update_noalloc(x: torch.Tensor, run_min: torch.Tensor, run_max: torch.Tensor,
+                             momentum: float, first_batch: bool, stream=None) -> None:
+    """btq_calib_update with the library's static scratch: nothing is
+    allocated, here or in the library (P*H at most 2^20)."""
+    dev = _device(x)
+    P, T, H = x.shape
+    _need(x, "x", _BF16, (P, T, H), dev)
+    _need(run_min, "run_min", (torch.float32,), (P, H), dev)
+    _need(run_max, "run_max", (torch.float32,), (P, H), dev)
+    sh, ctx = _launch(dev, stream)
+    with ctx:
+        st = _lib.load().btq_calib_update_noalloc(_ptr(_bits(x)), P, T, H, float(momentum),
+                                                  int(bool(first_batch)), _ptr(run_min),
+                                                  _ptr(run_max), sh)
+    _lib.check(st, "btq_calib_update_noalloc")
+
+
 def _select_outputs(run_min, run_max, k, out, per_shard=False) -> dict:
     dev = _device(run_min)
     P, H = run_min.shape

@@ -3,8 +3,17 @@
 // The contract of each call is documented in include/btq.h.
 #include <math.h>
 
+#include <mutex>
+
 #include "btq.h"
 #include "common.hpp"
+
+// Scratch of btq_calib_update_noalloc: a file-scope device array, one copy
+// on each GPU the library runs on, held until the process ends. Host code
+// never uses this name as an address (on the host it is only a stand-in);
+// it passes the device address that hipGetSymbolAddress returns for the
+// current device.
+static __device__ __align__(256) float scratch[BTQ_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace {
 
@@ -29,6 +38,28 @@ int hip_status(hipError_t e) { return e == hipSuccess ? BTQ_OK : BTQ_ERR_HIP; }
 int check_pitch(int64_t P, int64_t T, int64_t H, int64_t k, int64_t pitch) {
   if (pitch < (H - k + 1) / 2 || pitch > kMaxElems) return BTQ_ERR_SHAPE;
   if (T > 0 && pitch > 0 && T > kMaxElems / (P * pitch)) return BTQ_ERR_SHAPE;
+  return BTQ_OK;
+}
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];   // `scratch` on each device, looked up once
+
+// The current device's address of `scratch`: looked up on the first call on
+// that device, with it current, and kept.
+int scratch_address(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BTQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return BTQ_ERR_HIP;
+    }
+    g_scratch_addr[dev] = p;
+  }
+  *out = static_cast<float*>(g_scratch_addr[dev]);
   return BTQ_OK;
 }
 
@@ -73,6 +104,26 @@ int btq_calib_update(const uint16_t* x, int64_t P, int64_t T, int64_t H, float m
   const float c = 1.0f - a;   // one fp32 subtraction
   return hip_status(btq::launch_calib(x, P, T, H, a, c, first_batch != 0, run_min, run_max,
                                       (float*)workspace, (hipStream_t)stream));
+}
+
+int btq_calib_update_noalloc(const uint16_t* x, int64_t P, int64_t T, int64_t H, float momentum,
+                             int first_batch, float* run_min, float* run_max, void* stream) {
+  int st = check_dims(P, T, H, 1);
+  if (st != BTQ_OK) return st;
+  if (!x || !run_min || !run_max) return BTQ_ERR_ARG;
+  if (!(momentum >= 0.0f && momentum < 1.0f)) return BTQ_ERR_ARG;   // also rejects NaN
+  if (!aligned(x, 2) || !aligned(run_min, 4) || !aligned(run_max, 4)) return BTQ_ERR_ALIGN;
+  // the same kernels with as many token chunks as the scratch holds partials for
+  const btq::CalibPlan plan =
+      btq::calib_plan_capped(P, T, H, (int64_t)(BTQ_NOALLOC_SCRATCH_BYTES / sizeof(float)));
+  if (plan.nchunk < 1) return BTQ_ERR_SCRATCH;
+  float* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != BTQ_OK) return st;
+  const float a = momentum;
+  const float c = 1.0f - a;
+  return hip_status(btq::launch_calib_plan(x, P, T, H, a, c, first_batch != 0, run_min, run_max,
+                                           ws, plan, (hipStream_t)stream));
 }
 
 namespace {
@@ -260,6 +311,8 @@ const char* btq_status_str(int status) {
     case BTQ_ERR_ALIGN: return "pointer not aligned to its element type";
     case BTQ_ERR_WORKSPACE: return "workspace too small";
     case BTQ_ERR_HIP: return "HIP call failed";
+    case BTQ_ERR_SCRATCH:
+      return "P*H too large for the no-alloc scratch (2*P*H*4 bytes must fit BTQ_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown btq status";
   }
 }

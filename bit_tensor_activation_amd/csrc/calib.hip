@@ -160,9 +160,29 @@ CalibPlan calib_plan(int64_t P, int64_t T, int64_t H) {
   return plan;
 }
 
+CalibPlan calib_plan_capped(int64_t P, int64_t T, int64_t H, int64_t max_ws_floats) {
+  CalibPlan plan = calib_plan(P, T, H);
+  const int64_t fit = max_ws_floats / (2 * P * H);   // chunks whose partials fit
+  if (fit < 1) {
+    plan.nchunk = 0;
+    plan.rows_per_chunk = 0;
+    return plan;
+  }
+  if (plan.nchunk > fit) {
+    plan.rows_per_chunk = (T + fit - 1) / fit;
+    plan.nchunk = (T + plan.rows_per_chunk - 1) / plan.rows_per_chunk;
+  }
+  return plan;
+}
+
 hipError_t launch_calib(const uint16_t* x, int64_t P, int64_t T, int64_t H, float a, float c,
                         int first, float* run_min, float* run_max, float* ws, hipStream_t s) {
-  const CalibPlan plan = calib_plan(P, T, H);
+  return launch_calib_plan(x, P, T, H, a, c, first, run_min, run_max, ws, calib_plan(P, T, H), s);
+}
+
+hipError_t launch_calib_plan(const uint16_t* x, int64_t P, int64_t T, int64_t H, float a, float c,
+                             int first, float* run_min, float* run_max, float* ws,
+                             const CalibPlan& plan, hipStream_t s) {
   float* pmin = ws;
   float* pmax = ws + plan.nchunk * P * H;
   const dim3 grid((unsigned)((H + kCalCols - 1) / kCalCols), (unsigned)P, (unsigned)plan.nchunk);

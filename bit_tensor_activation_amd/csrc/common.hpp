@@ -129,8 +129,15 @@ struct CalibPlan {
   int64_t rows_per_chunk;
 };
 CalibPlan calib_plan(int64_t P, int64_t T, int64_t H);
+// The same plan with at most as many chunks as fit max_ws_floats floats of
+// partials (nchunk 0: not even one chunk fits).
+CalibPlan calib_plan_capped(int64_t P, int64_t T, int64_t H, int64_t max_ws_floats);
 hipError_t launch_calib(const uint16_t* x, int64_t P, int64_t T, int64_t H, float a, float c,
                         int first, float* run_min, float* run_max, float* ws, hipStream_t s);
+// ws holds 2*plan.nchunk*P*H floats.
+hipError_t launch_calib_plan(const uint16_t* x, int64_t P, int64_t T, int64_t H, float a, float c,
+                             int first, float* run_min, float* run_max, float* ws,
+                             const CalibPlan& plan, hipStream_t s);
 
 hipError_t launch_select(const float* run_min, const float* run_max, int64_t P, int64_t H,
                          int64_t k, float* scale, float* rscale, uint8_t* zp, int32_t* idx,

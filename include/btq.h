@@ -83,7 +83,8 @@ typedef enum {
   BTQ_ERR_SHAPE = -2,      /* P, T, H, k or the pitch out of range              */
   BTQ_ERR_ALIGN = -3,      /* pointer not aligned to its element type           */
   BTQ_ERR_WORKSPACE = -4,  /* workspace smaller than the *_workspace_bytes size */
-  BTQ_ERR_HIP = -5         /* a HIP call failed (hipGetLastError, cleared)      */
+  BTQ_ERR_HIP = -5,        /* a HIP call failed (hipGetLastError, cleared)      */
+  BTQ_ERR_SCRATCH = -6     /* sizes beyond btq_calib_update_noalloc's scratch    */
 } btq_status;
 
 /*
@@ -113,6 +114,27 @@ int btq_calib_update(const uint16_t *x, int64_t P, int64_t T, int64_t H,
 
 /* Workspace bytes for btq_calib_update (0 for invalid sizes). */
 size_t btq_calib_workspace_bytes(int64_t P, int64_t T, int64_t H);
+
+/*
+ * btq_calib_update without a workspace and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments, checks and results are those of btq_calib_update, bit for bit
+ * (the result does not depend on how the token axis is split). The partial
+ * extremes live in a static device array of BTQ_NOALLOC_SCRATCH_BYTES on
+ * each GPU, held until the process ends; the call uses as many token chunks
+ * as that array holds, so 2*P*H*4 bytes must fit it (P*H <= 2^20), else it
+ * returns BTQ_ERR_SCRATCH and enqueues nothing. It calls no hipMalloc or
+ * hipFree; its first call on a device looks up the array's address there.
+ * Every call on one GPU uses that GPU's one array: calls that may overlap
+ * on one GPU (different streams, or host threads) race and must be ordered
+ * by the caller. Nothing in the array needs an initial value.
+ */
+#define BTQ_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int btq_calib_update_noalloc(const uint16_t *x, int64_t P, int64_t T, int64_t H,
+                             float momentum, int first_batch,
+                             float *run_min, float *run_max, void *stream);
 
 /*
  * Selection -- "The Hybrid Quantization Algorithm", Calibration bullet
