@@ -223,16 +223,22 @@ void dq_window_kernel(
     cl[m] = lane < kStageLanes ? 4u * abase[m] + 8u * (uint32_t)lane : kOOB;
   // BF16 entry e = off[p] + j of a row is index ilo[p] + j of shard p
   uint32_t e_off[kOR];
+  int e_sp[kOR];   // the entry's shard
 #pragma unroll
   for (int r = 0; r < kOR; ++r) {
     const int e = r * kWave + lane;
-    e_off[r] = kOOB;
-    if (compact && e < E) {
-      int sp = 0;
+    int sp = 0, o = 0, lo = ilo[0];
 #pragma unroll
-      for (int p = 1; p < NP; ++p) sp = e >= off[p] ? p : sp;
-      e_off[r] = (uint32_t)(((int64_t)sp * T * k + ilo[sp] + (e - off[sp])) * 2);
+    for (int p = 1; p < NP; ++p) {
+      const bool ge = e >= off[p];
+      sp = ge ? p : sp;
+      o = ge ? off[p] : o;
+      lo = ge ? ilo[p] : lo;
     }
+    e_sp[r] = sp;
+    e_off[r] = (compact && e < E)
+                   ? (uint32_t)sp * (uint32_t)(T * k * 2) + (uint32_t)(lo + (e - o)) * 2u
+                   : kOOB;
   }
 
   // ---- the ring: the first kR rows' code spans and BF16 entries. One
@@ -283,8 +289,8 @@ void dq_window_kernel(
     uint32_t bf = 0;
 #pragma unroll
     for (int e = 0; e < kWinFeat; ++e) {
-      if (fm[m][e] >= 0 && fm[m][e] != INT_MAX) jf = min(jf, fm[m][e]);
-      if (fm[m][e] < 0) bf |= 1u << e;
+      jf = min(jf, fm[m][e] >= 0 ? fm[m][e] : INT_MAX);
+      bf |= (fm[m][e] < 0 ? 1u : 0u) << e;
     }
     bfm[m] = bf;
     // 8 bytes at cb hold every code of the window; kept inside the row
@@ -297,13 +303,12 @@ void dq_window_kernel(
     int hi = 0;
 #pragma unroll
     for (int e = 0; e < kWinFeat; ++e) {
-      uint32_t sel = 0x0Cu, msk = 0u;   // selector 0x0C gives a zero byte
-      if (fm[m][e] >= 0 && fm[m][e] != INT_MAX) {
-        const int n = fm[m][e] - 2 * base;   // nibble 0..15 of the 8 bytes
-        sel = (uint32_t)(n >> 1);
-        msk = (n & 1) ? 0xF0u : 0x0Fu;
-        hi |= (n & 1) << e;
-      }
+      // (selects, not branches; selector 0x0C gives a zero byte)
+      const bool q = fm[m][e] >= 0 && fm[m][e] != INT_MAX;
+      const int n = fm[m][e] - 2 * base;   // nibble 0..15 of the 8 bytes when q
+      const uint32_t sel = q ? (uint32_t)(n >> 1) : 0x0Cu;
+      const uint32_t msk = q ? ((n & 1) ? 0xF0u : 0x0Fu) : 0u;
+      hi |= (q ? (n & 1) : 0) << e;
       if (e < 4) {
         sa |= sel << (8 * e);
         ma |= msk << (8 * e);
@@ -336,7 +341,10 @@ void dq_window_kernel(
         int rank = 0;
 #pragma unroll
         for (int e = 0; e < kWinFeat; ++e) {
-          if (fm[p][e] < 0) inv[off[p] + (-1 - fm[p][e]) - ilo[p]] = pos0 + rank;
+          // a feature that is not BF16 on shard p writes the lane's dummy dword
+          const int at = fm[p][e] < 0 ? off[p] + (-1 - fm[p][e]) - ilo[p]
+                                      : (int)(reinterpret_cast<int*>(dummy) - inv) + lane;
+          inv[at] = pos0 + rank;
           rank += (any >> e) & 1;
         }
       }
@@ -345,18 +353,21 @@ void dq_window_kernel(
   // zero the table rows of this tile (int4 shards of a BF16 feature stay 0)
   for (int i = lane; i < nb_any * NP && compact; i += kWave) tab[i] = 0.0f;
   wave_lds_sync();
-  uint32_t e_dst[kOR];   // entry: LDS dword
+  uint32_t e_dst[kOR];   // entry: LDS dword (past the entries: the lane's dummy)
 #pragma unroll
   for (int r = 0; r < kOR; ++r) {
     const int e = r * kWave + lane;
-    e_dst[r] = (uint32_t)(dummy - tab) + lane;
-    if (compact && e < E) {
-      int sp = 0;
+    const bool live = compact && e < E;
+    int row;
+    if constexpr (kPs) {
+      row = inv[live ? e : 0];
+    } else {
+      int o = 0;
 #pragma unroll
-      for (int p = 1; p < NP; ++p) sp = e >= off[p] ? p : sp;
-      const int row = kPs ? inv[e] : e - off[sp];
-      e_dst[r] = (uint32_t)(row * NP + sp);
+      for (int p = 1; p < NP; ++p) o = e >= off[p] ? off[p] : o;
+      row = e - o;
     }
+    e_dst[r] = live ? (uint32_t)(row * NP + e_sp[r]) : (uint32_t)(dummy - tab) + lane;
   }
   wave_lds_sync();
 
@@ -364,6 +375,18 @@ void dq_window_kernel(
   // of a shard where the feature is BF16 has code 0 and scale 0, so it adds
   // exactly 0 whatever that shard's scale is.
   float sc[NP][kWinFeat], bias[kWinFeat];
+  // per map and feature: int4 or not, and the factor a high nibble's scale
+  // carries (selects, not branches: every lane runs the same instructions)
+  bool q4[NM][kWinFeat];
+  float mh[NM][kWinFeat];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+#pragma unroll
+    for (int e = 0; e < kWinFeat; ++e) {
+      q4[m][e] = fm[m][e] >= 0 && fm[m][e] != INT_MAX;
+      mh[m][e] = ((nib_hi[m] >> e) & 1) ? 0.0625f : 1.0f;
+    }
+  }
 #pragma unroll
   for (int e = 0; e < kWinFeat; ++e) bias[e] = 0.0f;
 #pragma unroll
@@ -373,10 +396,11 @@ void dq_window_kernel(
     for (int e = 0; e < kWinFeat; ++e) {
       const float s = __uint_as_float(sv[p][e >> 2][e & 3]);
       const float z = (float)((zv[p][e >> 2] >> (8 * (e & 3))) & 0xFFu);
-      const bool q4 = fm[m][e] >= 0 && fm[m][e] != INT_MAX;
-      // -sum_p z*s over the int4 shards, in shard order from +0
-      if (q4) bias[e] = fmaf(-z, s, bias[e]);
-      sc[p][e] = q4 ? s * (((nib_hi[m] >> e) & 1) ? 0.0625f : 1.0f) : 0.0f;
+      // -sum_p z*s over the int4 shards, in shard order from +0. With one
+      // set, a BF16 feature's constant is never used (its sum replaces it).
+      const float b = fmaf(-z, s, bias[e]);
+      bias[e] = (kPs && !q4[m][e]) ? bias[e] : b;
+      sc[p][e] = q4[m][e] ? s * mh[m][e] : 0.0f;
       settle(sc[p][e]);
     }
   }

@@ -308,6 +308,42 @@ def test_misaligned_parameter_arrays():
     run_both(calib, x, k, 0.9, param_offset=1)
 
 
+def test_bf16_sum_overflow_stays_in_its_feature():
+    """BF16 features whose shard sums overflow fp32: their outputs are +inf on
+    both sides (fp32 and bf16 receivers), and every other feature, the int4
+    ones that share their lane included, stays finite and within tolerance."""
+    P, T, H = 4, 6, 1024
+    feats = np.array([100, 101, 102, 600])   # 100-102 share a receiver lane with 96-103
+    say("case: BF16 sums that overflow to inf")
+    xb = W.draw(P, T, H, 5200, device=DEV).view(torch.bfloat16).clone()
+    ramp = torch.linspace(1.0e38, 3.0e38, P * T, device=DEV).reshape(P, T, 1)
+    xb[:, :, feats.tolist()] = ramp.to(torch.bfloat16)
+    x = xb.view(torch.int16)
+    rmin = torch.empty((P, H), dtype=torch.float32, device=DEV)
+    rmax = torch.empty_like(rmin)
+    B.btq_calib_update(x, rmin, rmax, 0.9, first_batch=True)
+    mn, mx = oracle_calib(u16(x), None, None, 0.9, first=True)
+    sel_g = B.btq_select_features(rmin, rmax, feats)
+    sel_o = O.select_features(mn, mx, feats)
+    torch.cuda.synchronize()
+    assert_selection_equal(sel_g, sel_o)
+    pk, ol = B.btq_compress_pack(x, len(feats), sel_g["rscale"], sel_g["zero_point"],
+                                 sel_g["outlier_idx"], sel_g["cmap"])
+    par = (sel_g["scale"], sel_g["zero_point"], sel_g["fmap"])
+    y = B.btq_decompress_reduce(pk, ol, H, *par)
+    y16 = B.btq_decompress_reduce_bf16(pk, ol, H, *par)
+    pk_o, ol_o = oracle_compress_rows(u16(x), sel_o)
+    y_o = O.decompress_reduce(pk_o, ol_o, sel_o["scale"], sel_o["zero_point"], sel_o["fmap"])
+    torch.cuda.synchronize()
+    assert np.isposinf(y_o[:, feats]).all()
+    yg = y.cpu().numpy()
+    assert np.array_equal(yg[:, feats].view(np.uint32), y_o[:, feats].view(np.uint32))
+    rest = np.setdiff1d(np.arange(H), feats)
+    assert np.isfinite(yg[:, rest]).all()
+    assert_y_close(yg[:, rest], y_o[:, rest], sel_o["scale"][:, rest], [])
+    assert torch.equal(y16, y.to(torch.bfloat16).view(torch.int16))
+
+
 def test_momentum_range():
     say("case: momentum 0 and the largest fp32 below 1; 1 is rejected")
     P, T, H = 2, 8, 64
