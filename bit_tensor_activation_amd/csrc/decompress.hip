@@ -99,23 +99,31 @@ __device__ __forceinline__ int first_lane_value(bool has, int v) {
   return m ? __builtin_amdgcn_readlane(v, __ffsll((unsigned long long)m) - 1) : 0;
 }
 
-// Staged code dwords per shard and row: every lane writes 8 bytes, the
-// first 33 lanes the tile's code span of at most 66 dwords.
-constexpr int kStageDwords = 2 * kWave;
+// Stage of one row's code spans, at the start of the wave's LDS: span dword
+// d of shard p at d*kSP + 2p, kSP = 2*NP + 1. A lane's window of every shard
+// is then two dwords at offsets 2p and 2p + kSP from one base, which the
+// instructions carry (no per-row address arithmetic); no two shards' dwords
+// are adjacent, so the compiler does not fuse writes that would need their
+// registers paired; the odd stride keeps the window reads free of bank
+// conflicts, and the span writes conflict at most 2 ways. Every lane writes
+// its 8 bytes (the first 33 lanes the tile's span of at most 66 dwords).
 constexpr int kStageLanes = 33;
+__host__ __device__ constexpr int stage_stride(int np) { return 2 * np + 1; }
 
-// LDS per wave of the window kernel, in dwords: the BF16 table (one row of
-// NP floats per BF16 feature of the tile, at most kOR*64 entries), the entry
-// -> table-row map of per-shard sets (kOR*64 ints), one private dummy dword
-// per lane for entries past the tile's count, for fp32 output the 2 KB row
-// that turns the lanes' 32-byte runs into whole-line stores, and the stage
-// of one row's code spans.
+// LDS per wave of the window kernel, in dwords: the stage of one row's code
+// spans (first, so that the window reads' offsets fit their instructions),
+// the BF16 table (one row of NP floats per BF16 feature of the tile, at most
+// kOR*64 entries), the entry -> table-row map of per-shard sets (kOR*64
+// ints), one private dummy dword per lane for entries past the tile's count,
+// and for fp32 output the 2 KB row that turns the lanes' 32-byte runs into
+// whole-line stores.
 template <int NP, int kOR, bool kPs>
 __host__ __device__ constexpr int win_tab_dwords() { return kPs ? NP * kOR * kWave : kOR * kWave; }
+__host__ __device__ constexpr int win_stage_dwords(int np) { return 2 * kWave * stage_stride(np); }
 template <int NP, int kOR, bool kPs, bool kBf>
 __host__ __device__ constexpr int win_lds_dwords() {
-  return win_tab_dwords<NP, kOR, kPs>() + (kPs ? kOR * kWave : 0) + kWave +
-         (kBf ? 0 : kWinTile) + NP * kStageDwords;
+  return win_stage_dwords(NP) + win_tab_dwords<NP, kOR, kPs>() + (kPs ? kOR * kWave : 0) +
+         kWave + (kBf ? 0 : kWinTile);
 }
 
 // NP: shards (1..8). kOR: BF16 entry registers per row. kR: ring depth.
@@ -133,6 +141,7 @@ void dq_window_kernel(
   constexpr int NM = kPs ? NP : 1;             // maps
   constexpr uint32_t kYB = kBf ? 2u : 4u;      // bytes per y value
   constexpr int kLds = win_lds_dwords<NP, kOR, kPs, kBf>();
+  constexpr int kSP = stage_stride(NP);
   extern __shared__ __align__(16) float dq_smem[];
   int64_t rb, sub;
   const int ntgrp = (ntiles + kDqWaves - 1) / kDqWaves;
@@ -146,11 +155,11 @@ void dq_window_kernel(
   const bool active = h0 < H;   // H is a multiple of 8: a lane is all in or all out
   const int64_t t0 = rb * rows_per_wave;
   const int nrows = (int)min(T - t0, (int64_t)rows_per_wave);   // >= 1
-  float* const tab = dq_smem + (size_t)wave * kLds;
+  uint32_t* const stage = reinterpret_cast<uint32_t*>(dq_smem + (size_t)wave * kLds);
+  float* const tab = dq_smem + (size_t)wave * kLds + win_stage_dwords(NP);
   int* const inv = reinterpret_cast<int*>(tab + win_tab_dwords<NP, kOR, kPs>());
   float* const dummy = tab + win_tab_dwords<NP, kOR, kPs>() + (kPs ? kOR * kWave : 0);
   float* const yrow = dummy + kWave;   // fp32 output only
-  uint32_t* const stage = reinterpret_cast<uint32_t*>(yrow + (kBf ? 0 : kWinTile));
 
   // ---- setup (a): the lane's map entries, scales and zero points
   const rsrc_t rf = make_rsrc(fmap, (uint32_t)(NM * (int64_t)H * 4));
@@ -431,10 +440,11 @@ void dq_window_kernel(
   // stores take an immediate zero scalar offset: a store wider than 64 bits
   // reads its data after issue, and only with an immediate scalar offset
   // does the compiler keep the next instruction from overwriting them)
-  auto row_rsrc = [&](int row) {
-    return make_rsrc(ybase + (int64_t)min(row, nrows - 1) * H * kYB,
-                     row < nrows ? (uint32_t)H * kYB : 0u);
-  };
+  const uint32_t ybytes_row = (uint32_t)H * kYB;
+  // wave-uniform switches of the row loop, held in scalar registers
+  const bool do_tab = __builtin_amdgcn_readfirstlane((int)(compact && nb_any > 0)) != 0;
+  const bool do_own = __builtin_amdgcn_readfirstlane((int)(compact && umax > 0)) != 0;
+  char* yrow_ptr = ybase;   // advanced by one row per row (uniform)
 
   int base = 0;
   do {
@@ -444,9 +454,12 @@ void dq_window_kernel(
       // the row's code spans and BF16 entries into LDS; then each lane's
       // code windows and the owners' first table row
 #pragma unroll
-      for (int p = 0; p < NP; ++p)
-        *reinterpret_cast<v2u*>(stage + p * kStageDwords + 2 * lane) = w[q][p];
-      if (compact && nb_any > 0) {
+      for (int p = 0; p < NP; ++p) {
+        uint32_t* const dst = stage + 2 * lane * kSP + 2 * p;
+        dst[0] = w[q][p][0];
+        dst[kSP] = w[q][p][1];
+      }
+      if (do_tab) {
 #pragma unroll
         for (int r = 0; r < kOR; ++r) tab[e_dst[r]] = __uint_as_float(ov[q][r] << 16);
       }
@@ -454,12 +467,12 @@ void dq_window_kernel(
       v2u x[NP];
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const uint32_t* src = stage + p * kStageDwords + dwin[kPs ? p : 0];
-        x[p] = v2u{src[0], src[1]};
+        const uint32_t* src = stage + dwin[kPs ? p : 0] * kSP + 2 * p;
+        x[p] = v2u{src[0], src[kSP]};
       }
       // the owner's first BF16 feature: its row summed in shard order from +0
       float o = 0.0f;
-      if (compact && umax > 0) {
+      if (do_own) {
         const float* t = tab + (cnt_any > 0 ? pos0 : 0) * NP;
         if constexpr (NP % 4 == 0) {
 #pragma unroll
@@ -493,7 +506,7 @@ void dq_window_kernel(
       // this row's registers are consumed: refill the slot kR rows ahead
       load_row(q, row + kR);
       issue_fence();
-      if (compact && umax > 0) {
+      if (do_own) {
         place(acc, e_first, o);
         int rest = any_rest;
         for (int u = 1; u < umax; ++u) {   // lanes with several BF16 features
@@ -505,7 +518,9 @@ void dq_window_kernel(
           rest &= rest - 1;
         }
       }
-      const rsrc_t ry = row_rsrc(row);
+      // (a row past the wave's last: no records, every store dropped)
+      const rsrc_t ry = make_rsrc(yrow_ptr, row < nrows ? ybytes_row : 0u);
+      yrow_ptr += ybytes_row;
       if constexpr (kBf) {
         __builtin_amdgcn_raw_buffer_store_b128(
             v4u{bf16_pair(acc[0], acc[1]), bf16_pair(acc[2], acc[3]), bf16_pair(acc[4], acc[5]),
