@@ -1,5 +1,6 @@
 """Generated gfx950 code (CPU): every HIP source is compiled to assembly and
-scanned for a hardware hazard.
+scanned for a hardware hazard and for the register budgets the kernels are
+designed around.
 
 A vector-memory store of more than 64 bits of data reads its data registers
 after it issues, so a VALU instruction that writes one of those registers
@@ -83,8 +84,48 @@ def test_scanner_finds_the_pattern():
     assert len(hazards(glob_bad)) == 1 and hazards(glob_addr) == []
 
 
-def test_no_valu_write_to_wide_store_data_on_the_next_instruction(tmp_path):
-    paths = build.device_asm(str(tmp_path))
+@pytest.fixture(scope="module")
+def asm_paths(tmp_path_factory):
+    return build.device_asm(str(tmp_path_factory.mktemp("asm")))
+
+
+def kernel_resources(paths):
+    """{kernel symbol: {field: value}} from the .amdhsa_kernel descriptors."""
+    out = {}
+    for p in paths:
+        text = open(p).read()
+        for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", text, re.S):
+            fields = dict(re.findall(r"\.amdhsa_(\w+)\s+(\d+)", m.group(2)))
+            out[m.group(1)] = {k: int(v) for k, v in fields.items()}
+    return out
+
+
+def test_no_kernel_spills_to_scratch(asm_paths):
+    res = kernel_resources(asm_paths)
+    assert len(res) > 40
+    spills = {k: r["private_segment_fixed_size"] for k, r in res.items()
+              if r.get("private_segment_fixed_size", 0)}
+    assert not spills, spills
+
+
+def test_receiver_register_budgets(asm_paths):
+    """The receiver's common form (one set, two entry registers) fits 3 waves
+    per SIMD (at most 168 registers); every form fits 2 (at most 256, so no
+    accumulator registers hold spills)."""
+    res = kernel_resources(asm_paths)
+    window = {k: r for k, r in res.items() if "dq_window_kernel" in k}
+    assert len(window) >= 64
+    for name, r in window.items():
+        regs = r["next_free_vgpr"]
+        assert regs <= 256, (name, regs)
+        m = re.search(r"dq_window_kernelILi(\d)ELi(\d)ELi(\d)ELb(\d)ELb(\d)E", name)
+        assert m, name
+        if m.group(2) == "2" and m.group(4) == "0":
+            assert regs <= 168, (name, regs)
+
+
+def test_no_valu_write_to_wide_store_data_on_the_next_instruction(asm_paths):
+    paths = asm_paths
     assert paths
     found = {}
     n_wide = 0
