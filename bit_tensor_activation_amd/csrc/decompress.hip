@@ -386,6 +386,10 @@ void dq_window_kernel(
   float sc[NP][kWinFeat], bias[kWinFeat];
   // per map and feature: int4 or not, and the factor a high nibble's scale
   // carries (selects, not branches: every lane runs the same instructions)
+  // (one set: a BF16 feature's factor is 0 and its products, even
+  // non-finite ones, stay in its own accumulator, which its BF16 sum
+  // replaces; per-shard sets select 0 so that a shard where the feature is
+  // BF16 adds exactly 0 to its int4 part)
   bool q4[NM][kWinFeat];
   float mh[NM][kWinFeat];
 #pragma unroll
@@ -394,6 +398,7 @@ void dq_window_kernel(
     for (int e = 0; e < kWinFeat; ++e) {
       q4[m][e] = fm[m][e] >= 0 && fm[m][e] != INT_MAX;
       mh[m][e] = ((nib_hi[m] >> e) & 1) ? 0.0625f : 1.0f;
+      if (!kPs) mh[m][e] = q4[m][e] ? mh[m][e] : 0.0f;
     }
   }
 #pragma unroll
@@ -409,7 +414,7 @@ void dq_window_kernel(
       // set, a BF16 feature's constant is never used (its sum replaces it).
       const float b = fmaf(-z, s, bias[e]);
       bias[e] = (kPs && !q4[m][e]) ? bias[e] : b;
-      sc[p][e] = q4[m][e] ? s * mh[m][e] : 0.0f;
+      sc[p][e] = kPs ? (q4[m][e] ? s * mh[m][e] : 0.0f) : s * mh[m][e];
       settle(sc[p][e]);
     }
   }
