@@ -13,14 +13,17 @@
 // whole cache lines. A 256-thread block takes 4 adjacent tiles of one block
 // of token rows; all blocks of a row block run on one XCD (xcd_unit_block).
 //  0. Setup, once per wave. The lane loads its 8 features' map entries, and
-//     each shard's scales and zero points, with contiguous loads. A shard's
-//     int4 features among the 8 take consecutive slots, so all their codes
-//     lie in the 8 bytes at the 4-byte aligned offset `cb` at or below the
-//     first one's byte; two byte selectors (v_perm_b32) place each code's
-//     byte under its feature, and a mask keeps its nibble. Each feature
-//     starts from the constant -sum_p z*s over its int4 shards, and a high
-//     nibble, kept in place as 16q, meets its scale divided by 16 (exact).
-//     The first kR token rows are issued once the map has arrived.
+//     each shard's scales and zero points, with contiguous loads. Two scalar
+//     map reads give the tile's code span and BF16 index runs, so the first
+//     kR token rows are issued right behind those loads. A shard's int4
+//     features among the 8 take consecutive slots, so all their codes lie in
+//     the 8 bytes at the 4-byte aligned offset `cb` at or below the first
+//     one's byte; two byte selectors (v_perm_b32) place each code's byte
+//     under its feature, and a mask keeps its nibble. Each feature starts
+//     from the constant -sum_p z*s over its int4 shards, and a high nibble,
+//     kept in place as 16q, meets its scale divided by 16 (exact). The setup
+//     is written with selects throughout: every lane runs the same
+//     instructions, with no per-lane branches.
 //  1. Per token row and shard, the tile's code span (at most 66 dwords) is
 //     one coalesced 8-byte load on the first 33 lanes, so every packed byte
 //     is requested once; the span goes through the wave's LDS stage, where
@@ -129,11 +132,10 @@ __host__ __device__ constexpr int win_lds_dwords() {
 // NP: shards (1..8). kOR: BF16 entry registers per row. kR: ring depth.
 // kPs: fmap is [P,H] (one set per shard) instead of [H]. kBf: y is bf16.
 // Waves per SIMD the register budget aims at: 3 (at most 168 registers) for
-// one set with two entry registers, 2 with four; one set per shard needs
-// more registers than 2 waves leave.
+// one set with two entry registers, else 2 (at most 256).
 template <int NP, int kOR, int kR, bool kPs, bool kBf>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(kPs ? 1 : (kOR == 2 ? 3 : 2))))
+__attribute__((amdgpu_waves_per_eu((!kPs && kOR == 2) ? 3 : 2)))
 void dq_window_kernel(
     const uint8_t* __restrict__ packed, int pitch, const uint16_t* __restrict__ outl, int64_t T,
     int H, int k, int ntiles, int rows_per_wave, int64_t nrowblk, const float* __restrict__ scale,
@@ -380,16 +382,13 @@ void dq_window_kernel(
   }
   wave_lds_sync();
 
-  // ---- per-lane constants (their loads are older than the ring). A term
-  // of a shard where the feature is BF16 has code 0 and scale 0, so it adds
-  // exactly 0 whatever that shard's scale is.
+  // ---- per-lane constants (their loads are older than the ring). Per map
+  // and feature: int4 or not, and the factor its scale carries (1/16 for a
+  // high nibble). A term of a shard where the feature is BF16 has code 0 and
+  // scale 0: with one set its products, even non-finite ones, stay in the
+  // feature's own accumulator, which its BF16 sum replaces; per-shard sets
+  // select scale 0 so that such a shard adds exactly 0 to the int4 part.
   float sc[NP][kWinFeat], bias[kWinFeat];
-  // per map and feature: int4 or not, and the factor a high nibble's scale
-  // carries (selects, not branches: every lane runs the same instructions)
-  // (one set: a BF16 feature's factor is 0 and its products, even
-  // non-finite ones, stay in its own accumulator, which its BF16 sum
-  // replaces; per-shard sets select 0 so that a shard where the feature is
-  // BF16 adds exactly 0 to its int4 part)
   bool q4[NM][kWinFeat];
   float mh[NM][kWinFeat];
 #pragma unroll
