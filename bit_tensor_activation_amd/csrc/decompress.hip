@@ -62,7 +62,13 @@ constexpr int kWinTile = kWave * kWinFeat;     // 512 features per wave-tile
 // HBM as busy as four, and measured up to 7% faster at large batches: fewer
 // requests in flight per CU, and fewer registers.
 constexpr int kDqRing = 2;
-constexpr int64_t kDqGeneration = 1024;        // waves at one per SIMD
+// Rows per wave: about 2048 waves (two per SIMD) when that leaves each wave
+// at least 16 rows, else about 1024 (one per SIMD); up to 64 rows. Two waves
+// of 16 rows took large prefill at T=2048 from 28.7 to 26.5 us; below 16
+// rows the setup's share costs more than the second wave hides.
+constexpr int64_t kDqWavesTwo = 2048;
+constexpr int64_t kDqWavesOne = 1024;
+constexpr int64_t kDqMinRowsTwo = 16;
 
 // fp32 -> bf16, round to nearest even, two values per instruction
 // (v_cvt_pk_bf16_f32): a in the low half, b in the high half.
@@ -674,9 +680,8 @@ static hipError_t launch_decompress_t(const uint8_t* packed, int64_t pitch, cons
                     P * T * pitch < lim && 64 * H * 4 < lim;
   if (fast) {
     const int ntiles = (int)((H + kWinTile - 1) / kWinTile);
-    // about kDqGeneration waves where the batch allows, each with at least a
-    // full ring of rows; up to 64 rows per wave
-    int64_t rpw64 = (ntiles * T + kDqGeneration - 1) / kDqGeneration;
+    int64_t rpw64 = (ntiles * T + kDqWavesTwo - 1) / kDqWavesTwo;
+    if (rpw64 < kDqMinRowsTwo) rpw64 = (ntiles * T + kDqWavesOne - 1) / kDqWavesOne;
     rpw64 = (rpw64 + kDqRing - 1) / kDqRing * kDqRing;
     if (rpw64 < kDqRing) rpw64 = kDqRing;
     if (rpw64 > 64) rpw64 = 64;
