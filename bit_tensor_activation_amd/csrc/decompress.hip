@@ -63,12 +63,16 @@ constexpr int kWinTile = kWave * kWinFeat;     // 512 features per wave-tile
 // requests in flight per CU, and fewer registers.
 constexpr int kDqRing = 2;
 // Rows per wave: about 2048 waves (two per SIMD) when that leaves each wave
-// at least 16 rows, else about 1024 (one per SIMD); up to 64 rows. Two waves
-// of 16 rows took large prefill at T=2048 from 28.7 to 26.5 us; below 16
-// rows the setup's share costs more than the second wave hides.
+// at least dq_min_rows_two rows, else about 1024 (one per SIMD); up to 64
+// rows. Two waves of 16 rows took large prefill at T=2048 from 28.7 to
+// 26.5 us. Below 16 rows the fp32 receiver's setup costs more than the
+// second wave hides; the bf16-output and per-shard receivers gain down to 8
+// (7B prefill, T=2048: bf16 21.9 -> 18.9 us, per-shard 29.1 -> 28.2 us).
 constexpr int64_t kDqWavesTwo = 2048;
 constexpr int64_t kDqWavesOne = 1024;
-constexpr int64_t kDqMinRowsTwo = 16;
+__host__ __device__ constexpr int64_t dq_min_rows_two(bool per_shard, bool bf16_out) {
+  return (per_shard || bf16_out) ? 8 : 16;
+}
 
 // fp32 -> bf16, round to nearest even, two values per instruction
 // (v_cvt_pk_bf16_f32): a in the low half, b in the high half.
@@ -78,6 +82,14 @@ __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{a, b}, v2bf));
 }
 __device__ __forceinline__ uint16_t bf16_rne(float f) { return (uint16_t)(bf16_pair(f, 0.0f) & 0xFFFFu); }
+
+// Marks a wave-uniform value as redefined here, in a scalar register (an
+// empty asm): its load must be complete at this point, and cannot be moved
+// below it.
+template <typename V>
+__device__ __forceinline__ void settle_s(V& v) {
+  asm volatile("" : "+s"(v));
+}
 
 // Wave-wide counts from ballots (no LDS round trips): v in [0, 15] per lane.
 __device__ __forceinline__ uint64_t lanes_below(int lane) {
@@ -201,13 +213,28 @@ void dq_window_kernel(
   uint32_t abase[NM];   // dword where the code span of a row starts
   int ilo[NP], nbp[NP], off[NP + 1];
   const bool last_tile = f0 + kWinTile >= H;
+  // Every map's two reads are issued together, from an index that is always
+  // in range (on the last tile the second is not used), and pinned in scalar
+  // registers before any is used: otherwise the compiler moves each read
+  // under the condition that uses it, with a wait of its own, and the maps'
+  // reads follow one another (eight round trips for per-shard sets).
+  const int fnext = last_tile ? f0 : f0 + kWinTile;
+  int fa[NM], fb[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     const int32_t* fr = fmap + (kPs ? (int64_t)m * H : 0);
-    const int fa = fr[f0];
-    const int fb = last_tile ? 0 : fr[f0 + kWinTile];
-    const int ia = fa >= 0 ? f0 - fa : -1 - fa;
-    const int ib = last_tile ? k : (fb >= 0 ? f0 + kWinTile - fb : -1 - fb);
+    fa[m] = fr[f0];
+    fb[m] = fr[fnext];
+  }
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    settle_s(fa[m]);
+    settle_s(fb[m]);
+  }
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const int ia = fa[m] >= 0 ? f0 - fa[m] : -1 - fa[m];
+    const int ib = last_tile ? k : (fb[m] >= 0 ? f0 + kWinTile - fb[m] : -1 - fb[m]);
     ilo[m] = ia;
     nbp[m] = ib - ia;
     // the lanes' 8-byte windows start at or after the first int4 slot's
@@ -681,7 +708,7 @@ static hipError_t launch_decompress_t(const uint8_t* packed, int64_t pitch, cons
   if (fast) {
     const int ntiles = (int)((H + kWinTile - 1) / kWinTile);
     int64_t rpw64 = (ntiles * T + kDqWavesTwo - 1) / kDqWavesTwo;
-    if (rpw64 < kDqMinRowsTwo) rpw64 = (ntiles * T + kDqWavesOne - 1) / kDqWavesOne;
+    if (rpw64 < dq_min_rows_two(kPs, kBf)) rpw64 = (ntiles * T + kDqWavesOne - 1) / kDqWavesOne;
     rpw64 = (rpw64 + kDqRing - 1) / kDqRing * kDqRing;
     if (rpw64 < kDqRing) rpw64 = kDqRing;
     if (rpw64 > 64) rpw64 = 64;
