@@ -83,6 +83,10 @@ __device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
 }
 __device__ __forceinline__ uint16_t bf16_rne(float f) { return (uint16_t)(bf16_pair(f, 0.0f) & 0xFFFFu); }
 
+// Byte 0 of v in all four bytes (v_perm_b32: selector 0 picks byte 0 of the
+// second operand).
+__device__ __forceinline__ uint32_t splat_byte0(uint32_t v) { return __builtin_amdgcn_perm(0u, v, 0u); }
+
 // Marks a wave-uniform value as redefined here, in a scalar register (an
 // empty asm): its load must be complete at this point, and cannot be moved
 // below it.
@@ -320,52 +324,59 @@ void dq_window_kernel(
     issue_fence();
   }
 
-  // ---- setup (b): per map, the code window and byte selectors
-  // fm[m][e] >= 0: int4 slot; < 0: BF16 index -1-fm. Inactive lanes: none.
-  int fm[NM][kWinFeat];
+  // ---- setup (b): per map, the code window and byte selectors.
+  // A map entry f >= 0 is an int4 slot, f < 0 the BF16 index -1-f; inactive
+  // lanes have neither. The lane's int4 features take consecutive slots from
+  // the first one's,
+  // jf, so feature e's nibble in the 8-byte window is n0 (jf's nibble) plus
+  // the number of int4 features before e. The selectors therefore follow
+  // from the lane's 8-bit int4 mask and n0; they are computed four features
+  // at a time, one byte per feature: the mask's bits spread to bytes by one
+  // multiplication, the ranks summed into bytes by another (no carries:
+  // every byte stays below 23).
   uint32_t dwin[NM], selA[NM], selB[NM], mskA[NM], mskB[NM], bfm[NM];
-  int nib_hi[NM];   // bit e: feature e's code is a high nibble
+  uint32_t i4A[NM], i4B[NM], hiA[NM], hiB[NM];   // per byte: int4 (1/0); high nibble (1/0)
+  int bf1[NM];   // BF16 index of the lane's first BF16 feature (the others follow it)
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
-#pragma unroll
-    for (int e = 0; e < kWinFeat; ++e) fm[m][e] = active ? (int)fv[m][e >> 2][e & 3] : INT_MAX;
-    int jf = INT_MAX;
-    uint32_t bf = 0;
+    uint32_t qm = 0, jf = 0xFFFFFFFFu, jb = 0u;
 #pragma unroll
     for (int e = 0; e < kWinFeat; ++e) {
-      jf = min(jf, fm[m][e] >= 0 ? fm[m][e] : INT_MAX);
-      bf |= (fm[m][e] < 0 ? 1u : 0u) << e;
+      const uint32_t f = fv[m][e >> 2][e & 3];
+      qm |= ((~f) >> 31) << e;
+      // as unsigned, the BF16 entries (negative) are above every slot, and
+      // the lowest BF16 index is the largest of them
+      jf = min(jf, f);
+      if (kPs) jb = max(jb, f);
     }
-    bfm[m] = bf;
+    qm = active ? qm : 0u;
+    bfm[m] = active ? (~qm & 0xFFu) : 0u;
+    bf1[m] = -1 - (int)jb;
     // 8 bytes at cb hold every code of the window; kept inside the row
     // (the launcher guarantees pitch >= 8)
-    int base = jf == INT_MAX ? 0 : ((jf >> 1) & ~3);
+    int base = qm ? (int)((jf >> 1) & ~3u) : 0;
     if (base + 8 > pitch) base -= 4;
     // the window's dword in the staged span (0 .. 64)
-    dwin[m] = jf == INT_MAX ? 0u : ((uint32_t)base >> 2) - abase[m];
-    uint32_t sa = 0, sb = 0, ma = 0, mb = 0;
-    int hi = 0;
-#pragma unroll
-    for (int e = 0; e < kWinFeat; ++e) {
-      // (selects, not branches; selector 0x0C gives a zero byte)
-      const bool q = fm[m][e] >= 0 && fm[m][e] != INT_MAX;
-      const int n = fm[m][e] - 2 * base;   // nibble 0..15 of the 8 bytes when q
-      const uint32_t sel = q ? (uint32_t)(n >> 1) : 0x0Cu;
-      const uint32_t msk = q ? ((n & 1) ? 0xF0u : 0x0Fu) : 0u;
-      hi |= (q ? (n & 1) : 0) << e;
-      if (e < 4) {
-        sa |= sel << (8 * e);
-        ma |= msk << (8 * e);
-      } else {
-        sb |= sel << (8 * (e - 4));
-        mb |= msk << (8 * (e - 4));
-      }
-    }
-    selA[m] = sa;
-    selB[m] = sb;
-    mskA[m] = ma;
-    mskB[m] = mb;
-    nib_hi[m] = hi;
+    dwin[m] = qm ? ((uint32_t)base >> 2) - abase[m] : 0u;
+    const uint32_t n0 = jf - 2u * (uint32_t)base;   // 0..15 when the lane has an int4 feature
+    const uint32_t sa = __umul24(qm & 0xFu, 0x204081u) & 0x01010101u;   // bit e -> byte e
+    const uint32_t sb = __umul24(qm >> 4, 0x204081u) & 0x01010101u;
+    // per byte: n0 plus the int4 features before it (exclusive prefix sums)
+    const uint32_t na = __umul24(sa, 0x010100u) + (sa << 24) + splat_byte0(n0);
+    const uint32_t nb = __umul24(sb, 0x010100u) + (sb << 24) +
+                        splat_byte0(n0 + (uint32_t)__builtin_popcount(sa));
+    // the code's byte (0x0C gives a zero byte) and nibble mask, zero where BF16
+    auto sel4 = [](uint32_t i4, uint32_t n, uint32_t& sel, uint32_t& msk, uint32_t& hi) {
+      const uint32_t keep = (i4 << 8) - i4;   // 0xFF where int4
+      sel = ((n >> 1) & 0x7F7F7F7Fu & keep) | (0x0C0C0C0Cu & ~keep);
+      const uint32_t odd = n & 0x01010101u;   // the code is a high nibble
+      msk = (0x0F0F0F0Fu ^ ((odd << 8) - odd)) & keep;
+      hi = odd & i4;
+    };
+    sel4(sa, na, selA[m], mskA[m], hiA[m]);
+    sel4(sb, nb, selB[m], mskB[m], hiB[m]);
+    i4A[m] = sa;
+    i4B[m] = sb;
   }
 
   // ---- setup (c): the lanes' BF16 features (wave counts from ballots) and
@@ -382,14 +393,18 @@ void dq_window_kernel(
     if (compact) {
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        int rank = 0;
+        // the lane's BF16 features on shard p are its entries from `first` on,
+        // in feature order; a feature that is not BF16 there writes the lane's
+        // dummy dword
+        const int first = off[p] + bf1[p] - ilo[p];
+        int rank = 0, rb = 0;
 #pragma unroll
         for (int e = 0; e < kWinFeat; ++e) {
-          // a feature that is not BF16 on shard p writes the lane's dummy dword
-          const int at = fm[p][e] < 0 ? off[p] + (-1 - fm[p][e]) - ilo[p]
-                                      : (int)(reinterpret_cast<int*>(dummy) - inv) + lane;
+          const bool is_bf = (bfm[p] >> e) & 1;
+          const int at = is_bf ? first + rb : (int)(reinterpret_cast<int*>(dummy) - inv) + lane;
           inv[at] = pos0 + rank;
           rank += (any >> e) & 1;
+          rb += is_bf ? 1 : 0;
         }
       }
     }
@@ -422,15 +437,15 @@ void dq_window_kernel(
   // feature's own accumulator, which its BF16 sum replaces; per-shard sets
   // select scale 0 so that such a shard adds exactly 0 to the int4 part.
   float sc[NP][kWinFeat], bias[kWinFeat];
-  bool q4[NM][kWinFeat];
-  float mh[NM][kWinFeat];
+  float mh[NM][kWinFeat];   // 1 (low nibble), 1/16 (high nibble), 0 (BF16 on the map)
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
 #pragma unroll
     for (int e = 0; e < kWinFeat; ++e) {
-      q4[m][e] = fm[m][e] >= 0 && fm[m][e] != INT_MAX;
-      mh[m][e] = ((nib_hi[m] >> e) & 1) ? 0.0625f : 1.0f;
-      if (!kPs) mh[m][e] = q4[m][e] ? mh[m][e] : 0.0f;
+      const int sh = 8 * (e & 3);
+      const float is4 = (float)(((e < 4 ? i4A[m] : i4B[m]) >> sh) & 0xFFu);
+      const float ishi = (float)(((e < 4 ? hiA[m] : hiB[m]) >> sh) & 0xFFu);
+      mh[m][e] = fmaf(-0.9375f, ishi, is4);   // exact
     }
   }
 #pragma unroll
@@ -445,8 +460,9 @@ void dq_window_kernel(
       // -sum_p z*s over the int4 shards, in shard order from +0. With one
       // set, a BF16 feature's constant is never used (its sum replaces it).
       const float b = fmaf(-z, s, bias[e]);
-      bias[e] = (kPs && !q4[m][e]) ? bias[e] : b;
-      sc[p][e] = kPs ? (q4[m][e] ? s * mh[m][e] : 0.0f) : s * mh[m][e];
+      const bool q4 = mh[m][e] != 0.0f;
+      bias[e] = (kPs && !q4) ? bias[e] : b;
+      sc[p][e] = kPs ? (q4 ? s * mh[m][e] : 0.0f) : s * mh[m][e];
       settle(sc[p][e]);
     }
   }
