@@ -276,15 +276,43 @@ def summarize_sq(sq_dir: str, note: str, n_simd: int = 1024, mhz: float = 2400.0
     return "\n".join(lines) + "\n"
 
 
+def _quantile(sorted_x, q):
+    """Linear-interpolation quantile of an ascending list."""
+    if not sorted_x:
+        return float("nan")
+    pos = q * (len(sorted_x) - 1)
+    lo = int(pos)
+    hi = min(lo + 1, len(sorted_x) - 1)
+    return sorted_x[lo] + (sorted_x[hi] - sorted_x[lo]) * (pos - lo)
+
+
+def trace_durations(trace_dir: str) -> dict:
+    """{kernel: [durations in ns]} of the libbtq dispatches in a rocprofv3
+    --kernel-trace run (End_Timestamp - Start_Timestamp per dispatch)."""
+    out = {}
+    for r in _csv_rows(trace_dir, "kernel_trace.csv"):
+        name = r.get("Kernel_Name", "")
+        if "btq::" in name and r.get("Start_Timestamp") and r.get("End_Timestamp"):
+            key = name.split("(")[0].replace("void ", "")
+            out.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return out
+
+
 def summarize_trace(trace_dir: str, note: str) -> str:
-    """The libbtq rows of a rocprofv3 --kernel-trace --stats run."""
+    """The libbtq rows of a rocprofv3 --kernel-trace --stats run: the stats
+    file's calls, average, min and max, and the median, p10 and p90 of the
+    per-dispatch durations in the trace file."""
+    durs = trace_durations(trace_dir)
     lines = ["# " + note.replace("\n", "\n# "),
-             "# kernel | calls | average ns | min ns | max ns | share of GPU time %"]
+             "# kernel | calls | average ns | median ns | p10 ns | p90 ns | min ns | max ns | "
+             "share of GPU time %"]
     for r in _csv_rows(trace_dir, "kernel_stats.csv"):
         if "btq::" in r["Name"]:
             name = r["Name"].split("(")[0].replace("void ", "")
-            lines.append(f"{name} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
-                         f"{r['MaxNs']} | {float(r['Percentage']):.2f}")
+            d = sorted(durs.get(name, []))
+            qs = " | ".join(f"{_quantile(d, q):.0f}" if d else "-" for q in (0.5, 0.1, 0.9))
+            lines.append(f"{name} | {r['Calls']} | {float(r['AverageNs']):.0f} | {qs} | "
+                         f"{r['MinNs']} | {r['MaxNs']} | {float(r['Percentage']):.2f}")
     return "\n".join(lines) + "\n"
 
 
@@ -582,7 +610,10 @@ def main() -> int:
 
     def kernel_entry(ms_list, nbytes):
         mean = sum(ms_list) / len(ms_list)
+        srt = sorted(ms_list)
         return {"mean_us": round(mean * 1e3, 2), "median_us": round(med(ms_list) * 1e3, 2),
+                "p10_us": round(_quantile(srt, 0.1) * 1e3, 2),
+                "p90_us": round(_quantile(srt, 0.9) * 1e3, 2),
                 "algorithmic_bytes": nbytes, "hbm_GBps": round(nbytes / (mean * 1e-3) / 1e9, 1),
                 "frac": round(nbytes / (mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                 "bf16_equiv_GBps": round(bf16_bytes / (mean * 1e-3) / 1e9, 1)}

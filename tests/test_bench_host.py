@@ -100,8 +100,21 @@ def test_trace_and_sq_summaries(tmp_path):
                ["void at::native::elementwise(x)", 3, 5.0, 4, 6, 1.0]])
     out = bench.summarize_trace(str(tmp_path / "t"), "note")
     rows = [l for l in out.splitlines() if not l.startswith("#")]
-    assert rows == ["btq::dq_window_kernel<8, 2, 4, false, false> | 10 | 19000 | 18000 | 22000 | "
-                    "12.50"]
+    # no per-dispatch trace file: no quantiles
+    assert rows == ["btq::dq_window_kernel<8, 2, 4, false, false> | 10 | 19000 | - | - | - | "
+                    "18000 | 22000 | 12.50"]
+    # durations 18000, 18100, ..., 18900 ns (ten dispatches, in shuffled order)
+    durs = [18000 + 100 * i for i in (3, 7, 0, 9, 1, 5, 2, 8, 4, 6)]
+    write_csv(str(tmp_path / "t" / "run_kernel_trace.csv"),
+              ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+              [["KERNEL_DISPATCH", "void btq::dq_window_kernel<8, 2, 4, false, false>(x)",
+                1000 * i, 1000 * i + d] for i, d in enumerate(durs)] +
+              [["KERNEL_DISPATCH", "void at::native::elementwise(x)", 5, 9]])
+    rows = [l for l in bench.summarize_trace(str(tmp_path / "t"), "note").splitlines()
+            if not l.startswith("#")]
+    # median 18450, p10 18090, p90 18810 (linear interpolation)
+    assert rows == ["btq::dq_window_kernel<8, 2, 4, false, false> | 10 | 19000 | 18450 | 18090 | "
+                    "18810 | 18000 | 22000 | 12.50"]
     hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
     vals = {"SQ_WAVE_CYCLES": 1000.0, "SQ_WAIT_INST_ANY": 590.0, "SQ_WAIT_ANY": 130.0,
             "SQ_ACTIVE_INST_VALU": 150.0, "SQ_ACTIVE_INST_LDS": 50.0,
