@@ -316,6 +316,21 @@ def summarize_trace(trace_dir: str, note: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+# Steps shorter than this (wall time, no instrumentation) are timed behind a
+# head start (gpu_head_start).
+SHORT_STEP_S = 60e-6
+
+
+def gpu_head_start(torch, n_ops: int) -> None:
+    """Queues a bounded spin kernel (torch's) on the current stream, long
+    enough for the host to enqueue about n_ops launches and event records
+    (about 25 us each at 2.4 GHz, at most 2000 of them) before the GPU reaches
+    them. Events around each launch then time the GPU's work: without it a
+    kernel shorter than the host's enqueue time waits for its own launch
+    after its start event has been stamped."""
+    torch.cuda._sleep(int(min(n_ops, 2000) * 60000))
+
+
 def algorithmic_bytes(P, T, H, k, y_bytes=4):
     """Bytes the method must move per launch, inputs once and outputs once:
     sender  P*T*H*2 (bf16 input) + P*T*(Bq + 2k) (message) + 5*P*H (rscale
@@ -592,17 +607,25 @@ def main() -> int:
         # Timed region 2: the same steps again with a HIP event around every
         # launch, on the launch stream (each kernel's duration). The events cost
         # a few microseconds per step, so region 1 alone gives the throughput.
+        # Steps shorter than the host's enqueue time (decode) give the GPU a
+        # head start, so that the events time its work and not the rate at
+        # which the host enqueues launches. Longer steps keep the host ahead
+        # by themselves, and there the spin's idle time measurably slows the
+        # kernels that follow it (2-4% at large prefill and stress).
+        short_steps = wall / args.steps < SHORT_STEP_S
         evs = [[hev.new() for _ in range(3)] for _ in range(args.steps)]
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
+        if short_steps:
+            gpu_head_start(torch, 5 * args.steps)
         for i in range(args.steps):
             st |= step(i, evs[i])
         torch.cuda.synchronize()
-        wall_ev = time.perf_counter() - t1
+        wall_ev = hev.ms(evs[0][0], evs[-1][2]) * 1e-3
         _lib.check(st, "instrumented steps")
         comp_ms = [hev.ms(e[0], e[1]) for e in evs]
         deco_ms = [hev.ms(e[1], e[2]) for e in evs]
         results[layout] = dict(wall=wall, wall_ev=wall_ev, comp_ms=comp_ms, deco_ms=deco_ms,
+                               short_steps=short_steps,
                                calls=(compress, decompress, comp_args, deco_args))
         log(f"{layout}: {wall / args.steps * 1e6:.1f} us per step, sender "
             f"{sum(comp_ms) / len(comp_ms) * 1e3:.1f} us, receiver "
@@ -639,6 +662,8 @@ def main() -> int:
             _lib.check(fn(*args_list[i % len(args_list)]), what)
         ev = [(hev.new(), hev.new()) for _ in range(n)]
         torch.cuda.synchronize()
+        if head["short_steps"]:
+            gpu_head_start(torch, 3 * n)
         s_ = 0
         for i in range(n):
             hev.record(ev[i][0], sh)
@@ -754,7 +779,9 @@ def main() -> int:
         "kernels": kernels,
         "timing": {"value": f"{args.steps} steps with no instrumentation between launches",
                    "kernels": f"the same {args.steps} steps again with HIP events around every "
-                              "launch on the launch stream (fence-free events)",
+                              "launch on the launch stream (fence-free events); steps shorter "
+                              "than 60 us are queued behind a spin kernel, so that the events "
+                              "time the GPU and not the host's enqueue rate",
                    "ms_per_step_instrumented": round(head["wall_ev"] / args.steps * 1e3, 5)},
         "offline": {"calib_batches": w.calib_batches, "calib_ms_total": round(calib_ms, 3),
                     "calib_GBps": round(w.calib_batches * P * w.calib_T * H * 2 / (calib_ms * 1e-3) / 1e9, 1),

@@ -26,14 +26,19 @@
 //     picks its 8 features' (rscale, zero point), before the buffer serves
 //     the rows. No block barrier.
 //  1. Each ring row arrives as one 16-byte load per lane (the span's first
-//     64 chunks) plus a narrow tail load for the chunks past 64 (BF16
-//     features and alignment slack). kSub rows at a time are staged in a
+//     64 chunks); the chunks past 64 (BF16 features and alignment slack)
+//     come with one tail load per pair of rows, lanes 0-31 for the first row
+//     and 32-63 for the second. kSub = 2 rows at a time are staged in a
 //     wave-private LDS buffer and their slots refilled kRing rows ahead.
 //  2. Each lane gathers its 8 features from LDS at fixed offsets, quantizes
 //     them, packs 8 nibbles into one dword and stores it: one coalesced
 //     256-byte store per wave and row.
-//  3. The lanes that own the tile's BF16 features copy their bf16 bits out of
-//     the same LDS buffer.
+//  3. The tile's BF16 features are copied out of the same LDS buffer, one
+//     store per pair of rows (lanes 0-31 the first row's first 32 features,
+//     32-63 the second's); features past the 32nd, rare, row by row.
+//     (Batching the tail loads and BF16 stores by pairs took the stress shape
+//     at k=32 from 481 to 475 us and large prefill from 121.6 to 118.2 us:
+//     each is a full wave instruction even when only a few lanes carry data.)
 // The staging layout pads 4 bytes after every 16-byte chunk, so lane l's
 // features start at dword 5*l and one gather spreads over all banks. All
 // global accesses go through per-wave buffer resources: ragged rows, idle
@@ -286,6 +291,7 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cmap,
     uint8_t* __restrict__ packed, int pitch, uint16_t* __restrict__ outl) {
   constexpr int buf_bytes = ring_row_bytes<kRemDw>();
+  static_assert(kSub == 2 && kR % 2 == 0, "tails and BF16 copies go by pairs of rows");
   extern __shared__ __align__(16) char smem[];
   // unit = (shard, row block); its ntgrp blocks of 4 adjacent tiles run on
   // one XCD
@@ -319,32 +325,48 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
   // main chunk: lane l loads span chunk l (zeros past the span)
   const uint32_t gmain = (lane < nch) ? (uint32_t)(a0 + 8 * lane) * 2u : kOOB;
   const uint32_t lmain = (uint32_t)lane * 20u;
-  // tail: dwords d = lane*kRemDw + i of the span past chunk 64; the launcher
-  // guarantees they fit (nch - 64 <= 16*kRemDw)
+  // tail: per pair of rows, the span past chunk 64; lanes 0-31 take the
+  // pair's first row and 32-63 its second. Each tail load instruction gives
+  // a row's 32 lanes kTW contiguous dwords each (instruction i: dwords
+  // 32*kTW*i + kTW*(lane & 31) ...). The launcher guarantees the tail fits
+  // (nch - 64 <= 16*kRemDw chunks = 32 lanes x kTD dwords).
+  constexpr int kTD = 2 * (kRemDw > 0 ? kRemDw : 1);   // tail dwords per lane and pair
+  constexpr int kTW = kTD == 2 ? 2 : 4;                // dwords per lane and instruction
+  constexpr int kTI = kTD / kTW;                       // tail instructions per pair
+  const int half = lane >> 5;
   const int ntail = max(nch - kWave, 0) * 4;
-  const int d0 = lane * (kRemDw > 0 ? kRemDw : 1);
-  const uint32_t gtail = (d0 < ntail) ? (uint32_t)(a0 + 8 * kWave + 2 * d0) * 2u : kOOB;
   const uint32_t rowb = (uint32_t)H * 2u;
+  auto tail_dw = [&](int i) { return kTW * (lane & 31) + 32 * kTW * i; };
+  uint32_t gtail[kTI];
+#pragma unroll
+  for (int i = 0; i < kTI; ++i)
+    gtail[i] = (tail_dw(i) < ntail)
+                   ? (uint32_t)(a0 + 8 * kWave + 2 * tail_dw(i)) * 2u + (uint32_t)half * rowb
+                   : kOOB;
 
-  constexpr int kT = kRemDw > 0 ? kRemDw : 1;
   v4u vm[kR];
-  uint32_t vt[kR][kT];
+  uint32_t vt[kR / 2][kTD];
   auto load = [&](int q, int row) {
     const bool ok = row < nrows;   // uniform
     const uint32_t so = (uint32_t)min(row, nrows - 1) * rowb;
     vm[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? gmain : kOOB, so, kStream);
-    if constexpr (kRemDw == 1) {
-      vt[q][0] = __builtin_amdgcn_raw_buffer_load_b32(rx, ok ? gtail : kOOB, so, kStream);
-    } else if constexpr (kRemDw == 2) {
-      const auto t = __builtin_amdgcn_raw_buffer_load_b64(rx, ok ? gtail : kOOB, so, kStream);
-      vt[q][0] = t[0];
-      vt[q][1] = t[1];
-    } else if constexpr (kRemDw == 4) {
-      const v4u t = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? gtail : kOOB, so, kStream);
-      vt[q][0] = t[0];
-      vt[q][1] = t[1];
-      vt[q][2] = t[2];
-      vt[q][3] = t[3];
+    if constexpr (kRemDw > 0) {
+      if ((q & 1) == 0) {   // the pair (row, row + 1): q is a compile-time slot
+        const bool ok2 = row + half < nrows;
+#pragma unroll
+        for (int i = 0; i < kTI; ++i) {
+          const uint32_t o = ok2 ? gtail[i] : kOOB;
+          if constexpr (kTW == 2) {
+            const auto t = __builtin_amdgcn_raw_buffer_load_b64(rx, o, so, kStream);
+            vt[q / 2][0] = t[0];
+            vt[q / 2][1] = t[1];
+          } else {
+            const v4u t = __builtin_amdgcn_raw_buffer_load_b128(rx, o, so, kStream);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vt[q / 2][4 * i + j] = t[j];
+          }
+        }
+      }
     }
   };
 
@@ -358,7 +380,7 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
   const v4u hB = __builtin_amdgcn_raw_buffer_load_b128(rc, (uint32_t)jj * 4u + 16u, 0, 0);
   const rsrc_t ri_ = make_rsrc(idx, (uint32_t)k * 4u);
   const uint32_t oh = __builtin_amdgcn_raw_buffer_load_b32(
-      ri_, (g.nout > 0) ? (uint32_t)(g.ilo + min(lane, g.nout - 1)) * 4u : kOOB, 0, 0);
+      ri_, (g.nout > 0) ? (uint32_t)(g.ilo + min(lane & 31, g.nout - 1)) * 4u : kOOB, 0, 0);
   // (b) the shard's parameters over the span: its nch <= 64 + 16*kRemDw
   // chunks of 8 features take 2*nch rscale and nch zero-point chunks
   constexpr int kNchMax = kWave + 16 * kRemDw;
@@ -391,11 +413,15 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
   }
   // (lanes past the last slot write the row's zero padding, up to the pitch)
   const uint32_t st_off = ((j0 >> 1) + 4 <= pitch) ? (uint32_t)(j0 >> 1) : kOOB;
+  // BF16 copy, per pair of rows: lane l takes feature (l & 31) of the tile's
+  // BF16 features in row `half` of the pair.
   // (used unconditionally: a load whose only use sits under a branch gets
   // sunk below the ring prologue, and its wait would then drain the ring;
   // with no BF16 feature oh reads 0 and the clamp keeps the offset in range)
-  const uint32_t oad = pad_byte_off((uint32_t)max((int)oh - a0, 0));
-  const uint32_t o_off = (lane < g.nout) ? (uint32_t)(g.ilo + lane) * 2u : kOOB;
+  const uint32_t oad = pad_byte_off((uint32_t)max((int)oh - a0, 0)) + (uint32_t)(half * buf_bytes);
+  const uint32_t o_off = ((lane & 31) < g.nout)
+                             ? (uint32_t)(g.ilo + (lane & 31)) * 2u + (uint32_t)(half * k) * 2u
+                             : kOOB;
 
   // nrows >= 1 here. The do-while has no entry guard: a guarded loop lets the
   // compiler sink the prologue loads below the guard, past the point where
@@ -409,18 +435,22 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
 #pragma unroll
       for (int r = 0; r < kSub; ++r) {
         const int q = sb * kSub + r;
-        char* b = buf + r * buf_bytes;
-        uint32_t* dm = reinterpret_cast<uint32_t*>(b + lmain);
+        uint32_t* dm = reinterpret_cast<uint32_t*>(buf + r * buf_bytes + lmain);
         dm[0] = vm[q][0];
         dm[1] = vm[q][1];
         dm[2] = vm[q][2];
         dm[3] = vm[q][3];
-        if constexpr (kRemDw > 0) {
+      }
+      if constexpr (kRemDw > 0) {   // the pair's tails: each lane into its row's buffer
+        char* bt = buf + half * buf_bytes;
 #pragma unroll
-          for (int i = 0; i < kRemDw; ++i) {
-            const int d = d0 + i;
+        for (int i = 0; i < kTI; ++i) {
+#pragma unroll
+          for (int j = 0; j < kTW; ++j) {
+            const int d = tail_dw(i) + j;
             if (d < ntail)
-              *reinterpret_cast<uint32_t*>(b + (kWave + (d >> 2)) * 20 + (d & 3) * 4) = vt[q][i];
+              *reinterpret_cast<uint32_t*>(bt + (kWave + (d >> 2)) * 20 + (d & 3) * 4) =
+                  vt[sb][kTW * i + j];
           }
         }
       }
@@ -446,15 +476,19 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
         w = active ? w : 0u;   // past the last slot: the row's zero padding
         __builtin_amdgcn_raw_buffer_store_b32(w, rp, ok ? st_off : kOOB, rr * (uint32_t)pitch,
                                               kStream);
-        const uint16_t b16 = *reinterpret_cast<const uint16_t*>(buf + r * buf_bytes + oad);
-        __builtin_amdgcn_raw_buffer_store_b16(b16, ro, ok ? o_off : kOOB, rr * (uint32_t)k * 2u, 0);
-        // tiles holding more than 64 BF16 features (uniform, rare)
-        for (int i = lane + kWave; i - lane < g.nout; i += kWave) {
+        // a tile's BF16 features past the 32nd (uniform, rare): row by row
+        for (int i = lane + 32; i - lane < g.nout; i += kWave) {
           const uint32_t o = pad_byte_off((uint32_t)(idx[g.ilo + min(i, g.nout - 1)] - a0));
           const uint16_t v16 = *reinterpret_cast<const uint16_t*>(buf + r * buf_bytes + o);
           const uint32_t off = (ok && i < g.nout) ? (uint32_t)(g.ilo + i) * 2u : kOOB;
           __builtin_amdgcn_raw_buffer_store_b16(v16, ro, off, rr * (uint32_t)k * 2u, 0);
         }
+      }
+      {   // the pair's first 32 BF16 features of each row, one store
+        const int rowa = base + sb * kSub;
+        const uint16_t b16 = *reinterpret_cast<const uint16_t*>(buf + oad);
+        __builtin_amdgcn_raw_buffer_store_b16(b16, ro, (rowa + half < nrows) ? o_off : kOOB,
+                                              (uint32_t)min(rowa, nrows - 1) * (uint32_t)k * 2u, 0);
       }
       wave_lds_sync();
     }
