@@ -346,6 +346,10 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
 
   v4u vm[kR];
   uint32_t vt[kR / 2][kTD];
+  // (The tail loads carry no streaming hint: their lines begin the next
+  // tile's span, which another wave reads too; without the hint the L2 keeps
+  // them, and stress k=32 took 470 instead of 475 us, 7B 32.8 instead of
+  // 33.5 us. The main loads keep it: without it 7B took 35.7 us.)
   auto load = [&](int q, int row) {
     const bool ok = row < nrows;   // uniform
     const uint32_t so = (uint32_t)min(row, nrows - 1) * rowb;
@@ -357,11 +361,11 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
         for (int i = 0; i < kTI; ++i) {
           const uint32_t o = ok2 ? gtail[i] : kOOB;
           if constexpr (kTW == 2) {
-            const auto t = __builtin_amdgcn_raw_buffer_load_b64(rx, o, so, kStream);
+            const auto t = __builtin_amdgcn_raw_buffer_load_b64(rx, o, so, 0);
             vt[q / 2][0] = t[0];
             vt[q / 2][1] = t[1];
           } else {
-            const v4u t = __builtin_amdgcn_raw_buffer_load_b128(rx, o, so, kStream);
+            const v4u t = __builtin_amdgcn_raw_buffer_load_b128(rx, o, so, 0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) vt[q / 2][4 * i + j] = t[j];
           }
