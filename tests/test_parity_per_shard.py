@@ -137,6 +137,34 @@ def test_per_shard_sets(P, T, H, k, extra, note):
             assert own <= set(sel_o["idx"][p].tolist())
 
 
+def shard_blocks(P, T, H, seed, width=16, factor=40.0):
+    """Normal data; shard p has `width` consecutive wide columns of its own,
+    starting at 520 + 8*p (so neighbouring shards' blocks overlap by half)."""
+    x = W.draw(P, T, H, seed, device=DEV)
+    xb = x.view(torch.bfloat16).clone()
+    for p in range(P):
+        a = 520 + 8 * p
+        xb[p][:, a:a + width] *= factor
+    return xb.view(torch.int16)
+
+
+@pytest.mark.parametrize("P,T,H,k", [(4, 6, 2048, 16), (8, 9, 2048, 24)],
+                         ids=["P4-k16", "P8-k24"])
+def test_per_shard_clustered_blocks(P, T, H, k):
+    """Every lane of a block has all 8 of its features BF16 on some shard and
+    int4 on others: the owners' loop over several BF16 features, the inverse
+    map's longest runs, and features whose BF16 and int4 terms mix across
+    shards, in the window kernel."""
+    say(f"case: per-shard clustered blocks P={P} T={T} H={H} k={k}")
+    calib = [shard_blocks(P, 8, H, 4300 + b) for b in range(2)]
+    x = shard_blocks(P, T, H, 4400)
+    assert window_receiver(P, H, B.btq_packed_pitch(H, k))
+    sel_g, sel_o = run_both(calib, x, k, 0.9)
+    for p in range(P):   # each shard's block is its BF16 set
+        a = 520 + 8 * p
+        assert set(range(a, a + 16)) <= set(sel_o["idx"][p].tolist())
+
+
 def test_signed_zero_ranges_rank_by_feature():
     # A width of -0 (run_max = -0, run_min = +0) ranks equal to +0: with all
     # ranges zero the sets are the lowest k features, for every rule.
