@@ -87,6 +87,15 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) { return (uint16_t)(bf16_p
 // second operand).
 __device__ __forceinline__ uint32_t splat_byte0(uint32_t v) { return __builtin_amdgcn_perm(0u, v, 0u); }
 
+// v[eu] (0 when eu is past the end), by selects.
+template <int N>
+__device__ __forceinline__ float pick8(const float (&v)[N], int eu) {
+  float r = 0.0f;
+#pragma unroll
+  for (int e = 0; e < N; ++e) r = (e == eu) ? v[e] : r;
+  return r;
+}
+
 // Marks a wave-uniform value as redefined here, in a scalar register (an
 // empty asm): its load must be complete at this point, and cannot be moved
 // below it.
@@ -155,15 +164,16 @@ __host__ __device__ constexpr int win_lds_dwords() {
 // kPs: fmap is [P,H] (one set per shard) instead of [H]. kBf: y is bf16.
 // Waves per SIMD the register budget aims at: 3 (at most 168 registers) for
 // one set with two entry registers, else 2 (at most 256).
-template <int NP, int kOR, int kR, bool kPs, bool kBf>
+template <int NP, int kOR, int kR, bool kPs, bool kBf, bool kAcc>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu((!kPs && kOR == 2) ? 3 : 2)))
+__attribute__((amdgpu_waves_per_eu((!kPs && kOR == 2 && !kAcc) ? 3 : 2)))
 void dq_window_kernel(
     const uint8_t* __restrict__ packed, int pitch, const uint16_t* __restrict__ outl, int64_t T,
     int H, int k, int ntiles, int rows_per_wave, int64_t nrowblk, const float* __restrict__ scale,
     const uint8_t* __restrict__ zp, const int32_t* __restrict__ fmap, void* __restrict__ y) {
   constexpr int NM = kPs ? NP : 1;             // maps
   constexpr uint32_t kYB = kBf ? 2u : 4u;      // bytes per y value
+  static_assert(!kAcc || (!kPs && !kBf), "shard groups: one set, fp32 output");
   constexpr int kLds = win_lds_dwords<NP, kOR, kPs, kBf>();
   constexpr int kSP = stage_stride(NP);
   extern __shared__ __align__(16) float dq_smem[];
@@ -302,8 +312,15 @@ void dq_window_kernel(
   const uint32_t shard_bytes = (uint32_t)(T * pitch);
   const rsrc_t ro = make_rsrc(outl + t0 * k, (uint32_t)(((NP - 1) * T + nrows) * (int64_t)k * 2));
   const rsrc_t rnone_o = make_rsrc(outl, 0u);
+  // kAcc (a later group of shards): y holds the sum over the earlier groups,
+  // and each row's values ride in the ring with its codes (a row past the
+  // wave's last is out of this descriptor's range)
+  const rsrc_t ryin = make_rsrc(static_cast<const char*>(y) + t0 * H * 4,
+                                kAcc ? (uint32_t)((int64_t)nrows * H * 4) : 0u);
+  const uint32_t yin_off = active ? (uint32_t)h0 * 4u : kOOB;
   v2u w[kR][NP];
   uint32_t ov[kR][kOR];
+  float yp[kAcc ? kR : 1][kWinFeat];
   auto load_row = [&](int q, int row) {
     const bool ok = row < nrows;   // uniform
     const uint32_t so = (uint32_t)min(row, nrows - 1) * (uint32_t)pitch;
@@ -317,6 +334,16 @@ void dq_window_kernel(
 #pragma unroll
     for (int r = 0; r < kOR; ++r)
       ov[q][r] = __builtin_amdgcn_raw_buffer_load_b16(ok ? ro : rnone_o, e_off[r], soo, 0);
+    if constexpr (kAcc) {
+      const uint32_t soy = (uint32_t)row * (uint32_t)H * 4u;
+      const v4u ya = __builtin_amdgcn_raw_buffer_load_b128(ryin, yin_off, soy, 0);
+      const v4u yb = __builtin_amdgcn_raw_buffer_load_b128(ryin, yin_off + 16u, soy, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        yp[q][e] = __uint_as_float(ya[e]);
+        yp[q][4 + e] = __uint_as_float(yb[e]);
+      }
+    }
   };
 #pragma unroll
   for (int q = 0; q < kR; ++q) {
@@ -524,8 +551,10 @@ void dq_window_kernel(
         x[p] = v2u{src[0], src[kSP]};
       }
       // the owner's first BF16 feature: its row summed in shard order from +0
+      // (a later group of shards: from the earlier groups' sum)
       float o = 0.0f;
       if (do_own) {
+        if constexpr (kAcc) o = pick8(yp[q], e_first);
         const float* t = tab + (cnt_any > 0 ? pos0 : 0) * NP;
         if constexpr (NP % 4 == 0) {
 #pragma unroll
@@ -541,7 +570,7 @@ void dq_window_kernel(
       issue_fence();   // the read goes out before the arithmetic below
       float acc[kWinFeat];
 #pragma unroll
-      for (int e = 0; e < kWinFeat; ++e) acc[e] = bias[e];
+      for (int e = 0; e < kWinFeat; ++e) acc[e] = kAcc ? __fadd_rn(yp[q][e], bias[e]) : bias[e];
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const int m = kPs ? p : 0;
@@ -556,6 +585,13 @@ void dq_window_kernel(
           acc[4 + bb] = fmaf((float)((b >> (8 * bb)) & 0xFFu), sc[p][4 + bb], acc[4 + bb]);
         }
       }
+      // (kAcc: the owners' later features still need this row's y after the
+      // refill below reloads its slot)
+      float yq[kAcc ? kWinFeat : 1];
+      if constexpr (kAcc) {
+#pragma unroll
+        for (int e = 0; e < kWinFeat; ++e) yq[e] = yp[q][e];
+      }
       // this row's registers are consumed: refill the slot kR rows ahead
       load_row(q, row + kR);
       issue_fence();
@@ -564,11 +600,21 @@ void dq_window_kernel(
         int rest = any_rest;
         for (int u = 1; u < umax; ++u) {   // lanes with several BF16 features
           const float* t = tab + (u < cnt_any ? pos0 + u : 0) * NP;
+          const int eu = rest ? __builtin_ctz(rest) : kWinFeat;
           float ou = 0.0f;
+          if constexpr (kAcc) ou = pick8(yq, eu);
 #pragma unroll
           for (int p = 0; p < NP; ++p) ou = __fadd_rn(ou, t[p]);
-          place(acc, rest ? __builtin_ctz(rest) : kWinFeat, ou);
+          place(acc, eu, ou);
           rest &= rest - 1;
+        }
+      }
+      if constexpr (kAcc) {
+        // the post-loop pass continues these BF16 features from what the
+        // earlier groups summed, so the loop stores that unchanged
+        if (!compact) {
+#pragma unroll
+          for (int e = 0; e < kWinFeat; ++e) acc[e] = ((any >> e) & 1) ? yq[e] : acc[e];
         }
       }
       // (a row past the wave's last: no records, every store dropped)
@@ -612,7 +658,8 @@ void dq_window_kernel(
       rest &= rest - 1;
       const int64_t h = h0 + e;
       for (int r = 0; r < nrows; ++r) {
-        float o = 0.0f;
+        char* d = ybase + ((int64_t)r * H + h) * kYB;
+        float o = kAcc ? *reinterpret_cast<const float*>(d) : 0.0f;
         for (int p = 0; p < NP; ++p) {
           const int f = fmap[(kPs ? (int64_t)p * H : 0) + h];
           const int64_t rowg = (int64_t)p * T + t0 + r;
@@ -626,7 +673,6 @@ void dq_window_kernel(
           }
           o = __fadd_rn(o, term);
         }
-        char* d = ybase + ((int64_t)r * H + h) * kYB;
         if constexpr (kBf)
           *reinterpret_cast<uint16_t*>(d) = bf16_rne(o);
         else
@@ -666,18 +712,18 @@ __global__ __launch_bounds__(256) void dq_general_kernel(
   }
 }
 
-template <int NP, int kOR, int kR, bool kPs, bool kBf>
+template <int NP, int kOR, int kR, bool kPs, bool kBf, bool kAcc>
 static void launch_window(const uint8_t* packed, int64_t pitch, const uint16_t* outl, int64_t T,
                           int64_t H, int64_t k, int ntiles, int rpw, int64_t nrowblk,
                           const float* scale, const uint8_t* zp, const int32_t* fmap, void* y,
                           hipStream_t s) {
   const int64_t ntgrp = (ntiles + kDqWaves - 1) / kDqWaves;
   const size_t lds = (size_t)kDqWaves * win_lds_dwords<NP, kOR, kPs, kBf>() * 4;
-  dq_window_kernel<NP, kOR, kR, kPs, kBf><<<(unsigned)xcd_grid(ntgrp, nrowblk), 256, lds, s>>>(
+  dq_window_kernel<NP, kOR, kR, kPs, kBf, kAcc><<<(unsigned)xcd_grid(ntgrp, nrowblk), 256, lds, s>>>(
       packed, (int)pitch, outl, T, (int)H, (int)k, ntiles, rpw, nrowblk, scale, zp, fmap, y);
 }
 
-template <bool kPs, bool kBf>
+template <bool kPs, bool kBf, bool kAcc>
 static void dispatch_window(int64_t P, bool wide, const uint8_t* packed, int64_t pitch,
                             const uint16_t* outl, int64_t T, int64_t H, int64_t k, int ntiles,
                             int rpw, int64_t nrowblk, const float* scale, const uint8_t* zp,
@@ -686,9 +732,9 @@ static void dispatch_window(int64_t P, bool wide, const uint8_t* packed, int64_t
 #define BTQ_WIN_CASE(n)                                                         \
   case n:                                                                       \
     if (wide)                                                                   \
-      launch_window<n, 4, kDqRing, kPs, kBf>(BTQ_WIN_ARGS);                     \
+      launch_window<n, 4, kDqRing, kPs, kBf, kAcc>(BTQ_WIN_ARGS);               \
     else                                                                        \
-      launch_window<n, 2, kDqRing, kPs, kBf>(BTQ_WIN_ARGS);                     \
+      launch_window<n, 2, kDqRing, kPs, kBf, kAcc>(BTQ_WIN_ARGS);               \
     break;
   switch (P) {
     BTQ_WIN_CASE(1)
@@ -711,31 +757,54 @@ static hipError_t launch_decompress_t(const uint8_t* packed, int64_t pitch, cons
                                       void* y, hipStream_t s) {
   const int64_t lim = int64_t(1) << 31;
   const int64_t nm = kPs ? P : 1;
-  // Window kernel: up to 8 shards; whole 8-feature lane windows; the code
-  // window of 8 bytes inside every row (pitch >= 8, dword-aligned rows);
-  // 16-byte aligned per-feature arrays and y; each descriptor under 2^31
-  // bytes (the parameter arrays, the whole message and outlier block).
-  const bool fast = P <= 8 && H % 8 == 0 && pitch >= 8 && pitch % 4 == 0 &&
-                    (uintptr_t)packed % 4 == 0 && (uintptr_t)fmap % 16 == 0 &&
-                    (uintptr_t)scale % 16 == 0 && (uintptr_t)zp % 8 == 0 &&
-                    (uintptr_t)y % 16 == 0 && (uintptr_t)outl % 2 == 0 &&
-                    nm * H * 4 < lim && P * H * 4 < lim && P * T * k * 2 < lim &&
-                    P * T * pitch < lim && 64 * H * 4 < lim;
-  if (fast) {
-    const int ntiles = (int)((H + kWinTile - 1) / kWinTile);
-    int64_t rpw64 = (ntiles * T + kDqWavesTwo - 1) / kDqWavesTwo;
-    if (rpw64 < dq_min_rows_two(kPs, kBf)) rpw64 = (ntiles * T + kDqWavesOne - 1) / kDqWavesOne;
-    rpw64 = (rpw64 + kDqRing - 1) / kDqRing * kDqRing;
-    if (rpw64 < kDqRing) rpw64 = kDqRing;
-    if (rpw64 > 64) rpw64 = 64;
-    const int rpw = (int)rpw64;
-    const int64_t nrowblk = (T + rpw - 1) / rpw;
+  // Window kernel: whole 8-feature lane windows; the code window of 8 bytes
+  // inside every row (pitch >= 8, dword-aligned rows); 16-byte aligned
+  // per-feature arrays and y; each descriptor under 2^31 bytes (the
+  // parameter arrays, and the message and outlier block of up to 8 shards).
+  const bool shape_ok = H % 8 == 0 && pitch >= 8 && pitch % 4 == 0 &&
+                        (uintptr_t)packed % 4 == 0 && (uintptr_t)fmap % 16 == 0 &&
+                        (uintptr_t)scale % 16 == 0 && (uintptr_t)zp % 8 == 0 &&
+                        (uintptr_t)y % 16 == 0 && (uintptr_t)outl % 2 == 0 &&
+                        nm * H * 4 < lim && 64 * H * 4 < lim;
+  auto group_ok = [&](int64_t np) {
+    return np * H * 4 < lim && np * T * k * 2 < lim && np * T * pitch < lim;
+  };
+  const int ntiles = (int)((H + kWinTile - 1) / kWinTile);
+  int64_t rpw64 = (ntiles * T + kDqWavesTwo - 1) / kDqWavesTwo;
+  if (rpw64 < dq_min_rows_two(kPs, kBf)) rpw64 = (ntiles * T + kDqWavesOne - 1) / kDqWavesOne;
+  rpw64 = (rpw64 + kDqRing - 1) / kDqRing * kDqRing;
+  if (rpw64 < kDqRing) rpw64 = kDqRing;
+  if (rpw64 > 64) rpw64 = 64;
+  const int rpw = (int)rpw64;
+  const int64_t nrowblk = (T + rpw - 1) / rpw;
+  if (P <= 8 && shape_ok && group_ok(P)) {
     // BF16 entry registers: 2 (128 entries per tile-row) while the tiles hold
     // at most 64 on average, else 4
     const bool wide = P * k > int64_t(kWave) * ntiles;
-    dispatch_window<kPs, kBf>(P, wide, packed, pitch, outl, T, H, k, ntiles, rpw, nrowblk,
-                              scale, zp, fmap, y, s);
+    dispatch_window<kPs, kBf, false>(P, wide, packed, pitch, outl, T, H, k, ntiles, rpw, nrowblk,
+                                     scale, zp, fmap, y, s);
     return hipGetLastError();
+  }
+  if constexpr (!kPs && !kBf) {
+    // More than 8 shards (one set, fp32 output): one launch per group of up
+    // to 8 shards, in shard order. The first writes y; each later one starts
+    // every feature from y, so BF16 features keep their sum in shard order
+    // from +0 across the groups.
+    if (P > 8 && shape_ok && group_ok(8)) {
+      for (int64_t g0 = 0; g0 < P; g0 += 8) {
+        const int64_t np = P - g0 < 8 ? P - g0 : 8;
+        const bool wide = np * k > int64_t(kWave) * ntiles;
+        const uint8_t* pk_g = packed + g0 * T * pitch;
+        const uint16_t* ol_g = outl + g0 * T * k;
+        if (g0 == 0)
+          dispatch_window<false, false, false>(np, wide, pk_g, pitch, ol_g, T, H, k, ntiles, rpw,
+                                               nrowblk, scale, zp, fmap, y, s);
+        else
+          dispatch_window<false, false, true>(np, wide, pk_g, pitch, ol_g, T, H, k, ntiles, rpw,
+                                              nrowblk, scale + g0 * H, zp + g0 * H, fmap, y, s);
+      }
+      return hipGetLastError();
+    }
   }
   int64_t blocks = (T * H + 255) / 256;
   if (blocks > 65536) blocks = 65536;

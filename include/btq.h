@@ -31,9 +31,10 @@
  *  - bf16 values are raw 16-bit patterns (uint16_t).
  *  - A pointer must be aligned to its element type (BTQ_ERR_ALIGN
  *    otherwise). Fast kernels run when x, packed, outliers and y are 16-byte
- *    aligned, the per-feature arrays 16-byte aligned, P <= 8 for the
- *    receiver, and H and H-k are multiples of 8; every other layout runs on
- *    a general kernel that is correct but much slower.
+ *    aligned, the per-feature arrays 16-byte aligned, and H and H-k are
+ *    multiples of 8 (the receivers: up to 8 shards per launch, see
+ *    btq_decompress_reduce); every other layout runs on a general kernel
+ *    that is correct but much slower.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call checks its arguments on the host, enqueues its kernels on
  *    `stream` and returns. It does not synchronize, print, throw or abort.
@@ -203,10 +204,13 @@ int btq_compress_pack(const uint16_t *x, int64_t P, int64_t T, int64_t H, int64_
  *   packed [P,T,Bq], outliers [P,T,k]   in, as written by btq_compress_pack
  *   scale fp32 [P,H], zero_point u8 [P,H], fmap i32 [H]   in
  *   y      fp32 [T,H]   out
- * Fast kernel: P <= 8, H a multiple of 8, Bq a multiple of 4 and at least
- * 8, 16-byte aligned scale, fmap and y, and the outlier block under 2^31
- * bytes. Anything else, such as more than 8 shards, takes a general kernel
- * (correct, much slower, and exactly the sequential sum).
+ * Fast kernel: H a multiple of 8, Bq a multiple of 4 and at least 8,
+ * 16-byte aligned scale, fmap and y, and the message and outlier block of
+ * every 8 shards under 2^31 bytes. More than 8 shards run it once per group
+ * of up to 8 shards, in shard order; each later group starts from the y the
+ * earlier ones wrote (y is read as well as written), so BF16 features keep
+ * their sequential sum. Anything else takes a general kernel (correct, much
+ * slower, and exactly the sequential sum).
  */
 int btq_decompress_reduce(const uint8_t *packed, const uint16_t *outliers,
                           int64_t P, int64_t T, int64_t H, int64_t k,
@@ -227,7 +231,9 @@ int64_t btq_packed_row_bytes(int64_t H, int64_t k);
  * The same sum as btq_decompress_reduce, rounded once from fp32 to bf16
  * (round to nearest even): y[t,h] = bf16(fp32 sum), bit for bit the rounding
  * of what btq_decompress_reduce writes. y is bf16 [T,H] (uint16 bits), 2-byte
- * aligned (16-byte aligned for the fast kernel).
+ * aligned (16-byte aligned for the fast kernel). More than 8 shards take the
+ * general kernel here (there is no fp32 buffer to carry a group's sum): the
+ * result is then the rounding of the sequential sum, bit for bit.
  */
 int btq_decompress_reduce_bf16(const uint8_t *packed, const uint16_t *outliers,
                                int64_t P, int64_t T, int64_t H, int64_t k,

@@ -84,8 +84,7 @@ def run_both(calib_xs, x, k, momentum, *, x_offset=0, param_offset=0, pitch=None
     torch.cuda.synchronize()
     assert_y_close(y.cpu().numpy(), y_o, sel_o["scale"], sel_o["idx"])
     assert_y_bf16_close(y16.cpu().numpy(), y_o, sel_o["scale"], sel_o["idx"])
-    # the bf16 output is one round-to-nearest-even of the fp32 output
-    assert torch.equal(y16, y.to(torch.bfloat16).view(torch.int16))
+    assert_bf16_is_rne(y16, y, y_o, P)
 
     # the same through the *_ex calls with a row pitch
     if pitch is None:
@@ -100,8 +99,20 @@ def run_both(calib_xs, x, k, momentum, *, x_offset=0, param_offset=0, pitch=None
                                       bf16=True)
     torch.cuda.synchronize()
     assert_y_close(yp.cpu().numpy(), y_o, sel_o["scale"], sel_o["idx"])
-    assert torch.equal(yp16, yp.to(torch.bfloat16).view(torch.int16))
+    assert_bf16_is_rne(yp16, yp, y_o, P)
     return sel_g, pk, ol, y
+
+
+def assert_bf16_is_rne(y16, y, y_o, P):
+    """Up to 8 shards the bf16 output is one round-to-nearest-even of the
+    fp32 output. With more, the fp32 output runs the window kernel once per
+    group of 8 shards and the bf16 output takes the general kernel, whose sum
+    is the oracle's: it is then the rounding of the oracle's y, bit for bit."""
+    if P <= 8:
+        assert torch.equal(y16, y.to(torch.bfloat16).view(torch.int16))
+    else:
+        ref = torch.from_numpy(np.ascontiguousarray(y_o)).to(torch.bfloat16).view(torch.int16)
+        assert torch.equal(y16.cpu(), ref), "bf16 y is not RNE(oracle y)"
 
 
 def test_tiny_workload_end_to_end():
@@ -125,7 +136,10 @@ CASES = [
     (7, 5, 1040, 0, "normal", [], "P=7, k=0"),
     (1, 40, 512, 0, "normal", [], "P=1, k=0, one full tile"),
     (2, 9, 256, 256, "normal", [1, 2], "k=H: all BF16"),
-    (9, 17, 512, 16, "laplace", [100, 101], "P=9: general receiver"),
+    (9, 17, 512, 16, "laplace", [100, 101], "P=9: groups of 8 and 1 shards"),
+    (16, 40, 2048, 64, "normal", list(range(5, 2048, 37)), "P=16: two groups of 8 shards"),
+    (12, 10, 2048, 64, "normal", list(range(700, 745)),
+     "P=12, 45 clustered BF16: post-loop pass in both groups"),
     (3, 5, 250, 7, "normal", [0, 249, 100], "H not a multiple of 4: general receiver"),
     (3, 40, 1028, 9, "normal", [5, 600, 1027], "H=1028: a partial last tile of 4-feature lanes"),
     (5, 33, 1032, 13, "normal", [1, 2, 3], "H-k odd: pad nibble, general sender"),
@@ -188,7 +202,7 @@ SET_CASES = [
     (4, 9, 4104, 5, "partial last tile"),
     (3, 5, 250, 0, "empty set"),
     (2, 4, 256, 256, "every feature"),
-    (9, 17, 512, 16, "P=9: general receiver"),
+    (9, 17, 512, 16, "P=9: groups of 8 and 1 shards"),
     (5, 3, 3000, 1500, "half the features"),
 ]
 
