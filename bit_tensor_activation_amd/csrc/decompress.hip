@@ -777,7 +777,11 @@ static hipError_t launch_decompress_t(const uint8_t* packed, int64_t pitch, cons
   if (rpw64 > 64) rpw64 = 64;
   const int rpw = (int)rpw64;
   const int64_t nrowblk = (T + rpw - 1) / rpw;
-  if (P <= 8 && shape_ok && group_ok(P)) {
+  // shards per launch: at most 8, and few enough that a group's message and
+  // outlier block stay under 2^31 bytes
+  int64_t gs = 8;
+  while (gs > 0 && !group_ok(gs)) --gs;
+  if (P <= gs && shape_ok) {
     // BF16 entry registers: 2 (128 entries per tile-row) while the tiles hold
     // at most 64 on average, else 4
     const bool wide = P * k > int64_t(kWave) * ntiles;
@@ -786,13 +790,14 @@ static hipError_t launch_decompress_t(const uint8_t* packed, int64_t pitch, cons
     return hipGetLastError();
   }
   if constexpr (!kPs && !kBf) {
-    // More than 8 shards (one set, fp32 output): one launch per group of up
-    // to 8 shards, in shard order. The first writes y; each later one starts
-    // every feature from y, so BF16 features keep their sum in shard order
-    // from +0 across the groups.
-    if (P > 8 && shape_ok && group_ok(8)) {
-      for (int64_t g0 = 0; g0 < P; g0 += 8) {
-        const int64_t np = P - g0 < 8 ? P - g0 : 8;
+    // More shards than one launch takes (more than 8, or a message past 2^31
+    // bytes; one set, fp32 output): one launch per group of gs shards, in
+    // shard order. The first writes y; each later one starts every feature
+    // from y, so BF16 features keep their sum in shard order from +0 across
+    // the groups.
+    if (P > gs && gs >= 1 && shape_ok) {
+      for (int64_t g0 = 0; g0 < P; g0 += gs) {
+        const int64_t np = P - g0 < gs ? P - g0 : gs;
         const bool wide = np * k > int64_t(kWave) * ntiles;
         const uint8_t* pk_g = packed + g0 * T * pitch;
         const uint16_t* ol_g = outl + g0 * T * k;

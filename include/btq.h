@@ -206,11 +206,12 @@ int btq_compress_pack(const uint16_t *x, int64_t P, int64_t T, int64_t H, int64_
  *   y      fp32 [T,H]   out
  * Fast kernel: H a multiple of 8, Bq a multiple of 4 and at least 8,
  * 16-byte aligned scale, fmap and y, and the message and outlier block of
- * every 8 shards under 2^31 bytes. More than 8 shards run it once per group
- * of up to 8 shards, in shard order; each later group starts from the y the
- * earlier ones wrote (y is read as well as written), so BF16 features keep
- * their sequential sum. Anything else takes a general kernel (correct, much
- * slower, and exactly the sequential sum).
+ * every 8 shards under 2^31 bytes. More than 8 shards, or a message past
+ * 2^31 bytes, run it once per group of shards (8, or fewer so that each
+ * group's message fits), in shard order; each later group starts from the y
+ * the earlier ones wrote (y is read as well as written), so BF16 features
+ * keep their sequential sum. Anything else takes a general kernel (correct,
+ * much slower, and exactly the sequential sum).
  */
 int btq_decompress_reduce(const uint8_t *packed, const uint16_t *outliers,
                           int64_t P, int64_t T, int64_t H, int64_t k,
