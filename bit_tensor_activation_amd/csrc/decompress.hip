@@ -127,11 +127,6 @@ __device__ __forceinline__ int wave_max8(int v) {   // v in [0, 8]
   for (int u = 1; u <= 8; ++u) m = __ballot(v >= u) ? u : m;
   return m;
 }
-// v of the lowest lane where `has` holds (0 if none).
-__device__ __forceinline__ int first_lane_value(bool has, int v) {
-  const uint64_t m = __ballot(has);
-  return m ? __builtin_amdgcn_readlane(v, __ffsll((unsigned long long)m) - 1) : 0;
-}
 
 // Stage of one row's code spans, at the start of the wave's LDS: span dword
 // d of shard p at d*kSP + 2p, kSP = 2*NP + 1. A lane's window of every shard
