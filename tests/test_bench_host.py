@@ -45,7 +45,7 @@ def test_algorithmic_bytes_by_hand():
     comp_ps, deco_ps = bench.algorithmic_bytes_per_shard(P, T, H, k)
     assert comp_ps == P * T * H * 2 + message + 9 * P * H
     assert deco_ps == message + T * H * 4 + 9 * P * H
-    # the stress rows of the survey's byte table (MB)
+    # the stress workload (P=8, T=16384, H=8192) at k = 0, 32, 256, in MB, worked by hand
     for kk, c_mb, d_mb in ((0, 2684.72, 1074.10), (32, 2691.01, 1080.39), (256, 2735.05, 1124.43)):
         c, d = bench.algorithmic_bytes(8, 16384, 8192, kk)
         assert round(c / 1e6, 2) == c_mb and round(d / 1e6, 2) == d_mb
