@@ -11,7 +11,9 @@ keeps no state between calls (GPU).
     inputs copied in between replays and eager work between them, match
     the eager calls on every replay (the kernels clear nothing with memset:
     every output byte is written by a kernel, so the graph holds only
-    kernel nodes); the same for the per-shard sender and receiver.
+    kernel nodes); the same for the per-shard sender and receiver, and for
+    the 16-shard receiver, whose two launches (the second adding to y) sit
+    in one graph.
 """
 import pytest
 import torch
@@ -146,6 +148,47 @@ def test_graph_replays_match_eager_calls():
             assert same_bytes(a, b), f"replay {rep}"
         pk.zero_()              # the next replay must write every byte again
         y.zero_()
+
+
+def test_graph_replays_shard_groups():
+    """16 shards: the fp32 receiver runs as two launches (the second adds to
+    y), captured in one graph; every replay must equal the eager calls, with
+    y cleared in between so the first group has to write it again."""
+    say("case: graph capture of the 16-shard receiver (two groups), 3 replays")
+    P16 = 16
+    draw16 = lambda seed: W.draw(P16, T, H, seed, sigma=0.5, cols=COLS, outlier_factor=60.0,
+                                 device=DEV)
+    rmin = torch.empty((P16, H), dtype=torch.float32, device=DEV)
+    rmax = torch.empty_like(rmin)
+    for b in range(2):
+        B.btq_calib_update(draw16(7800 + b), rmin, rmax, 0.9, b == 0)
+    sel = B.btq_select_outliers(rmin, rmax, K)
+    enc = (sel["rscale"], sel["zero_point"], sel["outlier_idx"], sel["cmap"])
+    dec = (sel["scale"], sel["zero_point"], sel["fmap"])
+    x_static = torch.empty((P16, T, H), dtype=torch.int16, device=DEV)
+    pk, ol = B.btq_compress_pack_ex(draw16(7900), K, *enc)
+    y = torch.empty((T, H), dtype=torch.float32, device=DEV)
+
+    def step():
+        B.btq_compress_pack_ex(x_static, K, *enc, packed=pk, outliers=ol)
+        B.btq_decompress_reduce_ex(pk, ol, H, *dec, y=y)
+
+    x_static.copy_(draw16(7901))
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        x_static.copy_(draw16(7910 + rep))
+        y.fill_(float("nan"))   # the first group must overwrite all of y
+        graph.replay()
+        torch.cuda.synchronize()
+        got = y.clone()
+        y.zero_()
+        step()
+        torch.cuda.synchronize()
+        assert same_bytes(got, y), f"replay {rep}"
 
 
 def test_graph_replays_per_shard_sets():
