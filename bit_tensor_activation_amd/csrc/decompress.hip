@@ -19,7 +19,9 @@
 //     features among the 8 take consecutive slots, so all their codes lie in
 //     the 8 bytes at the 4-byte aligned offset `cb` at or below the first
 //     one's byte; two byte selectors (v_perm_b32) place each code's byte
-//     under its feature, and a mask keeps its nibble. Each feature starts
+//     under its feature, and a mask keeps its nibble. The selectors and masks
+//     follow from the lane's 8-bit int4 mask and the first code's nibble, and
+//     are computed four features per instruction. Each feature starts
 //     from the constant -sum_p z*s over its int4 shards, and a high nibble,
 //     kept in place as 16q, meets its scale divided by 16 (exact). The setup
 //     is written with selects throughout: every lane runs the same
@@ -41,6 +43,11 @@
 //     feature sees it (not even a non-finite one). A tile with more entries
 //     than the registers hold recomputes its BF16 features after the row
 //     loop, term by term.
+//  3. Shard groups (one set, fp32 output): more than 8 shards, or a message
+//     past 2^31 bytes, run the window kernel once per group of shards, in
+//     shard order. A later group (kAcc) loads each row's y with its codes and
+//     continues every feature from it, BF16 sums included, so their shard
+//     order from +0 holds across groups.
 //
 // General kernel: one thread per (token, feature). It evaluates each term as
 // fl(q - z) * s, or the BF16 value, and adds the terms in shard order from
