@@ -4,7 +4,8 @@ receiver runs in shard groups), feature counts with and without 4- and
 tight (code bytes, multiple of 4) or padded pitches. Each shape runs the
 shared-set path and the per-shard path against the oracle, to the bars of
 the two parity suites they reuse, so whichever kernel each shape selects is
-checked. BTQ_RANDOM_SHAPES sets how many seeds run (24 by default)."""
+checked. BTQ_RANDOM_SHAPES sets how many seeds run (24 by default) and
+BTQ_RANDOM_T_MAX the largest token count (40 by default)."""
 import os
 import numpy as np
 import pytest
@@ -19,11 +20,14 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 
 
+T_MAX = int(os.environ.get("BTQ_RANDOM_T_MAX", "40"))
+
+
 def shape(seed):
     g = np.random.default_rng([20260, seed])
     P = int(g.integers(1, 17))
     H = int(g.choice([8, 4, 1])) * int(g.integers(2, 700))
-    T = int(g.integers(1, 41))
+    T = int(g.integers(1, T_MAX + 1))
     k = int(g.integers(0, H + 1)) if g.random() < 0.3 else int(g.integers(0, min(H, 80) + 1))
     code_bytes = (H - k + 1) // 2
     pick = g.random()
