@@ -162,13 +162,14 @@ __host__ __device__ constexpr int win_lds_dwords() {
          kWave + (kBf ? 0 : kWinTile);
 }
 
-// NP: shards (1..8). kOR: BF16 entry registers per row. kR: ring depth.
+// NP: shards (1..8). kOR: BF16 entry registers per row (0: k = 0, no BF16
+// entries to load). kR: ring depth.
 // kPs: fmap is [P,H] (one set per shard) instead of [H]. kBf: y is bf16.
 // Waves per SIMD the register budget aims at: 3 (at most 168 registers) for
 // one set with two entry registers, else 2 (at most 256).
 template <int NP, int kOR, int kR, bool kPs, bool kBf, bool kAcc>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu((!kPs && kOR == 2 && !kAcc) ? 3 : 2)))
+__attribute__((amdgpu_waves_per_eu((!kPs && kOR <= 2 && !kAcc) ? 3 : 2)))
 void dq_window_kernel(
     const uint8_t* __restrict__ packed, int pitch, const uint16_t* __restrict__ outl, int64_t T,
     int H, int k, int ntiles, int rows_per_wave, int64_t nrowblk, const float* __restrict__ scale,
@@ -282,8 +283,9 @@ void dq_window_kernel(
   for (int m = 0; m < NM; ++m)
     cl[m] = lane < kStageLanes ? 4u * abase[m] + 8u * (uint32_t)lane : kOOB;
   // BF16 entry e = off[p] + j of a row is index ilo[p] + j of shard p
-  uint32_t e_off[kOR];
-  int e_sp[kOR];   // the entry's shard
+  constexpr int kORA = kOR > 0 ? kOR : 1;   // array sizes (kOR = 0: no BF16 features)
+  uint32_t e_off[kORA];
+  int e_sp[kORA];   // the entry's shard
 #pragma unroll
   for (int r = 0; r < kOR; ++r) {
     const int e = r * kWave + lane;
@@ -321,7 +323,7 @@ void dq_window_kernel(
                                 kAcc ? (uint32_t)((int64_t)nrows * H * 4) : 0u);
   const uint32_t yin_off = active ? (uint32_t)h0 * 4u : kOOB;
   v2u w[kR][NP];
-  uint32_t ov[kR][kOR];
+  uint32_t ov[kR][kORA];
   float yp[kAcc ? kR : 1][kWinFeat];
   auto load_row = [&](int q, int row) {
     const bool ok = row < nrows;   // uniform
@@ -441,7 +443,7 @@ void dq_window_kernel(
   // zero the table rows of this tile (int4 shards of a BF16 feature stay 0)
   for (int i = lane; i < nb_any * NP && compact; i += kWave) tab[i] = 0.0f;
   wave_lds_sync();
-  uint32_t e_dst[kOR];   // entry: LDS dword (past the entries: the lane's dummy)
+  uint32_t e_dst[kORA];   // entry: LDS dword (past the entries: the lane's dummy)
 #pragma unroll
   for (int r = 0; r < kOR; ++r) {
     const int e = r * kWave + lane;
@@ -726,17 +728,23 @@ static void launch_window(const uint8_t* packed, int64_t pitch, const uint16_t* 
 }
 
 template <bool kPs, bool kBf, bool kAcc>
-static void dispatch_window(int64_t P, bool wide, const uint8_t* packed, int64_t pitch,
+static void dispatch_window(int64_t P, int kor, const uint8_t* packed, int64_t pitch,
                             const uint16_t* outl, int64_t T, int64_t H, int64_t k, int ntiles,
                             int rpw, int64_t nrowblk, const float* scale, const uint8_t* zp,
                             const int32_t* fmap, void* y, hipStream_t s) {
 #define BTQ_WIN_ARGS packed, pitch, outl, T, H, k, ntiles, rpw, nrowblk, scale, zp, fmap, y, s
 #define BTQ_WIN_CASE(n)                                                         \
   case n:                                                                       \
-    if (wide)                                                                   \
+    if (kor == 4) {                                                             \
       launch_window<n, 4, kDqRing, kPs, kBf, kAcc>(BTQ_WIN_ARGS);               \
-    else                                                                        \
+    } else if constexpr (kPs || kAcc) {                                         \
       launch_window<n, 2, kDqRing, kPs, kBf, kAcc>(BTQ_WIN_ARGS);               \
+    } else {                                                                    \
+      if (kor == 2)                                                             \
+        launch_window<n, 2, kDqRing, kPs, kBf, kAcc>(BTQ_WIN_ARGS);             \
+      else                                                                      \
+        launch_window<n, 0, kDqRing, kPs, kBf, kAcc>(BTQ_WIN_ARGS);             \
+    }                                                                           \
     break;
   switch (P) {
     BTQ_WIN_CASE(1)
@@ -779,16 +787,19 @@ static hipError_t launch_decompress_t(const uint8_t* packed, int64_t pitch, cons
   if (rpw64 > 64) rpw64 = 64;
   const int rpw = (int)rpw64;
   const int64_t nrowblk = (T + rpw - 1) / rpw;
+  // BF16 entry registers per row: none without BF16 features (one set); 2
+  // (128 entries per tile-row) while the tiles hold at most 64 on average;
+  // else 4
+  auto entry_regs = [&](int64_t np) {
+    return k == 0 ? 0 : (np * k > int64_t(kWave) * ntiles ? 4 : 2);
+  };
   // shards per launch: at most 8, and few enough that a group's message and
   // outlier block stay under 2^31 bytes
   int64_t gs = 8;
   while (gs > 0 && !group_ok(gs)) --gs;
   if (P <= gs && shape_ok) {
-    // BF16 entry registers: 2 (128 entries per tile-row) while the tiles hold
-    // at most 64 on average, else 4
-    const bool wide = P * k > int64_t(kWave) * ntiles;
-    dispatch_window<kPs, kBf, false>(P, wide, packed, pitch, outl, T, H, k, ntiles, rpw, nrowblk,
-                                     scale, zp, fmap, y, s);
+    dispatch_window<kPs, kBf, false>(P, entry_regs(P), packed, pitch, outl, T, H, k, ntiles, rpw,
+                                     nrowblk, scale, zp, fmap, y, s);
     return hipGetLastError();
   }
   if constexpr (!kPs && !kBf) {
@@ -800,14 +811,14 @@ static hipError_t launch_decompress_t(const uint8_t* packed, int64_t pitch, cons
     if (P > gs && gs >= 1 && shape_ok) {
       for (int64_t g0 = 0; g0 < P; g0 += gs) {
         const int64_t np = P - g0 < gs ? P - g0 : gs;
-        const bool wide = np * k > int64_t(kWave) * ntiles;
+        const int kor = entry_regs(np);
         const uint8_t* pk_g = packed + g0 * T * pitch;
         const uint16_t* ol_g = outl + g0 * T * k;
         if (g0 == 0)
-          dispatch_window<false, false, false>(np, wide, pk_g, pitch, ol_g, T, H, k, ntiles, rpw,
+          dispatch_window<false, false, false>(np, kor, pk_g, pitch, ol_g, T, H, k, ntiles, rpw,
                                                nrowblk, scale, zp, fmap, y, s);
         else
-          dispatch_window<false, false, true>(np, wide, pk_g, pitch, ol_g, T, H, k, ntiles, rpw,
+          dispatch_window<false, false, true>(np, kor, pk_g, pitch, ol_g, T, H, k, ntiles, rpw,
                                               nrowblk, scale + g0 * H, zp + g0 * H, fmap, y, s);
       }
       return hipGetLastError();

@@ -109,18 +109,19 @@ def test_no_kernel_spills_to_scratch(asm_paths):
 
 
 def test_receiver_register_budgets(asm_paths):
-    """The receiver's common form (one set, two entry registers, not a later
-    group of shards) fits 3 waves per SIMD (at most 168 registers); every
-    form fits 2 (at most 256, so no accumulator registers hold spills)."""
+    """The receiver's common forms (one set, two entry registers or none, not
+    a later group of shards) fit 3 waves per SIMD (at most 168 registers);
+    every form fits 2 (at most 256, so no accumulator registers hold
+    spills)."""
     res = kernel_resources(asm_paths)
     window = {k: r for k, r in res.items() if "dq_window_kernel" in k}
-    assert len(window) >= 80
+    assert len(window) >= 96
     for name, r in window.items():
         regs = r["next_free_vgpr"]
         assert regs <= 256, (name, regs)
         m = re.search(r"dq_window_kernelILi(\d)ELi(\d)ELi(\d)ELb(\d)ELb(\d)ELb(\d)E", name)
         assert m, name
-        if m.group(2) == "2" and m.group(4) == "0" and m.group(6) == "0":
+        if m.group(2) in ("0", "2") and m.group(4) == "0" and m.group(6) == "0":
             assert regs <= 168, (name, regs)
 
 
