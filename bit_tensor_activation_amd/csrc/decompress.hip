@@ -176,7 +176,7 @@ void dq_window_kernel(
     const uint8_t* __restrict__ zp, const int32_t* __restrict__ fmap, void* __restrict__ y) {
   constexpr int NM = kPs ? NP : 1;             // maps
   constexpr uint32_t kYB = kBf ? 2u : 4u;      // bytes per y value
-  static_assert(!kAcc || (!kPs && !kBf), "shard groups: one set, fp32 output");
+  static_assert(!kAcc || !kBf, "shard groups: fp32 output");
   constexpr int kLds = win_lds_dwords<NP, kOR, kPs, kBf>();
   constexpr int kSP = stage_stride(NP);
   extern __shared__ __align__(16) float dq_smem[];
@@ -368,6 +368,7 @@ void dq_window_kernel(
   uint32_t dwin[NM], selA[NM], selB[NM], mskA[NM], mskB[NM], bfm[NM];
   uint32_t i4A[NM], i4B[NM], hiA[NM], hiB[NM];   // per byte: int4 (1/0); high nibble (1/0)
   int bf1[NM];   // BF16 index of the lane's first BF16 feature (the others follow it)
+  uint32_t i4any = 0;   // features int4 on some map
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     uint32_t qm = 0, jf = 0xFFFFFFFFu, jb = 0u;
@@ -381,6 +382,7 @@ void dq_window_kernel(
       if (kPs) jb = max(jb, f);
     }
     qm = active ? qm : 0u;
+    i4any |= qm;
     bfm[m] = active ? (~qm & 0xFFu) : 0u;
     bf1[m] = -1 - (int)jb;
     // 8 bytes at cb hold every code of the window; kept inside the row
@@ -509,10 +511,18 @@ void dq_window_kernel(
   // The owner's BF16 sum into its feature eu: one set per shard adds it to
   // the int4 part; with one set it is the whole value (the int4 part is +0).
   // A select, so no other feature ever sees the sum.
+  // Features BF16 on every map (with one set: every BF16 feature). In a
+  // later group of shards their owner sum starts from the earlier groups' y
+  // and replaces the value, so a feature BF16 on every shard keeps its sum
+  // in shard order from +0 across groups; a feature with int4 terms in the
+  // group adds its BF16 sum to them.
+  const int allbf = kPs ? (any & ~(int)i4any) : any;
   auto place = [&](float (&acc)[kWinFeat], int eu, float o) {
 #pragma unroll
-    for (int e = 0; e < kWinFeat; ++e)
-      acc[e] = (e == eu) ? (kPs ? __fadd_rn(acc[e], o) : o) : acc[e];
+    for (int e = 0; e < kWinFeat; ++e) {
+      const bool repl = !kPs || (kAcc && ((allbf >> e) & 1));
+      acc[e] = (e == eu) ? (repl ? o : __fadd_rn(acc[e], o)) : acc[e];
+    }
   };
   const uint32_t st_off = active ? (uint32_t)h0 * kYB : kOOB;
   const uint32_t st_a = (f0 + 4 * lane < H) ? (uint32_t)(f0 + 4 * lane) * 4u : kOOB;
@@ -558,7 +568,7 @@ void dq_window_kernel(
       // (a later group of shards: from the earlier groups' sum)
       float o = 0.0f;
       if (do_own) {
-        if constexpr (kAcc) o = pick8(yp[q], e_first);
+        if constexpr (kAcc) o = ((allbf >> e_first) & 1) ? pick8(yp[q], e_first) : 0.0f;
         const float* t = tab + (cnt_any > 0 ? pos0 : 0) * NP;
         if constexpr (NP % 4 == 0) {
 #pragma unroll
@@ -606,7 +616,7 @@ void dq_window_kernel(
           const float* t = tab + (u < cnt_any ? pos0 + u : 0) * NP;
           const int eu = rest ? __builtin_ctz(rest) : kWinFeat;
           float ou = 0.0f;
-          if constexpr (kAcc) ou = pick8(yq, eu);
+          if constexpr (kAcc) ou = ((allbf >> eu) & 1) ? pick8(yq, eu) : 0.0f;
 #pragma unroll
           for (int p = 0; p < NP; ++p) ou = __fadd_rn(ou, t[p]);
           place(acc, eu, ou);
@@ -727,6 +737,11 @@ static void launch_window(const uint8_t* packed, int64_t pitch, const uint16_t* 
       packed, (int)pitch, outl, T, (int)H, (int)k, ntiles, rpw, nrowblk, scale, zp, fmap, y);
 }
 
+// Shards per group for per-shard sets: their kernels hold every shard's
+// selectors and scales in registers, and past 6 shards the earlier groups' y
+// no longer fits beside them.
+constexpr int kPsGroup = 6;
+
 template <bool kPs, bool kBf, bool kAcc>
 static void dispatch_window(int64_t P, int kor, const uint8_t* packed, int64_t pitch,
                             const uint16_t* outl, int64_t T, int64_t H, int64_t k, int ntiles,
@@ -735,7 +750,9 @@ static void dispatch_window(int64_t P, int kor, const uint8_t* packed, int64_t p
 #define BTQ_WIN_ARGS packed, pitch, outl, T, H, k, ntiles, rpw, nrowblk, scale, zp, fmap, y, s
 #define BTQ_WIN_CASE(n)                                                         \
   case n:                                                                       \
-    if (kor == 4) {                                                             \
+    if constexpr (kPs && kAcc && n > kPsGroup) {                                \
+      /* never launched: per-shard groups hold at most kPsGroup shards */       \
+    } else if (kor == 4) {                                                      \
       launch_window<n, 4, kDqRing, kPs, kBf, kAcc>(BTQ_WIN_ARGS);               \
     } else if constexpr (kPs || kAcc) {                                         \
       launch_window<n, 2, kDqRing, kPs, kBf, kAcc>(BTQ_WIN_ARGS);               \
@@ -802,24 +819,26 @@ static hipError_t launch_decompress_t(const uint8_t* packed, int64_t pitch, cons
                                      nrowblk, scale, zp, fmap, y, s);
     return hipGetLastError();
   }
-  if constexpr (!kPs && !kBf) {
+  if constexpr (!kBf) {
     // More shards than one launch takes (more than 8, or a message past 2^31
-    // bytes; one set, fp32 output): one launch per group of gs shards, in
-    // shard order. The first writes y; each later one starts every feature
-    // from y, so BF16 features keep their sum in shard order from +0 across
-    // the groups.
-    if (P > gs && gs >= 1 && shape_ok) {
-      for (int64_t g0 = 0; g0 < P; g0 += gs) {
-        const int64_t np = P - g0 < gs ? P - g0 : gs;
-        const int kor = entry_regs(np);
+    // bytes; fp32 output): one launch per group of shards, in shard order
+    // (gs shards, or at most kPsGroup with per-shard sets). The first writes
+    // y; each later one starts every feature from y, so a feature BF16 on
+    // every shard keeps its sum in shard order from +0 across the groups.
+    const int64_t gg = kPs ? (gs < kPsGroup ? gs : kPsGroup) : gs;
+    if (P > gs && gg >= 1 && shape_ok) {
+      for (int64_t g0 = 0; g0 < P; g0 += gg) {
+        const int64_t np = P - g0 < gg ? P - g0 : gg;
+        const int kor = kPs ? (np * k > int64_t(kWave) * ntiles ? 4 : 2) : entry_regs(np);
         const uint8_t* pk_g = packed + g0 * T * pitch;
         const uint16_t* ol_g = outl + g0 * T * k;
+        const int32_t* fm_g = kPs ? fmap + g0 * H : fmap;
         if (g0 == 0)
-          dispatch_window<false, false, false>(np, kor, pk_g, pitch, ol_g, T, H, k, ntiles, rpw,
-                                               nrowblk, scale, zp, fmap, y, s);
+          dispatch_window<kPs, false, false>(np, kor, pk_g, pitch, ol_g, T, H, k, ntiles, rpw,
+                                             nrowblk, scale, zp, fm_g, y, s);
         else
-          dispatch_window<false, false, true>(np, kor, pk_g, pitch, ol_g, T, H, k, ntiles, rpw,
-                                              nrowblk, scale + g0 * H, zp + g0 * H, fmap, y, s);
+          dispatch_window<kPs, false, true>(np, kor, pk_g, pitch, ol_g, T, H, k, ntiles, rpw,
+                                            nrowblk, scale + g0 * H, zp + g0 * H, fm_g, y, s);
       }
       return hipGetLastError();
     }

@@ -301,7 +301,9 @@ int btq_select_features(const float *run_min, const float *run_max,
  * btq_decompress_reduce_per_shard: btq_decompress_reduce with fmap [P,H]:
  *   term_p follows shard p's map. Features BF16 on every shard are summed in
  *   shard order from +0, exactly; the others are within the receiver's
- *   tolerance of the sequential sum.
+ *   tolerance of the sequential sum. Past 8 shards (or a message past 2^31
+ *   bytes) the fast kernel runs once per group of up to 6 shards, each
+ *   later group adding to y as in btq_decompress_reduce.
  */
 int btq_select_outliers_per_shard(const float *run_min, const float *run_max,
                                   int64_t P, int64_t H, int64_t k,
