@@ -73,6 +73,56 @@ __device__ __forceinline__ uint32_t quant4(uint32_t bits16, float r, float z) {
   return (uint32_t)q;
 }
 
+// A lane's 8 codes, quant4 of each feature, packed into one dword with
+// fewer instructions: the rounding, the zero point and the conversion to an
+// integer all stay in the float domain. With M = 1.5 * 2^23, fl(v + M) is
+// M + rint(v), rounded half to even, whenever |v| < 2^22; every other v
+// lands outside [M - z, M + 15 - z], on the side its sign gives. Clamping
+// fl(v + M) to those bounds therefore equals M - z + clamp(rint(v) + z, 0,
+// 15), and its bit pattern is 0x4B400000 + (q - z), an integer. Adding each
+// feature's pattern, shifted to its nibble, to the constant
+// -sum_e (0x4B400000 - z_e) << 4e leaves exactly the packed codes (mod
+// 2^32, with no carries between nibbles in the result).
+constexpr float kQMagic = 12582912.0f;   // 1.5 * 2^23, bits 0x4B400000
+struct Quant8 {
+  float lo[8], hi[8];   // M - z, M + 15 - z
+  uint32_t k;           // -sum_e (0x4B400000 - z_e) << 4e
+
+  __device__ __forceinline__ void init(const float zf[8]) {
+    k = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      lo[e] = kQMagic - zf[e];
+      hi[e] = kQMagic + (15.0f - zf[e]);
+      k -= (0x4B400000u - (uint32_t)zf[e]) << (4 * e);
+    }
+  }
+  __device__ __forceinline__ void settle_all() {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      settle(lo[e]);
+      settle(hi[e]);
+    }
+    settle(k);
+  }
+  __device__ __forceinline__ uint32_t pack(const uint32_t (&u)[8], const float (&rs)[8]) const {
+    uint32_t w = k;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = __fmul_rn(bf16_to_f32(u[e]), rs[e]);
+      const float c = __builtin_amdgcn_fmed3f(__fadd_rn(v, kQMagic), lo[e], hi[e]);
+      const uint32_t b = __float_as_uint(c);
+      // one shift-and-add per feature (left to itself the compiler spends
+      // three instructions on every two)
+      if (e == 0)
+        w += b;
+      else
+        asm("v_lshl_add_u32 %0, %1, %2, %0" : "+v"(w) : "v"(b), "n"(4 * e));
+    }
+    return w;
+  }
+};
+
 // Per-feature parameters of one shard over a tile's feature span
 // [a0, a0 + 8*nch): rscale as 16-byte chunks of 4 floats, zero points as
 // 8-byte chunks of 8 bytes. kR, kZ: chunks per lane that cover the widest
@@ -204,6 +254,8 @@ __global__ __launch_bounds__(256) void compress_kernel(
                      (int)hB[0], (int)hB[1], (int)hB[2], (int)hB[3]};
   float rs[8], zf[8];
   sp.pick(buf, nch, lane, a0, hh, rs, zf);   // (kCpRows*buf_bytes >= 40*nch)
+  Quant8 qz;
+  qz.init(zf);
   uint32_t ad[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) ad[e] = pad_byte_off((uint32_t)(hh[e] - a0));
@@ -244,9 +296,7 @@ __global__ __launch_bounds__(256) void compress_kernel(
     for (int r = 0; r < kCpRows; ++r) {
       const int row = s + r;
       if (row >= nrows) break;
-      uint32_t w = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w |= quant4(u[r][e], rs[e], zf[e]) << (4 * e);
+      uint32_t w = qz.pack(u[r], rs);
       w = active ? w : 0u;   // past the last slot: the row's zero padding
       __builtin_amdgcn_raw_buffer_store_b32(w, rp, st_off, (uint32_t)row * (uint32_t)pitch, kStream);
     }
@@ -408,13 +458,15 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
   // (kSub*buf_bytes = 40*kNchMax bytes: it holds any span's parameters)
   float rs[8], zf[8];
   sp.pick(buf, nch, lane, a0, hh, rs, zf);
+  Quant8 qz;
+  qz.init(zf);
   uint32_t ad[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     ad[e] = pad_byte_off((uint32_t)(hh[e] - a0));
     settle(rs[e]);
-    settle(zf[e]);
   }
+  qz.settle_all();
   // (lanes past the last slot write the row's zero padding, up to the pitch)
   const uint32_t st_off = ((j0 >> 1) + 4 <= pitch) ? (uint32_t)(j0 >> 1) : kOOB;
   // BF16 copy, per pair of rows: lane l takes feature (l & 31) of the tile's
@@ -474,9 +526,7 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
         const int row = base + sb * kSub + r;
         const bool ok = row < nrows;   // uniform
         const uint32_t rr = (uint32_t)min(row, nrows - 1);
-        uint32_t w = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w |= quant4(u[r][e], rs[e], zf[e]) << (4 * e);
+        uint32_t w = qz.pack(u[r], rs);
         w = active ? w : 0u;   // past the last slot: the row's zero padding
         __builtin_amdgcn_raw_buffer_store_b32(w, rp, ok ? st_off : kOOB, rr * (uint32_t)pitch,
                                               kStream);
