@@ -94,6 +94,30 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) { return (uint16_t)(bf16_p
 // second operand).
 __device__ __forceinline__ uint32_t splat_byte0(uint32_t v) { return __builtin_amdgcn_perm(0u, v, 0u); }
 
+// fma(c, s, acc) with the code c given as an f16 denormal, c * 2^-24, in
+// the low (fma_h0) or high (fma_h1) half of h, and s already multiplied by
+// 2^24: the product is exactly c times the true scale, and the sum is
+// rounded once, so the result is bit for bit that of fmaf((float)c, scale,
+// acc). One instruction per term (v_fma_mix_f32) in place of a byte
+// conversion and an fma; the compiler does not form it by itself.
+__device__ __forceinline__ float fma_h0(uint32_t h, float s24, float acc) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h), "v"(s24), "v"(acc));
+  return d;
+}
+__device__ __forceinline__ float fma_h1(uint32_t h, float s24, float acc) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "=v"(d)
+      : "v"(h), "v"(s24), "v"(acc));
+  return d;
+}
+constexpr float kTwo24 = 16777216.0f;
+// v_perm selectors that spread bytes 0, 1 (or 2, 3) of a dword to the low
+// bytes of its two 16-bit halves, with zero high bytes
+constexpr uint32_t kSpread01 = 0x0C010C00u;
+constexpr uint32_t kSpread23 = 0x0C030C02u;
+
 // v[eu] (0 when eu is past the end), by selects.
 template <int N>
 __device__ __forceinline__ float pick8(const float (&v)[N], int eu) {
@@ -469,8 +493,16 @@ void dq_window_kernel(
   // scale 0: with one set its products, even non-finite ones, stay in the
   // feature's own accumulator, which its BF16 sum replaces; per-shard sets
   // select scale 0 so that such a shard adds exactly 0 to the int4 part.
+  // One set: the scales are held multiplied by 2^24 (fma_h0/fma_h1). A
+  // scale of 2^104 or more would overflow there: a wave with such a lane
+  // (`huge`, never in practice) recomputes all its outputs term by term
+  // after the row loop. Per-shard sets, whose kernels have no registers to
+  // spare, convert each code and use fmaf.
+  constexpr bool kMix = !kPs;
+  constexpr float kMs = kMix ? kTwo24 : 1.0f;
   float sc[NP][kWinFeat], bias[kWinFeat];
-  float mh[NM][kWinFeat];   // 1 (low nibble), 1/16 (high nibble), 0 (BF16 on the map)
+  // the scale's factor: kMs (low nibble), kMs/16 (high nibble), 0 (BF16 on the map)
+  float mh[NM][kWinFeat];
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
 #pragma unroll
@@ -478,11 +510,12 @@ void dq_window_kernel(
       const int sh = 8 * (e & 3);
       const float is4 = (float)(((e < 4 ? i4A[m] : i4B[m]) >> sh) & 0xFFu);
       const float ishi = (float)(((e < 4 ? hiA[m] : hiB[m]) >> sh) & 0xFFu);
-      mh[m][e] = fmaf(-0.9375f, ishi, is4);   // exact
+      mh[m][e] = fmaf(-0.9375f, ishi, is4) * kMs;   // exact
     }
   }
 #pragma unroll
   for (int e = 0; e < kWinFeat; ++e) bias[e] = 0.0f;
+  bool over = false;
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int m = kPs ? p : 0;
@@ -496,11 +529,16 @@ void dq_window_kernel(
       const bool q4 = mh[m][e] != 0.0f;
       bias[e] = (kPs && !q4) ? bias[e] : b;
       sc[p][e] = kPs ? (q4 ? s * mh[m][e] : 0.0f) : s * mh[m][e];
+      if (kMix) over |= sc[p][e] > 3.0e38f;   // +inf: the scale times 2^24 overflowed
       settle(sc[p][e]);
     }
   }
 #pragma unroll
   for (int e = 0; e < kWinFeat; ++e) settle(bias[e]);
+  const bool huge = __ballot(over) != 0ull;   // uniform
+  // features the post-loop pass recomputes: every active one when huge,
+  // else the BF16 ones of a tile past its entry registers
+  const int redo = huge ? (active ? 0xFF : 0) : (compact ? 0 : any);
   // y stores. bf16: the lane's 8 values are 16 contiguous bytes, so one
   // store covers the wave's 1 KB. fp32: the lane's 32 bytes go through the
   // wave's LDS row (values 0-3 of every lane in the first half, 4-7 in the
@@ -590,14 +628,30 @@ void dq_window_kernel(
         const int m = kPs ? p : 0;
         uint32_t a = __builtin_amdgcn_perm(x[p][1], x[p][0], selA[m]) & mskA[m];
         uint32_t b = __builtin_amdgcn_perm(x[p][1], x[p][0], selB[m]) & mskB[m];
-        // kept whole: each byte converts with one v_cvt_f32_ubyteN
-        opaque(a);
-        opaque(b);
+        if constexpr (!kMix) {
+          // kept whole: each byte converts with one v_cvt_f32_ubyteN
+          opaque(a);
+          opaque(b);
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          acc[bb] = fmaf((float)((a >> (8 * bb)) & 0xFFu), sc[p][bb], acc[bb]);
-          acc[4 + bb] = fmaf((float)((b >> (8 * bb)) & 0xFFu), sc[p][4 + bb], acc[4 + bb]);
+          for (int bb = 0; bb < 4; ++bb) {
+            acc[bb] = fmaf((float)((a >> (8 * bb)) & 0xFFu), sc[p][bb], acc[bb]);
+            acc[4 + bb] = fmaf((float)((b >> (8 * bb)) & 0xFFu), sc[p][4 + bb], acc[4 + bb]);
+          }
+          continue;
         }
+        // one code byte per 16-bit half: f16 denormals
+        const uint32_t a01 = __builtin_amdgcn_perm(0u, a, kSpread01);
+        const uint32_t a23 = __builtin_amdgcn_perm(0u, a, kSpread23);
+        const uint32_t b01 = __builtin_amdgcn_perm(0u, b, kSpread01);
+        const uint32_t b23 = __builtin_amdgcn_perm(0u, b, kSpread23);
+        acc[0] = fma_h0(a01, sc[p][0], acc[0]);
+        acc[1] = fma_h1(a01, sc[p][1], acc[1]);
+        acc[2] = fma_h0(a23, sc[p][2], acc[2]);
+        acc[3] = fma_h1(a23, sc[p][3], acc[3]);
+        acc[4] = fma_h0(b01, sc[p][4], acc[4]);
+        acc[5] = fma_h1(b01, sc[p][5], acc[5]);
+        acc[6] = fma_h0(b23, sc[p][6], acc[6]);
+        acc[7] = fma_h1(b23, sc[p][7], acc[7]);
       }
       // (kAcc: the owners' later features still need this row's y after the
       // refill below reloads its slot)
@@ -624,11 +678,11 @@ void dq_window_kernel(
         }
       }
       if constexpr (kAcc) {
-        // the post-loop pass continues these BF16 features from what the
-        // earlier groups summed, so the loop stores that unchanged
-        if (!compact) {
+        // the post-loop pass continues these features from what the earlier
+        // groups summed, so the loop stores that unchanged
+        if (redo) {
 #pragma unroll
-          for (int e = 0; e < kWinFeat; ++e) acc[e] = ((any >> e) & 1) ? yq[e] : acc[e];
+          for (int e = 0; e < kWinFeat; ++e) acc[e] = ((redo >> e) & 1) ? yq[e] : acc[e];
         }
       }
       // (a row past the wave's last: no records, every store dropped)
@@ -659,14 +713,15 @@ void dq_window_kernel(
     base += kR;
   } while (base < nrows);
 
-  if (!compact) {   // uniform
+  if (!compact || huge) {   // uniform
     // More BF16 entries than the registers hold: the loop stored only the
-    // int4 part of these features. Once those stores are complete, each
-    // owner recomputes its BF16 features term by term (fl(q - z) * s or the
-    // BF16 value, in shard order from +0) and stores the sums. The maps and
-    // parameters are read again here, so the loop does not keep them live.
+    // int4 part of these features (or, when huge, nothing valid). Once those
+    // stores are complete, each owner recomputes these features term by
+    // term (fl(q - z) * s or the BF16 value, in shard order from +0) and
+    // stores the sums. The maps and parameters are read again here, so the
+    // loop does not keep them live.
     __builtin_amdgcn_s_waitcnt(0);
-    int rest = any;
+    int rest = redo;
     while (rest) {
       const int e = __builtin_ctz(rest);
       rest &= rest - 1;

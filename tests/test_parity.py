@@ -358,6 +358,28 @@ def test_bf16_sum_overflow_stays_in_its_feature():
     assert torch.equal(y16, y.to(torch.bfloat16).view(torch.int16))
 
 
+@pytest.mark.parametrize("P", [8, 12])
+def test_scales_past_2_to_104(P):
+    """int4 features whose scale is 2^104 or more (values near 1e33): the
+    receiver's fast arithmetic holds scales times 2^24, which would overflow,
+    so such waves recompute their outputs term by term. Every output, those
+    features' and their tiles' others, stays within the tolerance (P=12 also
+    runs a later group of shards that adds to y)."""
+    T, H = 40, 2048
+    feats = np.array([5, 300, 301, 1030, 2047])
+    huge = [700, 701, 1500]
+    say(f"case: scales past 2^104, P={P}")
+
+    def drawn(seed):
+        xb = W.draw(P, T, H, seed, device=DEV).view(torch.bfloat16).clone()
+        xb[:, :, huge] = xb[:, :, huge] * 1.0e33
+        return xb.view(torch.int16)
+
+    calib = [drawn(5400 + b) for b in range(2)]
+    sel, *_ = run_both(calib, drawn(5500), len(feats), 0.9, features=feats)
+    assert (sel["scale"][:, huge] >= 2.0 ** 104).all()
+
+
 def test_momentum_range():
     say("case: momentum 0 and the largest fp32 below 1; 1 is rejected")
     P, T, H = 2, 8, 64
