@@ -84,33 +84,57 @@ __device__ __forceinline__ uint32_t quant4(uint32_t bits16, float r, float z) {
 // -sum_e (0x4B400000 - z_e) << 4e leaves exactly the packed codes (mod
 // 2^32, with no carries between nibbles in the result).
 constexpr float kQMagic = 12582912.0f;   // 1.5 * 2^23, bits 0x4B400000
+// kLean: the zero point is added by a second float add, fl(fl(v + M) + z),
+// and the sum clamped to the constant bounds [M, M + 15]. For |v| < 2^22 the
+// add is exact (the sum stays below 2^24); a larger v stays past its bound
+// (v >= 2^22 gives at least M + 2^22, v <= -2^22 at most 2^23 + 15 < M). The
+// pattern is then 0x4B400000 + q and the constant -sum_e 0x4B400000 << 4e.
+// One more instruction per feature and 9 fewer registers: the widest-span
+// ring kernel keeps 4 waves per SIMD with it.
+template <bool kLean>
 struct Quant8 {
-  float lo[8], hi[8];   // M - z, M + 15 - z
-  uint32_t k;           // -sum_e (0x4B400000 - z_e) << 4e
+  float lo[kLean ? 1 : 8], hi[kLean ? 1 : 8];   // M - z, M + 15 - z
+  float zf[kLean ? 8 : 1];                      // z
+  uint32_t k;   // -sum_e (0x4B400000 - z_e) << 4e  (kLean: -sum_e 0x4B400000 << 4e)
 
-  __device__ __forceinline__ void init(const float zf[8]) {
+  __device__ __forceinline__ void init(const float (&z)[8]) {
     k = 0u;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      lo[e] = kQMagic - zf[e];
-      hi[e] = kQMagic + (15.0f - zf[e]);
-      k -= (0x4B400000u - (uint32_t)zf[e]) << (4 * e);
+      if constexpr (kLean) {
+        zf[e] = z[e];
+        k -= 0x4B400000u << (4 * e);
+      } else {
+        lo[e] = kQMagic - z[e];
+        hi[e] = kQMagic + (15.0f - z[e]);
+        k -= (0x4B400000u - (uint32_t)z[e]) << (4 * e);
+      }
     }
   }
   __device__ __forceinline__ void settle_all() {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      settle(lo[e]);
-      settle(hi[e]);
+      if constexpr (kLean) {
+        settle(zf[e]);
+      } else {
+        settle(lo[e]);
+        settle(hi[e]);
+      }
     }
     settle(k);
   }
+  // u: the 8 features' bf16 bits
   __device__ __forceinline__ uint32_t pack(const uint32_t (&u)[8], const float (&rs)[8]) const {
     uint32_t w = k;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float v = __fmul_rn(bf16_to_f32(u[e]), rs[e]);
-      const float c = __builtin_amdgcn_fmed3f(__fadd_rn(v, kQMagic), lo[e], hi[e]);
+      float c;
+      if constexpr (kLean)
+        c = __builtin_amdgcn_fmed3f(__fadd_rn(__fadd_rn(v, kQMagic), zf[e]), kQMagic,
+                                    kQMagic + 15.0f);
+      else
+        c = __builtin_amdgcn_fmed3f(__fadd_rn(v, kQMagic), lo[e], hi[e]);
       const uint32_t b = __float_as_uint(c);
       // one shift-and-add per feature (left to itself the compiler spends
       // three instructions on every two)
@@ -254,7 +278,7 @@ __global__ __launch_bounds__(256) void compress_kernel(
                      (int)hB[0], (int)hB[1], (int)hB[2], (int)hB[3]};
   float rs[8], zf[8];
   sp.pick(buf, nch, lane, a0, hh, rs, zf);   // (kCpRows*buf_bytes >= 40*nch)
-  Quant8 qz;
+  Quant8<false> qz;
   qz.init(zf);
   uint32_t ad[8];
 #pragma unroll
@@ -458,7 +482,7 @@ __global__ __launch_bounds__(256) void compress_ring_kernel(
   // (kSub*buf_bytes = 40*kNchMax bytes: it holds any span's parameters)
   float rs[8], zf[8];
   sp.pick(buf, nch, lane, a0, hh, rs, zf);
-  Quant8 qz;
+  Quant8<(kRemDw > 2)> qz;
   qz.init(zf);
   uint32_t ad[8];
 #pragma unroll

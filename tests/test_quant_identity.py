@@ -5,7 +5,8 @@ float-to-integer conversion: it clamps fl(fl(x*r) + M), M = 1.5 * 2^23, to
 [M - z, M + 15 - z] and takes the clamped float's bit pattern, which is
 0x4B400000 + (q - z). The packed dword is then the sum of the patterns
 shifted to their nibbles plus the constant -sum_e (0x4B400000 - z_e) << 4e,
-mod 2^32. This test restates both forms in float32 numpy and compares them
+mod 2^32. The widest-span kernel uses a form with fewer registers: it adds
+z as a second float add and clamps fl(fl(v + M) + z) to [M, M + 15]. This test restates both forms in float32 numpy and compares them
 over every finite bf16 pattern with a spread of scales and every zero
 point, plus random products near rounding ties. The GPU parity tests check
 the kernel itself.
@@ -26,6 +27,13 @@ def magic_bits(v, z):
     return c.view(np.uint32)
 
 
+def lean_bits(v, z):
+    """The form with fewer registers: fl(fl(v + M) + z) clamped to [M, M + 15]."""
+    s = ((v + M).astype(F32) + z).astype(F32)
+    c = np.minimum(np.maximum(s, M), M + F32(15)).astype(F32)
+    return c.view(np.uint32)
+
+
 def test_every_bf16_pattern():
     b = np.arange(65536, dtype=np.uint32)
     b = b[((b >> 7) & 0xFF) != 0xFF]   # finite patterns
@@ -39,6 +47,8 @@ def test_every_bf16_pattern():
             # one feature in nibble 0: the pattern minus (0x4B400000 - z)
             got = (bits - (np.uint32(0x4B400000) - np.uint32(z))).astype(np.uint32)
             assert np.array_equal(got, q), (r, z)
+            lean = (lean_bits(v, zf) - np.uint32(0x4B400000)).astype(np.uint32)
+            assert np.array_equal(lean, q), (r, z, "lean")
 
 
 def test_packed_sum_and_ties():
@@ -60,3 +70,9 @@ def test_packed_sum_and_ties():
         w += magic_bits(v[:, e], z[:, e]).astype(np.uint64) << np.uint64(4 * e)
     got = (w + k) & np.uint64(0xFFFFFFFF)
     assert np.array_equal(got, want)
+    kl = np.uint64(0)
+    wl = np.zeros(n, dtype=np.uint64)
+    for e in range(8):
+        kl -= np.uint64(0x4B400000) << np.uint64(4 * e)
+        wl += lean_bits(v[:, e], z[:, e]).astype(np.uint64) << np.uint64(4 * e)
+    assert np.array_equal((wl + kl) & np.uint64(0xFFFFFFFF), want)
