@@ -201,6 +201,8 @@ int btq_compress_pack(const uint16_t *x, int64_t P, int64_t T, int64_t H, int64_
  * sequential fp32 sum bit for bit. int4 features are evaluated as
  * fma(q_p, scale, acc) from the constant -sum_p zero_point*scale, which
  * stays within 1e-3*|y| + 1e-2*max_p scale[p,h] of the sequential sum.
+ * (The 512 features of a block that holds a scale of 2^104 or more are
+ * computed as the sequential sum itself.)
  *   packed [P,T,Bq], outliers [P,T,k]   in, as written by btq_compress_pack
  *   scale fp32 [P,H], zero_point u8 [P,H], fmap i32 [H]   in
  *   y      fp32 [T,H]   out
