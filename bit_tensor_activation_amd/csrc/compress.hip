@@ -31,8 +31,8 @@
 //     and 32-63 for the second. kSub = 2 rows at a time are staged in a
 //     wave-private LDS buffer and their slots refilled kRing rows ahead.
 //  2. Each lane gathers its 8 features from LDS at fixed offsets, quantizes
-//     them, packs 8 nibbles into one dword and stores it: one coalesced
-//     256-byte store per wave and row.
+//     them in the float domain (Quant8), packs 8 nibbles into one dword and
+//     stores it: one coalesced 256-byte store per wave and row.
 //  3. The tile's BF16 features are copied out of the same LDS buffer, one
 //     store per pair of rows (lanes 0-31 the first row's first 32 features,
 //     32-63 the second's); features past the 32nd, rare, row by row.

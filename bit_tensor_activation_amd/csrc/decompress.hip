@@ -31,7 +31,9 @@
 //     is requested once; the span goes through the wave's LDS stage, where
 //     each lane reads its 8-byte window. (Loading the overlapping windows
 //     straight from memory requests most bytes twice, and measured about
-//     15% slower.) Each term is one byte-to-float conversion and one fma.
+//     15% slower.) Each term is one v_fma_mix_f32: the code as an f16
+//     denormal times the scale held multiplied by 2^24 (per-shard sets: a
+//     byte-to-float conversion and an fma), bit for bit the same result.
 //  2. BF16 values: the tile's entries of every shard (a contiguous run of
 //     each shard's outlier block) ride in kOR registers across the wave,
 //     loaded coalesced. They are written to a per-wave LDS table with one
