@@ -531,7 +531,8 @@ void dq_window_kernel(
       const bool q4 = mh[m][e] != 0.0f;
       bias[e] = (kPs && !q4) ? bias[e] : b;
       sc[p][e] = kPs ? (q4 ? s * mh[m][e] : 0.0f) : s * mh[m][e];
-      if (kMix) over |= sc[p][e] > 3.0e38f;   // +inf: the scale times 2^24 overflowed
+      // (+-inf: the scale times 2^24 overflowed; a NaN scale too)
+      if (kMix) over |= !(fabsf(sc[p][e]) <= 3.0e38f);
       settle(sc[p][e]);
     }
   }
